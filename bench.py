@@ -1,0 +1,209 @@
+"""Throughput of the dual-codebook quantization loop on one MI355X.
+
+A step is one pass of the whole path over one synthetic decoder layer whose inputs are resident
+in HBM: importance of every activation stream, quantile init of every matrix, `iters` x (batched
+assign, batched refine) with bf16 tables on the last refine, the final assign, pack and dequant.
+
+Metric (value): bf16 weight bytes quantized per second per assign+refine iteration,
+2 * numel * iters / t_loop, with t_loop the HIP-event time of the loop region of a step.
+roofline: the dominant of the two loop kernels (assign, refine); achieved = its algorithmic bytes
+per launch / its mean launch duration (HIP events on the launch stream).
+cpu_baseline: the fp64 oracle, assign + refine on a sample matrix, timed on the host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(numel, S):
+    """Bytes one assign or one refine launch must move per weight: read W (2), write or read the
+    4-bit codes (0.5) and the selectors (1/S)."""
+    return numel * (2.0 + 0.5 + 1.0 / S)
+
+
+def cpu_baseline(W, I, g, S, n, budget_s=15.0):
+    """Oracle assign+refine iterations on one matrix (host copy), until about budget_s seconds."""
+    import numpy as np
+
+    from oracle import aaac_ref as ref
+
+    W64 = W.float().cpu().numpy().astype(np.float64)
+    I64 = I.cpu().numpy().astype(np.float64)
+    T0, T1 = ref.init_tables(W64, g, n)
+    its = 0
+    t0 = time.perf_counter()
+    while True:
+        a = ref.assign(W64, I64, T0, T1, g, S)
+        T0, T1 = ref.refine(W64, I64, a["codes"], a["sel"], T0, T1, g, S)
+        its += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or its >= 50:
+            break
+    return {"value": round(2.0 * W64.size * its / el / 1e9, 6), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": "%d oracle assign+refine iterations (fp64 NumPy, one thread) on the "
+                      "%dx%d matrix of the layer, %.1f s" % (its, W64.shape[0], W64.shape[1], el)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import post_weight_quantization_06_amd as pkg
+    from synth import layers as syn
+
+    L = pkg._lib
+    L.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = syn.config(args.config)
+    if cfg.layers != 1:
+        raise SystemExit("bench.py times one resident layer; config %d streams %d layers"
+                         % (args.config, cfg.layers))
+    g, S, n, iters = cfg.g, cfg.S, cfg.n, cfg.iters
+    mats = cfg.matrices
+    print("[bench] generating %s" % cfg.name, file=sys.stderr, flush=True)
+    Ws = [syn.make_weight(m.rows, m.cols, syn.seed_for(cfg.cfg_id, 0, m.tensor_id), dev)
+          for m in mats]
+    streams = cfg.x_streams()
+    Xs = {xid: syn.make_activations(cfg.tokens, K, syn.seed_for(cfg.cfg_id, 0, xid), dev)
+          for xid, K in streams}
+    torch.cuda.synchronize()
+    numel = sum(m.numel for m in mats)
+    Rs = [m.rows for m in mats]
+    Cs = [m.cols for m in mats]
+
+    # buffers and workspaces (allocated once)
+    acc = {xid: torch.zeros(K, dtype=torch.float64, device=dev) for xid, K in streams}
+    Iv = {xid: torch.empty(K, dtype=torch.float32, device=dev) for xid, K in streams}
+    ws_imp = {xid: L.workspace(L.workspace_bytes(L.OP_IMPORTANCE, cfg.tokens, K), dev)
+              for xid, K in streams}
+    ws_init = L.workspace(max(L.workspace_bytes(L.OP_INIT, R, C, g, S, n)
+                              for R, C in zip(Rs, Cs)), dev)
+    ws_a = L.workspace(L.batch_workspace_bytes(L.OP_ASSIGN, Rs, Cs, g, S, n), dev)
+    ws_r = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), dev)
+    Is = [Iv[m.x_id] for m in mats]
+    tabs = [torch.empty(2 * n, dtype=torch.float32, device=dev) for _ in mats]
+    codes = [torch.empty(m.numel // 2, dtype=torch.uint8, device=dev) for m in mats]
+    sels = [torch.empty(m.numel // S, dtype=torch.uint8, device=dev) for m in mats]
+    scales = [torch.empty(m.numel // g, dtype=torch.int16, device=dev) for m in mats]
+    bitmaps = [torch.empty((m.numel // S + 7) // 8, dtype=torch.uint8, device=dev)
+               if S < g else None for m in mats]
+    tb16 = [torch.empty(2 * n, dtype=torch.int16, device=dev) for _ in mats]
+    W_hat = [torch.empty_like(W) for W in Ws]
+    stream = torch.cuda.current_stream()
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(record):
+        marks = {"a": [], "r": []}
+        for xid, K in streams:
+            acc[xid].zero_()
+            L.aaac_importance(Xs[xid], acc[xid], Iv[xid], ws_imp[xid])
+        for i, W in enumerate(Ws):
+            L.aaac_init_quantiles(W, g, n, tabs[i], ws_init)
+        loop0 = ev()
+        for it in range(iters):
+            flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
+            e0 = ev()
+            L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels, ws_a)
+            e1 = ev()
+            L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, tabs, flags, ws_r)
+            e2 = ev()
+            marks["a"].append((e0, e1))
+            marks["r"].append((e1, e2))
+        loop1 = ev()
+        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels, ws_a)
+        for i, W in enumerate(Ws):
+            L.aaac_pack(W, g, S, n, sels[i], tabs[i], scales[i], bitmaps[i], tb16[i])
+            L.aaac_dequant(codes[i], scales[i], bitmaps[i], tb16[i], Rs[i], Cs[i], g, S, n,
+                           W_hat[i])
+        return loop0, loop1, marks
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    print("[bench] warmup done", file=sys.stderr, flush=True)
+    t_start = time.perf_counter()
+    s0 = ev()
+    recs = [step(True) for _ in range(args.steps)]
+    s1 = ev()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    step_ms = s0.elapsed_time(s1) / args.steps
+    loop_ms = sum(a.elapsed_time(b) for a, b, _ in recs) / args.steps
+    a_ms = [x.elapsed_time(y) for _, _, m in recs for x, y in m["a"]]
+    r_ms = [x.elapsed_time(y) for _, _, m in recs for x, y in m["r"]]
+    a_avg = sum(a_ms) / len(a_ms)
+    r_avg = sum(r_ms) / len(r_ms)
+    bytes_launch = algorithmic_bytes(numel, S)
+    dom, dom_ms = ("assign", a_avg) if a_avg >= r_avg else ("refine", r_avg)
+    achieved = bytes_launch / (dom_ms * 1e-3) / 1e9
+    value = 2.0 * numel * iters / (loop_ms * 1e-3) / 1e9
+    print("[bench] step %.3f ms, loop %.3f ms, assign %.1f us (%.0f GB/s), refine %.1f us "
+          "(%.0f GB/s), wall %.2f s" % (step_ms, loop_ms, a_avg * 1e3,
+                                        bytes_launch / a_avg / 1e6, r_avg * 1e3,
+                                        bytes_launch / r_avg / 1e6, wall),
+          file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu:
+        k = min(range(len(mats)), key=lambda i: mats[i].numel)
+        print("[bench] cpu baseline on %s" % mats[k].name, file=sys.stderr, flush=True)
+        cpu = cpu_baseline(Ws[k], Is[k], g, S, n, args.cpu_budget)
+    out = {
+        "metric": "bf16 weights quantized/sec per assign+refine iter (GB/s) and % of HBM peak",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "matrices": [[m.rows, m.cols] for m in mats],
+                   "numel": numel, "g": g, "S": S, "n": n, "iters": iters,
+                   "calib_tokens": cfg.tokens},
+        "loop_ms_per_step": round(loop_ms, 4),
+        "assign_us": round(a_avg * 1e3, 2),
+        "refine_us": round(r_avg * 1e3, 2),
+        "hbm_frac_assign": round(bytes_launch / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "hbm_frac_refine": round(bytes_launch / (r_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

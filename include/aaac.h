@@ -1,0 +1,185 @@
+/*
+ * aaac.h -- C ABI of the MI355X (gfx950) activation-aware dual-codebook 4-bit weight quantizer.
+ *
+ * Method: the gist.science summary page "기술 요약: AAAC (활성화 인식 적응형 코드북)"
+ * (arXiv 2605.08692), cited as "AAAC summary" with its section number. Each weight matrix gets two
+ * learned scalar tables T0, T1 of n entries (n = 16 for INT4, 15 for NVFP4; §2 mechanism 1); every
+ * group of g weights gets a positive scale; every selection group of S weights picks the table with
+ * the lower activation-weighted reconstruction error (§2 mechanism 2); the tables are refined as
+ * activation-weighted k-means centroids, alternating with the assignment (§2 mechanism 4); the
+ * result is stored as 4-bit codes, bf16 tables, and the table choice in the sign bit of the bf16
+ * scale or in a separate bitmap (§2 mechanism 3).
+ *
+ * Conventions for every call:
+ *  - W is bf16 [R, C] row-major (out x in), passed as uint16_t bit patterns. A scale group is g
+ *    consecutive weights of a row, a selection group S consecutive weights; groups never cross rows.
+ *  - Supported shapes: g and S powers of two with 8 <= S <= g <= 512, C % g == 0, R >= 1,
+ *    2 <= n <= 16, R * C < 2^40. Device pointers must be 16-byte aligned.
+ *  - All data pointers are DEVICE pointers owned by the caller. The library never allocates, frees
+ *    or synchronizes; every call checks its arguments on the host, enqueues its kernels on `stream`
+ *    (a hipStream_t; NULL means the default stream) and returns. Buffers must stay alive until the
+ *    stream work has completed.
+ *  - A failed check returns a non-zero status BEFORE anything is launched, so nothing is written.
+ *    AAAC_ERR_HIP reports a launch error seen through hipGetLastError; aaac_last_error() returns a
+ *    message for the last failure on the calling thread.
+ *  - Workspaces are caller-owned device buffers of at least aaac_workspace_bytes(...) bytes, 256-byte
+ *    aligned, and ZERO-FILLED before their first use; every call leaves its workspace zero-filled
+ *    again where that matters (the counters), so one workspace can be reused call after call on one
+ *    stream. Calls that overlap on different streams need different workspaces.
+ *  - Weights must be finite. Results are bitwise deterministic for given inputs and device.
+ *  - Tables are fp32 [2][n] (T0 then T1) while iterating; bf16 [2][n] bit patterns when packed.
+ */
+#ifndef AAAC_H
+#define AAAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t aaac_status;
+
+#define AAAC_OK 0
+#define AAAC_ERR_INVALID_ARG 1          /* null pointer, misaligned pointer, bad flag */
+#define AAAC_ERR_UNSUPPORTED_SHAPE 2    /* g, S, n, R, C outside the supported set */
+#define AAAC_ERR_WORKSPACE_TOO_SMALL 3  /* ws_bytes below aaac_workspace_bytes(...) */
+#define AAAC_ERR_HIP 4                  /* the HIP runtime reported an error */
+
+/* Workspace query operations. */
+#define AAAC_OP_IMPORTANCE 0
+#define AAAC_OP_INIT 1
+#define AAAC_OP_ASSIGN 2
+#define AAAC_OP_REFINE 3
+
+/* Flags of aaac_refine. */
+#define AAAC_REFINE_ROUND_BF16 1        /* round the new tables to bf16 (ties to even), stored as fp32 */
+
+/* Static description of a status code. Never NULL. */
+const char* aaac_status_string(aaac_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). Valid until the next call on
+ * this thread. */
+const char* aaac_last_error(void);
+
+/* Workspace bytes needed by one call of operation `op` on an [R, C] matrix (for IMPORTANCE, R is
+ * the token count T and C the column count K). Returns 0 for an unknown op or unsupported shape. */
+size_t aaac_workspace_bytes(int op, int64_t R, int64_t C, int g, int S, int n);
+
+/*
+ * Importance, AAAC summary §2 mechanism 2: I_k = sum_t X[t, k]^2 over the calibration tokens.
+ *
+ * X      fp32 [T, K] with row stride ldx >= K (elements); one chunk of the token stream.
+ * I_acc  fp64 [K], accumulated in place: I_acc[k] += sum_t X[t, k]^2 (fp32 squares are exact in
+ *        fp64). Zero it before the first chunk; chunks may follow in any number of calls.
+ * I_out  fp32 [K] or NULL; if given, receives I_acc rounded to fp32 after this chunk.
+ * ws     workspace of aaac_workspace_bytes(AAAC_OP_IMPORTANCE, T, K, 0, 0, 0) bytes.
+ * T == 0 is allowed (I_out is still written). The sum over a chunk is taken in a fixed order.
+ */
+aaac_status aaac_importance(const float* X, int64_t T, int64_t K, int64_t ldx, double* I_acc,
+                            float* I_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Table initialization, AAAC summary §2 mechanism 4: equally spaced quantiles of the normalized
+ * weight distribution, T1 shifted half a step. With s = max |w| over the scale group,
+ * u = fl32(w / s) (u = +0 when s = 0), V the ascending sort of all N = R*C values of u:
+ *   T0[j] = V[floor((2j + 1) N / (2n))],  T1[j] = V[min(N - 1, floor((j + 1) N / n))].
+ * Found by an exact radix select; tables fp32 [2][n] (output).
+ * ws: aaac_workspace_bytes(AAAC_OP_INIT, R, C, g, 0, n) bytes.
+ */
+aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, int n,
+                                float* tables, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Assign, AAAC summary §2 mechanisms 2 and 4. For every weight and table c, q_c is the entry
+ * nearest to u = w / s (ties to the lower index); for every selection group H,
+ *   E_c(H) = sum_{k in H} I_k (w_k - s T_c[q_c(k)])^2,   sel(H) = 1 iff E_1 < E_0,
+ * and the stored code is q_sel. The nearest entry is decided on exactly rounded fp32 residuals
+ * w - s T (a differing decision is only possible when the two squared distances agree to 2.4e-7
+ * relative); the selection compares E_1 - E_0 accumulated in fp32 over at most four terms and in
+ * fp64 beyond (a differing decision needs |E_1 - E_0| < 1e-6 max(E_0, E_1)).
+ *
+ * I       fp32 [C] importance (finite, >= 0).
+ * tables  fp32 [2][n], any order, duplicates allowed.
+ * codes   [R * C / 2] bytes, two codes per byte, the low nibble holds the even column.
+ * sel     [R * C / S] bytes, 0 = T0, 1 = T1, one per selection group in row-major order.
+ * err     NULL, or fp32 [R * C / S][2] receiving (E_0, E_1) per selection group (for checking).
+ * ws      aaac_workspace_bytes(AAAC_OP_ASSIGN, R, C, g, S, n) bytes (a lookup structure built from
+ *         the tables).
+ */
+aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                        const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
+                        float* err, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Refine, AAAC summary §2 mechanism 4 (activation-weighted k-means). For every table c and entry j,
+ * over the cell {weights with sel = c and code = j}:
+ *   num = sum I_k s w_k,  den = sum I_k s^2,   T_c[j] <- num / den if den > 0, else unchanged.
+ * num / den minimizes sum I (w - s t)^2 over t, i.e. it is the I s^2-weighted centroid of u.
+ * Sums run in fp32 over at most 64 terms per partial and in fp64 beyond, in a fixed order.
+ *
+ * codes, sel   as written by aaac_assign.
+ * tables_in    fp32 [2][n];  tables_out fp32 [2][n], may equal tables_in.
+ * flags        0 or AAAC_REFINE_ROUND_BF16 (round the new entries to bf16; used on the last
+ *              iteration so that the final assign runs against the stored tables).
+ * ws           aaac_workspace_bytes(AAAC_OP_REFINE, R, C, g, S, n) bytes.
+ */
+aaac_status aaac_refine(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                        const float* I, const uint8_t* codes, const uint8_t* sel,
+                        const float* tables_in, float* tables_out, int flags, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * Pack, AAAC summary §2 mechanism 3 and §4: the stored format.
+ *   scales  [R * C / g] bf16 bit patterns of s = max |w| over each scale group; when S == g the
+ *           sign bit holds the selector (1 = T1), when S < g it is 0.
+ *   bitmap  S < g: [ceil(R * C / S / 8)] bytes, bit i (byte i >> 3, bit i & 7) = selector of the
+ *           i-th selection group in row-major order (1 / S extra bits per weight). S == g: NULL.
+ *   tables_bf16 [2][n] bf16 bit patterns of the tables (ties to even).
+ * codes are already packed by aaac_assign and are not touched.
+ */
+aaac_status aaac_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                      const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
+                      uint16_t* tables_bf16, void* stream);
+
+/*
+ * Dequantize, AAAC summary §1 (the dequantized values are what inference uses) and §2 mechanism 3:
+ *   W_hat = bf16(|s| * T~_sel[q])  (the product of two bf16 values is exact in fp32; one rounding,
+ *   ties to even), with the selector read from the scale sign bit (bitmap == NULL, S == g) or from
+ *   the bitmap (S < g).
+ * W_hat  bf16 [R, C] bit patterns (output).
+ */
+aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
+                         const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
+                         uint16_t* W_hat, void* stream);
+
+/*
+ * Batched assign / refine over up to AAAC_MAX_BATCH matrices that share g, S and n (for example
+ * the seven linears of one decoder layer) in one launch each. Element i of every array describes
+ * matrix i exactly as the single-matrix call does; the results are bitwise identical to calling
+ * the single-matrix entry points one matrix at a time. refine updates tables[i] in place.
+ * The host arrays are read during the call only. ws: aaac_batch_workspace_bytes(op, count, R, C,
+ * g, S, n) bytes, same zero-fill rule as above.
+ */
+#define AAAC_MAX_BATCH 8
+
+size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int64_t* C, int g,
+                                  int S, int n);
+
+aaac_status aaac_assign_batch(int count, const uint16_t* const* W, const int64_t* R,
+                              const int64_t* C, int g, int S, int n, const float* const* I,
+                              const float* const* tables, uint8_t* const* codes,
+                              uint8_t* const* sel, void* ws, size_t ws_bytes, void* stream);
+
+aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t* R,
+                              const int64_t* C, int g, int S, int n, const float* const* I,
+                              const uint8_t* const* codes, const uint8_t* const* sel,
+                              float* const* tables, int flags, void* ws, size_t ws_bytes,
+                              void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AAAC_H */

@@ -1,0 +1,300 @@
+"""ctypes binding of libaaac.so (the C ABI in include/aaac.h).
+
+Argument marshalling only: every function here checks dtypes and devices of torch tensors, passes
+their device pointers and the current HIP stream to the C entry point of the same name, and turns
+a non-zero status into an exception. All arithmetic runs in the library's kernels. There is no
+fallback: if the library is missing or no GPU is visible, the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libaaac.so")
+
+AAAC_OK = 0
+AAAC_ERR_INVALID_ARG = 1
+AAAC_ERR_UNSUPPORTED_SHAPE = 2
+AAAC_ERR_WORKSPACE_TOO_SMALL = 3
+AAAC_ERR_HIP = 4
+
+OP_IMPORTANCE, OP_INIT, OP_ASSIGN, OP_REFINE = 0, 1, 2, 3
+REFINE_ROUND_BF16 = 1
+MAX_BATCH = 8
+
+EXPORTED = (
+    "aaac_status_string", "aaac_last_error", "aaac_workspace_bytes", "aaac_importance",
+    "aaac_init_quantiles", "aaac_assign", "aaac_refine", "aaac_pack", "aaac_dequant",
+    "aaac_batch_workspace_bytes", "aaac_assign_batch", "aaac_refine_batch",
+)
+
+
+class AAACError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+_lib = None
+
+c_i64 = ctypes.c_int64
+c_int = ctypes.c_int
+c_vp = ctypes.c_void_p
+c_size = ctypes.c_size_t
+P = ctypes.POINTER
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once) and declare every entry point's signature."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            "libaaac.so not found at %s: build it with `python -m "
+            "post_weight_quantization_06_amd.build` (hipcc, gfx950)" % path)
+    lib = ctypes.CDLL(path)
+    sig = {
+        "aaac_status_string": (ctypes.c_char_p, [c_int]),
+        "aaac_last_error": (ctypes.c_char_p, []),
+        "aaac_workspace_bytes": (c_size, [c_int, c_i64, c_i64, c_int, c_int, c_int]),
+        "aaac_batch_workspace_bytes": (c_size, [c_int, c_int, P(c_i64), P(c_i64), c_int, c_int,
+                                                c_int]),
+        "aaac_importance": (c_int, [c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_size, c_vp]),
+        "aaac_init_quantiles": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_size,
+                                        c_vp]),
+        "aaac_assign": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
+                                c_vp, c_vp, c_size, c_vp]),
+        "aaac_refine": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
+                                c_vp, c_int, c_vp, c_size, c_vp]),
+        "aaac_pack": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
+                              c_vp, c_vp]),
+        "aaac_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
+                                 c_vp]),
+        "aaac_assign_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
+                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp, c_size, c_vp]),
+        "aaac_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
+                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int, c_vp, c_size,
+                                      c_vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != AAAC_OK:
+        lib = load()
+        detail = lib.aaac_last_error().decode()
+        raise AAACError(status, "%s failed: %s (%s)" % (
+            what, lib.aaac_status_string(status).decode(), detail))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on the GPU (got %s)" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if numel is not None and t.numel() != numel:
+        raise ValueError("%s must hold %d elements (got %d)" % (name, numel, t.numel()))
+
+
+def workspace_bytes(op: int, R: int, C: int, g: int = 128, S: int = 128, n: int = 16) -> int:
+    return int(load().aaac_workspace_bytes(op, R, C, g, S, n))
+
+
+def batch_workspace_bytes(op: int, Rs: Sequence[int], Cs: Sequence[int], g: int, S: int,
+                          n: int) -> int:
+    k = len(Rs)
+    R = (c_i64 * k)(*Rs)
+    C = (c_i64 * k)(*Cs)
+    return int(load().aaac_batch_workspace_bytes(op, k, R, C, g, S, n))
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """Zero-filled device workspace of at least nbytes (torch allocations are 256-byte aligned)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------------------------------------
+# Entry points (same names as the C ABI).
+# ------------------------------------------------------------------------------------------------
+
+def aaac_importance(X: torch.Tensor, I_acc: torch.Tensor, I_out: Optional[torch.Tensor] = None,
+                    ws: Optional[torch.Tensor] = None, stream=None):
+    """I_acc += sum_t X[t, :]^2 (fp64); I_out = fp32(I_acc) if given. X: fp32 [T, K], row stride
+    X.stride(0)."""
+    lib = load()
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be 2-D with unit column stride")
+    if X.device.type != "cuda" or X.dtype != torch.float32:
+        raise TypeError("X must be fp32 on the GPU")
+    T, K = X.shape
+    _need(I_acc, "I_acc", torch.float64, K)
+    if I_out is not None:
+        _need(I_out, "I_out", torch.float32, K)
+    nb = lib.aaac_workspace_bytes(OP_IMPORTANCE, T, K, 0, 0, 0)
+    if ws is None:
+        ws = workspace(nb, X.device)
+    st = lib.aaac_importance(_ptr(X), T, K, X.stride(0), _ptr(I_acc), _ptr(I_out), _ptr(ws),
+                             ws.numel(), _stream(stream))
+    _check(st, "aaac_importance")
+    return I_acc
+
+
+def aaac_init_quantiles(W: torch.Tensor, g: int, n: int, tables: torch.Tensor,
+                        ws: Optional[torch.Tensor] = None, stream=None):
+    lib = load()
+    R, C = W.shape
+    _need(W, "W", torch.bfloat16)
+    _need(tables, "tables", torch.float32, 2 * n)
+    if ws is None:
+        ws = workspace(lib.aaac_workspace_bytes(OP_INIT, R, C, g, 0, n), W.device)
+    st = lib.aaac_init_quantiles(_ptr(W), R, C, g, n, _ptr(tables), _ptr(ws), ws.numel(),
+                                 _stream(stream))
+    _check(st, "aaac_init_quantiles")
+    return tables
+
+
+def aaac_assign(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, tables: torch.Tensor,
+                codes: torch.Tensor, sel: torch.Tensor, err: Optional[torch.Tensor] = None,
+                ws: Optional[torch.Tensor] = None, stream=None):
+    lib = load()
+    R, C = W.shape
+    _need(W, "W", torch.bfloat16)
+    _need(I, "I", torch.float32, C)
+    _need(tables, "tables", torch.float32, 2 * n)
+    _need(codes, "codes", torch.uint8, R * C // 2)
+    _need(sel, "sel", torch.uint8, R * C // S)
+    if err is not None:
+        _need(err, "err", torch.float32, 2 * (R * C // S))
+    if ws is None:
+        ws = workspace(lib.aaac_workspace_bytes(OP_ASSIGN, R, C, g, S, n), W.device)
+    st = lib.aaac_assign(_ptr(W), R, C, g, S, n, _ptr(I), _ptr(tables), _ptr(codes), _ptr(sel),
+                         _ptr(err), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "aaac_assign")
+
+
+def aaac_refine(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, codes: torch.Tensor,
+                sel: torch.Tensor, tables_in: torch.Tensor, tables_out: torch.Tensor,
+                flags: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
+    lib = load()
+    R, C = W.shape
+    _need(W, "W", torch.bfloat16)
+    _need(I, "I", torch.float32, C)
+    _need(codes, "codes", torch.uint8, R * C // 2)
+    _need(sel, "sel", torch.uint8, R * C // S)
+    _need(tables_in, "tables_in", torch.float32, 2 * n)
+    _need(tables_out, "tables_out", torch.float32, 2 * n)
+    if ws is None:
+        ws = workspace(lib.aaac_workspace_bytes(OP_REFINE, R, C, g, S, n), W.device)
+    st = lib.aaac_refine(_ptr(W), R, C, g, S, n, _ptr(I), _ptr(codes), _ptr(sel),
+                         _ptr(tables_in), _ptr(tables_out), flags, _ptr(ws), ws.numel(),
+                         _stream(stream))
+    _check(st, "aaac_refine")
+
+
+def aaac_pack(W: torch.Tensor, g: int, S: int, n: int, sel: torch.Tensor, tables: torch.Tensor,
+              scales: torch.Tensor, bitmap: Optional[torch.Tensor], tables_bf16: torch.Tensor,
+              stream=None):
+    lib = load()
+    R, C = W.shape
+    _need(W, "W", torch.bfloat16)
+    _need(sel, "sel", torch.uint8, R * C // S)
+    _need(tables, "tables", torch.float32, 2 * n)
+    _need(scales, "scales", torch.int16, R * C // g)
+    _need(tables_bf16, "tables_bf16", torch.int16, 2 * n)
+    if bitmap is not None:
+        _need(bitmap, "bitmap", torch.uint8, (R * C // S + 7) // 8)
+    st = lib.aaac_pack(_ptr(W), R, C, g, S, n, _ptr(sel), _ptr(tables), _ptr(scales),
+                       _ptr(bitmap), _ptr(tables_bf16), _stream(stream))
+    _check(st, "aaac_pack")
+
+
+def aaac_dequant(codes: torch.Tensor, scales: torch.Tensor, bitmap: Optional[torch.Tensor],
+                 tables_bf16: torch.Tensor, R: int, C: int, g: int, S: int, n: int,
+                 W_hat: torch.Tensor, stream=None):
+    lib = load()
+    _need(codes, "codes", torch.uint8, R * C // 2)
+    _need(scales, "scales", torch.int16, R * C // g)
+    _need(tables_bf16, "tables_bf16", torch.int16, 2 * n)
+    _need(W_hat, "W_hat", torch.bfloat16, R * C)
+    if bitmap is not None:
+        _need(bitmap, "bitmap", torch.uint8, (R * C // S + 7) // 8)
+    st = lib.aaac_dequant(_ptr(codes), _ptr(scales), _ptr(bitmap), _ptr(tables_bf16), R, C, g, S,
+                          n, _ptr(W_hat), _stream(stream))
+    _check(st, "aaac_dequant")
+
+
+def _arr(ctype, values):
+    return (ctype * len(values))(*values)
+
+
+def aaac_assign_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
+                      Is: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
+                      codes: Sequence[torch.Tensor], sels: Sequence[torch.Tensor],
+                      ws: Optional[torch.Tensor] = None, stream=None):
+    lib = load()
+    k = len(Ws)
+    Rs = [W.shape[0] for W in Ws]
+    Cs = [W.shape[1] for W in Ws]
+    for i in range(k):
+        _need(Ws[i], "W[%d]" % i, torch.bfloat16)
+        _need(Is[i], "I[%d]" % i, torch.float32, Cs[i])
+        _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
+        _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
+        _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
+    if ws is None:
+        ws = workspace(batch_workspace_bytes(OP_ASSIGN, Rs, Cs, g, S, n), Ws[0].device)
+    st = lib.aaac_assign_batch(
+        k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
+        _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in tables]),
+        _arr(c_vp, [t.data_ptr() for t in codes]), _arr(c_vp, [t.data_ptr() for t in sels]),
+        _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "aaac_assign_batch")
+
+
+def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
+                      Is: Sequence[torch.Tensor], codes: Sequence[torch.Tensor],
+                      sels: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
+                      flags: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
+    lib = load()
+    k = len(Ws)
+    Rs = [W.shape[0] for W in Ws]
+    Cs = [W.shape[1] for W in Ws]
+    for i in range(k):
+        _need(Ws[i], "W[%d]" % i, torch.bfloat16)
+        _need(Is[i], "I[%d]" % i, torch.float32, Cs[i])
+        _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
+        _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
+        _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
+    if ws is None:
+        ws = workspace(batch_workspace_bytes(OP_REFINE, Rs, Cs, g, S, n), Ws[0].device)
+    st = lib.aaac_refine_batch(
+        k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
+        _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in codes]),
+        _arr(c_vp, [t.data_ptr() for t in sels]), _arr(c_vp, [t.data_ptr() for t in tables]),
+        flags, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "aaac_refine_batch")

@@ -1,0 +1,333 @@
+// C ABI of the quantizer (declared in include/aaac.h): argument checks, workspace layout and
+// kernel launches on the caller's stream. Nothing here allocates, frees or synchronizes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <atomic>
+
+#include "aaac.h"
+#include "common.h"
+
+namespace aaac {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace aaac
+
+namespace {
+
+using namespace aaac;
+
+constexpr int64_t kMaxRefineBlocks = 1024;
+
+thread_local char g_err[512];
+
+aaac_status fail(aaac_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+aaac_status ok() {
+  g_err[0] = '\0';
+  return AAAC_OK;
+}
+
+aaac_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(AAAC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape rules shared by the matrix calls. need_S: the call uses the selection group.
+aaac_status check_shape(int64_t R, int64_t C, int g, int S, int n, bool need_S, const char* who) {
+  if (R < 1 || C < 8 || C % 8 != 0 || C >= ((int64_t)1 << 31))
+    return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: R=%lld C=%lld (need R >= 1, C >= 8, C %% 8 == 0)",
+                who, (long long)R, (long long)C);
+  if (R > (((int64_t)1 << 40) / C))
+    return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: R*C must stay below 2^40", who);
+  if (!pow2(g) || g < 8 || g > 512 || C % g != 0)
+    return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: g=%d (need a power of two in [8, 512] dividing C)",
+                who, g);
+  if (need_S && (!pow2(S) || S < 8 || S > g))
+    return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: S=%d (need a power of two in [8, g])", who, S);
+  if (n < 2 || n > 16)
+    return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: n=%d (need 2 <= n <= 16)", who, n);
+  return AAAC_OK;
+}
+
+size_t refine_ws_bytes(int count) { return (size_t)count * 64 * kMaxRefineBlocks * sizeof(double); }
+
+aaac_status check_batch(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                        int g, int S, int n, const char* who) {
+  if (count < 1 || count > AAAC_MAX_BATCH)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: count=%d (need 1..%d)", who, count, AAAC_MAX_BATCH);
+  if (!W || !R || !C) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    aaac_status st = check_shape(R[i], C[i], g, S, n, true, who);
+    if (st != AAAC_OK) return st;
+    if (!W[i] || !aligned(W[i], 16))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: W[%d] null or not 16-byte aligned", who, i);
+  }
+  return AAAC_OK;
+}
+
+aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                      int g, int S, int n, const float* const* I, const float* const* tables,
+                      uint8_t* const* codes, uint8_t* const* sel, float* err, void* ws,
+                      size_t ws_bytes, void* stream, const char* who) {
+  aaac_status st = check_batch(count, W, R, C, g, S, n, who);
+  if (st != AAAC_OK) return st;
+  if (!I || !tables || !codes || !sel) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    if (!I[i] || !aligned(I[i], 16) || !tables[i] || !aligned(tables[i], 4) || !codes[i] ||
+        !aligned(codes[i], 16) || !sel[i])
+      return fail(AAAC_ERR_INVALID_ARG,
+                  "%s: matrix %d: I, tables, codes or sel null or misaligned (I and codes need 16 "
+                  "bytes)", who, i);
+  }
+  if (err && !aligned(err, 4)) return fail(AAAC_ERR_INVALID_ARG, "%s: err misaligned", who);
+  const size_t need = (size_t)count * kLutBytes;
+  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
+  if (ws_bytes < need)
+    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  LutBatch lb{};
+  AssignBatch b{};
+  b.njobs = count;
+  b.g = g;
+  b.S = S;
+  b.n = n;
+  lb.n = n;
+  int64_t tb = 0;
+  for (int i = 0; i < count; ++i) {
+    uint8_t* lut = static_cast<uint8_t*>(ws) + (size_t)i * kLutBytes;
+    lb.tables[i] = tables[i];
+    lb.lut[i] = lut;
+    AssignJob& j = b.job[i];
+    j.geom = make_geom(R[i], C[i], tb);
+    tb += j.geom.ntasks;
+    j.W = W[i];
+    j.I = I[i];
+    j.tables = tables[i];
+    j.lut = lut;
+    j.codes = reinterpret_cast<uint32_t*>(codes[i]);
+    j.sel = sel[i];
+    j.err = err;
+  }
+  b.total_tasks = tb;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_lut_build(lb, count, s);
+  if (e != hipSuccess) return hip_status(e, who);
+  return hip_status(launch_assign(b, err != nullptr, s), who);
+}
+
+aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                      int g, int S, int n, const float* const* I, const uint8_t* const* codes,
+                      const uint8_t* const* sel, const float* const* tin, float* const* tout,
+                      int flags, void* ws, size_t ws_bytes, void* stream, const char* who) {
+  aaac_status st = check_batch(count, W, R, C, g, S, n, who);
+  if (st != AAAC_OK) return st;
+  if (flags & ~AAAC_REFINE_ROUND_BF16) return fail(AAAC_ERR_INVALID_ARG, "%s: unknown flags %d", who, flags);
+  if (!I || !codes || !sel || !tin || !tout) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    if (!I[i] || !aligned(I[i], 16) || !codes[i] || !aligned(codes[i], 16) || !sel[i] || !tin[i] ||
+        !tout[i] || !aligned(tin[i], 4) || !aligned(tout[i], 4))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: null or misaligned pointer", who, i);
+  }
+  const size_t need = refine_ws_bytes(count);
+  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
+  if (ws_bytes < need)
+    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  RefineBatch b{};
+  b.njobs = count;
+  b.g = g;
+  b.S = S;
+  b.n = n;
+  b.flags = flags;
+  int64_t tb = 0;
+  for (int i = 0; i < count; ++i) {
+    RefineJob& j = b.job[i];
+    j.geom = make_geom(R[i], C[i], tb);
+    tb += j.geom.ntasks;
+    j.W = W[i];
+    j.I = I[i];
+    j.codes = reinterpret_cast<const uint32_t*>(codes[i]);
+    j.sel = sel[i];
+    j.tables_in = tin[i];
+    j.tables_out = tout[i];
+  }
+  b.total_tasks = tb;
+  int64_t nb = refine_grid(tb);
+  if (nb > kMaxRefineBlocks) nb = kMaxRefineBlocks;
+  b.nblocks = (int32_t)nb;
+  b.partials = static_cast<double*>(ws);
+  return hip_status(launch_refine(b, static_cast<hipStream_t>(stream)), who);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* aaac_status_string(aaac_status status) {
+  switch (status) {
+    case AAAC_OK: return "ok";
+    case AAAC_ERR_INVALID_ARG: return "invalid argument";
+    case AAAC_ERR_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case AAAC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case AAAC_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* aaac_last_error(void) { return g_err; }
+
+size_t aaac_workspace_bytes(int op, int64_t R, int64_t C, int g, int S, int n) {
+  switch (op) {
+    case AAAC_OP_IMPORTANCE: {
+      if (R < 0 || C < 1) return 0;
+      const int ns = importance_splits(R, C);
+      return ns > 0 ? (size_t)ns * (size_t)C * sizeof(double) : 256;
+    }
+    case AAAC_OP_INIT:
+      if (check_shape(R, C, g, 8, n, false, "aaac_workspace_bytes") != AAAC_OK) return 0;
+      return init_workspace_bytes(R, C, n);
+    case AAAC_OP_ASSIGN:
+      if (check_shape(R, C, g, S, n, true, "aaac_workspace_bytes") != AAAC_OK) return 0;
+      return (size_t)kLutBytes;
+    case AAAC_OP_REFINE:
+      if (check_shape(R, C, g, S, n, true, "aaac_workspace_bytes") != AAAC_OK) return 0;
+      return refine_ws_bytes(1);
+    default:
+      return 0;
+  }
+}
+
+size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int64_t* C, int g,
+                                  int S, int n) {
+  if (count < 1 || count > AAAC_MAX_BATCH || !R || !C) return 0;
+  for (int i = 0; i < count; ++i)
+    if (check_shape(R[i], C[i], g, S, n, true, "aaac_batch_workspace_bytes") != AAAC_OK) return 0;
+  if (op == AAAC_OP_ASSIGN) return (size_t)count * kLutBytes;
+  if (op == AAAC_OP_REFINE) return refine_ws_bytes(count);
+  return 0;
+}
+
+aaac_status aaac_importance(const float* X, int64_t T, int64_t K, int64_t ldx, double* I_acc,
+                            float* I_out, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "aaac_importance";
+  if (T < 0 || K < 1 || ldx < K)
+    return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: T=%lld K=%lld ldx=%lld", who, (long long)T,
+                (long long)K, (long long)ldx);
+  if ((T > 0 && !X) || !I_acc || !aligned(I_acc, 8) || (I_out && !aligned(I_out, 4)) ||
+      (X && !aligned(X, 4)))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
+  const int ns = importance_splits(T, K);
+  const size_t need = ns > 0 ? (size_t)ns * (size_t)K * sizeof(double) : 0;
+  if (need && (!ws || !aligned(ws, 256)))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
+  if (ws_bytes < need)
+    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  return hip_status(launch_importance(X, T, K, ldx, I_acc, I_out, static_cast<double*>(ws), ns,
+                                      static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, int n,
+                                float* tables, void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "aaac_init_quantiles";
+  aaac_status st = check_shape(R, C, g, 8, n, false, who);
+  if (st != AAAC_OK) return st;
+  if (!W || !aligned(W, 16) || !tables || !aligned(tables, 4))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
+  const size_t need = init_workspace_bytes(R, C, n);
+  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
+  if (ws_bytes < need)
+    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  return hip_status(launch_init(W, R, C, g, n, tables, ws, static_cast<hipStream_t>(stream)), who);
+}
+
+aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                        const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
+                        float* err, void* ws, size_t ws_bytes, void* stream) {
+  return do_assign(1, &W, &R, &C, g, S, n, &I, &tables, &codes, &sel, err, ws, ws_bytes, stream,
+                   "aaac_assign");
+}
+
+aaac_status aaac_assign_batch(int count, const uint16_t* const* W, const int64_t* R,
+                              const int64_t* C, int g, int S, int n, const float* const* I,
+                              const float* const* tables, uint8_t* const* codes,
+                              uint8_t* const* sel, void* ws, size_t ws_bytes, void* stream) {
+  return do_assign(count, W, R, C, g, S, n, I, tables, codes, sel, nullptr, ws, ws_bytes, stream,
+                   "aaac_assign_batch");
+}
+
+aaac_status aaac_refine(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                        const float* I, const uint8_t* codes, const uint8_t* sel,
+                        const float* tables_in, float* tables_out, int flags, void* ws,
+                        size_t ws_bytes, void* stream) {
+  return do_refine(1, &W, &R, &C, g, S, n, &I, &codes, &sel, &tables_in, &tables_out, flags, ws,
+                   ws_bytes, stream, "aaac_refine");
+}
+
+aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t* R,
+                              const int64_t* C, int g, int S, int n, const float* const* I,
+                              const uint8_t* const* codes, const uint8_t* const* sel,
+                              float* const* tables, int flags, void* ws, size_t ws_bytes,
+                              void* stream) {
+  if (!tables) return fail(AAAC_ERR_INVALID_ARG, "aaac_refine_batch: null tables array");
+  const float* tin[AAAC_MAX_BATCH];
+  const int m = count < AAAC_MAX_BATCH ? (count > 0 ? count : 0) : AAAC_MAX_BATCH;
+  for (int i = 0; i < m; ++i) tin[i] = tables[i];
+  return do_refine(count, W, R, C, g, S, n, I, codes, sel, tin, tables, flags, ws, ws_bytes, stream,
+                   "aaac_refine_batch");
+}
+
+aaac_status aaac_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                      const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
+                      uint16_t* tables_bf16, void* stream) {
+  const char* who = "aaac_pack";
+  aaac_status st = check_shape(R, C, g, S, n, true, who);
+  if (st != AAAC_OK) return st;
+  if (!W || !aligned(W, 16) || !sel || !tables || !aligned(tables, 4) || !scales ||
+      !aligned(scales, 2) || !tables_bf16 || !aligned(tables_bf16, 2))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
+  if ((S < g) != (bitmap != nullptr))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: bitmap must be given exactly when S < g", who);
+  return hip_status(launch_pack(W, R, C, g, S, n, sel, tables, scales, bitmap, tables_bf16,
+                                static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
+                         const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
+                         uint16_t* W_hat, void* stream) {
+  const char* who = "aaac_dequant";
+  aaac_status st = check_shape(R, C, g, S, n, true, who);
+  if (st != AAAC_OK) return st;
+  if (!codes || !aligned(codes, 4) || !scales || !aligned(scales, 2) || !tables_bf16 ||
+      !aligned(tables_bf16, 2) || !W_hat || !aligned(W_hat, 16))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
+  if ((S < g) != (bitmap != nullptr))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: bitmap must be given exactly when S < g", who);
+  return hip_status(launch_dequant(codes, scales, bitmap, tables_bf16, R, C, g, S, n, W_hat,
+                                   static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+}  // extern "C"

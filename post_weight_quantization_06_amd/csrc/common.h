@@ -1,0 +1,179 @@
+// Shared definitions of the gfx950 kernels: lane mapping, bf16 helpers, job descriptors and the
+// host-side launchers that the C ABI (abi.hip) calls after validating its arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace aaac {
+
+// ------------------------------------------------------------------------------------------------
+// Lane mapping shared by the streaming kernels. A wave covers one "slab" of 512 consecutive columns
+// of a row: lane l owns columns [slab*512 + 8l, slab*512 + 8l + 8), i.e. one 16-byte load of bf16.
+// A workgroup of four waves walks kRowsPerTask rows of one slab (one "task"); tasks are numbered
+// row-block-major so that consecutive tasks read consecutive memory.
+// ------------------------------------------------------------------------------------------------
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kPerLane = 8;
+constexpr int kSlab = kWave * kPerLane;
+constexpr int kRowsPerWave = 8;
+constexpr int kRowsPerTask = kRowsPerWave * kWavesPerBlock;
+constexpr int kMaxJobs = 8;
+
+// ------------------------------------------------------------------------------------------------
+// Nearest-entry lookup structure (built per table pair by lut_build, consumed by assign).
+// u in [-1, 1] is mapped to one of kLutRecs records of 32 bytes by
+//   t = fma(w, Y, kLutMagic),  Y = 16 kLutBuckets / s,  offset = bits(t) & kLutMask
+// (t lies in [2^23, 2^24), so its low mantissa bits hold round(32 + 16 kLutBuckets (u + 1))).
+// Record rho covers u in [(32 rho - 32.5) / (16 kLutBuckets) - 1, (32 rho - 0.5) / (16 kLutBuckets) - 1];
+// it holds, per table, the two candidate entries A (wins ties) and B valid over that interval widened
+// by kLutSlack, and one byte with the index of each table's A (low nibble: table 0).
+// A record with B == A has a single candidate; a record whose table has more than two candidates
+// there (or non-consecutive indices) holds NaN for that table, which routes its group to the exact
+// fallback scan.
+// ------------------------------------------------------------------------------------------------
+constexpr int kLutRecs = 1024;
+constexpr int kLutBuckets = kLutRecs - 2;
+constexpr int kLutRecBytes = 32;
+constexpr int kLutBytes = kLutRecs * kLutRecBytes;
+constexpr uint32_t kLutMask = (kLutRecs - 1) * kLutRecBytes;
+constexpr float kLutScale = 16.0f * kLutBuckets;                   // 16352
+constexpr float kLutMagic = 8388608.0f + 32.0f + 16.0f * kLutBuckets;
+constexpr double kLutSlack = 0x1p-20;
+
+// Group scales outside [2^-30, 2^30] take the exact fallback (no fp32 over/underflow there).
+constexpr float kFastScaleMin = 0x1p-30f;
+constexpr float kFastScaleMax = 0x1p30f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Round a finite fp32 value to bf16, ties to even. Truncating 16 bits rounds down in magnitude; adding
+// 0x7fff rounds up every remainder above one half, and adding the kept least-significant bit as
+// well rounds an exact half up only when the kept part is odd. A carry out of the fraction moves
+// into the exponent, which is the correct next binade (or infinity past the largest finite value).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t b = __float_as_uint(x);
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Butterfly reductions over aligned blocks of `lanes` lanes (a power of two <= 64).
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, int lanes) {
+  for (int m = 1; m < lanes; m <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m));
+  return v;
+}
+__device__ __forceinline__ double block_sum_f64(double v, int lanes) {
+  for (int m = 1; m < lanes; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Largest |w| of the 8 bf16 of one lane, as the bf16 magnitude bit pattern (order-preserving).
+__device__ __forceinline__ uint32_t lane_absmax_bits(const uint4& v) {
+  uint32_t a = max(v.x & 0x7fffu, (v.x >> 16) & 0x7fffu);
+  uint32_t b = max(v.y & 0x7fffu, (v.y >> 16) & 0x7fffu);
+  uint32_t c = max(v.z & 0x7fffu, (v.z >> 16) & 0x7fffu);
+  uint32_t d = max(v.w & 0x7fffu, (v.w >> 16) & 0x7fffu);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float (&w)[8]) {
+  w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x);
+  w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
+  w[4] = bf16_lo(v.z); w[5] = bf16_hi(v.z);
+  w[6] = bf16_lo(v.w); w[7] = bf16_hi(v.w);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Job descriptors (kernel arguments, by value).
+// ------------------------------------------------------------------------------------------------
+struct MatrixGeom {
+  int64_t R;
+  int32_t C;
+  int32_t nslab;       // ceil(C / 512)
+  int64_t task_begin;  // first task of this job in the batch-wide numbering
+  int64_t ntasks;      // ceil(R / kRowsPerTask) * nslab
+};
+
+struct AssignJob {
+  MatrixGeom geom;
+  const uint16_t* W;
+  const float* I;
+  const float* tables;      // fp32 [2][n]
+  const uint8_t* lut;       // kLutBytes, built from `tables`
+  uint32_t* codes;          // [R * C / 8] dwords, 8 nibbles each
+  uint8_t* sel;             // [R * C / S]
+  float* err;               // nullable, [R * C / S][2]
+};
+
+struct AssignBatch {
+  AssignJob job[kMaxJobs];
+  int32_t njobs;
+  int32_t g, S, n;
+  int64_t total_tasks;
+};
+
+struct RefineJob {
+  MatrixGeom geom;
+  const uint16_t* W;
+  const float* I;
+  const uint32_t* codes;
+  const uint8_t* sel;
+  const float* tables_in;
+  float* tables_out;
+};
+
+struct RefineBatch {
+  RefineJob job[kMaxJobs];
+  int32_t njobs;
+  int32_t g, S, n;
+  int64_t total_tasks;
+  double* partials;         // [njobs][64][nblocks]
+  int32_t nblocks;          // grid size of the accumulation kernel
+  int32_t flags;
+};
+
+struct LutBatch {
+  const float* tables[kMaxJobs];
+  uint8_t* lut[kMaxJobs];
+  int32_t n;
+};
+
+// ------------------------------------------------------------------------------------------------
+// Host launchers (defined next to their kernels). All return hipSuccess or the launch error.
+// ------------------------------------------------------------------------------------------------
+int device_cu_count();
+
+hipError_t launch_lut_build(const LutBatch& b, int njobs, hipStream_t stream);
+hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream);
+hipError_t launch_refine(RefineBatch& b, hipStream_t stream);
+int refine_grid(int64_t total_tasks);
+
+hipError_t launch_importance(const float* X, int64_t T, int64_t K, int64_t ldx, double* I_acc,
+                             float* I_out, double* partials, int nsplit, hipStream_t stream);
+int importance_splits(int64_t T, int64_t K);
+
+size_t init_workspace_bytes(int64_t R, int64_t C, int n);
+hipError_t launch_init(const uint16_t* W, int64_t R, int64_t C, int g, int n, float* tables,
+                       void* ws, hipStream_t stream);
+
+hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                       const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
+                       uint16_t* tables_bf16, hipStream_t stream);
+hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
+                          const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
+                          uint16_t* W_hat, hipStream_t stream);
+
+inline MatrixGeom make_geom(int64_t R, int64_t C, int64_t task_begin) {
+  MatrixGeom m;
+  m.R = R;
+  m.C = (int32_t)C;
+  m.nslab = (int32_t)((C + kSlab - 1) / kSlab);
+  m.task_begin = task_begin;
+  m.ntasks = ((R + kRowsPerTask - 1) / kRowsPerTask) * (int64_t)m.nslab;
+  return m;
+}
+
+}  // namespace aaac

@@ -1,0 +1,243 @@
+// Table initialization (AAAC summary §2 mechanism 4): equally spaced quantiles of the normalized
+// weights, T1 half a step above T0, found by an exact radix select.
+//
+// u = fl32(w / s) (IEEE division; u = +0 when s = 0) is mapped to an order-preserving 32-bit key
+// (flip all bits of negatives, set the sign bit of non-negatives). The 2n target ranks are resolved
+// one byte at a time, most significant first: pass 1 histograms the top byte of every key; after
+// each pass a single workgroup walks the histogram of every target's current prefix to the byte
+// that holds its residual rank; passes 2-4 histogram the next byte of the keys whose prefix is one
+// of the (at most 2n) active prefixes. Integer counts make every step exact and order-free.
+//
+// Workspace: keys u32 [N] | hist u64 [32][256] | state (see InitState).
+#include "common.h"
+
+namespace aaac {
+
+namespace {
+
+constexpr int kTargets = 32;
+constexpr int kDigits = 256;
+
+struct InitState {
+  uint32_t prefix[kTargets];     // resolved high bytes of each target's key
+  uint64_t rank[kTargets];       // residual rank inside that prefix
+  uint32_t active[kTargets];     // sorted distinct prefixes of the current pass
+  uint32_t nactive;
+  uint32_t pad[3];
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct InitLayout {
+  uint32_t* keys;
+  unsigned long long* hist;
+  InitState* state;
+};
+
+InitLayout layout(void* ws, int64_t N) {
+  char* p = static_cast<char*>(ws);
+  InitLayout l;
+  l.keys = reinterpret_cast<uint32_t*>(p);
+  p += align256((size_t)N * 4);
+  l.hist = reinterpret_cast<unsigned long long*>(p);
+  p += align256(sizeof(unsigned long long) * kTargets * kDigits);
+  l.state = reinterpret_cast<InitState*>(p);
+  return l;
+}
+
+__device__ __forceinline__ uint32_t order_key(float u) {
+  const uint32_t b = __float_as_uint(u);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ void flush_hist(const uint32_t* lds, unsigned long long* hist, int bins) {
+  for (int i = threadIdx.x; i < bins; i += kBlock)
+    if (lds[i]) atomicAdd(hist + i, (unsigned long long)lds[i]);
+}
+
+}  // namespace
+
+// Pass 1: keys of all weights (same lane mapping as assign) and the histogram of their top byte.
+__global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __restrict__ W,
+                                                           MatrixGeom geom, int g,
+                                                           uint32_t* __restrict__ keys,
+                                                           unsigned long long* hist) {
+  __shared__ uint32_t h[kDigits];
+  const int tid = threadIdx.x;
+  h[tid] = 0;
+  __syncthreads();
+  const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = g / kPerLane;
+  for (int64_t task = blockIdx.x; task < geom.ntasks; task += gridDim.x) {
+    const int64_t rb = task / geom.nslab;
+    const int slab = (int)(task - rb * geom.nslab);
+    const int c0 = slab * kSlab + lane * kPerLane;
+    const bool active = c0 < geom.C;
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
+      if (r >= geom.R) break;
+      const int64_t base = r * (int64_t)geom.C + c0;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (active) v = *reinterpret_cast<const uint4*>(W + base);
+      const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
+      if (!active) continue;
+      const float s = __uint_as_float(amax << 16);
+      float w[8];
+      unpack8(v, w);
+      uint32_t k[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float u = s > 0.0f ? w[e] / s : 0.0f;
+        if (u == 0.0f) u = 0.0f;            // zero is unsigned
+        k[e] = order_key(u);
+        atomicAdd(&h[k[e] >> 24], 1u);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(keys + base);
+      dst[0] = make_uint4(k[0], k[1], k[2], k[3]);
+      dst[1] = make_uint4(k[4], k[5], k[6], k[7]);
+    }
+  }
+  __syncthreads();
+  flush_hist(h, hist, kDigits);
+}
+
+// Passes 2-4: histogram of byte `pass` (0-based from the top) of keys whose higher bytes match an
+// active prefix.
+__global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __restrict__ keys, int64_t N,
+                                                           int pass, const InitState* state,
+                                                           unsigned long long* hist) {
+  __shared__ uint32_t h[kTargets * kDigits];
+  __shared__ uint32_t act[kTargets];
+  __shared__ uint32_t nact;
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kTargets * kDigits; i += kBlock) h[i] = 0;
+  if (tid < kTargets) act[tid] = state->active[tid];
+  if (tid == 0) nact = state->nactive;
+  __syncthreads();
+  const int na = (int)nact;
+  const int pshift = 32 - 8 * pass;       // prefix = key >> pshift
+  const int dshift = 24 - 8 * pass;       // digit = (key >> dshift) & 255
+  const int64_t n4 = N / 4;
+  const uint4* k4 = reinterpret_cast<const uint4*>(keys);
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + tid; i < n4; i += (int64_t)gridDim.x * kBlock) {
+    const uint4 q = k4[i];
+    const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t pre = kk[e] >> pshift;
+      int lo = 0, hi = na;                 // first active prefix >= pre
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (act[mid] < pre) lo = mid + 1; else hi = mid;
+      }
+      if (lo < na && act[lo] == pre) atomicAdd(&h[lo * kDigits + ((kk[e] >> dshift) & 255u)], 1u);
+    }
+  }
+  __syncthreads();
+  flush_hist(h, hist, na * kDigits);
+}
+
+// One workgroup: move every target one byte down, rebuild the active prefix list, clear the
+// histogram; after the last pass write the tables.
+__global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N, int n,
+                                                             InitState* state,
+                                                             unsigned long long* hist,
+                                                             float* tables) {
+  const int tid = threadIdx.x;
+  const int nt = 2 * n;
+  __shared__ uint32_t newp[kTargets];
+  if (pass == 0 && tid < nt) {
+    // target ranks of reading: T0[j] at floor((2j+1) N / 2n), T1[j] at min(N-1, floor((j+1) N / n))
+    const int j = tid % n;
+    uint64_t r;
+    // N < 2^40, so (2j + 1) N < 2^45 fits in 64 bits
+    if (tid < n) {
+      r = (uint64_t)(2 * j + 1) * (uint64_t)N / (uint64_t)(2 * n);
+    } else {
+      r = (uint64_t)(j + 1) * (uint64_t)N / (uint64_t)n;
+      if (r > (uint64_t)(N - 1)) r = (uint64_t)(N - 1);
+    }
+    state->prefix[tid] = 0;
+    state->rank[tid] = r;
+  }
+  __syncthreads();
+  if (tid < nt) {
+    const uint32_t pre = state->prefix[tid];
+    int slot = 0;
+    if (pass > 0) {
+      const int na = (int)state->nactive;
+      while (slot < na && state->active[slot] != pre) ++slot;
+    }
+    uint64_t rank = state->rank[tid];
+    uint64_t cum = 0;
+    int d = 0;
+    for (; d < kDigits - 1; ++d) {
+      const uint64_t c = hist[slot * kDigits + d];
+      if (rank < cum + c) break;
+      cum += c;
+    }
+    newp[tid] = (pre << 8) | (uint32_t)d;
+    state->rank[tid] = rank - cum;
+  }
+  __syncthreads();
+  for (int i = tid; i < kTargets * kDigits; i += kBlock) hist[i] = 0ull;
+  if (tid < nt) state->prefix[tid] = newp[tid];
+  if (tid == 0) {
+    // sorted distinct prefixes (at most 32: insertion into a small sorted list)
+    uint32_t list[kTargets];
+    int m = 0;
+    for (int t = 0; t < nt; ++t) {
+      const uint32_t p = newp[t];
+      int pos = 0;
+      while (pos < m && list[pos] < p) ++pos;
+      if (pos < m && list[pos] == p) continue;
+      for (int q = m; q > pos; --q) list[q] = list[q - 1];
+      list[pos] = p;
+      ++m;
+    }
+    for (int t = 0; t < m; ++t) state->active[t] = list[t];
+    state->nactive = (uint32_t)m;
+  }
+  if (pass == 3 && tid < nt) tables[tid] = key_value(newp[tid]);
+}
+
+size_t init_workspace_bytes(int64_t R, int64_t C, int n) {
+  (void)n;
+  return align256((size_t)R * C * 4) + align256(sizeof(unsigned long long) * kTargets * kDigits) +
+         align256(sizeof(InitState));
+}
+
+hipError_t launch_init(const uint16_t* W, int64_t R, int64_t C, int g, int n, float* tables,
+                       void* ws, hipStream_t stream) {
+  const int64_t N = R * C;
+  InitLayout l = layout(ws, N);
+  const MatrixGeom geom = make_geom(R, C, 0);
+  const int64_t want = (int64_t)device_cu_count() * 4;
+  const int grid1 = (int)(geom.ntasks < want ? geom.ntasks : want);
+  hipLaunchKernelGGL(init_keys_kernel, dim3(grid1), dim3(kBlock), 0, stream, W, geom, g, l.keys,
+                     l.hist);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kBlock), 0, stream, 0, N, n, l.state,
+                     l.hist, tables);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t n4 = N / 4;
+  int64_t grid = (n4 + kBlock - 1) / kBlock;
+  const int64_t cap = (int64_t)device_cu_count() * 4;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  for (int pass = 1; pass < 4; ++pass) {
+    hipLaunchKernelGGL(init_pass_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, l.keys, N,
+                       pass, l.state, l.hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kBlock), 0, stream, pass, N, n, l.state,
+                       l.hist, tables);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace aaac

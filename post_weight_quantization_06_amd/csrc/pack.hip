@@ -1,0 +1,142 @@
+// Stored format (AAAC summary §2 mechanism 3, §4) and dequantization (§1).
+//
+// pack:    bf16 group scales with the selector in the sign bit (S == g) or a separate LSB-first
+//          bitmap of selectors (S < g), and the bf16 tables. The codes are written by assign.
+// dequant: W_hat = bf16(|s| * T~_sel[q]); the product of two bf16 values is exact in fp32 whenever
+//          it is a normal number, so there is a single rounding (ties to even); products below
+//          2^-126 are formed in fp64 and rounded once from there.
+#include "common.h"
+
+namespace aaac {
+
+__global__ __launch_bounds__(kBlock) void pack_scales_kernel(const uint16_t* __restrict__ W,
+                                                             MatrixGeom geom, int g, int S,
+                                                             const uint8_t* __restrict__ sel,
+                                                             uint16_t* __restrict__ scales) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = g / kPerLane;
+  for (int64_t task = blockIdx.x; task < geom.ntasks; task += gridDim.x) {
+    const int64_t rb = task / geom.nslab;
+    const int slab = (int)(task - rb * geom.nslab);
+    const int c0 = slab * kSlab + lane * kPerLane;
+    const bool active = c0 < geom.C;
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
+      if (r >= geom.R) break;
+      const int64_t base = r * (int64_t)geom.C + c0;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (active) v = *reinterpret_cast<const uint4*>(W + base);
+      const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
+      if (active && ((c0 >> 3) & (g8 - 1)) == 0) {
+        uint32_t word = amax;
+        if (S == g) word |= (sel[base / S] ? 1u : 0u) << 15;
+        scales[base / g] = (uint16_t)word;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void pack_bits_kernel(const uint8_t* __restrict__ sel,
+                                                           int64_t ngroups,
+                                                           uint8_t* __restrict__ bitmap,
+                                                           const float* __restrict__ tables,
+                                                           int n, uint16_t* __restrict__ tables_bf16) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i < 2 * n) tables_bf16[i] = (uint16_t)f32_to_bf16_rne(tables[i]);
+  if (bitmap == nullptr) return;
+  const int64_t nbytes = (ngroups + 7) / 8;
+  if (i >= nbytes) return;
+  uint32_t b = 0;
+  for (int k = 0; k < 8; ++k) {
+    const int64_t h = i * 8 + k;
+    if (h < ngroups && sel[h]) b |= 1u << k;
+  }
+  bitmap[i] = (uint8_t)b;
+}
+
+hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
+                       const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
+                       uint16_t* tables_bf16, hipStream_t stream) {
+  const MatrixGeom geom = make_geom(R, C, 0);
+  const int64_t want = (int64_t)device_cu_count() * 4;
+  const int grid = (int)(geom.ntasks < want ? geom.ntasks : want);
+  hipLaunchKernelGGL(pack_scales_kernel, dim3(grid), dim3(kBlock), 0, stream, W, geom, g, S, sel,
+                     scales);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t ngroups = R * C / S;
+  int64_t items = bitmap ? (ngroups + 7) / 8 : 0;
+  if (items < 2 * n) items = 2 * n;
+  hipLaunchKernelGGL(pack_bits_kernel, dim3((unsigned)((items + kBlock - 1) / kBlock)),
+                     dim3(kBlock), 0, stream, sel, ngroups, S < g ? bitmap : nullptr, tables, n,
+                     tables_bf16);
+  return hipGetLastError();
+}
+
+// fp64 value -> bf16 bits, ties to even, by exact scaling to the binade's quantum.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
+  if (x == 0.0) return (__double_as_longlong(x) >> 48) & 0x8000u;
+  const double ax = fabs(x);
+  const int e = ax < 0x1p-126 ? -126 : ilogb(ax);
+  const double q = ldexp(1.0, e - 7);
+  const double r = rint(ax / q) * q;
+  uint32_t bits = r >= 0x1p128 ? 0x7f80u : (__float_as_uint((float)r) >> 16);
+  if (x < 0.0) bits |= 0x8000u;
+  return bits;
+}
+
+__global__ __launch_bounds__(kBlock) void dequant_kernel(const uint32_t* __restrict__ codes,
+                                                         const uint16_t* __restrict__ scales,
+                                                         const uint8_t* __restrict__ bitmap,
+                                                         const uint16_t* __restrict__ tables_bf16,
+                                                         int64_t R, int64_t C, int g, int S, int n,
+                                                         uint4* __restrict__ out) {
+  __shared__ float tab[2][16];
+  if (threadIdx.x < 2 * n)
+    tab[threadIdx.x / n][threadIdx.x % n] = __uint_as_float((uint32_t)tables_bf16[threadIdx.x] << 16);
+  __syncthreads();
+  const int64_t nvec = R * C / 8;
+  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * kBlock) {
+    const int64_t base = i * 8;
+    const uint32_t cw = codes[i];
+    const uint32_t word = scales[base / g];
+    uint32_t sg;
+    if (bitmap == nullptr) {
+      sg = word >> 15;
+    } else {
+      const int64_t h = base / S;
+      sg = (bitmap[h >> 3] >> (h & 7)) & 1u;
+    }
+    const float s = __uint_as_float((word & 0x7fffu) << 16);
+    uint32_t o[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t q = (cw >> (4 * k)) & 15u;
+      const float t = tab[sg][q < (uint32_t)n ? q : 0];
+      const float p = s * t;
+      // exact in fp32 unless the product is a nonzero subnormal
+      o[k] = (s == 0.0f || t == 0.0f || fabsf(p) >= 0x1p-126f)
+                 ? f32_to_bf16_rne(p)
+                 : f64_to_bf16_bits((double)s * (double)t);
+    }
+    out[i] = make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
+                        o[6] | (o[7] << 16));
+  }
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
+                          const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
+                          uint16_t* W_hat, hipStream_t stream) {
+  const int64_t nvec = R * C / 8;
+  int64_t grid = (nvec + kBlock - 1) / kBlock;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  if (grid > cap) grid = cap;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                     reinterpret_cast<const uint32_t*>(codes), scales, S < g ? bitmap : nullptr,
+                     tables_bf16, R, C, g, S, n, reinterpret_cast<uint4*>(W_hat));
+  return hipGetLastError();
+}
+
+}  // namespace aaac

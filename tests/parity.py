@@ -1,0 +1,108 @@
+"""Comparison helpers for the GPU parity tests: HIP results against the fp64 oracle.
+
+Tolerances (derived in the design doc from the arithmetic of each kernel):
+  * codes: bit-exact, except a weight whose GPU entry is strictly farther than the oracle's nearest
+    one by less than CODE_BAND (relative squared distance); equal distances must pick the lower
+    index, so value ties are never exempt;
+  * selectors: bit-exact, except groups with |E1 - E0| < SEL_BAND * max(E0, E1) (oracle fp64);
+    a code in such a group is compared against the table the GPU chose;
+  * tables after refine: 1e-5 relative, the denominator floored at 1e-2 * max|T|;
+  * importance: 1e-12 relative in fp64 (summation order only);
+  * init tables, packed bytes and dequantized weights: bit-exact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import aaac_ref as ref
+
+CODE_BAND = 1e-6
+SEL_BAND = 1e-6
+TABLE_RTOL = 1e-5
+TABLE_FLOOR = 1e-2
+
+
+def to_np64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64) if t.dtype in (
+        torch.bfloat16, torch.float16, torch.float32) else t.detach().cpu().numpy().astype(np.float64)
+
+
+def unpack_gpu_codes(codes: torch.Tensor, R: int, C: int) -> np.ndarray:
+    return ref.unpack_codes(codes.cpu().numpy().reshape(R, C // 2), R, C)
+
+
+def oracle_assign_rows(W64, I64, T0, T1, g, S, chunk_rows=256):
+    """Oracle assign over row chunks (rows are independent; identical to one call)."""
+    parts = {"q0": [], "q1": [], "E0": [], "E1": [], "sel": [], "codes": []}
+    for r0 in range(0, W64.shape[0], chunk_rows):
+        a = ref.assign(W64[r0:r0 + chunk_rows], I64, T0, T1, g, S)
+        for k in parts:
+            parts[k].append(a[k])
+    return {k: np.concatenate(v, axis=0) for k, v in parts.items()}
+
+
+def check_assign(W64, I64, tables, g, S, gpu_codes, gpu_sel, gpu_err=None, chunk_rows=256):
+    """Compare one GPU assign with the oracle on the same inputs. Returns a dict of counts and
+    raises AssertionError on a mismatch outside the bands."""
+    T0 = np.asarray(tables[0], dtype=np.float64)
+    T1 = np.asarray(tables[1], dtype=np.float64)
+    R, C = W64.shape
+    a = oracle_assign_rows(W64, I64, T0, T1, g, S, chunk_rows)
+    sel_g = np.asarray(gpu_sel).reshape(R, C // S).astype(np.uint8)
+    q_g = np.asarray(gpu_codes).reshape(R, C)
+    E0, E1 = a["E0"], a["E1"]
+    sel_diff = sel_g != a["sel"]
+    sel_exempt = np.abs(E1 - E0) <= SEL_BAND * np.maximum(E0, E1)
+    bad_sel = sel_diff & ~sel_exempt
+    assert not bad_sel.any(), "selector mismatch outside the band at %s (E0=%r E1=%r)" % (
+        np.argwhere(bad_sel)[:5].tolist(), E0[bad_sel][:5], E1[bad_sel][:5])
+    # codes against the table the GPU chose
+    chosen = np.repeat(sel_g, S, axis=1).astype(bool)
+    q_o = np.where(chosen, a["q1"], a["q0"])
+    s = np.repeat(ref.group_scales(W64, g), g, axis=1)
+    code_diff = q_g != q_o
+    bad_code = np.zeros_like(code_diff)
+    if code_diff.any():
+        idx = np.argwhere(code_diff)
+        r, c = idx[:, 0], idx[:, 1]
+        T = np.where(chosen[r, c], 1, 0)
+        Ts = np.stack([T0, T1])
+        d_g = (W64[r, c] - s[r, c] * Ts[T, q_g[r, c]]) ** 2
+        d_o = (W64[r, c] - s[r, c] * Ts[T, q_o[r, c]]) ** 2
+        ok = (d_g > d_o) & (d_g - d_o <= CODE_BAND * d_g)
+        bad_code[r[~ok], c[~ok]] = True
+    assert not bad_code.any(), "code mismatch outside the band at %s" % (
+        np.argwhere(bad_code)[:5].tolist())
+    if gpu_err is not None:
+        e = np.asarray(gpu_err, dtype=np.float64).reshape(R, C // S, 2)
+        for k, Eo in ((0, E0), (1, E1)):
+            tol = 4e-6 * np.maximum(Eo, 1e-30) + 1e-30
+            bad = np.abs(e[..., k] - Eo) > tol
+            assert not bad.any(), "E%d mismatch at %s: gpu %r oracle %r" % (
+                k, np.argwhere(bad)[:5].tolist(), e[..., k][bad][:5], Eo[bad][:5])
+    return {"sel_exempt": int((sel_diff & sel_exempt).sum()), "code_exempt": int(code_diff.sum()),
+            "oracle": a}
+
+
+def check_tables(gpu, oracle, rtol=TABLE_RTOL):
+    gpu = np.asarray(gpu, dtype=np.float64).reshape(2, -1)
+    oracle = np.asarray(oracle, dtype=np.float64).reshape(2, -1)
+    scale = np.maximum(np.abs(oracle), TABLE_FLOOR * np.abs(oracle).max())
+    rel = np.abs(gpu - oracle) / scale
+    assert np.all(rel <= rtol), "table mismatch: max rel %.3g\n gpu=%r\n ora=%r" % (
+        rel.max(), gpu, oracle)
+    return float(rel.max())
+
+
+def oracle_refine(W64, I64, codes, sel, T_in, g, S, chunk_rows=1024):
+    n = T_in.shape[1]
+    num = np.zeros((2, n))
+    den = np.zeros((2, n))
+    for r0 in range(0, W64.shape[0], chunk_rows):
+        a, b = ref.refine_sums(W64[r0:r0 + chunk_rows], I64, codes[r0:r0 + chunk_rows],
+                               sel[r0:r0 + chunk_rows], g, S, n)
+        num += a
+        den += b
+    return np.stack(ref.refine_update(num, den, T_in[0], T_in[1])), num, den
