@@ -104,13 +104,13 @@ aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, 
  * tables  fp32 [2][n], any order, duplicates allowed.
  * codes   [R * C / 2] bytes, two codes per byte, the low nibble holds the even column.
  * sel     [R * C / S] bytes, 0 = T0, 1 = T1, one per selection group in row-major order.
- * err     NULL, or fp32 [R * C / S][2] receiving (E_0, E_1) per selection group (for checking).
+ * err     NULL, or fp64 [R * C / S][2] receiving (E_0, E_1) per selection group (for checking).
  * ws      aaac_workspace_bytes(AAAC_OP_ASSIGN, R, C, g, S, n) bytes (a lookup structure built from
  *         the tables).
  */
 aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
-                        float* err, void* ws, size_t ws_bytes, void* stream);
+                        double* err, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Refine, AAAC summary §2 mechanism 4 (activation-weighted k-means). For every table c and entry j,

@@ -189,7 +189,7 @@ def aaac_assign(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, tables
     _need(codes, "codes", torch.uint8, R * C // 2)
     _need(sel, "sel", torch.uint8, R * C // S)
     if err is not None:
-        _need(err, "err", torch.float32, 2 * (R * C // S))
+        _need(err, "err", torch.float64, 2 * (R * C // S))
     if ws is None:
         ws = workspace(lib.aaac_workspace_bytes(OP_ASSIGN, R, C, g, S, n), W.device)
     st = lib.aaac_assign(_ptr(W), R, C, g, S, n, _ptr(I), _ptr(tables), _ptr(codes), _ptr(sel),

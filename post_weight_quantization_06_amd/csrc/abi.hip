@@ -90,7 +90,7 @@ aaac_status check_batch(int count, const uint16_t* const* W, const int64_t* R, c
 
 aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
                       int g, int S, int n, const float* const* I, const float* const* tables,
-                      uint8_t* const* codes, uint8_t* const* sel, float* err, void* ws,
+                      uint8_t* const* codes, uint8_t* const* sel, double* err, void* ws,
                       size_t ws_bytes, void* stream, const char* who) {
   aaac_status st = check_batch(count, W, R, C, g, S, n, who);
   if (st != AAAC_OK) return st;
@@ -102,7 +102,7 @@ aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, con
                   "%s: matrix %d: I, tables, codes or sel null or misaligned (I and codes need 16 "
                   "bytes)", who, i);
   }
-  if (err && !aligned(err, 4)) return fail(AAAC_ERR_INVALID_ARG, "%s: err misaligned", who);
+  if (err && !aligned(err, 8)) return fail(AAAC_ERR_INVALID_ARG, "%s: err misaligned", who);
   const size_t need = (size_t)count * kLutBytes;
   if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
   if (ws_bytes < need)
@@ -264,7 +264,7 @@ aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, 
 
 aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
-                        float* err, void* ws, size_t ws_bytes, void* stream) {
+                        double* err, void* ws, size_t ws_bytes, void* stream) {
   return do_assign(1, &W, &R, &C, g, S, n, &I, &tables, &codes, &sel, err, ws, ws_bytes, stream,
                    "aaac_assign");
 }

@@ -65,12 +65,13 @@ __global__ __launch_bounds__(kBlock) void lut_build_kernel(LutBatch b) {
     sm[c] = finite ? m : 0;
   }
   __syncthreads();
-  const float qnan = __builtin_nanf("");
+  constexpr uint32_t kNaNBits = 0x7fc00000u;
   for (int rho = tid; rho < kLutRecs; rho += kBlock) {
     const double lo = (32.0 * rho - 32.5) / (16.0 * kLutBuckets) - 1.0 - kLutSlack;
     const double hi = (32.0 * rho - 0.5) / (16.0 * kLutBuckets) - 1.0 + kLutSlack;
-    float A[2], B[2];
+    uint32_t bits[4];
     uint32_t code = 0;
+#pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int m = sm[c];
       int below = 0, inside = 0;
@@ -79,22 +80,20 @@ __global__ __launch_bounds__(kBlock) void lut_build_kernel(LutBatch b) {
         below += (M < lo) ? 1 : 0;
         inside += (M >= lo && M <= hi) ? 1 : 0;
       }
-      if (m == 0 || inside > 1 || (inside == 1 && six[c][below + 1] != six[c][below] + 1)) {
-        A[c] = qnan;
-        B[c] = qnan;
-      } else if (inside == 0) {
-        A[c] = sv[c][below];
-        B[c] = sv[c][below];
-        code |= (uint32_t)six[c][below] << (4 * c);
-      } else {
-        A[c] = sv[c][below];
-        B[c] = sv[c][below + 1];
-        code |= (uint32_t)six[c][below] << (4 * c);
-      }
+      // indices clamped so that every read stays inside the arrays whatever the branch
+      const int j0 = below < 15 ? below : 15;
+      const int j1 = below + 1 < 15 ? below + 1 : 15;
+      const bool single = m > 0 && inside == 0;
+      const bool pair = m > 0 && inside == 1 && six[c][j1] == six[c][j0] + 1;
+      const uint32_t a = __float_as_uint(sv[c][j0]);
+      const uint32_t b = __float_as_uint(sv[c][j1]);
+      bits[2 * c] = (single || pair) ? a : kNaNBits;
+      bits[2 * c + 1] = single ? a : (pair ? b : kNaNBits);
+      code |= (single || pair) ? ((uint32_t)six[c][j0] << (4 * c)) : 0u;
     }
-    float4* rec = reinterpret_cast<float4*>(out + (size_t)rho * kLutRecBytes);
-    rec[0] = make_float4(A[0], B[0], A[1], B[1]);
-    reinterpret_cast<uint4*>(rec)[1] = make_uint4(code, 0u, 0u, 0u);
+    uint4* rec = reinterpret_cast<uint4*>(out + (size_t)rho * kLutRecBytes);
+    rec[0] = make_uint4(bits[0], bits[1], bits[2], bits[3]);
+    rec[1] = make_uint4(code, 0u, 0u, 0u);
   }
 }
 
@@ -239,8 +238,8 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* _
       const int64_t h = base / S;
       jb.sel[h] = (uint8_t)sel;
       if (WITH_ERR) {
-        jb.err[2 * h] = (float)o.E0;
-        jb.err[2 * h + 1] = (float)o.E1;
+        jb.err[2 * h] = o.E0;
+        jb.err[2 * h + 1] = o.E1;
       }
     }
   }

@@ -105,7 +105,7 @@ struct AssignJob {
   const uint8_t* lut;       // kLutBytes, built from `tables`
   uint32_t* codes;          // [R * C / 8] dwords, 8 nibbles each
   uint8_t* sel;             // [R * C / S]
-  float* err;               // nullable, [R * C / S][2]
+  double* err;              // nullable, [R * C / S][2]
 };
 
 struct AssignBatch {

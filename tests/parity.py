@@ -73,12 +73,16 @@ def check_assign(W64, I64, tables, g, S, gpu_codes, gpu_sel, gpu_err=None, chunk
         d_o = (W64[r, c] - s[r, c] * Ts[T, q_o[r, c]]) ** 2
         ok = (d_g > d_o) & (d_g - d_o <= CODE_BAND * d_g)
         bad_code[r[~ok], c[~ok]] = True
-    assert not bad_code.any(), "code mismatch outside the band at %s" % (
-        np.argwhere(bad_code)[:5].tolist())
+        detail = ["(r=%d c=%d w=%r s=%r table=%d gpu q=%d T=%r d=%r | oracle q=%d T=%r d=%r)" % (
+            r[i], c[i], W64[r[i], c[i]], s[r[i], c[i]], T[i], q_g[r[i], c[i]],
+            Ts[T[i], q_g[r[i], c[i]]], d_g[i], q_o[r[i], c[i]], Ts[T[i], q_o[r[i], c[i]]], d_o[i])
+            for i in np.flatnonzero(~ok)[:6]]
+    assert not bad_code.any(), "%d code mismatches outside the band: %s" % (
+        int(bad_code.sum()), "\n".join(detail))
     if gpu_err is not None:
         e = np.asarray(gpu_err, dtype=np.float64).reshape(R, C // S, 2)
         for k, Eo in ((0, E0), (1, E1)):
-            tol = 4e-6 * np.maximum(Eo, 1e-30) + 1e-30
+            tol = 2e-6 * np.maximum(Eo, 1e-300) + 1e-300
             bad = np.abs(e[..., k] - Eo) > tol
             assert not bad.any(), "E%d mismatch at %s: gpu %r oracle %r" % (
                 k, np.argwhere(bad)[:5].tolist(), e[..., k][bad][:5], Eo[bad][:5])

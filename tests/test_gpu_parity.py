@@ -48,7 +48,7 @@ def _assign(W, I, tables, g, S, n, err=True):
     R, C = W.shape
     codes = torch.empty(R * C // 2, dtype=torch.uint8, device=DEV)
     sel = torch.empty(R * C // S, dtype=torch.uint8, device=DEV)
-    e = torch.empty(2 * (R * C // S), dtype=torch.float32, device=DEV) if err else None
+    e = torch.empty(2 * (R * C // S), dtype=torch.float64, device=DEV) if err else None
     L.aaac_assign(W, g, S, n, I, tables, codes, sel, e)
     torch.cuda.synchronize()
     return codes, sel, e
