@@ -103,7 +103,6 @@ def main():
               for xid, K in streams}
     ws_init = L.workspace(max(L.workspace_bytes(L.OP_INIT, R, C, g, S, n)
                               for R, C in zip(Rs, Cs)), dev)
-    ws_a = L.workspace(L.batch_workspace_bytes(L.OP_ASSIGN, Rs, Cs, g, S, n), dev)
     ws_r = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), dev)
     Is = [Iv[m.x_id] for m in mats]
     tabs = [torch.empty(2 * n, dtype=torch.float32, device=dev) for _ in mats]
@@ -132,14 +131,14 @@ def main():
         for it in range(iters):
             flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
             e0 = ev()
-            L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels, ws_a)
+            L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
             e1 = ev()
             L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, tabs, flags, ws_r)
             e2 = ev()
             marks["a"].append((e0, e1))
             marks["r"].append((e1, e2))
         loop1 = ev()
-        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels, ws_a)
+        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
         for i, W in enumerate(Ws):
             L.aaac_pack(W, g, S, n, sels[i], tabs[i], scales[i], bitmaps[i], tb16[i])
             L.aaac_dequant(codes[i], scales[i], bitmaps[i], tb16[i], Rs[i], Cs[i], g, S, n,

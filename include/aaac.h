@@ -105,12 +105,11 @@ aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, 
  * codes   [R * C / 2] bytes, two codes per byte, the low nibble holds the even column.
  * sel     [R * C / S] bytes, 0 = T0, 1 = T1, one per selection group in row-major order.
  * err     NULL, or fp64 [R * C / S][2] receiving (E_0, E_1) per selection group (for checking).
- * ws      aaac_workspace_bytes(AAAC_OP_ASSIGN, R, C, g, S, n) bytes (a lookup structure built from
- *         the tables).
+ * One kernel; it needs no workspace (the lookup structure lives in LDS).
  */
 aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
-                        double* err, void* ws, size_t ws_bytes, void* stream);
+                        double* err, void* stream);
 
 /*
  * Refine, AAAC summary §2 mechanism 4 (activation-weighted k-means). For every table c and entry j,
@@ -118,6 +117,9 @@ aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, i
  *   num = sum I_k s w_k,  den = sum I_k s^2,   T_c[j] <- num / den if den > 0, else unchanged.
  * num / den minimizes sum I (w - s t)^2 over t, i.e. it is the I s^2-weighted centroid of u.
  * Sums run in fp32 over at most 64 terms per partial and in fp64 beyond, in a fixed order.
+ * One kernel: the last workgroup to finish a matrix (an integer ticket in the workspace) adds the
+ * per-workgroup partials and writes tables_out. The ticket is reset at the end of every call; a call
+ * that did not complete (a device fault) leaves the workspace to be zero-filled again.
  *
  * codes, sel   as written by aaac_assign.
  * tables_in    fp32 [2][n];  tables_out fp32 [2][n], may equal tables_in.
@@ -159,8 +161,9 @@ aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uin
  * the seven linears of one decoder layer) in one launch each. Element i of every array describes
  * matrix i exactly as the single-matrix call does; the results are bitwise identical to calling
  * the single-matrix entry points one matrix at a time. refine updates tables[i] in place.
- * The host arrays are read during the call only. ws: aaac_batch_workspace_bytes(op, count, R, C,
- * g, S, n) bytes, same zero-fill rule as above.
+ * The host arrays are read during the call only. The refine workspace holds
+ * aaac_batch_workspace_bytes(AAAC_OP_REFINE, count, R, C, g, S, n) bytes, same zero-fill rule as
+ * above; assign needs none.
  */
 #define AAAC_MAX_BATCH 8
 
@@ -170,7 +173,7 @@ size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int
 aaac_status aaac_assign_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,
                               const float* const* tables, uint8_t* const* codes,
-                              uint8_t* const* sel, void* ws, size_t ws_bytes, void* stream);
+                              uint8_t* const* sel, void* stream);
 
 aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,

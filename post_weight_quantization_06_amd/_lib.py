@@ -69,7 +69,7 @@ def load(path: str = LIB_PATH):
         "aaac_init_quantiles": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_size,
                                         c_vp]),
         "aaac_assign": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
-                                c_vp, c_vp, c_size, c_vp]),
+                                c_vp, c_vp]),
         "aaac_refine": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
                                 c_vp, c_int, c_vp, c_size, c_vp]),
         "aaac_pack": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
@@ -77,7 +77,7 @@ def load(path: str = LIB_PATH):
         "aaac_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
                                  c_vp]),
         "aaac_assign_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
-                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp, c_size, c_vp]),
+                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp]),
         "aaac_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
                                       P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int, c_vp, c_size,
                                       c_vp]),
@@ -180,7 +180,7 @@ def aaac_init_quantiles(W: torch.Tensor, g: int, n: int, tables: torch.Tensor,
 
 def aaac_assign(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, tables: torch.Tensor,
                 codes: torch.Tensor, sel: torch.Tensor, err: Optional[torch.Tensor] = None,
-                ws: Optional[torch.Tensor] = None, stream=None):
+                stream=None):
     lib = load()
     R, C = W.shape
     _need(W, "W", torch.bfloat16)
@@ -190,10 +190,8 @@ def aaac_assign(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, tables
     _need(sel, "sel", torch.uint8, R * C // S)
     if err is not None:
         _need(err, "err", torch.float64, 2 * (R * C // S))
-    if ws is None:
-        ws = workspace(lib.aaac_workspace_bytes(OP_ASSIGN, R, C, g, S, n), W.device)
     st = lib.aaac_assign(_ptr(W), R, C, g, S, n, _ptr(I), _ptr(tables), _ptr(codes), _ptr(sel),
-                         _ptr(err), _ptr(ws), ws.numel(), _stream(stream))
+                         _ptr(err), _stream(stream))
     _check(st, "aaac_assign")
 
 
@@ -255,7 +253,7 @@ def _arr(ctype, values):
 def aaac_assign_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
                       Is: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
                       codes: Sequence[torch.Tensor], sels: Sequence[torch.Tensor],
-                      ws: Optional[torch.Tensor] = None, stream=None):
+                      stream=None):
     lib = load()
     k = len(Ws)
     Rs = [W.shape[0] for W in Ws]
@@ -266,13 +264,11 @@ def aaac_assign_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
         _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
         _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
-    if ws is None:
-        ws = workspace(batch_workspace_bytes(OP_ASSIGN, Rs, Cs, g, S, n), Ws[0].device)
     st = lib.aaac_assign_batch(
         k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
         _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in tables]),
         _arr(c_vp, [t.data_ptr() for t in codes]), _arr(c_vp, [t.data_ptr() for t in sels]),
-        _ptr(ws), ws.numel(), _stream(stream))
+        _stream(stream))
     _check(st, "aaac_assign_batch")
 
 

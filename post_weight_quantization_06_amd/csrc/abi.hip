@@ -72,7 +72,10 @@ aaac_status check_shape(int64_t R, int64_t C, int g, int S, int n, bool need_S, 
   return AAAC_OK;
 }
 
-size_t refine_ws_bytes(int count) { return (size_t)count * 64 * kMaxRefineBlocks * sizeof(double); }
+// refine workspace: job counters (256 bytes), then fp64 partials [count][64][kMaxRefineBlocks]
+size_t refine_ws_bytes(int count) {
+  return 256 + (size_t)count * 64 * kMaxRefineBlocks * sizeof(double);
+}
 
 aaac_status check_batch(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
                         int g, int S, int n, const char* who) {
@@ -90,8 +93,8 @@ aaac_status check_batch(int count, const uint16_t* const* W, const int64_t* R, c
 
 aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
                       int g, int S, int n, const float* const* I, const float* const* tables,
-                      uint8_t* const* codes, uint8_t* const* sel, double* err, void* ws,
-                      size_t ws_bytes, void* stream, const char* who) {
+                      uint8_t* const* codes, uint8_t* const* sel, double* err, void* stream,
+                      const char* who) {
   aaac_status st = check_batch(count, W, R, C, g, S, n, who);
   if (st != AAAC_OK) return st;
   if (!I || !tables || !codes || !sel) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
@@ -103,38 +106,25 @@ aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, con
                   "bytes)", who, i);
   }
   if (err && !aligned(err, 8)) return fail(AAAC_ERR_INVALID_ARG, "%s: err misaligned", who);
-  const size_t need = (size_t)count * kLutBytes;
-  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
-  if (ws_bytes < need)
-    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
-  LutBatch lb{};
   AssignBatch b{};
   b.njobs = count;
   b.g = g;
   b.S = S;
   b.n = n;
-  lb.n = n;
   int64_t tb = 0;
   for (int i = 0; i < count; ++i) {
-    uint8_t* lut = static_cast<uint8_t*>(ws) + (size_t)i * kLutBytes;
-    lb.tables[i] = tables[i];
-    lb.lut[i] = lut;
     AssignJob& j = b.job[i];
     j.geom = make_geom(R[i], C[i], tb);
     tb += j.geom.ntasks;
     j.W = W[i];
     j.I = I[i];
     j.tables = tables[i];
-    j.lut = lut;
     j.codes = reinterpret_cast<uint32_t*>(codes[i]);
     j.sel = sel[i];
     j.err = err;
   }
   b.total_tasks = tb;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = launch_lut_build(lb, count, s);
-  if (e != hipSuccess) return hip_status(e, who);
-  return hip_status(launch_assign(b, err != nullptr, s), who);
+  return hip_status(launch_assign(b, err != nullptr, static_cast<hipStream_t>(stream)), who);
 }
 
 aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
@@ -176,7 +166,27 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
   int64_t nb = refine_grid(tb);
   if (nb > kMaxRefineBlocks) nb = kMaxRefineBlocks;
   b.nblocks = (int32_t)nb;
-  b.partials = static_cast<double*>(ws);
+  // workgroup b owns tasks [task_lo(b), task_lo(b + 1)); record which workgroups meet each job
+  auto owner = [&](int64_t t) {
+    int64_t lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (task_lo(mid, tb, nb) <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  int32_t slots = 1;
+  for (int i = 0; i < count; ++i) {
+    RefineJob& j = b.job[i];
+    const int64_t w0 = owner(j.geom.task_begin);
+    const int64_t w1 = owner(j.geom.task_begin + j.geom.ntasks - 1);
+    j.wg_lo = (int32_t)w0;
+    j.wg_count = (int32_t)(w1 - w0 + 1);
+    if (j.wg_count > slots) slots = j.wg_count;
+  }
+  b.slots = slots;
+  b.counters = static_cast<uint32_t*>(ws);
+  b.partials = reinterpret_cast<double*>(static_cast<char*>(ws) + 256);
   return hip_status(launch_refine(b, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -208,8 +218,7 @@ size_t aaac_workspace_bytes(int op, int64_t R, int64_t C, int g, int S, int n) {
       if (check_shape(R, C, g, 8, n, false, "aaac_workspace_bytes") != AAAC_OK) return 0;
       return init_workspace_bytes(R, C, n);
     case AAAC_OP_ASSIGN:
-      if (check_shape(R, C, g, S, n, true, "aaac_workspace_bytes") != AAAC_OK) return 0;
-      return (size_t)kLutBytes;
+      return 0;
     case AAAC_OP_REFINE:
       if (check_shape(R, C, g, S, n, true, "aaac_workspace_bytes") != AAAC_OK) return 0;
       return refine_ws_bytes(1);
@@ -223,7 +232,6 @@ size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int
   if (count < 1 || count > AAAC_MAX_BATCH || !R || !C) return 0;
   for (int i = 0; i < count; ++i)
     if (check_shape(R[i], C[i], g, S, n, true, "aaac_batch_workspace_bytes") != AAAC_OK) return 0;
-  if (op == AAAC_OP_ASSIGN) return (size_t)count * kLutBytes;
   if (op == AAAC_OP_REFINE) return refine_ws_bytes(count);
   return 0;
 }
@@ -264,16 +272,15 @@ aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, 
 
 aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
-                        double* err, void* ws, size_t ws_bytes, void* stream) {
-  return do_assign(1, &W, &R, &C, g, S, n, &I, &tables, &codes, &sel, err, ws, ws_bytes, stream,
-                   "aaac_assign");
+                        double* err, void* stream) {
+  return do_assign(1, &W, &R, &C, g, S, n, &I, &tables, &codes, &sel, err, stream, "aaac_assign");
 }
 
 aaac_status aaac_assign_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,
                               const float* const* tables, uint8_t* const* codes,
-                              uint8_t* const* sel, void* ws, size_t ws_bytes, void* stream) {
-  return do_assign(count, W, R, C, g, S, n, I, tables, codes, sel, nullptr, ws, ws_bytes, stream,
+                              uint8_t* const* sel, void* stream) {
+  return do_assign(count, W, R, C, g, S, n, I, tables, codes, sel, nullptr, stream,
                    "aaac_assign_batch");
 }
 

@@ -1,4 +1,4 @@
-// Assign step (AAAC summary §2 mechanisms 2 and 4) and the nearest-entry lookup structure it uses.
+// Assign step (AAAC summary §2 mechanisms 2 and 4).
 //
 // For every weight w of a scale group with scale s = max|w| and each table c, the nearest entry
 // q_c minimizes |u - T_c[j]| with u = w / s, ties to the lower index. Because s > 0 this is the
@@ -13,98 +13,109 @@
 // residual magnitude: fp32 over four weights, then fp64. The selection is D < 0 (ties keep T0).
 // Its rounding error is below 8 * 2^-24 (E_0 + E_1), so a selection can only differ from the exact
 // one when |E_1 - E_0| < 1e-6 max(E_0, E_1).
+//
+// Work split: workgroup b owns a contiguous range of tasks (kRowsPerTask rows of one 512-column
+// slab of one matrix); each of its waves issues the loads of all its rows of a task before it
+// processes the first one, and builds the lookup table in LDS whenever it moves to another matrix.
 #include "common.h"
 
 namespace aaac {
 
-// ------------------------------------------------------------------------------------------------
-// Lookup structure: one workgroup per table pair.
-// ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void lut_build_kernel(LutBatch b) {
-  const float* T = b.tables[blockIdx.x];
-  uint8_t* out = b.lut[blockIdx.x];
-  const int n = b.n;
-  __shared__ float sv[2][16];
-  __shared__ int six[2][16];
-  __shared__ double smid[2][16];
-  __shared__ int sm[2];
+namespace {
+
+struct LutScratch {
+  float raw[2][16];
+  int first[2][16];
+  float sv[2][16];          // distinct values, ascending
+  int six[2][16];           // lowest index holding each distinct value
+  int mlo[2][16];           // midpoint i lies in record rho iff mlo[i] <= rho <= mhi[i]
+  int mhi[2][16];           // and lies below record rho iff mhi[i] < rho
+  int m[2];                 // distinct values (0: the table has a non-finite entry)
+};
+
+constexpr uint32_t kNaNBits = 0x7fc00000u;
+
+// Build the lookup records for tables T (fp32 [2][n], global) into `lut` (LDS) with all threads of
+// the block. Also copies the raw tables to `tab` for the exact scan. Must be called by every thread;
+// ends with a barrier.
+__device__ void build_lut(const float* __restrict__ T, int n, uint8_t* lut, LutScratch& ls,
+                          float (*tab)[16]) {
   const int tid = threadIdx.x;
-  if (tid < 2) {
-    const int c = tid;
-    float v[16];
-    int ix[16];
-    bool finite = true;
-    for (int j = 0; j < n; ++j) {
-      v[j] = T[c * n + j];
-      ix[j] = j;
-      finite = finite && isfinite(v[j]);
-    }
-    // insertion sort by (value, index); equal values keep index order
-    for (int i = 1; i < n; ++i) {
-      float x = v[i];
-      int xi = ix[i];
-      int k = i - 1;
-      while (k >= 0 && v[k] > x) {
-        v[k + 1] = v[k];
-        ix[k + 1] = ix[k];
-        --k;
-      }
-      v[k + 1] = x;
-      ix[k + 1] = xi;
-    }
-    // distinct values, each with the lowest index that holds it (the argmin tie rule)
-    int m = 0;
-    for (int i = 0; i < n; ++i) {
-      if (m == 0 || v[i] != sv[c][m - 1]) {
-        sv[c][m] = v[i];
-        six[c][m] = ix[i];
-        ++m;
-      }
-    }
-    for (int i = 0; i + 1 < m; ++i) smid[c][i] = 0.5 * ((double)sv[c][i] + (double)sv[c][i + 1]);
-    sm[c] = finite ? m : 0;
+  if (tid < 32) {
+    const int c = tid >> 4, j = tid & 15;
+    const float x = j < n ? T[c * n + j] : 0.0f;
+    ls.raw[c][j] = x;
+    tab[c][j] = x;
   }
   __syncthreads();
-  constexpr uint32_t kNaNBits = 0x7fc00000u;
+  if (tid < 32) {
+    const int c = tid >> 4, j = tid & 15;
+    const float x = ls.raw[c][j];
+    bool first = j < n;
+    for (int k = 0; k < j; ++k) first = first && !(ls.raw[c][k] == x);
+    ls.first[c][j] = first ? 1 : 0;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    const int c = tid >> 4, j = tid & 15;
+    const float x = ls.raw[c][j];
+    int rank = 0, m = 0;
+    bool finite = true;
+    for (int k = 0; k < n; ++k) {
+      const float y = ls.raw[c][k];
+      finite = finite && isfinite(y);
+      if (ls.first[c][k]) {
+        ++m;
+        if (y < x) ++rank;
+      }
+    }
+    if (ls.first[c][j] && finite) {
+      ls.sv[c][rank] = x;
+      ls.six[c][rank] = j;
+    }
+    if (j == 0) ls.m[c] = finite ? m : 0;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    const int c = tid >> 4, i = tid & 15;
+    if (i + 1 < ls.m[c]) {
+      const double M = 0.5 * ((double)ls.sv[c][i] + (double)ls.sv[c][i + 1]);
+      const double hi = floor(((M + 1.0 + kLutSlack) * (16.0 * kLutBuckets) + 32.5) / 32.0);
+      const double lo = ceil(((M + 1.0 - kLutSlack) * (16.0 * kLutBuckets) + 0.5) / 32.0);
+      ls.mhi[c][i] = (int)fmin(fmax(hi, -1.0), 4096.0);
+      ls.mlo[c][i] = (int)fmin(fmax(lo, -1.0), 4096.0);
+    }
+  }
+  __syncthreads();
   for (int rho = tid; rho < kLutRecs; rho += kBlock) {
-    const double lo = (32.0 * rho - 32.5) / (16.0 * kLutBuckets) - 1.0 - kLutSlack;
-    const double hi = (32.0 * rho - 0.5) / (16.0 * kLutBuckets) - 1.0 + kLutSlack;
     uint32_t bits[4];
     uint32_t code = 0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int m = sm[c];
+      const int m = ls.m[c];
       int below = 0, inside = 0;
       for (int i = 0; i + 1 < m; ++i) {
-        const double M = smid[c][i];
-        below += (M < lo) ? 1 : 0;
-        inside += (M >= lo && M <= hi) ? 1 : 0;
+        below += (ls.mhi[c][i] < rho) ? 1 : 0;
+        inside += (ls.mlo[c][i] <= rho && rho <= ls.mhi[c][i]) ? 1 : 0;
       }
-      // indices clamped so that every read stays inside the arrays whatever the branch
+      // clamped indices keep every read inside the arrays whatever the branch
       const int j0 = below < 15 ? below : 15;
       const int j1 = below + 1 < 15 ? below + 1 : 15;
       const bool single = m > 0 && inside == 0;
-      const bool pair = m > 0 && inside == 1 && six[c][j1] == six[c][j0] + 1;
-      const uint32_t a = __float_as_uint(sv[c][j0]);
-      const uint32_t b = __float_as_uint(sv[c][j1]);
+      const bool pair = m > 0 && inside == 1 && ls.six[c][j1] == ls.six[c][j0] + 1;
+      const uint32_t a = __float_as_uint(ls.sv[c][j0]);
+      const uint32_t bb = __float_as_uint(ls.sv[c][j1]);
       bits[2 * c] = (single || pair) ? a : kNaNBits;
-      bits[2 * c + 1] = single ? a : (pair ? b : kNaNBits);
-      code |= (single || pair) ? ((uint32_t)six[c][j0] << (4 * c)) : 0u;
+      bits[2 * c + 1] = single ? a : (pair ? bb : kNaNBits);
+      code |= (single || pair) ? ((uint32_t)ls.six[c][j0] << (4 * c)) : 0u;
     }
-    uint4* rec = reinterpret_cast<uint4*>(out + (size_t)rho * kLutRecBytes);
+    uint4* rec = reinterpret_cast<uint4*>(lut + (size_t)rho * kLutRecBytes);
     rec[0] = make_uint4(bits[0], bits[1], bits[2], bits[3]);
     rec[1] = make_uint4(code, 0u, 0u, 0u);
   }
+  __syncthreads();
 }
 
-hipError_t launch_lut_build(const LutBatch& b, int njobs, hipStream_t stream) {
-  hipLaunchKernelGGL(lut_build_kernel, dim3(njobs), dim3(kBlock), 0, stream, b);
-  return hipGetLastError();
-}
-
-// ------------------------------------------------------------------------------------------------
-// Assign kernel.
-// ------------------------------------------------------------------------------------------------
 struct RowOut {
   double D;         // E_1 - E_0 of the lane's selection group (after the butterfly)
   double E0, E1;    // only with err output
@@ -152,11 +163,9 @@ __device__ __forceinline__ void slow_lane(const float (&w)[8], uint32_t amax, co
 
 template <bool WITH_ERR>
 __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* __restrict__ lut,
-                                           const float (*tab)[16], int n, int g8, int s8, int S,
-                                           int64_t r, int c0, bool active, const float (&Ik)[8]) {
-  const int64_t base = r * (int64_t)jb.geom.C + c0;
-  uint4 v = make_uint4(0u, 0u, 0u, 0u);
-  if (active) v = *reinterpret_cast<const uint4*>(jb.W + base);
+                                           const float (*tab)[16], int n, int g8, int s8,
+                                           int log2S, int64_t base, bool active, const uint4& v,
+                                           const float (&Ik)[8]) {
   const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
   const float s = __uint_as_float(amax << 16);
   float w[8];
@@ -234,8 +243,8 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* _
   const uint32_t packed = __builtin_amdgcn_perm(q, p, 0x06040200u);
   if (active) {
     jb.codes[base >> 3] = packed;
-    if (((c0 >> 3) & (s8 - 1)) == 0) {
-      const int64_t h = base / S;
+    if (((base >> 3) & (s8 - 1)) == 0) {
+      const int64_t h = base >> log2S;
       jb.sel[h] = (uint8_t)sel;
       if (WITH_ERR) {
         jb.err[2 * h] = o.E0;
@@ -245,27 +254,27 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* _
   }
 }
 
+}  // namespace
+
 template <bool WITH_ERR>
 __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
   __shared__ __align__(16) uint8_t lut[kLutBytes];
+  __shared__ LutScratch ls;
   __shared__ float tab[2][16];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int g8 = b.g / kPerLane, s8 = b.S / kPerLane, n = b.n, S = b.S;
+  const int g8 = b.g / kPerLane, s8 = b.S / kPerLane, n = b.n;
+  const int log2S = 31 - __builtin_clz((unsigned)b.S);
+  const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
   int cur = -1;
-  for (int64_t task = blockIdx.x; task < b.total_tasks; task += gridDim.x) {
+  for (int64_t task = task_lo(blockIdx.x, b.total_tasks, gridDim.x); task < t_end; ++task) {
     int j = 0;
     while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
     const AssignJob& jb = b.job[j];
     if (j != cur) {
       __syncthreads();
-      const uint4* src = reinterpret_cast<const uint4*>(jb.lut);
-      uint4* dst = reinterpret_cast<uint4*>(lut);
-#pragma unroll
-      for (int i = 0; i < kLutBytes / 16 / kBlock; ++i) dst[tid + i * kBlock] = src[tid + i * kBlock];
-      if (tid < 2 * n) tab[tid / n][tid % n] = jb.tables[tid];
-      __syncthreads();
+      build_lut(jb.tables, n, lut, ls, tab);
       cur = j;
     }
     const int64_t local = task - jb.geom.task_begin;
@@ -273,6 +282,16 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
     const int slab = (int)(local - rb * jb.geom.nslab);
     const int c0 = slab * kSlab + lane * kPerLane;
     const bool active = c0 < jb.geom.C;
+    const int64_t R = jb.geom.R, C = jb.geom.C;
+    const int64_t r0 = rb * kRowsPerTask + wave;
+    // issue the loads of every row of this task first
+    uint4 v[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+      v[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (active && r < R) v[i] = *reinterpret_cast<const uint4*>(jb.W + r * C + c0);
+    }
     float Ik[8];
     if (active) {
       const float4 i0 = *reinterpret_cast<const float4*>(jb.I + c0);
@@ -283,16 +302,25 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) Ik[k] = 0.0f;
     }
+#pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-      const int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
-      if (r >= jb.geom.R) break;
-      assign_row<WITH_ERR>(jb, lut, tab, n, g8, s8, S, r, c0, active, Ik);
+      const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+      if (r < R) assign_row<WITH_ERR>(jb, lut, tab, n, g8, s8, log2S, r * C + c0, active, v[i], Ik);
     }
   }
 }
 
 hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream) {
-  const int64_t want = (int64_t)device_cu_count() * 4;
+  static int per_cu[2] = {0, 0};
+  int& occ = per_cu[with_err ? 1 : 0];
+  if (occ <= 0) {
+    int blocks = 0;
+    const hipError_t e = with_err
+        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, assign_kernel<true>, kBlock, 0)
+        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, assign_kernel<false>, kBlock, 0);
+    occ = (e == hipSuccess && blocks > 0) ? blocks : 2;
+  }
+  const int64_t want = (int64_t)device_cu_count() * occ;
   const int grid = (int)(b.total_tasks < want ? b.total_tasks : want);
   if (grid <= 0) return hipSuccess;
   if (with_err)

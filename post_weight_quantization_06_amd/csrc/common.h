@@ -60,14 +60,51 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
-// Butterfly reductions over aligned blocks of `lanes` lanes (a power of two <= 64).
+// Butterfly reductions over aligned blocks of `lanes` lanes (a power of two <= 64). Within a row
+// of 16 lanes they use DPP: quad_perm [1,0,3,2] and [2,3,0,1] exchange partners at distance 1 and 2,
+// row_half_mirror and row_mirror bring in the other quad and the other half-row, whose lanes by then
+// all hold the same partial. Larger blocks finish with cross-row shuffles. Every lane of a block
+// performs the same additions on the same operands (addition commutes), so all lanes end with
+// bitwise identical totals.
+constexpr int kDppQuadXor1 = 0xB1;
+constexpr int kDppQuadXor2 = 0x4E;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = dpp_u32<CTRL>((uint32_t)b);
+  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, int lanes) {
-  for (int m = 1; m < lanes; m <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m));
+  if (lanes >= 2) v = max(v, dpp_u32<kDppQuadXor1>(v));
+  if (lanes >= 4) v = max(v, dpp_u32<kDppQuadXor2>(v));
+  if (lanes >= 8) v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  if (lanes >= 16) v = max(v, dpp_u32<kDppRowMirror>(v));
+  if (lanes >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  if (lanes >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
   return v;
 }
 __device__ __forceinline__ double block_sum_f64(double v, int lanes) {
-  for (int m = 1; m < lanes; m <<= 1) v += __shfl_xor(v, m);
+  if (lanes >= 2) v += dpp_f64<kDppQuadXor1>(v);
+  if (lanes >= 4) v += dpp_f64<kDppQuadXor2>(v);
+  if (lanes >= 8) v += dpp_f64<kDppRowHalfMirror>(v);
+  if (lanes >= 16) v += dpp_f64<kDppRowMirror>(v);
+  if (lanes >= 32) v += __shfl_xor(v, 16);
+  if (lanes >= 64) v += __shfl_xor(v, 32);
   return v;
+}
+
+// Contiguous share of `total` tasks for workgroup b of G: [task_lo(b), task_lo(b + 1)).
+__host__ __device__ __forceinline__ int64_t task_lo(int64_t b, int64_t total, int64_t G) {
+  return (b * total) / G;
 }
 
 // Largest |w| of the 8 bf16 of one lane, as the bf16 magnitude bit pattern (order-preserving).
@@ -102,7 +139,6 @@ struct AssignJob {
   const uint16_t* W;
   const float* I;
   const float* tables;      // fp32 [2][n]
-  const uint8_t* lut;       // kLutBytes, built from `tables`
   uint32_t* codes;          // [R * C / 8] dwords, 8 nibbles each
   uint8_t* sel;             // [R * C / S]
   double* err;              // nullable, [R * C / S][2]
@@ -123,6 +159,8 @@ struct RefineJob {
   const uint8_t* sel;
   const float* tables_in;
   float* tables_out;
+  int32_t wg_lo;            // first workgroup whose task range meets this job
+  int32_t wg_count;         // number of such workgroups
 };
 
 struct RefineBatch {
@@ -130,15 +168,11 @@ struct RefineBatch {
   int32_t njobs;
   int32_t g, S, n;
   int64_t total_tasks;
-  double* partials;         // [njobs][64][nblocks]
-  int32_t nblocks;          // grid size of the accumulation kernel
+  double* partials;         // [njobs][64][slots]
+  uint32_t* counters;       // [njobs], zero between calls
+  int32_t nblocks;          // grid size
+  int32_t slots;            // largest wg_count of the batch
   int32_t flags;
-};
-
-struct LutBatch {
-  const float* tables[kMaxJobs];
-  uint8_t* lut[kMaxJobs];
-  int32_t n;
 };
 
 // ------------------------------------------------------------------------------------------------
@@ -146,7 +180,6 @@ struct LutBatch {
 // ------------------------------------------------------------------------------------------------
 int device_cu_count();
 
-hipError_t launch_lut_build(const LutBatch& b, int njobs, hipStream_t stream);
 hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream);
 hipError_t launch_refine(RefineBatch& b, hipStream_t stream);
 int refine_grid(int64_t total_tasks);

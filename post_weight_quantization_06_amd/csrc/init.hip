@@ -8,7 +8,9 @@
 // that holds its residual rank; passes 2-4 histogram the next byte of the keys whose prefix is one
 // of the (at most 2n) active prefixes. Integer counts make every step exact and order-free.
 //
-// Workspace: keys u32 [N] | hist u64 [32][256] | state (see InitState).
+// Workspace: hist u64 [32][256] | state (see InitState) | keys u32 [N]. The histogram and the state
+// sit at fixed offsets, so a workspace reused for a matrix of another size still starts from the
+// zero histogram the previous call left behind.
 #include "common.h"
 
 namespace aaac {
@@ -34,14 +36,14 @@ struct InitLayout {
   InitState* state;
 };
 
-InitLayout layout(void* ws, int64_t N) {
+InitLayout layout(void* ws) {
   char* p = static_cast<char*>(ws);
   InitLayout l;
-  l.keys = reinterpret_cast<uint32_t*>(p);
-  p += align256((size_t)N * 4);
   l.hist = reinterpret_cast<unsigned long long*>(p);
   p += align256(sizeof(unsigned long long) * kTargets * kDigits);
   l.state = reinterpret_cast<InitState*>(p);
+  p += align256(sizeof(InitState));
+  l.keys = reinterpret_cast<uint32_t*>(p);
   return l;
 }
 
@@ -213,7 +215,7 @@ size_t init_workspace_bytes(int64_t R, int64_t C, int n) {
 hipError_t launch_init(const uint16_t* W, int64_t R, int64_t C, int g, int n, float* tables,
                        void* ws, hipStream_t stream) {
   const int64_t N = R * C;
-  InitLayout l = layout(ws, N);
+  InitLayout l = layout(ws);
   const MatrixGeom geom = make_geom(R, C, 0);
   const int64_t want = (int64_t)device_cu_count() * 4;
   const int grid1 = (int)(geom.ntasks < want ? geom.ntasks : want);

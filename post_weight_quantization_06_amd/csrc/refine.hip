@@ -4,12 +4,15 @@
 // the weights whose selection group chose c and whose code is j; the new entry is num / den (the
 // minimizer of sum I (w - s t)^2), or the old entry if the cell is empty.
 //
-// Accumulation: every thread owns a private column of 64 fp32 bins in LDS (32 cells x {num, den},
-// laid out [bin][thread] so a wave's adds hit 64 different banks) and adds at most 64 terms into a
-// bin before it moves the bin into fp64 registers. Workgroups then reduce their 256 threads in a
-// fixed order and write one fp64 partial per (cell, workgroup); a second kernel adds the partials of
-// each cell in a fixed order and divides. No float atomics touch global memory and every order is
-// fixed, so results are bitwise reproducible.
+// Accumulation: each term is exact in fp64 (s w and s^2 have at most 16 significant bits, times
+// the 24-bit I), and every thread adds its terms into a private column of 64 fp64 bins in LDS
+// (32 cells x {num, den}, laid out [bin][thread]) with ds_add_f64. When a workgroup leaves a matrix
+// it reduces its 256 columns in a fixed order and writes one fp64 partial per (bin, workgroup); the
+// last workgroup to finish that matrix (an integer ticket) adds the partials in workgroup order and
+// divides. Every order is fixed, so results are bitwise reproducible.
+//
+// The bins take 128 KB, one workgroup per CU; to keep enough bytes in flight each wave loads the
+// rows of its next task before it accumulates the current one.
 #include "common.h"
 
 namespace aaac {
@@ -17,152 +20,87 @@ namespace aaac {
 namespace {
 
 constexpr int kCells = 32;   // 2 tables x 16 entries
-constexpr int kVals = 64;    // num and den per cell
+constexpr int kVals = 64;    // num (bins 0-31) and den (bins 32-63)
 
 struct RefineShared {
-  float num[kCells][kBlock];
-  float den[kCells][kBlock];
+  double bins[kVals][kBlock];
 };
 
-// Fixed-order reduction of acc[64] over the 256 threads of the block; thread t < 32 of half h
-// returns value 32 h + t through `out`. Uses the (zero) bins as scratch and zeroes them again.
-__device__ void block_reduce_acc(RefineShared& sh, double (&acc)[kVals], double* out_lo,
-                                 double* out_hi) {
-  const int tid = threadIdx.x;
-  double* scratch = reinterpret_cast<double*>(&sh);   // 64 KB = 32 x 256 doubles
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    __syncthreads();
-#pragma unroll
-    for (int v = 0; v < 32; ++v) scratch[v * kBlock + tid] = acc[32 * h + v];
-    __syncthreads();
-    const int v = tid & 31, part = tid >> 5;
-    double s = 0.0;
-    for (int i = 0; i < 32; ++i) {
-      const int col = part * 32 + ((i + v) & 31);
-      s += scratch[v * kBlock + col];
-    }
-    __syncthreads();
-    scratch[v * 8 + part] = s;
-    __syncthreads();
-    if (tid < 32) {
-      double t = 0.0;
-      for (int p = 0; p < 8; ++p) t += scratch[tid * 8 + p];
-      if (h == 0) *out_lo = t; else *out_hi = t;
-    }
-  }
-  __syncthreads();
-  for (int k = 0; k < kCells; ++k) {
-    sh.num[k][tid] = 0.0f;
-    sh.den[k][tid] = 0.0f;
-  }
-  __syncthreads();
-}
+struct TaskRows {
+  uint4 v[kRowsPerWave];
+  uint32_t cw[kRowsPerWave];
+  uint32_t sb[kRowsPerWave];
+  float I[kPerLane];
+  int64_t r0;
+  int job;
+  int c0;
+  bool active;
+};
 
-__device__ __forceinline__ void flush_bins(RefineShared& sh, double (&acc)[kVals]) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void load_task(const RefineBatch& b, int64_t task, int log2S,
+                                          TaskRows& t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int j = 0;
+  while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
+  const RefineJob& jb = b.job[j];
+  const int64_t local = task - jb.geom.task_begin;
+  const int64_t rb = local / jb.geom.nslab;
+  const int slab = (int)(local - rb * jb.geom.nslab);
+  t.job = j;
+  t.c0 = slab * kSlab + lane * kPerLane;
+  t.active = t.c0 < jb.geom.C;
+  t.r0 = rb * kRowsPerTask + wave;
+  const int64_t R = jb.geom.R, C = jb.geom.C;
 #pragma unroll
-  for (int k = 0; k < kCells; ++k) {
-    acc[k] += (double)sh.num[k][tid];
-    acc[kCells + k] += (double)sh.den[k][tid];
-    sh.num[k][tid] = 0.0f;
-    sh.den[k][tid] = 0.0f;
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
+    t.v[i] = make_uint4(0u, 0u, 0u, 0u);
+    t.cw[i] = 0;
+    t.sb[i] = 0;
+    if (t.active && r < R) {
+      const int64_t base = r * C + t.c0;
+      t.v[i] = *reinterpret_cast<const uint4*>(jb.W + base);
+      t.cw[i] = jb.codes[base >> 3];
+      t.sb[i] = jb.sel[base >> log2S];
+    }
   }
-}
-
-__device__ __forceinline__ void write_partials(const RefineBatch& b, int job, double lo,
-                                               double hi) {
-  // thread t < 32 holds values t (num of cell t) and 32 + t (den of cell t)
-  const int tid = threadIdx.x;
-  if (tid < 32) {
-    double* base = b.partials + (size_t)job * kVals * b.nblocks;
-    base[(size_t)tid * b.nblocks + blockIdx.x] = lo;
-    base[(size_t)(32 + tid) * b.nblocks + blockIdx.x] = hi;
+  if (t.active) {
+    const float4 i0 = *reinterpret_cast<const float4*>(jb.I + t.c0);
+    const float4 i1 = *reinterpret_cast<const float4*>(jb.I + t.c0 + 4);
+    t.I[0] = i0.x; t.I[1] = i0.y; t.I[2] = i0.z; t.I[3] = i0.w;
+    t.I[4] = i1.x; t.I[5] = i1.y; t.I[6] = i1.z; t.I[7] = i1.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t.I[k] = 0.0f;
   }
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kBlock, 2) void refine_accum_kernel(RefineBatch b) {
-  __shared__ RefineShared sh;
+__device__ __forceinline__ void accumulate_task(const RefineBatch& b, const TaskRows& t, int g8,
+                                                RefineShared& sh) {
   const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int g8 = b.g / kPerLane, S = b.S;
-  for (int k = 0; k < kCells; ++k) {
-    sh.num[k][tid] = 0.0f;
-    sh.den[k][tid] = 0.0f;
-  }
-  double acc[kVals];
+  const int64_t R = b.job[t.job].geom.R;
+  double Id[8];
 #pragma unroll
-  for (int k = 0; k < kVals; ++k) acc[k] = 0.0;
-  int cur = -1;
-  uint32_t touched = 0;
-  for (int64_t task = blockIdx.x; task < b.total_tasks; task += gridDim.x) {
-    int j = 0;
-    while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
-    if (j != cur) {
-      if (cur >= 0) {
-        double lo = 0.0, hi = 0.0;
-        block_reduce_acc(sh, acc, &lo, &hi);
-        write_partials(b, cur, lo, hi);
+  for (int k = 0; k < 8; ++k) Id[k] = (double)t.I[k];
 #pragma unroll
-        for (int k = 0; k < kVals; ++k) acc[k] = 0.0;
-      }
-      cur = j;
-      touched |= 1u << j;
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
+    if (r >= R) continue;
+    const uint32_t amax = block_max_u32(lane_absmax_bits(t.v[i]), g8);
+    if (!t.active) continue;
+    const float s = __uint_as_float(amax << 16);
+    const double s2 = (double)(s * s);          // exact: s has 8 significant bits
+    float w[8];
+    unpack8(t.v[i], w);
+    const int cbase = t.sb[i] ? 16 : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int cell = cbase + ((t.cw[i] >> (4 * k)) & 15u);
+      atomicAdd(&sh.bins[cell][tid], Id[k] * (double)(s * w[k]));   // s w exact in fp32
+      atomicAdd(&sh.bins[kCells + cell][tid], Id[k] * s2);
     }
-    const RefineJob& jb = b.job[j];
-    const int64_t local = task - jb.geom.task_begin;
-    const int64_t rb = local / jb.geom.nslab;
-    const int slab = (int)(local - rb * jb.geom.nslab);
-    const int c0 = slab * kSlab + lane * kPerLane;
-    const bool active = c0 < jb.geom.C;
-    float Ik[8];
-    if (active) {
-      const float4 i0 = *reinterpret_cast<const float4*>(jb.I + c0);
-      const float4 i1 = *reinterpret_cast<const float4*>(jb.I + c0 + 4);
-      Ik[0] = i0.x; Ik[1] = i0.y; Ik[2] = i0.z; Ik[3] = i0.w;
-      Ik[4] = i1.x; Ik[5] = i1.y; Ik[6] = i1.z; Ik[7] = i1.w;
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) Ik[k] = 0.0f;
-    }
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
-      if (r >= jb.geom.R) break;
-      const int64_t base = r * (int64_t)jb.geom.C + c0;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      uint32_t cw = 0, sb = 0;
-      if (active) {
-        v = *reinterpret_cast<const uint4*>(jb.W + base);
-        cw = jb.codes[base >> 3];
-        sb = jb.sel[base / S];
-      }
-      const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
-      const float s = __uint_as_float(amax << 16);
-      if (active) {
-        float w[8];
-        unpack8(v, w);
-        const int cbase = sb ? 16 : 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int cell = cbase + ((cw >> (4 * k)) & 15u);
-          const float t = Ik[k] * s;
-          atomicAdd(&sh.num[cell][tid], t * w[k]);
-          atomicAdd(&sh.den[cell][tid], t * s);
-        }
-      }
-    }
-    flush_bins(sh, acc);
   }
-  if (cur >= 0) {
-    double lo = 0.0, hi = 0.0;
-    block_reduce_acc(sh, acc, &lo, &hi);
-    write_partials(b, cur, lo, hi);
-  }
-  for (int j = 0; j < b.njobs; ++j)
-    if (!(touched & (1u << j))) write_partials(b, j, 0.0, 0.0);
 }
 
 // Round a finite fp64 value to bf16 (ties to even) directly, without an intermediate fp32
@@ -178,48 +116,109 @@ __device__ __forceinline__ float f64_to_bf16_value(double x) {
   return (float)copysign(r, x);
 }
 
-__global__ __launch_bounds__(kBlock) void refine_finalize_kernel(RefineBatch b) {
-  const int j = blockIdx.x / kCells, cell = blockIdx.x % kCells;
-  const int c = cell >> 4, idx = cell & 15;
-  if (idx >= b.n) return;
+// Publish this workgroup's partial of job j (and zero the bins); the last workgroup of the job adds
+// all partials and writes the tables.
+__device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
   const int tid = threadIdx.x;
-  const double* pn = b.partials + ((size_t)j * kVals + cell) * b.nblocks;
-  const double* pd = b.partials + ((size_t)j * kVals + kCells + cell) * b.nblocks;
-  double sn = 0.0, sd = 0.0;
-  for (int i = tid; i < b.nblocks; i += kBlock) {
-    sn += pn[i];
-    sd += pd[i];
-  }
-  __shared__ double rn[kBlock], rd[kBlock];
-  rn[tid] = sn;
-  rd[tid] = sd;
+  const RefineJob& jb = b.job[j];
+  __shared__ double part4[4][kVals];
+  __shared__ uint32_t ticket;
   __syncthreads();
-  for (int w = kBlock / 2; w > 0; w >>= 1) {
-    if (tid < w) {
-      rn[tid] += rn[tid + w];
-      rd[tid] += rd[tid + w];
+  {
+    // value v = tid & 63 over the 64 columns of quarter q = tid >> 6, in a fixed (rotated) order
+    const int v = tid & 63, q = tid >> 6;
+    double s = 0.0;
+    for (int i = 0; i < 64; ++i) s += sh.bins[v][q * 64 + ((i + v) & 63)];
+    part4[q][v] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kVals; ++k) sh.bins[k][tid] = 0.0;
+  double* part = b.partials + (size_t)j * kVals * b.slots;
+  const int slot = (int)blockIdx.x - jb.wg_lo;
+  if (tid < kVals) {
+    const double tot = ((part4[0][tid] + part4[1][tid]) + part4[2][tid]) + part4[3][tid];
+    part[(size_t)tid * b.slots + slot] = tot;
+    __threadfence();
+  }
+  __syncthreads();
+  if (tid == 0) ticket = atomicAdd(b.counters + j, 1u);
+  __syncthreads();
+  if (ticket != (uint32_t)(jb.wg_count - 1)) return;
+  // last workgroup of this job: every partial is visible after the fence
+  __threadfence();
+  {
+    const int v = tid & 63, q = tid >> 6;
+    const int cnt = jb.wg_count;
+    const int s0 = (q * cnt) / 4, s1 = ((q + 1) * cnt) / 4;
+    double s = 0.0;
+    for (int i = s0; i < s1; ++i) s += part[(size_t)v * b.slots + i];
+    part4[q][v] = s;
+  }
+  __syncthreads();
+  if (tid < kCells) {
+    const int c = tid >> 4, idx = tid & 15;
+    const double nsum = ((part4[0][tid] + part4[1][tid]) + part4[2][tid]) + part4[3][tid];
+    const double dsum = ((part4[0][kCells + tid] + part4[1][kCells + tid]) + part4[2][kCells + tid]) +
+                        part4[3][kCells + tid];
+    if (idx < b.n) {
+      const float old = jb.tables_in[c * b.n + idx];
+      const double val = dsum > 0.0 ? nsum / dsum : (double)old;
+      jb.tables_out[c * b.n + idx] = (b.flags & 1) ? f64_to_bf16_value(val) : (float)val;
     }
-    __syncthreads();
   }
-  if (tid == 0) {
-    const RefineJob& jb = b.job[j];
-    const float old = jb.tables_in[c * b.n + idx];
-    const double val = rd[0] > 0.0 ? rn[0] / rd[0] : (double)old;
-    jb.tables_out[c * b.n + idx] = (b.flags & 1) ? f64_to_bf16_value(val) : (float)val;
+  if (tid == 0) b.counters[j] = 0u;
+  __syncthreads();
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
+  __shared__ RefineShared sh;
+  const int tid = threadIdx.x;
+  const int g8 = b.g / kPerLane;
+  const int log2S = 31 - __builtin_clz((unsigned)b.S);
+#pragma unroll
+  for (int k = 0; k < kVals; ++k) sh.bins[k][tid] = 0.0;
+  const int64_t t_begin = task_lo(blockIdx.x, b.total_tasks, gridDim.x);
+  const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
+  // two statically named buffers: the rows of task t + 1 load while task t accumulates
+  TaskRows A, B;
+  int cur = -1;
+  if (t_begin < t_end) load_task(b, t_begin, log2S, A);
+  for (int64_t task = t_begin; task < t_end; task += 2) {
+    if (task + 1 < t_end) load_task(b, task + 1, log2S, B);
+    if (A.job != cur) {
+      if (cur >= 0) finish_job(b, cur, sh);
+      cur = A.job;
+    }
+    accumulate_task(b, A, g8, sh);
+    if (task + 1 >= t_end) break;
+    if (task + 2 < t_end) load_task(b, task + 2, log2S, A);
+    if (B.job != cur) {
+      finish_job(b, cur, sh);
+      cur = B.job;
+    }
+    accumulate_task(b, B, g8, sh);
   }
+  if (cur >= 0) finish_job(b, cur, sh);
 }
 
 int refine_grid(int64_t total_tasks) {
-  const int64_t want = (int64_t)device_cu_count() * 2;
+  static int occ = 0;
+  if (occ <= 0) {
+    int blocks = 0;
+    const hipError_t e =
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, refine_kernel, kBlock, 0);
+    occ = (e == hipSuccess && blocks > 0) ? blocks : 1;
+  }
+  const int64_t want = (int64_t)device_cu_count() * occ;
   return (int)(total_tasks < want ? total_tasks : want);
 }
 
 hipError_t launch_refine(RefineBatch& b, hipStream_t stream) {
   if (b.nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(refine_accum_kernel, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(refine_finalize_kernel, dim3(b.njobs * kCells), dim3(kBlock), 0, stream, b);
+  hipLaunchKernelGGL(refine_kernel, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
   return hipGetLastError();
 }
 

@@ -99,17 +99,13 @@ def quantize_matrices(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], g:
         for b0, group in _batches(list(range(k))):
             sl = slice(b0, b0 + len(group))
             Wb, Ib = Ws[sl], Is[sl]
-            ws_a = wsp.get(("assign", b0), L.batch_workspace_bytes(
-                L.OP_ASSIGN, Rs[sl], Cs[sl], g, S, n))
-            L.aaac_assign_batch(Wb, g, S, n, Ib, tabs[sl], codes[sl], sels[sl], ws_a)
+            L.aaac_assign_batch(Wb, g, S, n, Ib, tabs[sl], codes[sl], sels[sl])
             ws_r = wsp.get(("refine", b0), L.batch_workspace_bytes(
                 L.OP_REFINE, Rs[sl], Cs[sl], g, S, n))
             L.aaac_refine_batch(Wb, g, S, n, Ib, codes[sl], sels[sl], tabs[sl], flags, ws_r)
     for b0, group in _batches(list(range(k))):
         sl = slice(b0, b0 + len(group))
-        ws_a = wsp.get(("assign", b0), L.batch_workspace_bytes(L.OP_ASSIGN, Rs[sl], Cs[sl], g, S,
-                                                              n))
-        L.aaac_assign_batch(Ws[sl], g, S, n, Is[sl], tabs[sl], codes[sl], sels[sl], ws_a)
+        L.aaac_assign_batch(Ws[sl], g, S, n, Is[sl], tabs[sl], codes[sl], sels[sl])
     out = []
     for i in range(k):
         R, C = Rs[i], Cs[i]

@@ -100,6 +100,48 @@ def test_init_quantiles_bit_exact(R, C, g, n):
     assert np.array_equal(_np(tables), want), (_np(tables), want)
 
 
+def test_init_workspace_reused_across_sizes():
+    """One zero-filled workspace serves several calls of different sizes (the call leaves its
+    counters zero); every table equals a call on a fresh workspace."""
+    _say("init workspace reuse")
+    shapes = [(512, 4096), (128, 4096), (64, 1024), (700, 2048)]
+    big = max(L.workspace_bytes(L.OP_INIT, R, C, 128, 128, 16) for R, C in shapes)
+    ws = L.workspace(big, DEV)
+    for i, (R, C) in enumerate(shapes):
+        W = _weight(R, C, 200 + i)
+        t_shared = torch.empty(32, dtype=torch.float32, device=DEV)
+        t_fresh = torch.empty(32, dtype=torch.float32, device=DEV)
+        L.aaac_init_quantiles(W, 128, 16, t_shared, ws)
+        L.aaac_init_quantiles(W, 128, 16, t_fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(t_shared, t_fresh), (R, C)
+
+
+def test_refine_workspace_reused_across_batches():
+    _say("refine workspace reuse")
+    g, S, n = 128, 128, 16
+    Ws = [_weight(R, 1024, 210 + R) for R in (512, 96, 1000)]
+    Is = [_importance(1024, 64, 220)[2]] * 3
+    ws = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, [W.shape[0] for W in Ws],
+                                             [1024] * 3, g, S, n), DEV)
+    for sub_ in ([0, 1, 2], [1], [2, 0]):
+        W_, I_ = [Ws[i] for i in sub_], [Is[i] for i in sub_]
+        tabs = []
+        for W in W_:
+            t = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+            L.aaac_init_quantiles(W, g, n, t)
+            tabs.append(t)
+        codes = [torch.empty(W.numel() // 2, dtype=torch.uint8, device=DEV) for W in W_]
+        sels = [torch.empty(W.numel() // S, dtype=torch.uint8, device=DEV) for W in W_]
+        L.aaac_assign_batch(W_, g, S, n, I_, tabs, codes, sels)
+        fresh = [t.clone() for t in tabs]
+        L.aaac_refine_batch(W_, g, S, n, I_, codes, sels, tabs, 0, ws)
+        L.aaac_refine_batch(W_, g, S, n, I_, codes, sels, fresh, 0)
+        torch.cuda.synchronize()
+        for a, b in zip(tabs, fresh):
+            assert torch.equal(a, b)
+
+
 def test_init_quantiles_zero_groups_and_ties():
     _say("init zero groups")
     W = _weight(64, 256, 5)
