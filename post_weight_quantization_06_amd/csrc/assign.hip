@@ -33,19 +33,26 @@ struct LutScratch {
   int m[2];                 // distinct values (0: the table has a non-finite entry)
 };
 
-constexpr uint32_t kNaNBits = 0x7fc00000u;
+// The lookup structure in LDS: per record the byte offsets of the two candidate pairs and the code
+// base, and per table the pair arrays.
+struct Lut {
+  uint8_t off0[kLutRecs];
+  uint8_t off1[kLutRecs];
+  uint8_t code[kLutRecs];
+  float2 pairs[2][kPairs];
+  float tab[2][16];         // the raw tables, for the exact scan
+};
 
-// Build the lookup records for tables T (fp32 [2][n], global) into `lut` (LDS) with all threads of
-// the block. Also copies the raw tables to `tab` for the exact scan. Must be called by every thread;
-// ends with a barrier.
-__device__ void build_lut(const float* __restrict__ T, int n, uint8_t* lut, LutScratch& ls,
-                          float (*tab)[16]) {
+// Build the lookup structure for tables T (fp32 [2][n], global) with all threads of the block.
+// Must be called by every thread; ends with a barrier.
+__device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScratch& ls) {
   const int tid = threadIdx.x;
+  const float qnan = __uint_as_float(0x7fc00000u);
   if (tid < 32) {
     const int c = tid >> 4, j = tid & 15;
     const float x = j < n ? T[c * n + j] : 0.0f;
     ls.raw[c][j] = x;
-    tab[c][j] = x;
+    lut.tab[c][j] = x;
   }
   __syncthreads();
   if (tid < 32) {
@@ -54,6 +61,11 @@ __device__ void build_lut(const float* __restrict__ T, int n, uint8_t* lut, LutS
     bool first = j < n;
     for (int k = 0; k < j; ++k) first = first && !(ls.raw[c][k] == x);
     ls.first[c][j] = first ? 1 : 0;
+    // pair j: {T[j], T[j + 1]}, the entry past the end reads as +inf
+    const float nxt = (j + 1 < n) ? ls.raw[c][j + 1 < 16 ? j + 1 : 15] : __builtin_inff();
+    lut.pairs[c][j] = make_float2(j < n ? x : __builtin_inff(), nxt);
+    if (j < 2) lut.pairs[c][16 + j] = j == 0 ? make_float2(__builtin_inff(), __builtin_inff())
+                                             : make_float2(qnan, qnan);
   }
   __syncthreads();
   if (tid < 32) {
@@ -80,15 +92,16 @@ __device__ void build_lut(const float* __restrict__ T, int n, uint8_t* lut, LutS
     const int c = tid >> 4, i = tid & 15;
     if (i + 1 < ls.m[c]) {
       const double M = 0.5 * ((double)ls.sv[c][i] + (double)ls.sv[c][i + 1]);
-      const double hi = floor(((M + 1.0 + kLutSlack) * (16.0 * kLutBuckets) + 32.5) / 32.0);
-      const double lo = ceil(((M + 1.0 - kLutSlack) * (16.0 * kLutBuckets) + 0.5) / 32.0);
+      const double S = (double)kLutScale;
+      const double hi = floor((M + 1.0 + kLutSlack) * S + 1.5);
+      const double lo = ceil((M + 1.0 - kLutSlack) * S + 0.5);
       ls.mhi[c][i] = (int)fmin(fmax(hi, -1.0), 4096.0);
       ls.mlo[c][i] = (int)fmin(fmax(lo, -1.0), 4096.0);
     }
   }
   __syncthreads();
   for (int rho = tid; rho < kLutRecs; rho += kBlock) {
-    uint32_t bits[4];
+    uint32_t off[2];
     uint32_t code = 0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -101,17 +114,17 @@ __device__ void build_lut(const float* __restrict__ T, int n, uint8_t* lut, LutS
       // clamped indices keep every read inside the arrays whatever the branch
       const int j0 = below < 15 ? below : 15;
       const int j1 = below + 1 < 15 ? below + 1 : 15;
+      // one candidate: pair {T[i], T[i + 1]} whose second entry is never strictly nearer inside
+      // the record; two candidates: only when they are consecutive entries i, i + 1
       const bool single = m > 0 && inside == 0;
       const bool pair = m > 0 && inside == 1 && ls.six[c][j1] == ls.six[c][j0] + 1;
-      const uint32_t a = __float_as_uint(ls.sv[c][j0]);
-      const uint32_t bb = __float_as_uint(ls.sv[c][j1]);
-      bits[2 * c] = (single || pair) ? a : kNaNBits;
-      bits[2 * c + 1] = single ? a : (pair ? bb : kNaNBits);
-      code |= (single || pair) ? ((uint32_t)ls.six[c][j0] << (4 * c)) : 0u;
+      const int i0 = ls.six[c][j0];
+      off[c] = (uint32_t)((single || pair) ? i0 : kNaNPair) * 8u;
+      code |= (single || pair) ? ((uint32_t)i0 << (4 * c)) : 0u;
     }
-    uint4* rec = reinterpret_cast<uint4*>(lut + (size_t)rho * kLutRecBytes);
-    rec[0] = make_uint4(bits[0], bits[1], bits[2], bits[3]);
-    rec[1] = make_uint4(code, 0u, 0u, 0u);
+    lut.off0[rho] = (uint8_t)off[0];
+    lut.off1[rho] = (uint8_t)off[1];
+    lut.code[rho] = (uint8_t)code;
   }
   __syncthreads();
 }
@@ -161,12 +174,11 @@ __device__ __forceinline__ void slow_lane(const float (&w)[8], uint32_t amax, co
   o.Q = Qw;
 }
 
-template <bool WITH_ERR>
-__device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* __restrict__ lut,
-                                           const float (*tab)[16], int n, int g8, int s8,
-                                           int log2S, int64_t base, bool active, const uint4& v,
-                                           const float (&Ik)[8]) {
-  const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
+template <bool WITH_ERR, int G8, int S8>
+__device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, int n, int g8,
+                                           int s8, int log2S, int64_t base, bool active,
+                                           const uint4& v, const float (&Ik)[8]) {
+  const uint32_t amax = block_max_u32_t<G8>(lane_absmax_bits(v), g8);
   const float s = __uint_as_float(amax << 16);
   float w[8];
   unpack8(v, w);
@@ -182,13 +194,16 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* _
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const float t = __builtin_fmaf(w[k], Y, kLutMagic);
-    const uint32_t off = __float_as_uint(t) & kLutMask;
-    const float4 rec = *reinterpret_cast<const float4*>(lut + off);
-    const uint32_t cb = lut[off + 16];
-    const float r0a = __builtin_fmaf(nse, rec.x, w[k]);
-    const float r0b = __builtin_fmaf(nse, rec.y, w[k]);
-    const float r1a = __builtin_fmaf(nse, rec.z, w[k]);
-    const float r1b = __builtin_fmaf(nse, rec.w, w[k]);
+    const uint32_t rho = __float_as_uint(t) & kLutMask;
+    const uint32_t cb = lut.code[rho];
+    const float2 p0 = *reinterpret_cast<const float2*>(
+        reinterpret_cast<const uint8_t*>(lut.pairs[0]) + lut.off0[rho]);
+    const float2 p1 = *reinterpret_cast<const float2*>(
+        reinterpret_cast<const uint8_t*>(lut.pairs[1]) + lut.off1[rho]);
+    const float r0a = __builtin_fmaf(nse, p0.x, w[k]);
+    const float r0b = __builtin_fmaf(nse, p0.y, w[k]);
+    const float r1a = __builtin_fmaf(nse, p1.x, w[k]);
+    const float r1b = __builtin_fmaf(nse, p1.y, w[k]);
     const bool d0 = fabsf(r0b) < fabsf(r0a);
     const bool d1 = fabsf(r1b) < fabsf(r1a);
     const float m0 = fminf(fabsf(r0a), fabsf(r0b));
@@ -213,9 +228,9 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* _
     }
   }
   RowOut o;
-  o.D = block_sum_f64(accd, s8);
-  o.E0 = WITH_ERR ? block_sum_f64(e0d, s8) : 0.0;
-  o.E1 = WITH_ERR ? block_sum_f64(e1d, s8) : 0.0;
+  o.D = block_sum_f64_t<S8>(accd, s8);
+  o.E0 = WITH_ERR ? block_sum_f64_t<S8>(e0d, s8) : 0.0;
+  o.E1 = WITH_ERR ? block_sum_f64_t<S8>(e1d, s8) : 0.0;
   o.P = Pw;
   o.Q = Qw;
   if (zero) {
@@ -226,11 +241,11 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* _
   const bool bad = active && (!fast_scale || !(fabs(o.D) < __builtin_inf()));
   if (__any(bad)) {
     RowOut so;
-    slow_lane<WITH_ERR>(w, amax, Ik, tab, n, so);
-    so.D = block_sum_f64(so.D, s8);
+    slow_lane<WITH_ERR>(w, amax, Ik, lut.tab, n, so);
+    so.D = block_sum_f64_t<S8>(so.D, s8);
     if (WITH_ERR) {
-      so.E0 = block_sum_f64(so.E0, s8);
-      so.E1 = block_sum_f64(so.E1, s8);
+      so.E0 = block_sum_f64_t<S8>(so.E0, s8);
+      so.E1 = block_sum_f64_t<S8>(so.E1, s8);
     }
     if (bad) o = so;
   }
@@ -256,11 +271,10 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const uint8_t* _
 
 }  // namespace
 
-template <bool WITH_ERR>
+template <bool WITH_ERR, int G8, int S8>
 __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
-  __shared__ __align__(16) uint8_t lut[kLutBytes];
+  __shared__ Lut lut;
   __shared__ LutScratch ls;
-  __shared__ float tab[2][16];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -274,7 +288,7 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
     const AssignJob& jb = b.job[j];
     if (j != cur) {
       __syncthreads();
-      build_lut(jb.tables, n, lut, ls, tab);
+      build_lut(jb.tables, n, lut, ls);
       cur = j;
     }
     const int64_t local = task - jb.geom.task_begin;
@@ -305,29 +319,39 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
-      if (r < R) assign_row<WITH_ERR>(jb, lut, tab, n, g8, s8, log2S, r * C + c0, active, v[i], Ik);
+      if (r < R)
+        assign_row<WITH_ERR, G8, S8>(jb, lut, n, g8, s8, log2S, r * C + c0, active, v[i], Ik);
     }
   }
 }
 
-hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream) {
-  static int per_cu[2] = {0, 0};
-  int& occ = per_cu[with_err ? 1 : 0];
+template <bool WITH_ERR, int G8, int S8>
+hipError_t launch_assign_t(const AssignBatch& b, hipStream_t stream) {
+  static int occ = 0;
   if (occ <= 0) {
     int blocks = 0;
-    const hipError_t e = with_err
-        ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, assign_kernel<true>, kBlock, 0)
-        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, assign_kernel<false>, kBlock, 0);
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &blocks, assign_kernel<WITH_ERR, G8, S8>, kBlock, 0);
     occ = (e == hipSuccess && blocks > 0) ? blocks : 2;
   }
   const int64_t want = (int64_t)device_cu_count() * occ;
   const int grid = (int)(b.total_tasks < want ? b.total_tasks : want);
   if (grid <= 0) return hipSuccess;
-  if (with_err)
-    hipLaunchKernelGGL(assign_kernel<true>, dim3(grid), dim3(kBlock), 0, stream, b);
-  else
-    hipLaunchKernelGGL(assign_kernel<false>, dim3(grid), dim3(kBlock), 0, stream, b);
+  hipLaunchKernelGGL((assign_kernel<WITH_ERR, G8, S8>), dim3(grid), dim3(kBlock), 0, stream, b);
   return hipGetLastError();
+}
+
+template <bool WITH_ERR>
+hipError_t launch_assign_g(const AssignBatch& b, hipStream_t stream) {
+  const int g8 = b.g / kPerLane, s8 = b.S / kPerLane;
+  if (g8 == 16 && s8 == 16) return launch_assign_t<WITH_ERR, 16, 16>(b, stream);   // g = S = 128
+  if (g8 == 16 && s8 == 2) return launch_assign_t<WITH_ERR, 16, 2>(b, stream);     // g 128, S 16
+  if (g8 == 2 && s8 == 2) return launch_assign_t<WITH_ERR, 2, 2>(b, stream);       // g = S = 16
+  return launch_assign_t<WITH_ERR, 0, 0>(b, stream);
+}
+
+hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream) {
+  return with_err ? launch_assign_g<true>(b, stream) : launch_assign_g<false>(b, stream);
 }
 
 }  // namespace aaac

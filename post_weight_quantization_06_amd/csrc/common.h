@@ -24,25 +24,25 @@ constexpr int kRowsPerTask = kRowsPerWave * kWavesPerBlock;
 constexpr int kMaxJobs = 8;
 
 // ------------------------------------------------------------------------------------------------
-// Nearest-entry lookup structure (built per table pair by lut_build, consumed by assign).
-// u in [-1, 1] is mapped to one of kLutRecs records of 32 bytes by
-//   t = fma(w, Y, kLutMagic),  Y = 16 kLutBuckets / s,  offset = bits(t) & kLutMask
-// (t lies in [2^23, 2^24), so its low mantissa bits hold round(32 + 16 kLutBuckets (u + 1))).
-// Record rho covers u in [(32 rho - 32.5) / (16 kLutBuckets) - 1, (32 rho - 0.5) / (16 kLutBuckets) - 1];
-// it holds, per table, the two candidate entries A (wins ties) and B valid over that interval widened
-// by kLutSlack, and one byte with the index of each table's A (low nibble: table 0).
-// A record with B == A has a single candidate; a record whose table has more than two candidates
-// there (or non-consecutive indices) holds NaN for that table, which routes its group to the exact
-// fallback scan.
+// Nearest-entry lookup structure (built in LDS by the assign kernel from the two tables).
+// u in [-1, 1] maps to record rho = bits(t) & kLutMask with
+//   t = fma(w, Y, kLutMagic),  Y = kLutScale / s,
+// t lies in [2^23, 2^24), so its low mantissa bits hold round(1 + kLutScale (u + 1)); record rho
+// covers u in [(rho - 1.5) / kLutScale - 1, (rho - 0.5) / kLutScale - 1]. For each table the record
+// holds the byte offset of a candidate pair {T[i], T[i+1]} in a small pair array (T[n] reads as
+// +inf), valid over that interval widened by kLutSlack: the nearest entry there is T[i], or T[i+1]
+// past the one midpoint the record contains. A record that would need other candidates points at a
+// NaN pair, which routes its group to the exact full scan. A third byte array holds the code base
+// i0 | i1 << 4. Three byte arrays and two 18-pair arrays: a few KB of LDS, and the pair reads hit at
+// most 18 distinct addresses per wave, so they never conflict.
 // ------------------------------------------------------------------------------------------------
 constexpr int kLutRecs = 1024;
-constexpr int kLutBuckets = kLutRecs - 2;
-constexpr int kLutRecBytes = 32;
-constexpr int kLutBytes = kLutRecs * kLutRecBytes;
-constexpr uint32_t kLutMask = (kLutRecs - 1) * kLutRecBytes;
-constexpr float kLutScale = 16.0f * kLutBuckets;                   // 16352
-constexpr float kLutMagic = 8388608.0f + 32.0f + 16.0f * kLutBuckets;
+constexpr uint32_t kLutMask = kLutRecs - 1;
+constexpr float kLutScale = 0.5f * (kLutRecs - 2);                    // 511
+constexpr float kLutMagic = 8388608.0f + 1.0f + 0.5f * (kLutRecs - 2);
 constexpr double kLutSlack = 0x1p-20;
+constexpr int kPairs = 18;                 // pair i < 17: {T[i], T[i + 1]}; pair 17: NaN
+constexpr int kNaNPair = 17;
 
 // Group scales outside [2^-30, 2^30] take the exact fallback (no fp32 over/underflow there).
 constexpr float kFastScaleMin = 0x1p-30f;
@@ -81,6 +81,30 @@ __device__ __forceinline__ double dpp_f64(double v) {
   const uint32_t lo = dpp_u32<CTRL>((uint32_t)b);
   const uint32_t hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// LANES > 0: block size known at compile time; LANES == 0: use the runtime value `lanes`.
+template <int LANES>
+__device__ __forceinline__ uint32_t block_max_u32_t(uint32_t v, int lanes) {
+  if (LANES > 0) lanes = LANES;
+  if (lanes >= 2) v = max(v, dpp_u32<kDppQuadXor1>(v));
+  if (lanes >= 4) v = max(v, dpp_u32<kDppQuadXor2>(v));
+  if (lanes >= 8) v = max(v, dpp_u32<kDppRowHalfMirror>(v));
+  if (lanes >= 16) v = max(v, dpp_u32<kDppRowMirror>(v));
+  if (lanes >= 32) v = max(v, (uint32_t)__shfl_xor((int)v, 16));
+  if (lanes >= 64) v = max(v, (uint32_t)__shfl_xor((int)v, 32));
+  return v;
+}
+template <int LANES>
+__device__ __forceinline__ double block_sum_f64_t(double v, int lanes) {
+  if (LANES > 0) lanes = LANES;
+  if (lanes >= 2) v += dpp_f64<kDppQuadXor1>(v);
+  if (lanes >= 4) v += dpp_f64<kDppQuadXor2>(v);
+  if (lanes >= 8) v += dpp_f64<kDppRowHalfMirror>(v);
+  if (lanes >= 16) v += dpp_f64<kDppRowMirror>(v);
+  if (lanes >= 32) v += __shfl_xor(v, 16);
+  if (lanes >= 64) v += __shfl_xor(v, 32);
+  return v;
 }
 
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, int lanes) {
