@@ -7,7 +7,9 @@ assign, batched refine) with bf16 tables on the last refine, the final assign, p
 Metric (value): bf16 weight bytes quantized per second per assign+refine iteration,
 2 * numel * iters / t_loop, with t_loop the HIP-event time of the loop region of a step.
 roofline: the dominant of the two loop kernels (assign, refine); achieved = its algorithmic bytes
-per launch / its mean launch duration (HIP events on the launch stream).
+per launch / its mean launch duration (HIP events on the launch stream); traffic = its HBM bytes per
+launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a plain copy), or null
+when that summary was taken on other kernel sources or on another workload.
 cpu_baseline: the fp64 oracle, assign + refine on a sample matrix, timed on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu]
@@ -24,6 +26,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_assign_refine_llama8b_layer.json")
 
 
 def algorithmic_bytes(numel, S):
@@ -73,6 +76,7 @@ def main():
     import torch
 
     import post_weight_quantization_06_amd as pkg
+    from post_weight_quantization_06_amd import pmc_traffic
     from synth import layers as syn
 
     L = pkg._lib
@@ -145,6 +149,13 @@ def main():
                            W_hat[i])
         return loop0, loop1, marks
 
+    # one plain device-to-device copy of 1 GiB, outside the timed region: the reference launch that
+    # HBM byte counters (FETCH_SIZE / WRITE_SIZE) are scaled by
+    calib_src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
@@ -170,6 +181,10 @@ def main():
                                         bytes_launch / a_avg / 1e6, r_avg * 1e3,
                                         bytes_launch / r_avg / 1e6, wall),
           file=sys.stderr, flush=True)
+    traffic = None
+    if args.config == 2:
+        t = pmc_traffic.load_traffic(TRAFFIC_SUMMARY, dom)
+        traffic = None if t is None else int(round(t))
     cpu = None
     if not args.no_cpu:
         k = min(range(len(mats)), key=lambda i: mats[i].numel)
@@ -198,7 +213,9 @@ def main():
         "hbm_frac_refine": round(bytes_launch / (r_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes per launch",
+                     "algorithmic_bytes": int(round(bytes_launch))},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

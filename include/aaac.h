@@ -116,7 +116,8 @@ aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, i
  * over the cell {weights with sel = c and code = j}:
  *   num = sum I_k s w_k,  den = sum I_k s^2,   T_c[j] <- num / den if den > 0, else unchanged.
  * num / den minimizes sum I (w - s t)^2 over t, i.e. it is the I s^2-weighted centroid of u.
- * Sums run in fp32 over at most 64 terms per partial and in fp64 beyond, in a fixed order.
+ * Every term is exact in fp64 and is added in fp64, per thread, then across threads and workgroups
+ * in a fixed order, so the result is bitwise reproducible.
  * One kernel: the last workgroup to finish a matrix (an integer ticket in the workspace) adds the
  * per-workgroup partials and writes tables_out. The ticket is reset at the end of every call; a call
  * that did not complete (a device fault) leaves the workspace to be zero-filled again.

@@ -60,7 +60,7 @@ aaac_status check_shape(int64_t R, int64_t C, int g, int S, int n, bool need_S, 
   if (R < 1 || C < 8 || C % 8 != 0 || C >= ((int64_t)1 << 31))
     return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: R=%lld C=%lld (need R >= 1, C >= 8, C %% 8 == 0)",
                 who, (long long)R, (long long)C);
-  if (R > (((int64_t)1 << 40) / C))
+  if (R > ((((int64_t)1 << 40) - 1) / C))
     return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: R*C must stay below 2^40", who);
   if (!pow2(g) || g < 8 || g > 512 || C % g != 0)
     return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: g=%d (need a power of two in [8, 512] dividing C)",
