@@ -20,23 +20,30 @@ namespace aaac {
 namespace {
 
 constexpr int kCells = 32;   // 2 tables x 16 entries
-constexpr int kVals = 64;    // num (bins 0-31) and den (bins 32-63)
+constexpr int kVals = 64;    // value v = 2 cell + {0: num, 1: den}
 
+// bins[cell][sum][thread]: a thread's num and den of one cell are 2 KB apart (one immediate
+// offset), and the 64 lanes of a wave touch 64 consecutive doubles (no bank conflicts).
 struct RefineShared {
-  double bins[kVals][kBlock];
+  double bins[kCells][2][kBlock];
 };
 
 struct TaskRows {
   uint4 v[kRowsPerWave];
   uint32_t cw[kRowsPerWave];
   uint32_t sb[kRowsPerWave];
-  float I[kPerLane];
+  float4 I0, I1;
   int64_t r0;
+  int64_t R;
   int job;
-  int c0;
   bool active;
 };
 
+// Issue every load of one task without branches: a lane past the last column, or a row past the
+// last row, reads an in-bounds element of the same matrix instead, and its contribution is dropped
+// where it is used (zero importance for the lane; rows past the end are skipped). Loads that are
+// never conditional let the compiler wait for exactly the task being used while later tasks' loads
+// stay in flight.
 __device__ __forceinline__ void load_task(const RefineBatch& b, int64_t task, int log2S,
                                           TaskRows& t) {
   const int lane = threadIdx.x & (kWave - 1);
@@ -47,59 +54,58 @@ __device__ __forceinline__ void load_task(const RefineBatch& b, int64_t task, in
   const int64_t local = task - jb.geom.task_begin;
   const int64_t rb = local / jb.geom.nslab;
   const int slab = (int)(local - rb * jb.geom.nslab);
-  t.job = j;
-  t.c0 = slab * kSlab + lane * kPerLane;
-  t.active = t.c0 < jb.geom.C;
-  t.r0 = rb * kRowsPerTask + wave;
+  const int c0 = slab * kSlab + lane * kPerLane;
   const int64_t R = jb.geom.R, C = jb.geom.C;
+  t.active = c0 < C;
+  const int64_t cl = t.active ? c0 : 0;
+  t.job = j;
+  t.R = R;
+  t.r0 = rb * kRowsPerTask + wave;
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
-    const int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
-    t.v[i] = make_uint4(0u, 0u, 0u, 0u);
-    t.cw[i] = 0;
-    t.sb[i] = 0;
-    if (t.active && r < R) {
-      const int64_t base = r * C + t.c0;
-      t.v[i] = *reinterpret_cast<const uint4*>(jb.W + base);
-      t.cw[i] = jb.codes[base >> 3];
-      t.sb[i] = jb.sel[base >> log2S];
-    }
+    int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
+    r = r < R ? r : R - 1;
+    const int64_t base = r * C + cl;
+    t.v[i] = *reinterpret_cast<const uint4*>(jb.W + base);
+    t.cw[i] = jb.codes[base >> 3];
+    t.sb[i] = jb.sel[base >> log2S];
   }
-  if (t.active) {
-    const float4 i0 = *reinterpret_cast<const float4*>(jb.I + t.c0);
-    const float4 i1 = *reinterpret_cast<const float4*>(jb.I + t.c0 + 4);
-    t.I[0] = i0.x; t.I[1] = i0.y; t.I[2] = i0.z; t.I[3] = i0.w;
-    t.I[4] = i1.x; t.I[5] = i1.y; t.I[6] = i1.z; t.I[7] = i1.w;
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) t.I[k] = 0.0f;
-  }
+  t.I0 = *reinterpret_cast<const float4*>(jb.I + cl);
+  t.I1 = *reinterpret_cast<const float4*>(jb.I + cl + 4);
 }
 
-__device__ __forceinline__ void accumulate_task(const RefineBatch& b, const TaskRows& t, int g8,
-                                                RefineShared& sh) {
+template <int G8>
+__device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, RefineShared& sh) {
   const int tid = threadIdx.x;
-  const int64_t R = b.job[t.job].geom.R;
+  const float If[8] = {t.I0.x, t.I0.y, t.I0.z, t.I0.w, t.I1.x, t.I1.y, t.I1.z, t.I1.w};
   double Id[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) Id[k] = (double)t.I[k];
+  for (int k = 0; k < 8; ++k) Id[k] = t.active ? (double)If[k] : 0.0;
+  char* const lds = reinterpret_cast<char*>(&sh.bins[0][0][0]) + tid * sizeof(double);
+  // the scales of all rows first: eight independent lane reductions (an inactive lane reads a
+  // group of its own matrix, so its scale is finite and its zero importance drops its terms)
+  float s[kRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i)
+    s[i] = __uint_as_float(block_max_u32_t<G8>(lane_absmax_bits(t.v[i]), g8) << 16);
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
-    const int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
-    if (r >= R) continue;
-    const uint32_t amax = block_max_u32(lane_absmax_bits(t.v[i]), g8);
-    if (!t.active) continue;
-    const float s = __uint_as_float(amax << 16);
-    const double s2 = (double)(s * s);          // exact: s has 8 significant bits
+    // rows past the end of the matrix are the same for the whole wave
+    if (t.r0 + (int64_t)kWavesPerBlock * i >= t.R) break;
+    const double s2 = (double)(s[i] * s[i]);     // exact: s has 8 significant bits
     float w[8];
     unpack8(t.v[i], w);
-    const int cbase = t.sb[i] ? 16 : 0;
+    char* const row = lds + (t.sb[i] ? 16 * sizeof(sh.bins[0]) : 0);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int cell = cbase + ((t.cw[i] >> (4 * k)) & 15u);
-      atomicAdd(&sh.bins[cell][tid], Id[k] * (double)(s * w[k]));   // s w exact in fp32
-      atomicAdd(&sh.bins[kCells + cell][tid], Id[k] * s2);
+      const uint32_t q = (t.cw[i] >> (4 * k)) & 15u;
+      double* const p = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
+      atomicAdd(p, Id[k] * (double)(s[i] * w[k]));    // s w is exact in fp32
+      atomicAdd(p + kBlock, Id[k] * s2);
     }
+    // one row at a time: interleaving rows would push the live registers past the 256 a lane can
+    // address and spill loaded values that are still in flight
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -128,12 +134,12 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
     // value v = tid & 63 over the 64 columns of quarter q = tid >> 6, in a fixed (rotated) order
     const int v = tid & 63, q = tid >> 6;
     double s = 0.0;
-    for (int i = 0; i < 64; ++i) s += sh.bins[v][q * 64 + ((i + v) & 63)];
+    for (int i = 0; i < 64; ++i) s += sh.bins[v >> 1][v & 1][q * 64 + ((i + v) & 63)];
     part4[q][v] = s;
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kVals; ++k) sh.bins[k][tid] = 0.0;
+  for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
   double* part = b.partials + (size_t)j * kVals * b.slots;
   const int slot = (int)blockIdx.x - jb.wg_lo;
   if (tid < kVals) {
@@ -158,9 +164,9 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
   __syncthreads();
   if (tid < kCells) {
     const int c = tid >> 4, idx = tid & 15;
-    const double nsum = ((part4[0][tid] + part4[1][tid]) + part4[2][tid]) + part4[3][tid];
-    const double dsum = ((part4[0][kCells + tid] + part4[1][kCells + tid]) + part4[2][kCells + tid]) +
-                        part4[3][kCells + tid];
+    const int vn = 2 * tid, vd = 2 * tid + 1;
+    const double nsum = ((part4[0][vn] + part4[1][vn]) + part4[2][vn]) + part4[3][vn];
+    const double dsum = ((part4[0][vd] + part4[1][vd]) + part4[2][vd]) + part4[3][vd];
     if (idx < b.n) {
       const float old = jb.tables_in[c * b.n + idx];
       const double val = dsum > 0.0 ? nsum / dsum : (double)old;
@@ -173,52 +179,61 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
 
 }  // namespace
 
+template <int G8>
 __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
   __shared__ RefineShared sh;
   const int tid = threadIdx.x;
   const int g8 = b.g / kPerLane;
   const int log2S = 31 - __builtin_clz((unsigned)b.S);
 #pragma unroll
-  for (int k = 0; k < kVals; ++k) sh.bins[k][tid] = 0.0;
+  for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
   const int64_t t_begin = task_lo(blockIdx.x, b.total_tasks, gridDim.x);
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
-  // two statically named buffers: the rows of task t + 1 load while task t accumulates
+  // three statically named buffers: the rows of tasks t + 1 and t + 2 are in flight while task t
+  // accumulates
+  // two statically named buffers: the rows of task t + 1 are in flight while task t accumulates
+  // (26 loads per task and wave, so both tasks stay within the 63 loads a wave can track)
   TaskRows A, B;
   int cur = -1;
+  const int64_t last = t_end - 1;
+  // the prefetch index is clamped to the last task: past the end a buffer reloads that task and is
+  // never used
+#define AAAC_NEXT(x) ((x) < last ? (x) : last)
   if (t_begin < t_end) load_task(b, t_begin, log2S, A);
   for (int64_t task = t_begin; task < t_end; task += 2) {
-    if (task + 1 < t_end) load_task(b, task + 1, log2S, B);
+    load_task(b, AAAC_NEXT(task + 1), log2S, B);
     if (A.job != cur) {
       if (cur >= 0) finish_job(b, cur, sh);
       cur = A.job;
     }
-    accumulate_task(b, A, g8, sh);
+    accumulate_task<G8>(A, g8, sh);
     if (task + 1 >= t_end) break;
-    if (task + 2 < t_end) load_task(b, task + 2, log2S, A);
+    load_task(b, AAAC_NEXT(task + 2), log2S, A);
     if (B.job != cur) {
       finish_job(b, cur, sh);
       cur = B.job;
     }
-    accumulate_task(b, B, g8, sh);
+    accumulate_task<G8>(B, g8, sh);
   }
+#undef AAAC_NEXT
   if (cur >= 0) finish_job(b, cur, sh);
 }
 
+// The bins fill most of the LDS: one workgroup per CU.
 int refine_grid(int64_t total_tasks) {
-  static int occ = 0;
-  if (occ <= 0) {
-    int blocks = 0;
-    const hipError_t e =
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, refine_kernel, kBlock, 0);
-    occ = (e == hipSuccess && blocks > 0) ? blocks : 1;
-  }
-  const int64_t want = (int64_t)device_cu_count() * occ;
+  const int64_t want = (int64_t)device_cu_count();
   return (int)(total_tasks < want ? total_tasks : want);
 }
 
 hipError_t launch_refine(RefineBatch& b, hipStream_t stream) {
   if (b.nblocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(refine_kernel, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
+  const int g8 = b.g / kPerLane;
+  if (g8 == 16)
+    hipLaunchKernelGGL(refine_kernel<16>, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
+  else if (g8 == 2)
+    hipLaunchKernelGGL(refine_kernel<2>, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
+  else
+    hipLaunchKernelGGL(refine_kernel<0>, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
   return hipGetLastError();
 }
 
