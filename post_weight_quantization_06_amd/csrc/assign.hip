@@ -138,7 +138,7 @@ struct RowOut {
 // Exact fallback for one lane: full scan of both tables on scaled operands (w and s multiplied by a
 // power of two that brings s into [1, 4), so no residual under- or overflows).
 template <bool WITH_ERR>
-__device__ __forceinline__ void slow_lane(const float (&w)[8], uint32_t amax, const float (&Ik)[8],
+__device__ __forceinline__ void slow_lane(const float* w, uint32_t amax, const float* Ik,
                                           const float (*tab)[16], int n, RowOut& o) {
   const uint32_t E = min(max(amax >> 7, 1u), 253u);
   const float P = __uint_as_float((254u - E) << 23);
@@ -271,6 +271,246 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
 
 }  // namespace
 
+// ---------------------------------------------------------------------------------------------
+// Wide mapping for selection groups of at least 16 weights: a lane holds 16 consecutive weights
+// (two 16-byte loads), a wave row covers 1024 columns, a task is 16 rows x 1024 columns (four rows
+// per wave). The per-row work (scale, selection sum, code compaction) is spread over twice as many
+// weights as in the 8-weight mapping.
+// ---------------------------------------------------------------------------------------------
+constexpr int kWideLane = 16;
+constexpr int kWideSlab = kWave * kWideLane;
+constexpr int kWideRowsPerWave = 4;
+constexpr int kWideRowsPerTask = kWideRowsPerWave * kWavesPerBlock;
+
+// Nearest entries of one weight in both tables from the lookup structure (see the layout above):
+// returns the code byte q0 | q1 << 4 and accumulates I (m1^2 - m0^2) (and the two errors).
+template <bool WITH_ERR>
+__device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, const Lut& lut,
+                                                  float Ik, float& acc, float& a0, float& a1) {
+  const float t = __builtin_fmaf(w, Y, kLutMagic);
+  const uint32_t rho = __float_as_uint(t) & kLutMask;
+  const uint32_t cb = lut.code[rho];
+  const float2 p0 = *reinterpret_cast<const float2*>(
+      reinterpret_cast<const uint8_t*>(lut.pairs[0]) + lut.off0[rho]);
+  const float2 p1 = *reinterpret_cast<const float2*>(
+      reinterpret_cast<const uint8_t*>(lut.pairs[1]) + lut.off1[rho]);
+  const float r0a = __builtin_fmaf(nse, p0.x, w);
+  const float r0b = __builtin_fmaf(nse, p0.y, w);
+  const float r1a = __builtin_fmaf(nse, p1.x, w);
+  const float r1b = __builtin_fmaf(nse, p1.y, w);
+  const bool d0 = fabsf(r0b) < fabsf(r0a);
+  const bool d1 = fabsf(r1b) < fabsf(r1a);
+  const float m0 = fminf(fabsf(r0a), fabsf(r0b));
+  const float m1 = fminf(fabsf(r1a), fabsf(r1b));
+  const float e0 = m0 * m0;
+  acc = __builtin_fmaf(Ik, __builtin_fmaf(m1, m1, -e0), acc);
+  if (WITH_ERR) {
+    a0 = __builtin_fmaf(Ik, e0, a0);
+    a1 = __builtin_fmaf(Ik, m1 * m1, a1);
+  }
+  return cb + (d0 ? 1u : 0u) + (d1 ? 16u : 0u);
+}
+
+// Keep the nibble of table `sel` from four code bytes (q0 | q1 << 4): bytes 0 and 2 of the result
+// hold two codes each.
+__device__ __forceinline__ uint32_t select_nibbles(uint32_t P, uint32_t sel) {
+  uint32_t p = (P >> (sel ? 4u : 0u)) & 0x0F0F0F0Fu;
+  return p | (p >> 4);
+}
+
+// Exact fallback for one lane of the wide mapping, reading its 16 weights and importances again
+// from memory (they are in cache) so that the fast path keeps no copies in registers: full scan of
+// both tables on operands scaled by a power of two that brings s into [1, 4). Codes come back as
+// bytes q0 | q1 << 4, weight k in byte k of (lo, hi).
+template <bool WITH_ERR>
+__device__ __noinline__ void slow_lane16(const uint16_t* __restrict__ wp,
+                                         const float* __restrict__ ip, uint32_t amax,
+                                         const float (*tab)[16], int n, double& D, double& E0,
+                                         double& E1, uint64_t& lo, uint64_t& hi) {
+  const uint32_t E = min(max(amax >> 7, 1u), 253u);
+  const float P = __uint_as_float((254u - E) << 23);
+  const float sp = __uint_as_float(amax << 16) * P;
+  double d = 0.0, e0 = 0.0, e1 = 0.0;
+  uint64_t cl = 0, ch = 0;
+#pragma unroll 1
+  for (int k = 0; k < kWideLane; ++k) {
+    const float wv = __uint_as_float((uint32_t)wp[k] << 16) * P;
+    const double Ik = (double)ip[k];
+    float best0 = __builtin_inff(), best1 = __builtin_inff();
+    uint32_t q0 = 0, q1 = 0;
+    for (int j = 0; j < n; ++j) {
+      const float r0 = fabsf(__builtin_fmaf(-sp, tab[0][j], wv));
+      const float r1 = fabsf(__builtin_fmaf(-sp, tab[1][j], wv));
+      if (r0 < best0) { best0 = r0; q0 = j; }
+      if (r1 < best1) { best1 = r1; q1 = j; }
+    }
+    const double b0 = (double)best0 * (double)best0;
+    const double b1 = (double)best1 * (double)best1;
+    d += Ik * (b1 - b0);
+    if (WITH_ERR) {
+      e0 += Ik * b0;
+      e1 += Ik * b1;
+    }
+    const uint64_t c = (uint64_t)(q0 | (q1 << 4));
+    if (k < 8) cl |= c << (8 * k); else ch |= c << (8 * (k - 8));
+  }
+  const double inv = 1.0 / ((double)P * (double)P);
+  D = d;
+  E0 = e0 * inv;
+  E1 = e1 * inv;
+  lo = cl;
+  hi = ch;
+}
+
+template <bool WITH_ERR, int G16, int S16>
+__device__ __forceinline__ void assign_row16(const AssignJob& jb, const Lut& lut, int n, int g16,
+                                             int s16, int log2S, int64_t base, bool active,
+                                             const uint16_t* wsafe, const float* isafe,
+                                             const uint4& va, const uint4& vb,
+                                             const float (&Ik)[16]) {
+  const uint32_t amax = block_max_u32_t<G16>(lane_absmax16_bits(va, vb), g16);
+  const float s = __uint_as_float(amax << 16);
+  float w[16];
+  {
+    float wa[8], wb[8];
+    unpack8(va, wa);
+    unpack8(vb, wb);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      w[k] = wa[k];
+      w[8 + k] = wb[k];
+    }
+  }
+  const bool zero = (s == 0.0f);
+  const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
+  const float se = zero ? 1.0f : s;
+  const float Y = kLutScale * __builtin_amdgcn_rcpf(se);
+  const float nse = -se;
+
+  double accd = 0.0, e0d = 0.0, e1d = 0.0;
+  uint32_t P[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // four weights per fp32 partial, then fp64
+    float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t c = lookup_weight<WITH_ERR>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc,
+                                                 a0, a1);
+      word |= c << (8 * k);
+    }
+    P[q] = word;
+    accd = (q == 0) ? (double)acc : accd + (double)acc;
+    if (WITH_ERR) {
+      e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
+      e1d = (q == 0) ? (double)a1 : e1d + (double)a1;
+    }
+    // four weights' lookups in flight at a time keep the live registers within three waves per
+    // SIMD; the other waves hide the LDS latency
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  double D = block_sum_f64_t<S16>(accd, s16);
+  double E0 = WITH_ERR ? block_sum_f64_t<S16>(e0d, s16) : 0.0;
+  double E1 = WITH_ERR ? block_sum_f64_t<S16>(e1d, s16) : 0.0;
+  if (zero) {
+    D = 0.0;
+    E0 = 0.0;
+    E1 = 0.0;
+  }
+  const bool bad = active && (!fast_scale || !(fabs(D) < __builtin_inf()));
+  if (__any(bad)) {
+    double lD, lE0, lE1;
+    uint64_t clo, chi;
+    slow_lane16<WITH_ERR>(wsafe, isafe, amax, lut.tab, n, lD, lE0, lE1, clo, chi);
+    const double sD = block_sum_f64_t<S16>(lD, s16);
+    double sE0 = 0.0, sE1 = 0.0;
+    if (WITH_ERR) {
+      sE0 = block_sum_f64_t<S16>(lE0, s16);
+      sE1 = block_sum_f64_t<S16>(lE1, s16);
+    }
+    if (bad) {
+      D = sD;
+      E0 = sE0;
+      E1 = sE1;
+      P[0] = (uint32_t)clo;
+      P[1] = (uint32_t)(clo >> 32);
+      P[2] = (uint32_t)chi;
+      P[3] = (uint32_t)(chi >> 32);
+    }
+  }
+  const uint32_t sel = (D < 0.0) ? 1u : 0u;
+  const uint32_t lo = __builtin_amdgcn_perm(select_nibbles(P[1], sel), select_nibbles(P[0], sel),
+                                            0x06040200u);
+  const uint32_t hi = __builtin_amdgcn_perm(select_nibbles(P[3], sel), select_nibbles(P[2], sel),
+                                            0x06040200u);
+  if (active) {
+    *reinterpret_cast<uint2*>(jb.codes + (base >> 3)) = make_uint2(lo, hi);
+    if (((base >> 4) & (s16 - 1)) == 0) {
+      const int64_t h = base >> log2S;
+      jb.sel[h] = (uint8_t)sel;
+      if (WITH_ERR) {
+        jb.err[2 * h] = E0;
+        jb.err[2 * h + 1] = E1;
+      }
+    }
+  }
+}
+
+template <bool WITH_ERR, int G16, int S16>
+__global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
+  __shared__ Lut lut;
+  __shared__ LutScratch ls;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane, n = b.n;
+  const int log2S = 31 - __builtin_clz((unsigned)b.S);
+  const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
+  int cur = -1;
+  for (int64_t task = task_lo(blockIdx.x, b.total_tasks, gridDim.x); task < t_end; ++task) {
+    int j = 0;
+    while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
+    const AssignJob& jb = b.job[j];
+    if (j != cur) {
+      __syncthreads();
+      build_lut(jb.tables, n, lut, ls);
+      cur = j;
+    }
+    const int64_t local = task - jb.geom.task_begin;
+    const int64_t rb = local / jb.geom.nslab;
+    const int slab = (int)(local - rb * jb.geom.nslab);
+    const int c0 = slab * kWideSlab + lane * kWideLane;
+    const bool active = c0 < jb.geom.C;
+    const int64_t cl = active ? c0 : 0;       // inactive lanes read an element of their own matrix
+    const int64_t R = jb.geom.R, C = jb.geom.C;
+    const int64_t r0 = rb * kWideRowsPerTask + wave;
+    // every load of the task first, unconditional (rows past the end read the last row and are
+    // skipped below; that test is the same for the whole wave)
+    uint4 va[kWideRowsPerWave], vb[kWideRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kWideRowsPerWave; ++i) {
+      int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+      r = r < R ? r : R - 1;
+      const uint16_t* p = jb.W + r * C + cl;
+      va[i] = *reinterpret_cast<const uint4*>(p);
+      vb[i] = *reinterpret_cast<const uint4*>(p + 8);
+    }
+    float Ik[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
+      Ik[4 * q] = x.x; Ik[4 * q + 1] = x.y; Ik[4 * q + 2] = x.z; Ik[4 * q + 3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < kWideRowsPerWave; ++i) {
+      const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+      if (r >= R) break;
+      assign_row16<WITH_ERR, G16, S16>(jb, lut, n, g16, s16, log2S, r * C + c0, active,
+                                        jb.W + r * C + cl, jb.I + cl, va[i], vb[i], Ik);
+    }
+  }
+}
+
 template <bool WITH_ERR, int G8, int S8>
 __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
   __shared__ Lut lut;
@@ -341,12 +581,43 @@ hipError_t launch_assign_t(const AssignBatch& b, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool WITH_ERR, int G16, int S16>
+hipError_t launch_assign_wide_t(const AssignBatch& b, hipStream_t stream) {
+  static int occ = 0;
+  if (occ <= 0) {
+    int blocks = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &blocks, assign_wide_kernel<WITH_ERR, G16, S16>, kBlock, 0);
+    occ = (e == hipSuccess && blocks > 0) ? blocks : 2;
+  }
+  const int64_t want = (int64_t)device_cu_count() * occ;
+  const int grid = (int)(b.total_tasks < want ? b.total_tasks : want);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL((assign_wide_kernel<WITH_ERR, G16, S16>), dim3(grid), dim3(kBlock), 0, stream,
+                     b);
+  return hipGetLastError();
+}
+
 template <bool WITH_ERR>
 hipError_t launch_assign_g(const AssignBatch& b, hipStream_t stream) {
+  if (b.S >= kWideLane) {
+    // same jobs, task numbering of the wide mapping
+    AssignBatch w = b;
+    int64_t tb = 0;
+    for (int i = 0; i < w.njobs; ++i) {
+      w.job[i].geom = make_geom(b.job[i].geom.R, b.job[i].geom.C, tb, kWideSlab,
+                                kWideRowsPerTask);
+      tb += w.job[i].geom.ntasks;
+    }
+    w.total_tasks = tb;
+    const int g16 = b.g / kWideLane, s16 = b.S / kWideLane;
+    if (g16 == 8 && s16 == 8) return launch_assign_wide_t<WITH_ERR, 8, 8>(w, stream);   // 128/128
+    if (g16 == 8 && s16 == 1) return launch_assign_wide_t<WITH_ERR, 8, 1>(w, stream);   // 128/16
+    if (g16 == 1 && s16 == 1) return launch_assign_wide_t<WITH_ERR, 1, 1>(w, stream);   // 16/16
+    return launch_assign_wide_t<WITH_ERR, 0, 0>(w, stream);
+  }
   const int g8 = b.g / kPerLane, s8 = b.S / kPerLane;
-  if (g8 == 16 && s8 == 16) return launch_assign_t<WITH_ERR, 16, 16>(b, stream);   // g = S = 128
-  if (g8 == 16 && s8 == 2) return launch_assign_t<WITH_ERR, 16, 2>(b, stream);     // g 128, S 16
-  if (g8 == 2 && s8 == 2) return launch_assign_t<WITH_ERR, 2, 2>(b, stream);       // g = S = 16
+  if (g8 == 16 && s8 == 16) return launch_assign_t<WITH_ERR, 16, 16>(b, stream);
   return launch_assign_t<WITH_ERR, 0, 0>(b, stream);
 }
 

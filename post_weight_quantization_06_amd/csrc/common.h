@@ -77,9 +77,12 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
 }
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
+  // every control used here reads a lane of the same 16-lane row, so no lane keeps an old value:
+  // mov_dpp needs no initialised destination
   const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = dpp_u32<CTRL>((uint32_t)b);
-  const uint32_t hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, true);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF,
+                                                         true);
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
@@ -140,6 +143,21 @@ __device__ __forceinline__ uint32_t lane_absmax_bits(const uint4& v) {
   return max(max(a, b), max(c, d));
 }
 
+// Largest |w| of the 16 bf16 of two 16-byte loads, as the bf16 magnitude bit pattern: sign bits
+// cleared, then packed 16-bit maxima.
+__device__ __forceinline__ uint32_t lane_absmax16_bits(const uint4& a, const uint4& b) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t m = 0x7fff7fffu;
+  const u16x2 x0 = __builtin_bit_cast(u16x2, a.x & m), x1 = __builtin_bit_cast(u16x2, a.y & m);
+  const u16x2 x2 = __builtin_bit_cast(u16x2, a.z & m), x3 = __builtin_bit_cast(u16x2, a.w & m);
+  const u16x2 x4 = __builtin_bit_cast(u16x2, b.x & m), x5 = __builtin_bit_cast(u16x2, b.y & m);
+  const u16x2 x6 = __builtin_bit_cast(u16x2, b.z & m), x7 = __builtin_bit_cast(u16x2, b.w & m);
+  const u16x2 y = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_elementwise_max(x0, x1), __builtin_elementwise_max(x2, x3)),
+      __builtin_elementwise_max(__builtin_elementwise_max(x4, x5), __builtin_elementwise_max(x6, x7)));
+  return max((uint32_t)y.x, (uint32_t)y.y);
+}
+
 __device__ __forceinline__ void unpack8(const uint4& v, float (&w)[8]) {
   w[0] = bf16_lo(v.x); w[1] = bf16_hi(v.x);
   w[2] = bf16_lo(v.y); w[3] = bf16_hi(v.y);
@@ -153,9 +171,9 @@ __device__ __forceinline__ void unpack8(const uint4& v, float (&w)[8]) {
 struct MatrixGeom {
   int64_t R;
   int32_t C;
-  int32_t nslab;       // ceil(C / 512)
+  int32_t nslab;       // ceil(C / slab width)
   int64_t task_begin;  // first task of this job in the batch-wide numbering
-  int64_t ntasks;      // ceil(R / kRowsPerTask) * nslab
+  int64_t ntasks;      // ceil(R / rows per task) * nslab
 };
 
 struct AssignJob {
@@ -223,13 +241,14 @@ hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, const ui
                           const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
                           uint16_t* W_hat, hipStream_t stream);
 
-inline MatrixGeom make_geom(int64_t R, int64_t C, int64_t task_begin) {
+inline MatrixGeom make_geom(int64_t R, int64_t C, int64_t task_begin, int slab = kSlab,
+                            int rows_per_task = kRowsPerTask) {
   MatrixGeom m;
   m.R = R;
   m.C = (int32_t)C;
-  m.nslab = (int32_t)((C + kSlab - 1) / kSlab);
+  m.nslab = (int32_t)((C + slab - 1) / slab);
   m.task_begin = task_begin;
-  m.ntasks = ((R + kRowsPerTask - 1) / kRowsPerTask) * (int64_t)m.nslab;
+  m.ntasks = ((R + rows_per_task - 1) / rows_per_task) * (int64_t)m.nslab;
   return m;
 }
 
