@@ -153,7 +153,7 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
   int64_t tb = 0;
   for (int i = 0; i < count; ++i) {
     RefineJob& j = b.job[i];
-    j.geom = make_geom(R[i], C[i], tb);
+    j.geom = refine_geom(R[i], C[i], tb, S);
     tb += j.geom.ntasks;
     j.W = W[i];
     j.I = I[i];

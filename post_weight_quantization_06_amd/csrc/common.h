@@ -225,6 +225,8 @@ int device_cu_count();
 hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream);
 hipError_t launch_refine(RefineBatch& b, hipStream_t stream);
 int refine_grid(int64_t total_tasks);
+// Task geometry of the refine kernel for one matrix (it depends on the selection group size).
+MatrixGeom refine_geom(int64_t R, int64_t C, int64_t task_begin, int S);
 
 hipError_t launch_importance(const float* X, int64_t T, int64_t K, int64_t ldx, double* I_acc,
                              float* I_out, double* partials, int nsplit, hipStream_t stream);

@@ -13,6 +13,8 @@
 //
 // The bins take 128 KB, one workgroup per CU; to keep enough bytes in flight each wave loads the
 // rows of its next task before it accumulates the current one.
+#include <type_traits>
+
 #include "common.h"
 
 namespace aaac {
@@ -109,6 +111,106 @@ __device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, Refin
   }
 }
 
+// Wide mapping for selection groups of at least 16 weights: a lane holds 16 consecutive weights,
+// a wave row covers 1024 columns, a task is 16 rows x 1024 columns (four rows per wave).
+constexpr int kWideLane = 16;
+constexpr int kWideSlab = kWave * kWideLane;
+constexpr int kWideRowsPerWave = 4;
+constexpr int kWideRowsPerTask = kWideRowsPerWave * kWavesPerBlock;
+
+struct TaskRows16 {
+  uint4 va[kWideRowsPerWave], vb[kWideRowsPerWave];
+  uint2 cw[kWideRowsPerWave];
+  uint32_t sb[kWideRowsPerWave];
+  float4 I[4];
+  int64_t r0;
+  int64_t R;
+  int job;
+  bool active;
+};
+
+__device__ __forceinline__ void load_task16(const RefineBatch& b, int64_t task, int log2S,
+                                            TaskRows16& t) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int j = 0;
+  while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
+  const RefineJob& jb = b.job[j];
+  const int64_t local = task - jb.geom.task_begin;
+  const int64_t rb = local / jb.geom.nslab;
+  const int slab = (int)(local - rb * jb.geom.nslab);
+  const int c0 = slab * kWideSlab + lane * kWideLane;
+  const int64_t R = jb.geom.R, C = jb.geom.C;
+  t.active = c0 < C;
+  const int64_t cl = t.active ? c0 : 0;
+  t.job = j;
+  t.R = R;
+  t.r0 = rb * kWideRowsPerTask + wave;
+#pragma unroll
+  for (int i = 0; i < kWideRowsPerWave; ++i) {
+    int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
+    r = r < R ? r : R - 1;
+    const int64_t base = r * C + cl;
+    t.va[i] = *reinterpret_cast<const uint4*>(jb.W + base);
+    t.vb[i] = *reinterpret_cast<const uint4*>(jb.W + base + 8);
+    t.cw[i] = *reinterpret_cast<const uint2*>(jb.codes + (base >> 3));
+    t.sb[i] = jb.sel[base >> log2S];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
+}
+
+template <int G16>
+__device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, RefineShared& sh) {
+  const int tid = threadIdx.x;
+  const float If[16] = {t.I[0].x, t.I[0].y, t.I[0].z, t.I[0].w, t.I[1].x, t.I[1].y,
+                        t.I[1].z, t.I[1].w, t.I[2].x, t.I[2].y, t.I[2].z, t.I[2].w,
+                        t.I[3].x, t.I[3].y, t.I[3].z, t.I[3].w};
+  char* const lds = reinterpret_cast<char*>(&sh.bins[0][0][0]) + tid * sizeof(double);
+  float s[kWideRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kWideRowsPerWave; ++i)
+    s[i] = __uint_as_float(block_max_u32_t<G16>(lane_absmax16_bits(t.va[i], t.vb[i]), g16)
+                           << 16);
+#pragma unroll
+  for (int i = 0; i < kWideRowsPerWave; ++i) {
+    if (t.r0 + (int64_t)kWavesPerBlock * i >= t.R) break;
+    const double s2 = (double)(s[i] * s[i]);     // exact: s has 8 significant bits
+    float w[16];
+    unpack8(t.va[i], *reinterpret_cast<float(*)[8]>(&w[0]));
+    unpack8(t.vb[i], *reinterpret_cast<float(*)[8]>(&w[8]));
+    char* const row = lds + (t.sb[i] ? 16 * sizeof(sh.bins[0]) : 0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t word = k < 8 ? t.cw[i].x : t.cw[i].y;
+      const uint32_t q = (word >> (4 * (k & 7))) & 15u;
+      double* const p = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
+      const double Id = t.active ? (double)If[k] : 0.0;
+      atomicAdd(p, Id * (double)(s[i] * w[k]));    // s w is exact in fp32
+      atomicAdd(p + kBlock, Id * s2);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The two task layouts behind one name each, chosen by the buffer type.
+__device__ __forceinline__ void load_rows(const RefineBatch& b, int64_t task, int log2S,
+                                          TaskRows& t) {
+  load_task(b, task, log2S, t);
+}
+__device__ __forceinline__ void load_rows(const RefineBatch& b, int64_t task, int log2S,
+                                          TaskRows16& t) {
+  load_task16(b, task, log2S, t);
+}
+template <int GL>
+__device__ __forceinline__ void accumulate_rows(const TaskRows& t, int gl, RefineShared& sh) {
+  accumulate_task<GL>(t, gl, sh);
+}
+template <int GL>
+__device__ __forceinline__ void accumulate_rows(const TaskRows16& t, int gl, RefineShared& sh) {
+  accumulate_task16<GL>(t, gl, sh);
+}
+
 // Round a finite fp64 value to bf16 (ties to even) directly, without an intermediate fp32
 // rounding: the quantum of x's binade (8 significant bits; below 2^-126 the fixed subnormal quantum
 // 2^-133) divides x exactly, rint rounds half to even, and the product is exact.
@@ -179,44 +281,47 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
 
 }  // namespace
 
-template <int G8>
+template <bool WIDE, int GL>
 __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
   __shared__ RefineShared sh;
   const int tid = threadIdx.x;
-  const int g8 = b.g / kPerLane;
+  const int gl = b.g / (WIDE ? kWideLane : kPerLane);   // lanes per scale group
   const int log2S = 31 - __builtin_clz((unsigned)b.S);
 #pragma unroll
   for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
   const int64_t t_begin = task_lo(blockIdx.x, b.total_tasks, gridDim.x);
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
-  // three statically named buffers: the rows of tasks t + 1 and t + 2 are in flight while task t
-  // accumulates
   // two statically named buffers: the rows of task t + 1 are in flight while task t accumulates
-  // (26 loads per task and wave, so both tasks stay within the 63 loads a wave can track)
-  TaskRows A, B;
+  typedef typename std::conditional<WIDE, TaskRows16, TaskRows>::type Rows;
+  Rows A, B;
   int cur = -1;
   const int64_t last = t_end - 1;
   // the prefetch index is clamped to the last task: past the end a buffer reloads that task and is
   // never used
 #define AAAC_NEXT(x) ((x) < last ? (x) : last)
-  if (t_begin < t_end) load_task(b, t_begin, log2S, A);
+  if (t_begin < t_end) load_rows(b, t_begin, log2S, A);
   for (int64_t task = t_begin; task < t_end; task += 2) {
-    load_task(b, AAAC_NEXT(task + 1), log2S, B);
+    load_rows(b, AAAC_NEXT(task + 1), log2S, B);
     if (A.job != cur) {
       if (cur >= 0) finish_job(b, cur, sh);
       cur = A.job;
     }
-    accumulate_task<G8>(A, g8, sh);
+    accumulate_rows<GL>(A, gl, sh);
     if (task + 1 >= t_end) break;
-    load_task(b, AAAC_NEXT(task + 2), log2S, A);
+    load_rows(b, AAAC_NEXT(task + 2), log2S, A);
     if (B.job != cur) {
       finish_job(b, cur, sh);
       cur = B.job;
     }
-    accumulate_task<G8>(B, g8, sh);
+    accumulate_rows<GL>(B, gl, sh);
   }
 #undef AAAC_NEXT
   if (cur >= 0) finish_job(b, cur, sh);
+}
+
+MatrixGeom refine_geom(int64_t R, int64_t C, int64_t task_begin, int S) {
+  return S >= kWideLane ? make_geom(R, C, task_begin, kWideSlab, kWideRowsPerTask)
+                        : make_geom(R, C, task_begin);
 }
 
 // The bins fill most of the LDS: one workgroup per CU.
@@ -227,13 +332,18 @@ int refine_grid(int64_t total_tasks) {
 
 hipError_t launch_refine(RefineBatch& b, hipStream_t stream) {
   if (b.nblocks <= 0) return hipSuccess;
-  const int g8 = b.g / kPerLane;
-  if (g8 == 16)
-    hipLaunchKernelGGL(refine_kernel<16>, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
-  else if (g8 == 2)
-    hipLaunchKernelGGL(refine_kernel<2>, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
-  else
-    hipLaunchKernelGGL(refine_kernel<0>, dim3(b.nblocks), dim3(kBlock), 0, stream, b);
+  const dim3 grid(b.nblocks), block(kBlock);
+  if (b.S >= kWideLane) {
+    const int g16 = b.g / kWideLane;
+    if (g16 == 8)
+      hipLaunchKernelGGL((refine_kernel<true, 8>), grid, block, 0, stream, b);
+    else if (g16 == 1)
+      hipLaunchKernelGGL((refine_kernel<true, 1>), grid, block, 0, stream, b);
+    else
+      hipLaunchKernelGGL((refine_kernel<true, 0>), grid, block, 0, stream, b);
+  } else {
+    hipLaunchKernelGGL((refine_kernel<false, 0>), grid, block, 0, stream, b);
+  }
   return hipGetLastError();
 }
 
