@@ -127,24 +127,11 @@ aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, con
   return hip_status(launch_assign(b, err != nullptr, static_cast<hipStream_t>(stream)), who);
 }
 
-aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
-                      int g, int S, int n, const float* const* I, const uint8_t* const* codes,
-                      const uint8_t* const* sel, const float* const* tin, float* const* tout,
-                      int flags, void* ws, size_t ws_bytes, void* stream, const char* who) {
-  aaac_status st = check_batch(count, W, R, C, g, S, n, who);
-  if (st != AAAC_OK) return st;
-  if (flags & ~AAAC_REFINE_ROUND_BF16) return fail(AAAC_ERR_INVALID_ARG, "%s: unknown flags %d", who, flags);
-  if (!I || !codes || !sel || !tin || !tout) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
-  for (int i = 0; i < count; ++i) {
-    if (!I[i] || !aligned(I[i], 16) || !codes[i] || !aligned(codes[i], 16) || !sel[i] || !tin[i] ||
-        !tout[i] || !aligned(tin[i], 4) || !aligned(tout[i], 4))
-      return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: null or misaligned pointer", who, i);
-  }
-  const size_t need = refine_ws_bytes(count);
-  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
-  if (ws_bytes < need)
-    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
-  RefineBatch b{};
+// Batch description shared by refine and the fused assign + accumulate: task geometry, grid,
+// and the workgroup range that meets each job (its slots in the partials).
+void build_refine_batch(RefineBatch& b, int count, const uint16_t* const* W, const int64_t* R,
+                        const int64_t* C, int g, int S, int n, const float* const* I, int flags,
+                        void* ws) {
   b.njobs = count;
   b.g = g;
   b.S = S;
@@ -157,10 +144,6 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
     tb += j.geom.ntasks;
     j.W = W[i];
     j.I = I[i];
-    j.codes = reinterpret_cast<const uint32_t*>(codes[i]);
-    j.sel = sel[i];
-    j.tables_in = tin[i];
-    j.tables_out = tout[i];
   }
   b.total_tasks = tb;
   int64_t nb = refine_grid(tb);
@@ -187,8 +170,43 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
   b.slots = slots;
   b.counters = static_cast<uint32_t*>(ws);
   b.partials = reinterpret_cast<double*>(static_cast<char*>(ws) + 256);
+}
+
+aaac_status check_refine_ws(int count, void* ws, size_t ws_bytes, const char* who) {
+  const size_t need = refine_ws_bytes(count);
+  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
+  if (ws_bytes < need)
+    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  return AAAC_OK;
+}
+
+aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                      int g, int S, int n, const float* const* I, const uint8_t* const* codes,
+                      const uint8_t* const* sel, const float* const* tin, float* const* tout,
+                      int flags, void* ws, size_t ws_bytes, void* stream, const char* who) {
+  aaac_status st = check_batch(count, W, R, C, g, S, n, who);
+  if (st != AAAC_OK) return st;
+  if (flags & ~AAAC_REFINE_ROUND_BF16) return fail(AAAC_ERR_INVALID_ARG, "%s: unknown flags %d", who, flags);
+  if (!I || !codes || !sel || !tin || !tout) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    if (!I[i] || !aligned(I[i], 16) || !codes[i] || !aligned(codes[i], 16) || !sel[i] || !tin[i] ||
+        !tout[i] || !aligned(tin[i], 4) || !aligned(tout[i], 4))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: null or misaligned pointer", who, i);
+  }
+  st = check_refine_ws(count, ws, ws_bytes, who);
+  if (st != AAAC_OK) return st;
+  RefineBatch b{};
+  build_refine_batch(b, count, W, R, C, g, S, n, I, flags, ws);
+  for (int i = 0; i < count; ++i) {
+    RefineJob& j = b.job[i];
+    j.codes = reinterpret_cast<const uint32_t*>(codes[i]);
+    j.sel = sel[i];
+    j.tables_in = tin[i];
+    j.tables_out = tout[i];
+  }
   return hip_status(launch_refine(b, static_cast<hipStream_t>(stream)), who);
 }
+
 
 }  // namespace
 

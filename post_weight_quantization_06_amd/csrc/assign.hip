@@ -1,133 +1,16 @@
-// Assign step (AAAC summary §2 mechanisms 2 and 4).
+// Assign step (AAAC summary §2 mechanisms 2 and 4): nearest entries in both tables, selection of
+// the table with the lower activation-weighted error, selected codes and selectors written out.
+// The lookup structure, the per-weight search and the selection are in lookup.h.
 //
-// For every weight w of a scale group with scale s = max|w| and each table c, the nearest entry
-// q_c minimizes |u - T_c[j]| with u = w / s, ties to the lower index. Because s > 0 this is the
-// same as minimizing |w - s T_c[j]|, and the kernel decides it on r = fma(-s, T, w), the exactly
-// rounded residual: when the rounded magnitudes differ, the exact ones differ the same way, and
-// when they are equal the two squared distances agree to 2^-22 relative. Candidates come from a
-// 1024-record table indexed by an approximate u, built so that each record lists every entry that
-// can be nearest anywhere in (a slightly widened copy of) its interval; a record that would need
-// more than two candidates routes its group to an exact full scan.
-//
-// Per selection group the kernel forms D = E_1 - E_0 = sum I_k (m_1^2 - m_0^2) with m_c the chosen
-// residual magnitude: fp32 over four weights, then fp64. The selection is D < 0 (ties keep T0).
-// Its rounding error is below 8 * 2^-24 (E_0 + E_1), so a selection can only differ from the exact
-// one when |E_1 - E_0| < 1e-6 max(E_0, E_1).
-//
-// Work split: workgroup b owns a contiguous range of tasks (kRowsPerTask rows of one 512-column
-// slab of one matrix); each of its waves issues the loads of all its rows of a task before it
-// processes the first one, and builds the lookup table in LDS whenever it moves to another matrix.
-#include "common.h"
+// Work split: workgroup b owns a contiguous range of tasks (rows x one column slab of one matrix);
+// each of its waves issues the loads of all its rows of a task before it processes the first one,
+// and the workgroup rebuilds the lookup structure in LDS whenever it moves to another matrix. Two
+// mappings: 16 weights per lane for selection groups of 16 or more, 8 weights per lane otherwise.
+#include "lookup.h"
 
 namespace aaac {
 
 namespace {
-
-struct LutScratch {
-  float raw[2][16];
-  int first[2][16];
-  float sv[2][16];          // distinct values, ascending
-  int six[2][16];           // lowest index holding each distinct value
-  int mlo[2][16];           // midpoint i lies in record rho iff mlo[i] <= rho <= mhi[i]
-  int mhi[2][16];           // and lies below record rho iff mhi[i] < rho
-  int m[2];                 // distinct values (0: the table has a non-finite entry)
-};
-
-// The lookup structure in LDS: per record the byte offsets of the two candidate pairs and the code
-// base, and per table the pair arrays.
-struct Lut {
-  uint8_t off0[kLutRecs];
-  uint8_t off1[kLutRecs];
-  uint8_t code[kLutRecs];
-  float2 pairs[2][kPairs];
-  float tab[2][16];         // the raw tables, for the exact scan
-};
-
-// Build the lookup structure for tables T (fp32 [2][n], global) with all threads of the block.
-// Must be called by every thread; ends with a barrier.
-__device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScratch& ls) {
-  const int tid = threadIdx.x;
-  const float qnan = __uint_as_float(0x7fc00000u);
-  if (tid < 32) {
-    const int c = tid >> 4, j = tid & 15;
-    const float x = j < n ? T[c * n + j] : 0.0f;
-    ls.raw[c][j] = x;
-    lut.tab[c][j] = x;
-  }
-  __syncthreads();
-  if (tid < 32) {
-    const int c = tid >> 4, j = tid & 15;
-    const float x = ls.raw[c][j];
-    bool first = j < n;
-    for (int k = 0; k < j; ++k) first = first && !(ls.raw[c][k] == x);
-    ls.first[c][j] = first ? 1 : 0;
-    // pair j: {T[j], T[j + 1]}, the entry past the end reads as +inf
-    const float nxt = (j + 1 < n) ? ls.raw[c][j + 1 < 16 ? j + 1 : 15] : __builtin_inff();
-    lut.pairs[c][j] = make_float2(j < n ? x : __builtin_inff(), nxt);
-    if (j < 2) lut.pairs[c][16 + j] = j == 0 ? make_float2(__builtin_inff(), __builtin_inff())
-                                             : make_float2(qnan, qnan);
-  }
-  __syncthreads();
-  if (tid < 32) {
-    const int c = tid >> 4, j = tid & 15;
-    const float x = ls.raw[c][j];
-    int rank = 0, m = 0;
-    bool finite = true;
-    for (int k = 0; k < n; ++k) {
-      const float y = ls.raw[c][k];
-      finite = finite && isfinite(y);
-      if (ls.first[c][k]) {
-        ++m;
-        if (y < x) ++rank;
-      }
-    }
-    if (ls.first[c][j] && finite) {
-      ls.sv[c][rank] = x;
-      ls.six[c][rank] = j;
-    }
-    if (j == 0) ls.m[c] = finite ? m : 0;
-  }
-  __syncthreads();
-  if (tid < 32) {
-    const int c = tid >> 4, i = tid & 15;
-    if (i + 1 < ls.m[c]) {
-      const double M = 0.5 * ((double)ls.sv[c][i] + (double)ls.sv[c][i + 1]);
-      const double S = (double)kLutScale;
-      const double hi = floor((M + 1.0 + kLutSlack) * S + 1.5);
-      const double lo = ceil((M + 1.0 - kLutSlack) * S + 0.5);
-      ls.mhi[c][i] = (int)fmin(fmax(hi, -1.0), 4096.0);
-      ls.mlo[c][i] = (int)fmin(fmax(lo, -1.0), 4096.0);
-    }
-  }
-  __syncthreads();
-  for (int rho = tid; rho < kLutRecs; rho += kBlock) {
-    uint32_t off[2];
-    uint32_t code = 0;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int m = ls.m[c];
-      int below = 0, inside = 0;
-      for (int i = 0; i + 1 < m; ++i) {
-        below += (ls.mhi[c][i] < rho) ? 1 : 0;
-        inside += (ls.mlo[c][i] <= rho && rho <= ls.mhi[c][i]) ? 1 : 0;
-      }
-      // clamped indices keep every read inside the arrays whatever the branch
-      const int j0 = below < 15 ? below : 15;
-      const int j1 = below + 1 < 15 ? below + 1 : 15;
-      // one candidate: pair {T[i], T[i + 1]} whose second entry is never strictly nearer inside
-      // the record; two candidates: only when they are consecutive entries i, i + 1
-      const bool single = m > 0 && inside == 0;
-      const bool pair = m > 0 && inside == 1 && ls.six[c][j1] == ls.six[c][j0] + 1;
-      const int i0 = ls.six[c][j0];
-      off[c] = (uint32_t)((single || pair) ? i0 : kNaNPair) * 8u;
-      code |= (single || pair) ? ((uint32_t)i0 << (4 * c)) : 0u;
-    }
-    lut.off0[rho] = (uint8_t)off[0];
-    lut.off1[rho] = (uint8_t)off[1];
-    lut.code[rho] = (uint8_t)code;
-  }
-  __syncthreads();
-}
 
 struct RowOut {
   double D;         // E_1 - E_0 of the lane's selection group (after the butterfly)
@@ -271,190 +154,15 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
 
 }  // namespace
 
-// ---------------------------------------------------------------------------------------------
-// Wide mapping for selection groups of at least 16 weights: a lane holds 16 consecutive weights
-// (two 16-byte loads), a wave row covers 1024 columns, a task is 16 rows x 1024 columns (four rows
-// per wave). The per-row work (scale, selection sum, code compaction) is spread over twice as many
-// weights as in the 8-weight mapping.
-// ---------------------------------------------------------------------------------------------
-constexpr int kWideLane = 16;
-constexpr int kWideSlab = kWave * kWideLane;
-constexpr int kWideRowsPerWave = 4;
-constexpr int kWideRowsPerTask = kWideRowsPerWave * kWavesPerBlock;
-
-// Nearest entries of one weight in both tables from the lookup structure (see the layout above):
-// returns the code byte q0 | q1 << 4 and accumulates I (m1^2 - m0^2) (and the two errors).
-template <bool WITH_ERR>
-__device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, const Lut& lut,
-                                                  float Ik, float& acc, float& a0, float& a1) {
-  const float t = __builtin_fmaf(w, Y, kLutMagic);
-  const uint32_t rho = __float_as_uint(t) & kLutMask;
-  const uint32_t cb = lut.code[rho];
-  const float2 p0 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[0]) + lut.off0[rho]);
-  const float2 p1 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[1]) + lut.off1[rho]);
-  const float r0a = __builtin_fmaf(nse, p0.x, w);
-  const float r0b = __builtin_fmaf(nse, p0.y, w);
-  const float r1a = __builtin_fmaf(nse, p1.x, w);
-  const float r1b = __builtin_fmaf(nse, p1.y, w);
-  const bool d0 = fabsf(r0b) < fabsf(r0a);
-  const bool d1 = fabsf(r1b) < fabsf(r1a);
-  const float m0 = fminf(fabsf(r0a), fabsf(r0b));
-  const float m1 = fminf(fabsf(r1a), fabsf(r1b));
-  const float e0 = m0 * m0;
-  acc = __builtin_fmaf(Ik, __builtin_fmaf(m1, m1, -e0), acc);
-  if (WITH_ERR) {
-    a0 = __builtin_fmaf(Ik, e0, a0);
-    a1 = __builtin_fmaf(Ik, m1 * m1, a1);
-  }
-  return cb + (d0 ? 1u : 0u) + (d1 ? 16u : 0u);
-}
-
-// Keep the nibble of table `sel` from four code bytes (q0 | q1 << 4): bytes 0 and 2 of the result
-// hold two codes each.
-__device__ __forceinline__ uint32_t select_nibbles(uint32_t P, uint32_t sel) {
-  uint32_t p = (P >> (sel ? 4u : 0u)) & 0x0F0F0F0Fu;
-  return p | (p >> 4);
-}
-
-// Exact fallback for one lane of the wide mapping, reading its 16 weights and importances again
-// from memory (they are in cache) so that the fast path keeps no copies in registers: full scan of
-// both tables on operands scaled by a power of two that brings s into [1, 4). Codes come back as
-// bytes q0 | q1 << 4, weight k in byte k of (lo, hi).
-template <bool WITH_ERR>
-__device__ __noinline__ void slow_lane16(const uint16_t* __restrict__ wp,
-                                         const float* __restrict__ ip, uint32_t amax,
-                                         const float (*tab)[16], int n, double& D, double& E0,
-                                         double& E1, uint64_t& lo, uint64_t& hi) {
-  const uint32_t E = min(max(amax >> 7, 1u), 253u);
-  const float P = __uint_as_float((254u - E) << 23);
-  const float sp = __uint_as_float(amax << 16) * P;
-  double d = 0.0, e0 = 0.0, e1 = 0.0;
-  uint64_t cl = 0, ch = 0;
-#pragma unroll 1
-  for (int k = 0; k < kWideLane; ++k) {
-    const float wv = __uint_as_float((uint32_t)wp[k] << 16) * P;
-    const double Ik = (double)ip[k];
-    float best0 = __builtin_inff(), best1 = __builtin_inff();
-    uint32_t q0 = 0, q1 = 0;
-    for (int j = 0; j < n; ++j) {
-      const float r0 = fabsf(__builtin_fmaf(-sp, tab[0][j], wv));
-      const float r1 = fabsf(__builtin_fmaf(-sp, tab[1][j], wv));
-      if (r0 < best0) { best0 = r0; q0 = j; }
-      if (r1 < best1) { best1 = r1; q1 = j; }
-    }
-    const double b0 = (double)best0 * (double)best0;
-    const double b1 = (double)best1 * (double)best1;
-    d += Ik * (b1 - b0);
-    if (WITH_ERR) {
-      e0 += Ik * b0;
-      e1 += Ik * b1;
-    }
-    const uint64_t c = (uint64_t)(q0 | (q1 << 4));
-    if (k < 8) cl |= c << (8 * k); else ch |= c << (8 * (k - 8));
-  }
-  const double inv = 1.0 / ((double)P * (double)P);
-  D = d;
-  E0 = e0 * inv;
-  E1 = e1 * inv;
-  lo = cl;
-  hi = ch;
-}
-
 template <bool WITH_ERR, int G16, int S16>
 __device__ __forceinline__ void assign_row16(const AssignJob& jb, const Lut& lut, int n, int g16,
                                              int s16, int log2S, int64_t base, bool active,
                                              const uint16_t* wsafe, const float* isafe,
                                              const uint4& va, const uint4& vb,
                                              const float (&Ik)[16]) {
-  const uint32_t amax = block_max_u32_t<G16>(lane_absmax16_bits(va, vb), g16);
-  const float s = __uint_as_float(amax << 16);
-  float w[16];
-  {
-    float wa[8], wb[8];
-    unpack8(va, wa);
-    unpack8(vb, wb);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      w[k] = wa[k];
-      w[8 + k] = wb[k];
-    }
-  }
-  const bool zero = (s == 0.0f);
-  const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
-  const float se = zero ? 1.0f : s;
-  const float Y = kLutScale * __builtin_amdgcn_rcpf(se);
-  const float nse = -se;
-
-  double accd = 0.0, e0d = 0.0, e1d = 0.0;
-  uint32_t P[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // four weights per fp32 partial, then fp64
-    float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
-    uint32_t word = 0;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t c = lookup_weight<WITH_ERR>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc,
-                                                 a0, a1);
-      word |= c << (8 * k);
-    }
-    P[q] = word;
-    accd = (q == 0) ? (double)acc : accd + (double)acc;
-    if (WITH_ERR) {
-      e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
-      e1d = (q == 0) ? (double)a1 : e1d + (double)a1;
-    }
-    // four weights' lookups in flight at a time keep the live registers within three waves per
-    // SIMD; the other waves hide the LDS latency
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  double D = block_sum_f64_t<S16>(accd, s16);
-  double E0 = WITH_ERR ? block_sum_f64_t<S16>(e0d, s16) : 0.0;
-  double E1 = WITH_ERR ? block_sum_f64_t<S16>(e1d, s16) : 0.0;
-  if (zero) {
-    D = 0.0;
-    E0 = 0.0;
-    E1 = 0.0;
-  }
-  const bool bad = active && (!fast_scale || !(fabs(D) < __builtin_inf()));
-  if (__any(bad)) {
-    double lD, lE0, lE1;
-    uint64_t clo, chi;
-    slow_lane16<WITH_ERR>(wsafe, isafe, amax, lut.tab, n, lD, lE0, lE1, clo, chi);
-    const double sD = block_sum_f64_t<S16>(lD, s16);
-    double sE0 = 0.0, sE1 = 0.0;
-    if (WITH_ERR) {
-      sE0 = block_sum_f64_t<S16>(lE0, s16);
-      sE1 = block_sum_f64_t<S16>(lE1, s16);
-    }
-    if (bad) {
-      D = sD;
-      E0 = sE0;
-      E1 = sE1;
-      P[0] = (uint32_t)clo;
-      P[1] = (uint32_t)(clo >> 32);
-      P[2] = (uint32_t)chi;
-      P[3] = (uint32_t)(chi >> 32);
-    }
-  }
-  const uint32_t sel = (D < 0.0) ? 1u : 0u;
-  const uint32_t lo = __builtin_amdgcn_perm(select_nibbles(P[1], sel), select_nibbles(P[0], sel),
-                                            0x06040200u);
-  const uint32_t hi = __builtin_amdgcn_perm(select_nibbles(P[3], sel), select_nibbles(P[2], sel),
-                                            0x06040200u);
-  if (active) {
-    *reinterpret_cast<uint2*>(jb.codes + (base >> 3)) = make_uint2(lo, hi);
-    if (((base >> 4) & (s16 - 1)) == 0) {
-      const int64_t h = base >> log2S;
-      jb.sel[h] = (uint8_t)sel;
-      if (WITH_ERR) {
-        jb.err[2 * h] = E0;
-        jb.err[2 * h + 1] = E1;
-      }
-    }
-  }
+  Row16 o;
+  row16_core<WITH_ERR, G16, S16>(lut, n, g16, s16, active, wsafe, isafe, va, vb, Ik, o);
+  if (active) store_row16<WITH_ERR>(o, jb.codes, jb.sel, jb.err, s16, log2S, base);
 }
 
 template <bool WITH_ERR, int G16, int S16>

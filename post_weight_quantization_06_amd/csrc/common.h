@@ -21,6 +21,15 @@ constexpr int kPerLane = 8;
 constexpr int kSlab = kWave * kPerLane;
 constexpr int kRowsPerWave = 8;
 constexpr int kRowsPerTask = kRowsPerWave * kWavesPerBlock;
+
+// Wide mapping for selection groups of at least 16 weights: a lane holds 16 consecutive weights
+// (two 16-byte loads), a wave row covers 1024 columns, a task is 16 rows x 1024 columns (four rows
+// per wave). The per-row work (scale, selection sum, code compaction) is spread over twice as many
+// weights as in the 8-weight mapping.
+constexpr int kWideLane = 16;
+constexpr int kWideSlab = kWave * kWideLane;
+constexpr int kWideRowsPerWave = 4;
+constexpr int kWideRowsPerTask = kWideRowsPerWave * kWavesPerBlock;
 constexpr int kMaxJobs = 8;
 
 // ------------------------------------------------------------------------------------------------

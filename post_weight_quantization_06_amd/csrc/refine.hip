@@ -111,13 +111,6 @@ __device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, Refin
   }
 }
 
-// Wide mapping for selection groups of at least 16 weights: a lane holds 16 consecutive weights,
-// a wave row covers 1024 columns, a task is 16 rows x 1024 columns (four rows per wave).
-constexpr int kWideLane = 16;
-constexpr int kWideSlab = kWave * kWideLane;
-constexpr int kWideRowsPerWave = 4;
-constexpr int kWideRowsPerTask = kWideRowsPerWave * kWavesPerBlock;
-
 struct TaskRows16 {
   uint4 va[kWideRowsPerWave], vb[kWideRowsPerWave];
   uint2 cw[kWideRowsPerWave];

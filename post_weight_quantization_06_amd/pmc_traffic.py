@@ -23,9 +23,22 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
-# kernels whose traffic is summarised, keyed by a name fragment of the dispatch
-KERNELS = {"assign": "assign_kernel", "refine": "refine_kernel"}
-KERNEL_SOURCES = {"assign": ["assign.hip", "common.h"], "refine": ["refine.hip", "common.h"]}
+# kernels whose traffic is summarised: name prefixes of the dispatches (after "void ")
+KERNELS = {
+    "assign": ("aaac::assign_wide_kernel<", "aaac::assign_kernel<"),
+    "refine": ("aaac::refine_kernel<",),
+}
+KERNEL_SOURCES = {
+    "assign": ["assign.hip", "lookup.h", "common.h"],
+    "refine": ["refine.hip", "common.h"],
+}
+
+
+def _is(kernel_name, key):
+    name = kernel_name[5:] if kernel_name.startswith("void ") else kernel_name
+    return name.startswith(KERNELS[key])
+
+
 COPY_BYTES = 1 << 30       # the calibration copy: 2^28 fp32 values
 COPY_NAME = "copyBuffer"
 
@@ -46,8 +59,8 @@ def _per_kernel(path, counter):
         raise SystemExit("%s: no calibration copy dispatch" % path)
     calib = max(copy)                                  # the 1 GiB copy is the largest one
     out = {}
-    for key, frag in KERNELS.items():
-        vals = [float(r["Counter_Value"]) for r in rows if frag in r["Kernel_Name"]]
+    for key in KERNELS:
+        vals = [float(r["Counter_Value"]) for r in rows if _is(r["Kernel_Name"], key)]
         if vals:
             out[key] = (sum(vals) / len(vals), len(vals))
     return calib, out
