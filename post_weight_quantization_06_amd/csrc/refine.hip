@@ -30,6 +30,62 @@ struct RefineShared {
   double bins[kCells][2][kBlock];
 };
 
+// Position of the next task to load, kept in scalar registers. The fields of a matrix are read
+// from the kernel arguments only when the cursor enters it: scalar memory reads share a wait
+// counter with LDS operations, so reading them for every task would make the wave wait for all of
+// its LDS adds in flight. Row block and slab advance by counting instead of dividing.
+struct TaskCursor {
+  int64_t task;          // the task the next load reads
+  int64_t last;          // last task of this workgroup: the cursor stops there
+  int64_t job_end;       // first task past the current matrix
+  int64_t rb;            // row block of `task`
+  int64_t R, C;
+  int32_t slab, nslab;
+  int32_t job;
+  const uint16_t* W;
+  const float* I;
+  const uint32_t* codes;
+  const uint8_t* sel;
+};
+
+__device__ __forceinline__ void cursor_enter(const RefineBatch& b, int j, TaskCursor& c) {
+  const RefineJob& jb = b.job[j];
+  c.job = j;
+  c.job_end = jb.geom.task_begin + jb.geom.ntasks;
+  c.nslab = jb.geom.nslab;
+  c.R = jb.geom.R;
+  c.C = jb.geom.C;
+  c.W = jb.W;
+  c.I = jb.I;
+  c.codes = jb.codes;
+  c.sel = jb.sel;
+}
+
+__device__ __forceinline__ void cursor_init(const RefineBatch& b, int64_t task, int64_t last,
+                                            TaskCursor& c) {
+  int j = 0;
+  while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
+  cursor_enter(b, j, c);
+  c.task = task;
+  c.last = last;
+  const int64_t local = task - b.job[j].geom.task_begin;
+  c.rb = local / c.nslab;
+  c.slab = (int32_t)(local - c.rb * c.nslab);
+}
+
+__device__ __forceinline__ void cursor_next(const RefineBatch& b, TaskCursor& c) {
+  if (c.task >= c.last) return;
+  ++c.task;
+  if (c.task >= c.job_end) {
+    cursor_enter(b, c.job + 1, c);
+    c.rb = 0;
+    c.slab = 0;
+  } else if (++c.slab == c.nslab) {
+    c.slab = 0;
+    ++c.rb;
+  }
+}
+
 struct TaskRows {
   uint4 v[kRowsPerWave];
   uint32_t cw[kRowsPerWave];
@@ -46,18 +102,13 @@ struct TaskRows {
 // where it is used (zero importance for the lane; rows past the end are skipped). Loads that are
 // never conditional let the compiler wait for exactly the task being used while later tasks' loads
 // stay in flight.
-__device__ __forceinline__ void load_task(const RefineBatch& b, int64_t task, int log2S,
-                                          TaskRows& t) {
+__device__ __forceinline__ void load_task(const TaskCursor& c, int log2S, TaskRows& t) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  int j = 0;
-  while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
-  const RefineJob& jb = b.job[j];
-  const int64_t local = task - jb.geom.task_begin;
-  const int64_t rb = local / jb.geom.nslab;
-  const int slab = (int)(local - rb * jb.geom.nslab);
-  const int c0 = slab * kSlab + lane * kPerLane;
-  const int64_t R = jb.geom.R, C = jb.geom.C;
+  const int c0 = c.slab * kSlab + lane * kPerLane;
+  const int64_t R = c.R, C = c.C;
+  const int64_t rb = c.rb;
+  const int j = c.job;
   t.active = c0 < C;
   const int64_t cl = t.active ? c0 : 0;
   t.job = j;
@@ -68,12 +119,12 @@ __device__ __forceinline__ void load_task(const RefineBatch& b, int64_t task, in
     int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
     r = r < R ? r : R - 1;
     const int64_t base = r * C + cl;
-    t.v[i] = *reinterpret_cast<const uint4*>(jb.W + base);
-    t.cw[i] = jb.codes[base >> 3];
-    t.sb[i] = jb.sel[base >> log2S];
+    t.v[i] = *reinterpret_cast<const uint4*>(c.W + base);
+    t.cw[i] = c.codes[base >> 3];
+    t.sb[i] = c.sel[base >> log2S];
   }
-  t.I0 = *reinterpret_cast<const float4*>(jb.I + cl);
-  t.I1 = *reinterpret_cast<const float4*>(jb.I + cl + 4);
+  t.I0 = *reinterpret_cast<const float4*>(c.I + cl);
+  t.I1 = *reinterpret_cast<const float4*>(c.I + cl + 4);
 }
 
 template <int G8>
@@ -122,18 +173,13 @@ struct TaskRows16 {
   bool active;
 };
 
-__device__ __forceinline__ void load_task16(const RefineBatch& b, int64_t task, int log2S,
-                                            TaskRows16& t) {
+__device__ __forceinline__ void load_task16(const TaskCursor& c, int log2S, TaskRows16& t) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  int j = 0;
-  while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
-  const RefineJob& jb = b.job[j];
-  const int64_t local = task - jb.geom.task_begin;
-  const int64_t rb = local / jb.geom.nslab;
-  const int slab = (int)(local - rb * jb.geom.nslab);
-  const int c0 = slab * kWideSlab + lane * kWideLane;
-  const int64_t R = jb.geom.R, C = jb.geom.C;
+  const int c0 = c.slab * kWideSlab + lane * kWideLane;
+  const int64_t R = c.R, C = c.C;
+  const int64_t rb = c.rb;
+  const int j = c.job;
   t.active = c0 < C;
   const int64_t cl = t.active ? c0 : 0;
   t.job = j;
@@ -144,13 +190,13 @@ __device__ __forceinline__ void load_task16(const RefineBatch& b, int64_t task, 
     int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
     r = r < R ? r : R - 1;
     const int64_t base = r * C + cl;
-    t.va[i] = *reinterpret_cast<const uint4*>(jb.W + base);
-    t.vb[i] = *reinterpret_cast<const uint4*>(jb.W + base + 8);
-    t.cw[i] = *reinterpret_cast<const uint2*>(jb.codes + (base >> 3));
-    t.sb[i] = jb.sel[base >> log2S];
+    t.va[i] = *reinterpret_cast<const uint4*>(c.W + base);
+    t.vb[i] = *reinterpret_cast<const uint4*>(c.W + base + 8);
+    t.cw[i] = *reinterpret_cast<const uint2*>(c.codes + (base >> 3));
+    t.sb[i] = c.sel[base >> log2S];
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
+  for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(c.I + cl + 4 * q);
 }
 
 template <int G16>
@@ -187,13 +233,11 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
 }
 
 // The two task layouts behind one name each, chosen by the buffer type.
-__device__ __forceinline__ void load_rows(const RefineBatch& b, int64_t task, int log2S,
-                                          TaskRows& t) {
-  load_task(b, task, log2S, t);
+__device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, TaskRows& t) {
+  load_task(c, log2S, t);
 }
-__device__ __forceinline__ void load_rows(const RefineBatch& b, int64_t task, int log2S,
-                                          TaskRows16& t) {
-  load_task16(b, task, log2S, t);
+__device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, TaskRows16& t) {
+  load_task16(c, log2S, t);
 }
 template <int GL>
 __device__ __forceinline__ void accumulate_rows(const TaskRows& t, int gl, RefineShared& sh) {
@@ -288,27 +332,29 @@ __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
   typedef typename std::conditional<WIDE, TaskRows16, TaskRows>::type Rows;
   Rows A, B;
   int cur = -1;
-  const int64_t last = t_end - 1;
-  // the prefetch index is clamped to the last task: past the end a buffer reloads that task and is
-  // never used
-#define AAAC_NEXT(x) ((x) < last ? (x) : last)
-  if (t_begin < t_end) load_rows(b, t_begin, log2S, A);
+  if (t_begin >= t_end) return;
+  // the cursor stops at the last task: past the end a buffer reloads that task and is never used
+  TaskCursor c;
+  cursor_init(b, t_begin, t_end - 1, c);
+  load_rows(c, log2S, A);
+  cursor_next(b, c);
   for (int64_t task = t_begin; task < t_end; task += 2) {
-    load_rows(b, AAAC_NEXT(task + 1), log2S, B);
+    load_rows(c, log2S, B);
+    cursor_next(b, c);
     if (A.job != cur) {
       if (cur >= 0) finish_job(b, cur, sh);
       cur = A.job;
     }
     accumulate_rows<GL>(A, gl, sh);
     if (task + 1 >= t_end) break;
-    load_rows(b, AAAC_NEXT(task + 2), log2S, A);
+    load_rows(c, log2S, A);
+    cursor_next(b, c);
     if (B.job != cur) {
       finish_job(b, cur, sh);
       cur = B.job;
     }
     accumulate_rows<GL>(B, gl, sh);
   }
-#undef AAAC_NEXT
   if (cur >= 0) finish_job(b, cur, sh);
 }
 
