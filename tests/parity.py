@@ -100,6 +100,21 @@ def check_tables(gpu, oracle, rtol=TABLE_RTOL):
     return float(rel.max())
 
 
+def check_tables_bf16(gpu, oracle, rtol=TABLE_RTOL):
+    """Tables rounded to bf16 on the last refine: each GPU entry must be the bf16 rounding of a
+    value within the table tolerance of the oracle's (a value that close to a rounding midpoint may
+    round either way)."""
+    gpu = np.asarray(gpu, dtype=np.float64).reshape(2, -1)
+    oracle = np.asarray(oracle, dtype=np.float64).reshape(2, -1)
+    assert np.array_equal(ref.bf16_round(gpu), gpu), "tables are not bf16 values"
+    scale = np.maximum(np.abs(oracle), TABLE_FLOOR * np.abs(oracle).max())
+    lo = ref.bf16_round(oracle - rtol * scale)
+    hi = ref.bf16_round(oracle + rtol * scale)
+    ok = (gpu >= np.minimum(lo, hi)) & (gpu <= np.maximum(lo, hi))
+    assert ok.all(), "bf16 table mismatch at %s:\n gpu=%r\n ora=%r" % (
+        np.argwhere(~ok).tolist(), gpu, oracle)
+
+
 def oracle_refine(W64, I64, codes, sel, T_in, g, S, chunk_rows=1024):
     n = T_in.shape[1]
     num = np.zeros((2, n))
