@@ -2,8 +2,8 @@
 //
 // Pass 1: the token axis is cut into `nsplit` contiguous ranges; a thread owns VEC consecutive
 // columns of one range and sums the exact fp64 squares in token order (coalesced: a wave reads
-// 64 * VEC consecutive floats of a row). Pass 2: one thread per column adds the range sums in range
-// order to the running fp64 accumulator and writes the fp32 copy. Fixed order, no atomics.
+// 64 * VEC consecutive floats of a row). Pass 2 adds the range sums to the running fp64
+// accumulator and writes the fp32 copy. Fixed order, no atomics.
 #include "common.h"
 
 namespace aaac {
@@ -53,16 +53,33 @@ __global__ __launch_bounds__(kBlock) void importance_partial_kernel(const float*
   for (int v = 0; v < VEC; ++v) out[v] = acc[v];
 }
 
+// Pass 2: a workgroup takes 16 columns; thread group q (16 of them) adds the range sums q, q + 16,
+// q + 32, ... of its column in that order, then group 0 adds the 16 group sums in group order to
+// the running accumulator. Every order is fixed.
+constexpr int kFinCols = 16;
+constexpr int kFinGroups = kBlock / kFinCols;
+
 __global__ __launch_bounds__(kBlock) void importance_finalize_kernel(const double* __restrict__ partials,
                                                                      int nsplit, int64_t K,
                                                                      double* I_acc, float* I_out) {
-  const int64_t k = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (k >= K) return;
+  __shared__ double part[kFinGroups][kFinCols];
+  const int c = threadIdx.x % kFinCols, q = threadIdx.x / kFinCols;
+  const int64_t k = (int64_t)blockIdx.x * kFinCols + c;
   double s = 0.0;
-  for (int i = 0; i < nsplit; ++i) s += partials[(int64_t)i * K + k];
-  const double tot = I_acc[k] + s;
-  I_acc[k] = tot;
-  if (I_out) I_out[k] = (float)tot;
+  if (k < K) {
+#pragma unroll 8
+    for (int i = q; i < nsplit; i += kFinGroups) s += partials[(int64_t)i * K + k];
+  }
+  part[q][c] = s;
+  __syncthreads();
+  if (q == 0 && k < K) {
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < kFinGroups; ++i) sum += part[i][c];
+    const double tot = I_acc[k] + sum;
+    I_acc[k] = tot;
+    if (I_out) I_out[k] = (float)tot;
+  }
 }
 
 int importance_splits(int64_t T, int64_t K) {
@@ -93,7 +110,7 @@ hipError_t launch_importance(const float* X, int64_t T, int64_t K, int64_t ldx, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(importance_finalize_kernel, dim3((unsigned)((K + kBlock - 1) / kBlock)),
+  hipLaunchKernelGGL(importance_finalize_kernel, dim3((unsigned)((K + kFinCols - 1) / kFinCols)),
                      dim3(kBlock), 0, stream, partials, nsplit, K, I_acc, I_out);
   return hipGetLastError();
 }

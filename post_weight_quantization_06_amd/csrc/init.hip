@@ -107,19 +107,40 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __res
 }
 
 // Passes 2-4: histogram of byte `pass` (0-based from the top) of keys whose higher bytes match an
-// active prefix.
+// active prefix. The active prefixes (at most 32, sorted) are found through a 256-slot table
+// indexed by the prefix's low byte; a slot holds up to two prefixes, and a slot that would need
+// more sends its keys to a binary search of the sorted list.
 __global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __restrict__ keys, int64_t N,
                                                            int pass, const InitState* state,
                                                            unsigned long long* hist) {
   __shared__ uint32_t h[kTargets * kDigits];
   __shared__ uint32_t act[kTargets];
+  __shared__ uint32_t slot_pre[kDigits][2];    // prefixes in the slot
+  __shared__ int32_t slot_idx[kDigits][2];     // their positions in the list; -1 empty, -2 overflow
   __shared__ uint32_t nact;
   const int tid = threadIdx.x;
   for (int i = tid; i < kTargets * kDigits; i += kBlock) h[i] = 0;
   if (tid < kTargets) act[tid] = state->active[tid];
   if (tid == 0) nact = state->nactive;
+  slot_idx[tid][0] = -1;
+  slot_idx[tid][1] = -1;
   __syncthreads();
   const int na = (int)nact;
+  if (tid < kDigits) {
+    // thread = slot: collect the active prefixes whose low byte is this slot, in list order
+    int m = 0;
+    for (int t = 0; t < na; ++t) {
+      if ((act[t] & 255u) != (uint32_t)tid) continue;
+      if (m < 2) {
+        slot_pre[tid][m] = act[t];
+        slot_idx[tid][m] = t;
+      } else {
+        slot_idx[tid][0] = -2;
+      }
+      ++m;
+    }
+  }
+  __syncthreads();
   const int pshift = 32 - 8 * pass;       // prefix = key >> pshift
   const int dshift = 24 - 8 * pass;       // digit = (key >> dshift) & 255
   const int64_t n4 = N / 4;
@@ -130,12 +151,21 @@ __global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __res
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t pre = kk[e] >> pshift;
-      int lo = 0, hi = na;                 // first active prefix >= pre
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (act[mid] < pre) lo = mid + 1; else hi = mid;
+      const int sl = (int)(pre & 255u);
+      const int i0 = slot_idx[sl][0];
+      int hit = -1;
+      if (i0 >= 0) {
+        if (slot_pre[sl][0] == pre) hit = i0;
+        else if (slot_idx[sl][1] >= 0 && slot_pre[sl][1] == pre) hit = slot_idx[sl][1];
+      } else if (i0 == -2) {
+        int lo = 0, hi = na;               // first active prefix >= pre
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (act[mid] < pre) lo = mid + 1; else hi = mid;
+        }
+        if (lo < na && act[lo] == pre) hit = lo;
       }
-      if (lo < na && act[lo] == pre) atomicAdd(&h[lo * kDigits + ((kk[e] >> dshift) & 255u)], 1u);
+      if (hit >= 0) atomicAdd(&h[hit * kDigits + ((kk[e] >> dshift) & 255u)], 1u);
     }
   }
   __syncthreads();
@@ -143,7 +173,8 @@ __global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __res
 }
 
 // One workgroup: move every target one byte down, rebuild the active prefix list, clear the
-// histogram; after the last pass write the tables.
+// histogram; after the last pass write the tables. The histogram rows are first copied to LDS with
+// all threads (one coalesced read each) so that each target walks its row there.
 __global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N, int n,
                                                              InitState* state,
                                                              unsigned long long* hist,
@@ -151,6 +182,8 @@ __global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N
   const int tid = threadIdx.x;
   const int nt = 2 * n;
   __shared__ uint32_t newp[kTargets];
+  __shared__ unsigned long long hl[kTargets * kDigits];
+  __shared__ uint32_t first[kTargets];
   if (pass == 0 && tid < nt) {
     // target ranks of reading: T0[j] at floor((2j+1) N / 2n), T1[j] at min(N-1, floor((j+1) N / n))
     const int j = tid % n;
@@ -165,19 +198,21 @@ __global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N
     state->prefix[tid] = 0;
     state->rank[tid] = r;
   }
+  const int rows = pass == 0 ? 1 : (int)state->nactive;
+  for (int i = tid; i < rows * kDigits; i += kBlock) hl[i] = hist[i];
   __syncthreads();
   if (tid < nt) {
     const uint32_t pre = state->prefix[tid];
     int slot = 0;
     if (pass > 0) {
-      const int na = (int)state->nactive;
-      while (slot < na && state->active[slot] != pre) ++slot;
+      while (slot < rows && state->active[slot] != pre) ++slot;
     }
     uint64_t rank = state->rank[tid];
     uint64_t cum = 0;
     int d = 0;
+    const unsigned long long* row = hl + slot * kDigits;
     for (; d < kDigits - 1; ++d) {
-      const uint64_t c = hist[slot * kDigits + d];
+      const uint64_t c = row[d];
       if (rank < cum + c) break;
       cum += c;
     }
@@ -186,22 +221,24 @@ __global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N
   }
   __syncthreads();
   for (int i = tid; i < kTargets * kDigits; i += kBlock) hist[i] = 0ull;
-  if (tid < nt) state->prefix[tid] = newp[tid];
+  if (tid < nt) {
+    state->prefix[tid] = newp[tid];
+    // first occurrence of this prefix among the targets
+    uint32_t f = 1;
+    for (int t = 0; t < tid; ++t) f = (newp[t] == newp[tid]) ? 0u : f;
+    first[tid] = f;
+  }
+  __syncthreads();
+  if (tid < nt && first[tid]) {
+    // position in the sorted list of distinct prefixes
+    int pos = 0;
+    for (int t = 0; t < nt; ++t) pos += (first[t] && newp[t] < newp[tid]) ? 1 : 0;
+    state->active[pos] = newp[tid];
+  }
   if (tid == 0) {
-    // sorted distinct prefixes (at most 32: insertion into a small sorted list)
-    uint32_t list[kTargets];
-    int m = 0;
-    for (int t = 0; t < nt; ++t) {
-      const uint32_t p = newp[t];
-      int pos = 0;
-      while (pos < m && list[pos] < p) ++pos;
-      if (pos < m && list[pos] == p) continue;
-      for (int q = m; q > pos; --q) list[q] = list[q - 1];
-      list[pos] = p;
-      ++m;
-    }
-    for (int t = 0; t < m; ++t) state->active[t] = list[t];
-    state->nactive = (uint32_t)m;
+    uint32_t m = 0;
+    for (int t = 0; t < nt; ++t) m += first[t];
+    state->nactive = m;
   }
   if (pass == 3 && tid < nt) tables[tid] = key_value(newp[tid]);
 }
