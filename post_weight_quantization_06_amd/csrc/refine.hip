@@ -219,14 +219,24 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
     unpack8(t.va[i], *reinterpret_cast<float(*)[8]>(&w[0]));
     unpack8(t.vb[i], *reinterpret_cast<float(*)[8]>(&w[8]));
     char* const row = lds + (t.sb[i] ? 16 * sizeof(sh.bins[0]) : 0);
+    // every term of the row first, then every add: with one wave per SIMD, an add issued right
+    // after the multiply that feeds it would wait for that result
+    double num[16], den[16];
+    double* p[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const uint32_t word = k < 8 ? t.cw[i].x : t.cw[i].y;
       const uint32_t q = (word >> (4 * (k & 7))) & 15u;
-      double* const p = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
+      p[k] = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
       const double Id = t.active ? (double)If[k] : 0.0;
-      atomicAdd(p, Id * (double)(s[i] * w[k]));    // s w is exact in fp32
-      atomicAdd(p + kBlock, Id * s2);
+      num[k] = Id * (double)(s[i] * w[k]);       // s w is exact in fp32
+      den[k] = Id * s2;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      atomicAdd(p[k], num[k]);
+      atomicAdd(p[k] + kBlock, den[k]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -270,11 +280,15 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
   __shared__ uint32_t ticket;
   __syncthreads();
   {
-    // value v = tid & 63 over the 64 columns of quarter q = tid >> 6, in a fixed (rotated) order
+    // value v = tid & 63 over the 64 columns of quarter q = tid >> 6: four interleaved sums over a
+    // rotated column order (no bank conflicts), all reads issued before the adds, combined in a
+    // fixed order
     const int v = tid & 63, q = tid >> 6;
-    double s = 0.0;
-    for (int i = 0; i < 64; ++i) s += sh.bins[v >> 1][v & 1][q * 64 + ((i + v) & 63)];
-    part4[q][v] = s;
+    const double* col = &sh.bins[v >> 1][v & 1][q * 64];
+    double a[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int i = 0; i < 64; ++i) a[i & 3] += col[(i + v) & 63];
+    part4[q][v] = (a[0] + a[1]) + (a[2] + a[3]);
   }
   __syncthreads();
 #pragma unroll
@@ -293,11 +307,22 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
   // last workgroup of this job: every partial is visible after the fence
   __threadfence();
   {
+    // the partials of value v, quarter q of the workgroups: eight loads in flight per step, added
+    // in workgroup order
     const int v = tid & 63, q = tid >> 6;
     const int cnt = jb.wg_count;
     const int s0 = (q * cnt) / 4, s1 = ((q + 1) * cnt) / 4;
+    const double* pv = part + (size_t)v * b.slots;
     double s = 0.0;
-    for (int i = s0; i < s1; ++i) s += part[(size_t)v * b.slots + i];
+    int i = s0;
+    for (; i + 8 <= s1; i += 8) {
+      double x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = pv[i + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += x[u];
+    }
+    for (; i < s1; ++i) s += pv[i];
     part4[q][v] = s;
   }
   __syncthreads();
