@@ -198,26 +198,64 @@ __global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N
     state->prefix[tid] = 0;
     state->rank[tid] = r;
   }
-  const int rows = pass == 0 ? 1 : (int)state->nactive;
-  for (int i = tid; i < rows * kDigits; i += kBlock) hl[i] = hist[i];
+  __shared__ uint32_t act_s[kTargets], pre_s[kTargets];
+  __shared__ uint64_t rank_s[kTargets];
+  __shared__ int rows_s;
+  if (tid == 0) rows_s = pass == 0 ? 1 : (int)state->nactive;
+  if (tid < kTargets) {
+    act_s[tid] = state->active[tid];
+    pre_s[tid] = state->prefix[tid];
+    rank_s[tid] = state->rank[tid];
+  }
   __syncthreads();
-  if (tid < nt) {
-    const uint32_t pre = state->prefix[tid];
-    int slot = 0;
-    if (pass > 0) {
-      while (slot < rows && state->active[slot] != pre) ++slot;
+  const int rows = rows_s;
+  {
+    // the whole histogram region (always allocated) in one round of loads: a thread issues all of
+    // its 32 loads before it stores any
+    unsigned long long v[kTargets];
+#pragma unroll
+    for (int r = 0; r < kTargets; ++r) v[r] = hist[r * kDigits + tid];
+#pragma unroll
+    for (int r = 0; r < kTargets; ++r) hl[r * kDigits + tid] = v[r];
+  }
+  __syncthreads();
+  {
+    // wave w resolves targets w, w + 4, ...: lane l holds the count of digits 4l .. 4l + 3 of the
+    // target's row, an inclusive scan over the wave finds the lane whose digits hold the rank,
+    // and that lane walks its four digits
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    for (int t = wave; t < nt; t += kWavesPerBlock) {
+      const uint32_t pre = pre_s[t];
+      int slot = 0;
+      if (pass > 0) {
+        // the row of this target's prefix: one compare per lane, first match
+        const unsigned long long m = __ballot(lane < rows && act_s[lane & (kTargets - 1)] == pre);
+        slot = m ? __builtin_ctzll(m) : rows;
+      }
+      const uint64_t rank = rank_s[t];
+      const unsigned long long* row = hl + slot * kDigits + 4 * lane;
+      const uint64_t c0 = row[0], c1 = row[1], c2 = row[2], c3 = row[3];
+      const uint64_t mine = c0 + c1 + c2 + c3;
+      uint64_t incl = mine;
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) {
+        const uint64_t other = (uint64_t)__shfl_up((unsigned long long)incl, d);
+        if (lane >= d) incl += other;
+      }
+      const uint64_t excl = incl - mine;
+      // the first lane whose inclusive count exceeds the rank (the last lane if none does)
+      const unsigned long long hit = __ballot(rank < incl);
+      const int owner = hit ? __builtin_ctzll(hit) : kWave - 1;
+      if (lane == owner) {
+        uint64_t cum = excl;
+        int d = 4 * lane;
+        if (rank >= cum + c0 && d < kDigits - 1) { cum += c0; ++d;
+          if (rank >= cum + c1 && d < kDigits - 1) { cum += c1; ++d;
+            if (rank >= cum + c2 && d < kDigits - 1) { cum += c2; ++d; } } }
+        newp[t] = (pre << 8) | (uint32_t)d;
+        state->rank[t] = rank - cum;
+      }
     }
-    uint64_t rank = state->rank[tid];
-    uint64_t cum = 0;
-    int d = 0;
-    const unsigned long long* row = hl + slot * kDigits;
-    for (; d < kDigits - 1; ++d) {
-      const uint64_t c = row[d];
-      if (rank < cum + c) break;
-      cum += c;
-    }
-    newp[tid] = (pre << 8) | (uint32_t)d;
-    state->rank[tid] = rank - cum;
   }
   __syncthreads();
   for (int i = tid; i < kTargets * kDigits; i += kBlock) hist[i] = 0ull;
