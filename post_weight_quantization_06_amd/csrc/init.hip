@@ -68,9 +68,13 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __res
                                                            MatrixGeom geom, int g,
                                                            uint32_t* __restrict__ keys,
                                                            unsigned long long* hist) {
-  __shared__ uint32_t h[kDigits];
+  // eight copies of the histogram, by lane & 7: most keys share a few top bytes, and adds to one
+  // address from many lanes of an instruction are serialized
+  constexpr int kCopies = 8;
+  __shared__ uint32_t h[kCopies][kDigits];
   const int tid = threadIdx.x;
-  h[tid] = 0;
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c) h[c][tid] = 0;
   __syncthreads();
   const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = g / kPerLane;
   for (int64_t task = blockIdx.x; task < geom.ntasks; task += gridDim.x) {
@@ -95,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __res
         float u = s > 0.0f ? w[e] / s : 0.0f;
         if (u == 0.0f) u = 0.0f;            // zero is unsigned
         k[e] = order_key(u);
-        atomicAdd(&h[k[e] >> 24], 1u);
+        atomicAdd(&h[tid & (kCopies - 1)][k[e] >> 24], 1u);
       }
       uint4* dst = reinterpret_cast<uint4*>(keys + base);
       dst[0] = make_uint4(k[0], k[1], k[2], k[3]);
@@ -103,61 +107,76 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __res
     }
   }
   __syncthreads();
-  flush_hist(h, hist, kDigits);
+  uint32_t tot = 0;
+#pragma unroll
+  for (int c = 0; c < kCopies; ++c) tot += h[c][tid];
+  if (tot) atomicAdd(hist + tid, (unsigned long long)tot);
 }
 
 // Passes 2-4: histogram of byte `pass` (0-based from the top) of keys whose higher bytes match an
 // active prefix. The active prefixes (at most 32, sorted) are found through a 256-slot table
-// indexed by the prefix's low byte; a slot holds up to two prefixes, and a slot that would need
-// more sends its keys to a binary search of the sorted list.
+// indexed by the prefix's low byte; a slot holds one prefix, and a slot that would need more sends
+// its keys to a binary search of the sorted list.
 __global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __restrict__ keys, int64_t N,
                                                            int pass, const InitState* state,
                                                            unsigned long long* hist) {
   __shared__ uint32_t h[kTargets * kDigits];
   __shared__ uint32_t act[kTargets];
-  __shared__ uint32_t slot_pre[kDigits][2];    // prefixes in the slot
-  __shared__ int32_t slot_idx[kDigits][2];     // their positions in the list; -1 empty, -2 overflow
+  // slot entry: (prefix, position in the list); position -1 = no prefix, -2 = several prefixes
+  // (those keys use a binary search of the sorted list)
+  __shared__ uint2 slot[kDigits];
   __shared__ uint32_t nact;
   const int tid = threadIdx.x;
   for (int i = tid; i < kTargets * kDigits; i += kBlock) h[i] = 0;
   if (tid < kTargets) act[tid] = state->active[tid];
   if (tid == 0) nact = state->nactive;
-  slot_idx[tid][0] = -1;
-  slot_idx[tid][1] = -1;
   __syncthreads();
   const int na = (int)nact;
-  if (tid < kDigits) {
-    // thread = slot: collect the active prefixes whose low byte is this slot, in list order
+  {
+    // thread = slot: the active prefixes whose low byte is this slot
     int m = 0;
+    uint32_t pfx = 0;
+    int at = -1;
     for (int t = 0; t < na; ++t) {
       if ((act[t] & 255u) != (uint32_t)tid) continue;
-      if (m < 2) {
-        slot_pre[tid][m] = act[t];
-        slot_idx[tid][m] = t;
+      if (m == 0) {
+        pfx = act[t];
+        at = t;
       } else {
-        slot_idx[tid][0] = -2;
+        at = -2;
       }
       ++m;
     }
+    slot[tid] = make_uint2(pfx, (uint32_t)at);
   }
   __syncthreads();
   const int pshift = 32 - 8 * pass;       // prefix = key >> pshift
   const int dshift = 24 - 8 * pass;       // digit = (key >> dshift) & 255
   const int64_t n4 = N / 4;
   const uint4* k4 = reinterpret_cast<const uint4*>(keys);
-  for (int64_t i = (int64_t)blockIdx.x * kBlock + tid; i < n4; i += (int64_t)gridDim.x * kBlock) {
-    const uint4 q = k4[i];
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  // four 16-byte loads in flight per thread: unconditional at clamped indices, the out-of-range
+  // ones then ignored
+  constexpr int kUnroll = 4;
+  for (int64_t i0 = (int64_t)blockIdx.x * kBlock + tid; i0 < n4; i0 += kUnroll * stride) {
+    uint4 qs[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t i = i0 + u * stride;
+      qs[u] = k4[i < n4 ? i : n4 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+    if (i0 + u * stride >= n4) break;
+    const uint4 q = qs[u];
     const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t pre = kk[e] >> pshift;
-      const int sl = (int)(pre & 255u);
-      const int i0 = slot_idx[sl][0];
-      int hit = -1;
-      if (i0 >= 0) {
-        if (slot_pre[sl][0] == pre) hit = i0;
-        else if (slot_idx[sl][1] >= 0 && slot_pre[sl][1] == pre) hit = slot_idx[sl][1];
-      } else if (i0 == -2) {
+      const uint2 en = slot[pre & 255u];
+      const int i0 = (int)en.y;
+      int hit = (i0 >= 0 && en.x == pre) ? i0 : -1;
+      if (i0 == -2) {
         int lo = 0, hi = na;               // first active prefix >= pre
         while (lo < hi) {
           const int mid = (lo + hi) >> 1;
@@ -166,6 +185,7 @@ __global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __res
         if (lo < na && act[lo] == pre) hit = lo;
       }
       if (hit >= 0) atomicAdd(&h[hit * kDigits + ((kk[e] >> dshift) & 255u)], 1u);
+    }
     }
   }
   __syncthreads();
