@@ -156,13 +156,16 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
 
 template <bool WITH_ERR, int G16, int S16>
 __device__ __forceinline__ void assign_row16(const AssignJob& jb, const Lut& lut, int n, int g16,
-                                             int s16, int log2S, int64_t base, bool active,
-                                             const uint16_t* wsafe, const float* isafe,
-                                             const uint4& va, const uint4& vb,
-                                             const float (&Ik)[16]) {
+                                             int s16, int log2S, int64_t r, int c0,
+                                             bool active, const uint16_t* wsafe,
+                                             const float* isafe, const uint4& va,
+                                             const uint4& vb, const float (&Ik)[16]) {
   Row16 o;
   row16_core<WITH_ERR, G16, S16>(lut, n, g16, s16, active, wsafe, isafe, va, vb, Ik, o);
-  if (active) store_row16<WITH_ERR>(o, jb.codes, jb.sel, jb.err, s16, log2S, base);
+  const int64_t rc = r * jb.geom.C;          // wave-uniform; a multiple of S
+  if (active)
+    store_row16<WITH_ERR>(o, jb.codes + (rc >> 3), jb.sel + (rc >> log2S),
+                          WITH_ERR ? jb.err + 2 * (rc >> log2S) : nullptr, s16, log2S, c0);
 }
 
 template <bool WITH_ERR, int G16, int S16>
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
   __shared__ Lut lut;
   __shared__ LutScratch ls;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = wave_index();
   const int g16 = b.g / kWideLane, s16 = b.S / kWideLane, n = b.n;
   const int log2S = 31 - __builtin_clz((unsigned)b.S);
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
     const int slab = (int)(local - rb * jb.geom.nslab);
     const int c0 = slab * kWideSlab + lane * kWideLane;
     const bool active = c0 < jb.geom.C;
-    const int64_t cl = active ? c0 : 0;       // inactive lanes read an element of their own matrix
+    const int cl = active ? c0 : 0;           // inactive lanes read an element of their own matrix
     const int64_t R = jb.geom.R, C = jb.geom.C;
     const int64_t r0 = rb * kWideRowsPerTask + wave;
     // every load of the task first, unconditional (rows past the end read the last row and are
@@ -199,9 +202,9 @@ __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
     for (int i = 0; i < kWideRowsPerWave; ++i) {
       int64_t r = r0 + (int64_t)kWavesPerBlock * i;
       r = r < R ? r : R - 1;
-      const uint16_t* p = jb.W + r * C + cl;
-      va[i] = *reinterpret_cast<const uint4*>(p);
-      vb[i] = *reinterpret_cast<const uint4*>(p + 8);
+      const uint16_t* p = jb.W + r * C;         // wave-uniform row base
+      va[i] = *reinterpret_cast<const uint4*>(p + cl);
+      vb[i] = *reinterpret_cast<const uint4*>(p + cl + 8);
     }
     float Ik[16];
 #pragma unroll
@@ -213,7 +216,7 @@ __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
     for (int i = 0; i < kWideRowsPerWave; ++i) {
       const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
       if (r >= R) break;
-      assign_row16<WITH_ERR, G16, S16>(jb, lut, n, g16, s16, log2S, r * C + c0, active,
+      assign_row16<WITH_ERR, G16, S16>(jb, lut, n, g16, s16, log2S, r, c0, active,
                                         jb.W + r * C + cl, jb.I + cl, va[i], vb[i], Ik);
     }
   }

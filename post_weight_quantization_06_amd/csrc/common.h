@@ -57,6 +57,12 @@ constexpr int kNaNPair = 17;
 constexpr float kFastScaleMin = 0x1p-30f;
 constexpr float kFastScaleMax = 0x1p30f;
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value: row indices and
+// row base addresses derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 

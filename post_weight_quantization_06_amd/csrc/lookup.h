@@ -302,19 +302,22 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
 
 // Store the selected codes (8 bytes), and once per selection group the selector (and errors).
 template <bool WITH_ERR>
-__device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes, uint8_t* sel,
-                                            double* err, int s16, int log2S, int64_t base) {
+// codes_row, sel_row and err_row point at the row's first code word, selector and error pair
+// (wave-uniform); c0 is the lane's first column. Rows start on a selection-group boundary, so the
+// lane's offsets within the row follow from c0 alone.
+__device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes_row, uint8_t* sel_row,
+                                            double* err_row, int s16, int log2S, int c0) {
   const uint32_t lo = __builtin_amdgcn_perm(select_nibbles(o.P[1], o.sel),
                                             select_nibbles(o.P[0], o.sel), 0x06040200u);
   const uint32_t hi = __builtin_amdgcn_perm(select_nibbles(o.P[3], o.sel),
                                             select_nibbles(o.P[2], o.sel), 0x06040200u);
-  *reinterpret_cast<uint2*>(codes + (base >> 3)) = make_uint2(lo, hi);
-  if (((base >> 4) & (s16 - 1)) == 0) {
-    const int64_t h = base >> log2S;
-    sel[h] = (uint8_t)o.sel;
+  *reinterpret_cast<uint2*>(codes_row + (c0 >> 3)) = make_uint2(lo, hi);
+  if (((c0 >> 4) & (s16 - 1)) == 0) {
+    const int h = c0 >> log2S;
+    sel_row[h] = (uint8_t)o.sel;
     if (WITH_ERR) {
-      err[2 * h] = o.E0;
-      err[2 * h + 1] = o.E1;
+      err_row[2 * h] = o.E0;
+      err_row[2 * h + 1] = o.E1;
     }
   }
 }
