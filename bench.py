@@ -11,6 +11,8 @@ per launch / its mean launch duration (HIP events on the launch stream); traffic
 launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a plain copy), or null
 when that summary was taken on other kernel sources or on another workload.
 cpu_baseline: the fp64 oracle, assign + refine on a sample matrix, timed on the host.
+inference: after the timed steps, the decode GEMV over the packed layer and the AWQ pre-scale of
+the layer, each against the HBM peak (outside the metric).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu]
 """
@@ -57,6 +59,66 @@ def cpu_baseline(W, I, g, S, n, budget_s=15.0):
             "cores": 1, "kind": "oracle",
             "sample": "%d oracle assign+refine iterations (fp64 NumPy, one thread) on the "
                       "%dx%d matrix of the layer, %.1f s" % (its, W64.shape[0], W64.shape[1], el)}
+
+
+def inference_side(L, torch, dev, stream, mats, codes, scales, bitmaps, tb16, Ws, Is, g, S, n,
+                   reps=8):
+    """The two entry points around the loop, timed on this layer after the quantization steps:
+    the decode GEMV over every packed matrix in one launch (batch 1), with 512 MB read between
+    launches so that the packed weights come from HBM and not from the 256 MB last-level cache,
+    and the AWQ pre-scale of every matrix (read W, write W_scaled)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    Rs = [m.rows for m in mats]
+    Cs = [m.cols for m in mats]
+    xs = [torch.randn(1, C, device=dev, generator=gen).to(torch.bfloat16) for C in Cs]
+    ys = [torch.empty(R, device=dev) for R in Rs]
+    flush = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+    bms = None if S == g else bitmaps
+    gemv_bytes = sum(R * C // 2 + 2 * (R * C // g) + ((R * C // S + 7) // 8 if S < g else 0)
+                     + 2 * C + 4 * R for R, C in zip(Rs, Cs))
+    ts = []
+    for r in range(reps + 1):
+        flush.sum()                    # reads 512 MB: evicts the packed layer with clean lines
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        L.aaac_gemv_batch(codes, scales, bms, tb16, Rs, Cs, g, S, n, xs, ys)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if r:
+            ts.append(e0.elapsed_time(e1))
+    del flush
+    gemv_ms = sorted(ts)[len(ts) // 2]
+    a = [torch.exp(0.5 * torch.randn(C, device=dev, generator=gen)) for C in Cs]
+    W_s = [torch.empty_like(W) for W in Ws]
+    I_s = [torch.empty_like(I) for I in Is]
+    ts = []
+    for r in range(3):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i, W in enumerate(Ws):
+            L.aaac_awq_prescale(W, a[i], W_s[i], Is[i], I_s[i])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    awq_ms = min(ts)
+    awq_bytes = sum(4 * R * C + 12 * C for R, C in zip(Rs, Cs))
+    gb = gemv_bytes / (gemv_ms * 1e-3) / 1e9
+    ab = awq_bytes / (awq_ms * 1e-3) / 1e9
+    return {
+        "gemv": {"workload": "decode GEMV, batch 1, every linear of the layer in one launch, "
+                             "packed weights cold in HBM",
+                 "us_per_launch": round(gemv_ms * 1e3, 2), "bytes_per_launch": gemv_bytes,
+                 "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(gb / HBM_PEAK_GBS, 4)},
+        "awq_prescale": {"workload": "W diag(a) and I / a^2 for every linear of the layer, "
+                                     "one launch per matrix",
+                         "us_per_layer": round(awq_ms * 1e3, 2), "bytes": awq_bytes,
+                         "achieved": round(ab, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ab / HBM_PEAK_GBS, 4)},
+    }
 
 
 def main():
@@ -185,6 +247,12 @@ def main():
     if args.config == 2:
         t = pmc_traffic.load_traffic(TRAFFIC_SUMMARY, dom)
         traffic = None if t is None else int(round(t))
+    inference = inference_side(L, torch, dev, stream, mats, codes, scales, bitmaps, tb16, Ws, Is,
+                               g, S, n)
+    print("[bench] gemv %.1f us (%.0f GB/s), awq prescale %.1f us (%.0f GB/s)" % (
+        inference["gemv"]["us_per_launch"], inference["gemv"]["achieved"],
+        inference["awq_prescale"]["us_per_layer"], inference["awq_prescale"]["achieved"]),
+        file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu:
         k = min(range(len(mats)), key=lambda i: mats[i].numel)
@@ -217,6 +285,7 @@ def main():
                      "traffic_unit": "bytes per launch",
                      "algorithmic_bytes": int(round(bytes_launch))},
         "cpu_baseline": cpu,
+        "inference": inference,
     }
     print(json.dumps(out), flush=True)
 

@@ -158,6 +158,50 @@ aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uin
                          uint16_t* W_hat, void* stream);
 
 /*
+ * Decode GEMV on the packed format, AAAC summary §1 (4-bit weights with 16-bit activations, W4A16;
+ * the dequantized values are the weights inference uses) and §2 mechanism 3 (the stored format):
+ *   y[b, r] = sum_c |s(r, c)| * T~_sel(r, c)[q(r, c)] * x[b, c]      for b < B
+ * The weight is the exact product of the bf16 scale and the bf16 table entry (both are bf16, so the
+ * product is exact in fp32); unlike aaac_dequant it is not rounded to bf16 first. Sums run in fp32
+ * in a fixed order (bitwise reproducible): within a scale group, then scaled by |s|, then across
+ * groups; a code >= n reads entry 0, as in aaac_dequant.
+ * codes, scales, bitmap, tables_bf16  as written by aaac_assign / aaac_pack (bitmap NULL iff S == g).
+ *                                     codes 16-byte aligned, scales 8-byte aligned.
+ * x   bf16 [B, C] bit patterns (row stride C), 16-byte aligned; 1 <= B <= 4.
+ * y   fp32 [B, R] (output, row stride R).
+ * Shapes as for the other calls, and C % 32 == 0.
+ */
+aaac_status aaac_gemv(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
+                      const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
+                      const uint16_t* x, int B, float* y, void* stream);
+
+/* aaac_gemv over up to AAAC_MAX_BATCH matrices sharing g, S, n and B in one launch (for example
+ * every linear of a decoder layer for one decode step). bitmap is an array of count pointers when
+ * S < g, else NULL. Results are bitwise identical to one aaac_gemv call per matrix. */
+aaac_status aaac_gemv_batch(int count, const uint8_t* const* codes, const uint16_t* const* scales,
+                            const uint8_t* const* bitmap, const uint16_t* const* tables_bf16,
+                            const int64_t* R, const int64_t* C, int g, int S, int n,
+                            const uint16_t* const* x, int B, float* const* y, void* stream);
+
+/*
+ * AWQ composition hook, AAAC summary §4 (AAAC on weights that AWQ scaled before quantization; the
+ * search for the scales is not part of this library). Given a positive finite per-column scale
+ * a [C] (fp32), prepares the inputs that quantize W diag(a) against the importance that matches
+ * it, the energy of the inputs x / a that the scaled matrix sees at inference:
+ *   W_scaled[r, c] = bf16(W[r, c] * a[c])   exact product, one rounding (ties to even); a product
+ *                                           past the bf16 range becomes infinite, so choose a that
+ *                                           keeps the weights finite
+ *   I_scaled[c]    = fp32(I[c] / a[c]^2)    one fp64 division of exact operands, then fp32
+ * W, W_scaled  bf16 [R, C]; W_scaled may be W (in place). 16-byte aligned.
+ * a            fp32 [C], 16-byte aligned.
+ * I, I_scaled  fp32 [C], both NULL or both given; I_scaled may be I.
+ * The rest of the pipeline then runs on (W_scaled, I_scaled) unchanged. Shapes: R >= 1, C >= 8,
+ * C % 8 == 0, R * C < 2^40.
+ */
+aaac_status aaac_awq_prescale(const uint16_t* W, int64_t R, int64_t C, const float* a,
+                              const float* I, uint16_t* W_scaled, float* I_scaled, void* stream);
+
+/*
  * Batched assign / refine over up to AAAC_MAX_BATCH matrices that share g, S and n (for example
  * the seven linears of one decoder layer) in one launch each. Element i of every array describes
  * matrix i exactly as the single-matrix call does; the results are bitwise identical to calling

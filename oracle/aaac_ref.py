@@ -32,6 +32,9 @@ Readings taken where the page is silent (each is restated where it is used):
   R8  storage: code byte = q[2i] | q[2i+1] << 4; S == g: scale word = bf16(s) | sigma << 15;
       S < g: scale sign 0 and an LSB-first bitmap over the row-major selection groups.
   R9  dequant: w_hat = bf16(|s| * T~_sigma[q]).
+  R14 decode GEMV: y = sum_c |s| T~_sigma[q] x_c with the exact product of scale and entry; the
+      bf16 rounding of R9 belongs to materializing W_hat, which the GEMV never does.
+  R15 AWQ composition: quantize bf16(W * a) with importance I / a^2 for a caller-given a > 0.
 
 Pins (tests/test_oracle_pins.py): every function below is pinned against something other than
 itself -- torch's bf16 conversion, integer-exact sums, np.partition, exhaustive code search on tiny
@@ -50,6 +53,7 @@ __all__ = [
     "importance", "group_scales", "normalized",
     "init_tables", "nearest", "assign", "refine_sums", "refine_update", "refine",
     "total_error", "quantize", "pack", "dequant", "storage_bytes",
+    "decoded_weights", "gemv", "awq_prescale",
 ]
 
 
@@ -321,6 +325,46 @@ def dequant(code_bytes, scales, bitmap, tables_u16, R, C, g, S):
     tabs = np.stack([bits_to_float(tables_u16[0]), bits_to_float(tables_u16[1])])
     vals = _per_weight(s, g) * tabs[_per_weight(sel.astype(np.int64), S), q]
     return bf16_round(vals)
+
+
+# ----------------------------------------------------------------------------------------------
+# Inference side of the packed format (AAAC summary §1: W4A16 deployment, the dequantized values
+# are the weights inference uses) and the AWQ composition (§4).
+# ----------------------------------------------------------------------------------------------
+
+def decoded_weights(code_bytes, scales, bitmap, tables_u16, R, C, g, S):
+    """[R, C] fp64 |s| * T~_sigma[q] straight from the packed format, without the bf16 rounding
+    that dequant applies to store W_hat (reading R14). Both factors are bf16 values, so the product
+    is exact."""
+    q = unpack_codes(code_bytes, R, C)
+    sel = unpack_selectors(scales, bitmap, R, C, g, S)
+    s = bits_to_float(np.asarray(scales, dtype=np.uint16).reshape(R, C // g) & 0x7FFF)
+    tabs = np.stack([bits_to_float(tables_u16[0]), bits_to_float(tables_u16[1])])
+    return _per_weight(s, g) * tabs[_per_weight(sel.astype(np.int64), S), q]
+
+
+def gemv(code_bytes, scales, bitmap, tables_u16, R, C, g, S, x):
+    """Decode GEMV on the packed format: y[b, r] = sum_c |s| T~_sigma[q] x[b, c] in fp64 (every
+    product is exact: three bf16 factors), for x [B, C] of bf16 values. Returns (y [B, R],
+    a [B, R]) where a = sum_c |term| scales the rounding bound of an fp32 evaluation."""
+    Wd = decoded_weights(code_bytes, scales, bitmap, tables_u16, R, C, g, S)
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    return x @ Wd.T, np.abs(x) @ np.abs(Wd).T
+
+
+def awq_prescale(W, a, I=None):
+    """Inputs for quantizing W diag(a) (AAAC after AWQ's weight scaling, §4; reading R15):
+    W_scaled = bf16(W * a) per column, from the exact fp64 product, and, if I is given,
+    I_scaled = fp32(I / a^2) from one fp64 division of exact operands. The scaled matrix sees the
+    inputs x / a at inference, whose energy is I / a^2, so the weighted error of W_scaled under
+    I_scaled is the error of the original matrix."""
+    W = np.asarray(W, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float32).astype(np.float64)
+    Ws = bf16_round(W * a[None, :])
+    if I is None:
+        return Ws, None
+    I = np.asarray(I, dtype=np.float32).astype(np.float64)
+    return Ws, (I / (a * a)).astype(np.float32)
 
 
 def storage_bytes(n, num_matrices=1):

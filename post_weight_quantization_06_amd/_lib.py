@@ -30,7 +30,8 @@ MAX_BATCH = 8
 EXPORTED = (
     "aaac_status_string", "aaac_last_error", "aaac_workspace_bytes", "aaac_importance",
     "aaac_init_quantiles", "aaac_assign", "aaac_refine", "aaac_pack", "aaac_dequant",
-    "aaac_batch_workspace_bytes", "aaac_assign_batch", "aaac_refine_batch",
+    "aaac_batch_workspace_bytes", "aaac_assign_batch", "aaac_refine_batch", "aaac_awq_prescale",
+    "aaac_gemv", "aaac_gemv_batch",
 )
 
 
@@ -81,6 +82,12 @@ def load(path: str = LIB_PATH):
         "aaac_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
                                       P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int, c_vp, c_size,
                                       c_vp]),
+        "aaac_awq_prescale": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "aaac_gemv": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
+                              c_int, c_vp, c_vp]),
+        "aaac_gemv_batch": (c_int, [c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), P(c_i64),
+                                    P(c_i64), c_int, c_int, c_int, P(c_vp), c_int, P(c_vp),
+                                    c_vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -294,3 +301,64 @@ def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _arr(c_vp, [t.data_ptr() for t in sels]), _arr(c_vp, [t.data_ptr() for t in tables]),
         flags, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "aaac_refine_batch")
+
+
+def aaac_awq_prescale(W: torch.Tensor, a: torch.Tensor, W_scaled: torch.Tensor,
+                      I: Optional[torch.Tensor] = None, I_scaled: Optional[torch.Tensor] = None,
+                      stream=None):
+    """W_scaled = bf16(W * a) per column, I_scaled = fp32(I / a^2) (in place allowed)."""
+    lib = load()
+    R, C = W.shape
+    _need(W, "W", torch.bfloat16)
+    _need(a, "a", torch.float32, C)
+    _need(W_scaled, "W_scaled", torch.bfloat16, R * C)
+    if I is not None:
+        _need(I, "I", torch.float32, C)
+    if I_scaled is not None:
+        _need(I_scaled, "I_scaled", torch.float32, C)
+    st = lib.aaac_awq_prescale(_ptr(W), R, C, _ptr(a), _ptr(I), _ptr(W_scaled), _ptr(I_scaled),
+                               _stream(stream))
+    _check(st, "aaac_awq_prescale")
+
+
+def aaac_gemv(codes: torch.Tensor, scales: torch.Tensor, bitmap: Optional[torch.Tensor],
+              tables_bf16: torch.Tensor, R: int, C: int, g: int, S: int, n: int,
+              x: torch.Tensor, y: torch.Tensor, stream=None):
+    """y [B, R] fp32 = decoded packed weights times x [B, C] bf16 (see aaac.h)."""
+    lib = load()
+    B = x.shape[0] if x.dim() == 2 else 1
+    _need(codes, "codes", torch.uint8, R * C // 2)
+    _need(scales, "scales", torch.int16, R * C // g)
+    _need(tables_bf16, "tables_bf16", torch.int16, 2 * n)
+    _need(x, "x", torch.bfloat16, B * C)
+    _need(y, "y", torch.float32, B * R)
+    if bitmap is not None:
+        _need(bitmap, "bitmap", torch.uint8, (R * C // S + 7) // 8)
+    st = lib.aaac_gemv(_ptr(codes), _ptr(scales), _ptr(bitmap), _ptr(tables_bf16), R, C, g, S, n,
+                       _ptr(x), B, _ptr(y), _stream(stream))
+    _check(st, "aaac_gemv")
+
+
+def aaac_gemv_batch(codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
+                    bitmaps: Optional[Sequence[torch.Tensor]], tables_bf16: Sequence[torch.Tensor],
+                    Rs: Sequence[int], Cs: Sequence[int], g: int, S: int, n: int,
+                    xs: Sequence[torch.Tensor], ys: Sequence[torch.Tensor], stream=None):
+    lib = load()
+    k = len(codes)
+    B = xs[0].shape[0] if xs[0].dim() == 2 else 1
+    for i in range(k):
+        R, C = Rs[i], Cs[i]
+        _need(codes[i], "codes[%d]" % i, torch.uint8, R * C // 2)
+        _need(scales[i], "scales[%d]" % i, torch.int16, R * C // g)
+        _need(tables_bf16[i], "tables_bf16[%d]" % i, torch.int16, 2 * n)
+        _need(xs[i], "x[%d]" % i, torch.bfloat16, B * C)
+        _need(ys[i], "y[%d]" % i, torch.float32, B * R)
+        if bitmaps is not None:
+            _need(bitmaps[i], "bitmap[%d]" % i, torch.uint8, (R * C // S + 7) // 8)
+    bm = None if bitmaps is None else _arr(c_vp, [t.data_ptr() for t in bitmaps])
+    st = lib.aaac_gemv_batch(
+        k, _arr(c_vp, [t.data_ptr() for t in codes]), _arr(c_vp, [t.data_ptr() for t in scales]),
+        bm, _arr(c_vp, [t.data_ptr() for t in tables_bf16]), _arr(c_i64, list(Rs)),
+        _arr(c_i64, list(Cs)), g, S, n, _arr(c_vp, [t.data_ptr() for t in xs]), B,
+        _arr(c_vp, [t.data_ptr() for t in ys]), _stream(stream))
+    _check(st, "aaac_gemv_batch")

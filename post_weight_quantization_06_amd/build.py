@@ -13,7 +13,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libaaac.so")
-SOURCES = ["abi.hip", "assign.hip", "refine.hip", "importance.hip", "init.hip", "pack.hip"]
+SOURCES = ["abi.hip", "assign.hip", "refine.hip", "importance.hip", "init.hip", "pack.hip",
+           "awq.hip", "gemv.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

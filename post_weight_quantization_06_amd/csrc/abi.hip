@@ -208,6 +208,63 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
 }
 
 
+aaac_status do_gemv(int count, const uint8_t* const* codes, const uint16_t* const* scales,
+                    const uint8_t* const* bitmap, const uint16_t* const* tables,
+                    const int64_t* R, const int64_t* C, int g, int S, int n,
+                    const uint16_t* const* x, int B, float* const* y, void* stream,
+                    const char* who) {
+  if (count < 1 || count > AAAC_MAX_BATCH || !codes || !scales || !tables || !R || !C || !x || !y)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: count=%d (need 1..%d) and non-null arrays", who, count,
+                AAAC_MAX_BATCH);
+  if (B < 1 || B > 4) return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: B=%d (need 1..4)", who, B);
+  int order[AAAC_MAX_BATCH];
+  for (int i = 0; i < count; ++i) {
+    aaac_status st = check_shape(R[i], C[i], g, S, n, true, who);
+    if (st != AAAC_OK) return st;
+    if (C[i] % 32 != 0)
+      return fail(AAAC_ERR_UNSUPPORTED_SHAPE, "%s: C=%lld (need C %% 32 == 0)", who,
+                  (long long)C[i]);
+    const uint8_t* bm = bitmap ? bitmap[i] : nullptr;
+    if (!codes[i] || !aligned(codes[i], 16) || !scales[i] || !aligned(scales[i], 8) ||
+        !tables[i] || !aligned(tables[i], 2) || !x[i] || !aligned(x[i], 16) || !y[i] ||
+        !aligned(y[i], 4))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: null or misaligned pointer", who, i);
+    if ((S < g) != (bm != nullptr))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: bitmap must be given exactly when S < g", who);
+    // widest matrices first: their tasks are the longest, so they start first
+    int k = i;
+    while (k > 0 && C[order[k - 1]] < C[i]) {
+      order[k] = order[k - 1];
+      --k;
+    }
+    order[k] = i;
+  }
+  GemvBatch b = {};
+  b.njobs = count;
+  b.B = B;
+  b.g = g;
+  b.S = S;
+  b.n = n;
+  int64_t t = 0;
+  for (int k = 0; k < count; ++k) {
+    const int i = order[k];
+    GemvJob& jb = b.job[k];
+    jb.codes = codes[i];
+    jb.scales = scales[i];
+    jb.bitmap = bitmap ? bitmap[i] : nullptr;
+    jb.tables = tables[i];
+    jb.x = x[i];
+    jb.y = y[i];
+    jb.R = R[i];
+    jb.C = C[i];
+    jb.task_begin = t;
+    jb.split = gemv_split(C[i]);
+    t += gemv_tasks(R[i], C[i]);
+  }
+  b.total_tasks = t;
+  return hip_status(launch_gemv(b, static_cast<hipStream_t>(stream)), who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -353,6 +410,39 @@ aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uin
   return hip_status(launch_dequant(codes, scales, bitmap, tables_bf16, R, C, g, S, n, W_hat,
                                    static_cast<hipStream_t>(stream)),
                     who);
+}
+
+aaac_status aaac_awq_prescale(const uint16_t* W, int64_t R, int64_t C, const float* a,
+                              const float* I, uint16_t* W_scaled, float* I_scaled, void* stream) {
+  const char* who = "aaac_awq_prescale";
+  if (R < 1 || C < 8 || C % 8 != 0 || C >= ((int64_t)1 << 31) ||
+      R > ((((int64_t)1 << 40) - 1) / C))
+    return fail(AAAC_ERR_UNSUPPORTED_SHAPE,
+                "%s: R=%lld C=%lld (need R >= 1, C >= 8, C %% 8 == 0, R*C < 2^40)", who,
+                (long long)R, (long long)C);
+  if (!W || !aligned(W, 16) || !a || !aligned(a, 16) || !W_scaled || !aligned(W_scaled, 16))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
+  if ((I == nullptr) != (I_scaled == nullptr) || (I && (!aligned(I, 4) || !aligned(I_scaled, 4))))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: I and I_scaled must be given together, 4-byte aligned",
+                who);
+  return hip_status(launch_awq_prescale(W, R, C, a, I, W_scaled, I_scaled,
+                                        static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+aaac_status aaac_gemv(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
+                      const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
+                      const uint16_t* x, int B, float* y, void* stream) {
+  return do_gemv(1, &codes, &scales, bitmap ? &bitmap : nullptr, &tables_bf16, &R, &C, g, S, n,
+                 &x, B, &y, stream, "aaac_gemv");
+}
+
+aaac_status aaac_gemv_batch(int count, const uint8_t* const* codes, const uint16_t* const* scales,
+                            const uint8_t* const* bitmap, const uint16_t* const* tables_bf16,
+                            const int64_t* R, const int64_t* C, int g, int S, int n,
+                            const uint16_t* const* x, int B, float* const* y, void* stream) {
+  return do_gemv(count, codes, scales, bitmap, tables_bf16, R, C, g, S, n, x, B, y, stream,
+                 "aaac_gemv_batch");
 }
 
 }  // extern "C"

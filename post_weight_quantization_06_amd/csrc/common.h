@@ -257,6 +257,30 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, in
 hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
                           const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
                           uint16_t* W_hat, hipStream_t stream);
+// Decode GEMV over up to kMaxJobs packed matrices that share g, S, n and the batch size B.
+struct GemvJob {
+  const uint8_t* codes;      // [R, C / 2]
+  const uint16_t* scales;    // [R, C / g]
+  const uint8_t* bitmap;     // S < g, else null
+  const uint16_t* tables;    // bf16 [2][n]
+  const uint16_t* x;         // bf16 [B, C]
+  float* y;                  // [B, R]
+  int64_t R, C;
+  int64_t task_begin;        // first workgroup task of this matrix
+  int split;                 // waves per row block (1, 2 or 4), from the slab count
+};
+struct GemvBatch {
+  GemvJob job[kMaxJobs];
+  int njobs, B, g, S, n;
+  int64_t total_tasks;
+};
+int gemv_split(int64_t C);
+int64_t gemv_tasks(int64_t R, int64_t C);
+hipError_t launch_gemv(const GemvBatch& b, hipStream_t stream);
+
+hipError_t launch_awq_prescale(const uint16_t* W, int64_t R, int64_t C, const float* a,
+                               const float* I, uint16_t* W_scaled, float* I_scaled,
+                               hipStream_t stream);
 
 inline MatrixGeom make_geom(int64_t R, int64_t C, int64_t task_begin, int slab = kSlab,
                             int rows_per_task = kRowsPerTask) {

@@ -141,3 +141,15 @@ def test_batch_calls_reject_bad_counts(lib):
     assert lib.aaac_assign_batch(9, P, R, C, 128, 128, 16, P, P, P, P, None) == INVALID
     assert lib.aaac_refine_batch(1, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE,
                                  ctypes.c_size_t(16), None) == WS_SMALL
+
+
+def test_awq_prescale_rejects_bad_arguments(lib):
+    f = lib.aaac_awq_prescale
+    assert f(FAKE, i64(4), i64(12), FAKE, FAKE, FAKE, FAKE, None) == SHAPE      # C % 8
+    assert f(FAKE, i64(0), i64(16), FAKE, FAKE, FAKE, FAKE, None) == SHAPE      # R < 1
+    assert f(FAKE, i64(1 << 21), i64(1 << 19), FAKE, None, FAKE, None, None) == SHAPE
+    assert f(None, i64(4), i64(16), FAKE, FAKE, FAKE, FAKE, None) == INVALID
+    assert f(FAKE, i64(4), i64(16), ctypes.c_void_p((1 << 20) + 4), None, FAKE, None,
+             None) == INVALID                                                  # a misaligned
+    assert f(FAKE, i64(4), i64(16), FAKE, FAKE, FAKE, None, None) == INVALID    # I without I_scaled
+    assert b"I_scaled" in lib.aaac_last_error()
