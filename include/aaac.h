@@ -226,6 +226,20 @@ aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t
                               float* const* tables, int flags, void* ws, size_t ws_bytes,
                               void* stream);
 
+/*
+ * One iteration of the alternation (AAAC summary §2 mechanism 4) in one launch: the batched assign
+ * against tables[i], writing codes[i] and sel[i], then the batched refine from those codes,
+ * updating tables[i] in place (flags as for aaac_refine_batch). Codes, selectors and tables are
+ * bitwise those of aaac_assign_batch followed by aaac_refine_batch with the same arguments. With
+ * S >= 16 the two steps share one kernel (assign and accumulate waves side by side in each
+ * workgroup); with S = 8 the call makes the two launches. Workspace: as aaac_refine_batch.
+ */
+aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const int64_t* R,
+                                     const int64_t* C, int g, int S, int n,
+                                     const float* const* I, float* const* tables,
+                                     uint8_t* const* codes, uint8_t* const* sel, int flags,
+                                     void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

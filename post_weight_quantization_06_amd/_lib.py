@@ -31,7 +31,7 @@ EXPORTED = (
     "aaac_status_string", "aaac_last_error", "aaac_workspace_bytes", "aaac_importance",
     "aaac_init_quantiles", "aaac_assign", "aaac_refine", "aaac_pack", "aaac_dequant",
     "aaac_batch_workspace_bytes", "aaac_assign_batch", "aaac_refine_batch", "aaac_awq_prescale",
-    "aaac_gemv", "aaac_gemv_batch",
+    "aaac_gemv", "aaac_gemv_batch", "aaac_assign_refine_batch",
 )
 
 
@@ -83,6 +83,9 @@ def load(path: str = LIB_PATH):
                                       P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int, c_vp, c_size,
                                       c_vp]),
         "aaac_awq_prescale": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "aaac_assign_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
+                                             c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int,
+                                             c_vp, c_size, c_vp]),
         "aaac_gemv": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
                               c_int, c_vp, c_vp]),
         "aaac_gemv_batch": (c_int, [c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), P(c_i64),
@@ -301,6 +304,31 @@ def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _arr(c_vp, [t.data_ptr() for t in sels]), _arr(c_vp, [t.data_ptr() for t in tables]),
         flags, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "aaac_refine_batch")
+
+
+def aaac_assign_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
+                             Is: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
+                             codes: Sequence[torch.Tensor], sels: Sequence[torch.Tensor],
+                             flags: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
+    """One assign + refine iteration in one launch (tables updated in place)."""
+    lib = load()
+    k = len(Ws)
+    Rs = [W.shape[0] for W in Ws]
+    Cs = [W.shape[1] for W in Ws]
+    for i in range(k):
+        _need(Ws[i], "W[%d]" % i, torch.bfloat16)
+        _need(Is[i], "I[%d]" % i, torch.float32, Cs[i])
+        _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
+        _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
+        _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
+    if ws is None:
+        ws = workspace(batch_workspace_bytes(OP_REFINE, Rs, Cs, g, S, n), Ws[0].device)
+    st = lib.aaac_assign_refine_batch(
+        k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
+        _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in tables]),
+        _arr(c_vp, [t.data_ptr() for t in codes]), _arr(c_vp, [t.data_ptr() for t in sels]),
+        flags, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "aaac_assign_refine_batch")
 
 
 def aaac_awq_prescale(W: torch.Tensor, a: torch.Tensor, W_scaled: torch.Tensor,

@@ -412,6 +412,53 @@ aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uin
                     who);
 }
 
+aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const int64_t* R,
+                                     const int64_t* C, int g, int S, int n,
+                                     const float* const* I, float* const* tables,
+                                     uint8_t* const* codes, uint8_t* const* sel, int flags,
+                                     void* ws, size_t ws_bytes, void* stream) {
+  const char* who = "aaac_assign_refine_batch";
+  aaac_status st = check_batch(count, W, R, C, g, S, n, who);
+  if (st != AAAC_OK) return st;
+  if (flags & ~AAAC_REFINE_ROUND_BF16)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: unknown flags %d", who, flags);
+  if (!I || !tables || !codes || !sel) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    if (!I[i] || !aligned(I[i], 16) || !tables[i] || !aligned(tables[i], 4) || !codes[i] ||
+        !aligned(codes[i], 16) || !sel[i])
+      return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: null or misaligned pointer", who, i);
+  }
+  st = check_refine_ws(count, ws, ws_bytes, who);
+  if (st != AAAC_OK) return st;
+  if (S < kWideLane) {
+    // 8-weight selection groups: the two launches
+    const float* tin[AAAC_MAX_BATCH];
+    for (int i = 0; i < count; ++i) tin[i] = tables[i];
+    st = do_assign(count, W, R, C, g, S, n, I, tin, codes, sel, nullptr, stream, who);
+    if (st != AAAC_OK) return st;
+    const uint8_t* cc[AAAC_MAX_BATCH];
+    const uint8_t* sc[AAAC_MAX_BATCH];
+    for (int i = 0; i < count; ++i) {
+      cc[i] = codes[i];
+      sc[i] = sel[i];
+    }
+    return do_refine(count, W, R, C, g, S, n, I, cc, sc, tin, tables, flags, ws, ws_bytes, stream,
+                     who);
+  }
+  RefineBatch b{};
+  build_refine_batch(b, count, W, R, C, g, S, n, I, flags, ws);
+  for (int i = 0; i < count; ++i) {
+    RefineJob& j = b.job[i];
+    j.codes = reinterpret_cast<const uint32_t*>(codes[i]);
+    j.sel = sel[i];
+    j.codes_out = reinterpret_cast<uint32_t*>(codes[i]);
+    j.sel_out = sel[i];
+    j.tables_in = tables[i];
+    j.tables_out = tables[i];
+  }
+  return hip_status(launch_assign_refine(b, static_cast<hipStream_t>(stream)), who);
+}
+
 aaac_status aaac_awq_prescale(const uint16_t* W, int64_t R, int64_t C, const float* a,
                               const float* I, uint16_t* W_scaled, float* I_scaled, void* stream) {
   const char* who = "aaac_awq_prescale";

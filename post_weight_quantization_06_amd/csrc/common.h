@@ -216,6 +216,8 @@ struct RefineJob {
   const uint8_t* sel;
   const float* tables_in;
   float* tables_out;
+  uint32_t* codes_out;      // fused assign + accumulate only: where the assign step writes
+  uint8_t* sel_out;
   int32_t wg_lo;            // first workgroup whose task range meets this job
   int32_t wg_count;         // number of such workgroups
 };
@@ -240,6 +242,9 @@ int device_cu_count();
 hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream);
 hipError_t launch_refine(RefineBatch& b, hipStream_t stream);
 int refine_grid(int64_t total_tasks);
+// One launch doing a batched assign and then a batched refine on its codes (selection groups of at
+// least 16 weights); same geometry and workspace as the refine launch, same results bit for bit.
+hipError_t launch_assign_refine(RefineBatch& b, hipStream_t stream);
 // Task geometry of the refine kernel for one matrix (it depends on the selection group size).
 MatrixGeom refine_geom(int64_t R, int64_t C, int64_t task_begin, int S);
 

@@ -99,7 +99,7 @@ __device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScrat
     }
   }
   __syncthreads();
-  for (int rho = tid; rho < kLutRecs; rho += kBlock) {
+  for (int rho = tid; rho < kLutRecs; rho += (int)blockDim.x) {
     uint32_t off[2];
     uint32_t code = 0;
 #pragma unroll

@@ -16,6 +16,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "lookup.h"
 
 namespace aaac {
 
@@ -199,9 +200,13 @@ __device__ __forceinline__ void load_task16(const TaskCursor& c, int log2S, Task
   for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(c.I + cl + 4 * q);
 }
 
-template <int G16>
-__device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, RefineShared& sh) {
-  const int tid = threadIdx.x;
+// col: this thread's column of bins (its index among the accumulating threads). PART: weights
+// whose terms are formed before their adds are issued (16: the whole row; 8: half a row, for
+// kernels that must keep registers low). The adds go out in the same order either way.
+template <int G16, int PART = 16>
+__device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, RefineShared& sh,
+                                                  int col) {
+  const int tid = col;
   const float If[16] = {t.I[0].x, t.I[0].y, t.I[0].z, t.I[0].w, t.I[1].x, t.I[1].y,
                         t.I[1].z, t.I[1].w, t.I[2].x, t.I[2].y, t.I[2].z, t.I[2].w,
                         t.I[3].x, t.I[3].y, t.I[3].z, t.I[3].w};
@@ -221,24 +226,28 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
     char* const row = lds + (t.sb[i] ? 16 * sizeof(sh.bins[0]) : 0);
     // every term of the row first, then every add: with one wave per SIMD, an add issued right
     // after the multiply that feeds it would wait for that result
-    double num[16], den[16];
-    double* p[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t word = k < 8 ? t.cw[i].x : t.cw[i].y;
-      const uint32_t q = (word >> (4 * (k & 7))) & 15u;
-      p[k] = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
-      const double Id = t.active ? (double)If[k] : 0.0;
-      num[k] = Id * (double)(s[i] * w[k]);       // s w is exact in fp32
-      den[k] = Id * s2;
-    }
-    __builtin_amdgcn_sched_barrier(0);
+    for (int h = 0; h < 16; h += PART) {
+      double num[PART], den[PART];
+      double* p[PART];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      atomicAdd(p[k], num[k]);
-      atomicAdd(p[k] + kBlock, den[k]);
+      for (int u = 0; u < PART; ++u) {
+        const int k = h + u;
+        const uint32_t word = k < 8 ? t.cw[i].x : t.cw[i].y;
+        const uint32_t q = (word >> (4 * (k & 7))) & 15u;
+        p[u] = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
+        const double Id = t.active ? (double)If[k] : 0.0;
+        num[u] = Id * (double)(s[i] * w[k]);       // s w is exact in fp32
+        den[u] = Id * s2;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < PART; ++u) {
+        atomicAdd(p[u], num[u]);
+        atomicAdd(p[u] + kBlock, den[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -255,7 +264,7 @@ __device__ __forceinline__ void accumulate_rows(const TaskRows& t, int gl, Refin
 }
 template <int GL>
 __device__ __forceinline__ void accumulate_rows(const TaskRows16& t, int gl, RefineShared& sh) {
-  accumulate_task16<GL>(t, gl, sh);
+  accumulate_task16<GL>(t, gl, sh, threadIdx.x);
 }
 
 // Round a finite fp64 value to bf16 (ties to even) directly, without an intermediate fp32
@@ -272,14 +281,16 @@ __device__ __forceinline__ float f64_to_bf16_value(double x) {
 }
 
 // Publish this workgroup's partial of job j (and zero the bins); the last workgroup of the job adds
-// all partials and writes the tables.
-__device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
-  const int tid = threadIdx.x;
+// all partials and writes the tables. Every thread of the workgroup calls it (it holds barriers);
+// tid is the caller's index among the kBlock accumulating threads, and threads outside [0, kBlock)
+// only take part in the barriers.
+__device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int tid) {
+  const bool act = tid >= 0 && tid < kBlock;
   const RefineJob& jb = b.job[j];
   __shared__ double part4[4][kVals];
   __shared__ uint32_t ticket;
   __syncthreads();
-  {
+  if (act) {
     // value v = tid & 63 over the 64 columns of quarter q = tid >> 6: four interleaved sums over a
     // rotated column order (no bank conflicts), all reads issued before the adds, combined in a
     // fixed order
@@ -291,11 +302,13 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
     part4[q][v] = (a[0] + a[1]) + (a[2] + a[3]);
   }
   __syncthreads();
+  if (act) {
 #pragma unroll
-  for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
+    for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
+  }
   double* part = b.partials + (size_t)j * kVals * b.slots;
   const int slot = (int)blockIdx.x - jb.wg_lo;
-  if (tid < kVals) {
+  if (act && tid < kVals) {
     const double tot = ((part4[0][tid] + part4[1][tid]) + part4[2][tid]) + part4[3][tid];
     part[(size_t)tid * b.slots + slot] = tot;
     __threadfence();
@@ -306,7 +319,7 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
   if (ticket != (uint32_t)(jb.wg_count - 1)) return;
   // last workgroup of this job: every partial is visible after the fence
   __threadfence();
-  {
+  if (act) {
     // the partials of value v, quarter q of the workgroups: eight loads in flight per step, added
     // in workgroup order
     const int v = tid & 63, q = tid >> 6;
@@ -326,7 +339,7 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh) {
     part4[q][v] = s;
   }
   __syncthreads();
-  if (tid < kCells) {
+  if (act && tid < kCells) {
     const int c = tid >> 4, idx = tid & 15;
     const int vn = 2 * tid, vd = 2 * tid + 1;
     const double nsum = ((part4[0][vn] + part4[1][vn]) + part4[2][vn]) + part4[3][vn];
@@ -367,7 +380,7 @@ __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
     load_rows(c, log2S, B);
     cursor_next(b, c);
     if (A.job != cur) {
-      if (cur >= 0) finish_job(b, cur, sh);
+      if (cur >= 0) finish_job(b, cur, sh, threadIdx.x);
       cur = A.job;
     }
     accumulate_rows<GL>(A, gl, sh);
@@ -375,12 +388,204 @@ __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
     load_rows(c, log2S, A);
     cursor_next(b, c);
     if (B.job != cur) {
-      finish_job(b, cur, sh);
+      finish_job(b, cur, sh, threadIdx.x);
       cur = B.job;
     }
     accumulate_rows<GL>(B, gl, sh);
   }
-  if (cur >= 0) finish_job(b, cur, sh);
+  if (cur >= 0) finish_job(b, cur, sh, threadIdx.x);
+}
+
+// ------------------------------------------------------------------------------------------------
+// Fused assign + accumulate: one launch per iteration of the loop (AAAC summary §2 mechanism 4,
+// the alternation of assignment and refinement).
+//
+// A workgroup of 16 waves: 12 assign waves and 4 accumulate waves, one workgroup per CU (the
+// accumulate waves hold the 128 KB of bins). The workgroup walks the same task range as a refine
+// workgroup, in steps of up to three tasks of one matrix. In step s the assign waves run the assign
+// of step s's tasks (four waves per task, the thread mapping of the assign kernel) and write codes
+// and selectors; the accumulate waves add up step s - 1 exactly as the refine kernel does (same
+// thread per column, same task and row order, same finish), reading the codes just written from
+// L2 and the selectors from LDS. Assign and accumulate waves share each SIMD, so one's VALU work
+// overlaps the other's LDS adds. Results are bitwise those of the assign launch followed by the
+// refine launch.
+// ------------------------------------------------------------------------------------------------
+constexpr int kFusedAssignWaves = 12;
+constexpr int kFusedGroups = kFusedAssignWaves / kWavesPerBlock;          // tasks per step
+constexpr int kFusedThreads = (kFusedAssignWaves + kWavesPerBlock) * kWave;
+constexpr int kFusedAcc0 = kFusedAssignWaves * kWave;                    // first accumulate thread
+
+namespace {
+
+struct FusedShared {
+  RefineShared rs;
+  Lut lut;
+  LutScratch ls;
+  // selector of each (task of the step, row of the task, lane) as written by the assign waves;
+  // two copies, for the step being assigned and the step being accumulated
+  uint8_t sig[2][kFusedGroups][kWideRowsPerTask][kWave];
+};
+
+// Tasks [lo, hi) of the step starting at `task`: up to kFusedGroups tasks, all of one matrix.
+__device__ __forceinline__ void fused_step(const RefineBatch& b, int64_t task, int64_t t_end,
+                                           int& job, int64_t& hi) {
+  int j = 0;
+  while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
+  const int64_t job_end = b.job[j].geom.task_begin + b.job[j].geom.ntasks;
+  hi = task + kFusedGroups;
+  hi = hi < job_end ? hi : job_end;
+  hi = hi < t_end ? hi : t_end;
+  job = j;
+}
+
+template <int G16, int S16>
+__device__ __forceinline__ void fused_assign_task(const RefineBatch& b, const RefineJob& jb,
+                                                  int64_t task, int w, int buf, int grp,
+                                                  const Lut& lut, FusedShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane, n = b.n;
+  const int log2S = 31 - __builtin_clz((unsigned)b.S);
+  const int64_t local = task - jb.geom.task_begin;
+  const int64_t rb = local / jb.geom.nslab;
+  const int slab = (int)(local - rb * jb.geom.nslab);
+  const int c0 = slab * kWideSlab + lane * kWideLane;
+  const bool active = c0 < jb.geom.C;
+  const int cl = active ? c0 : 0;
+  const int64_t R = jb.geom.R, C = jb.geom.C;
+  const int64_t r0 = rb * kWideRowsPerTask + w;
+  uint4 va[kWideRowsPerWave], vb[kWideRowsPerWave];
+#pragma unroll
+  for (int i = 0; i < kWideRowsPerWave; ++i) {
+    int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+    r = r < R ? r : R - 1;
+    const uint16_t* p = jb.W + r * C;
+    va[i] = *reinterpret_cast<const uint4*>(p + cl);
+    vb[i] = *reinterpret_cast<const uint4*>(p + cl + 8);
+  }
+  float Ik[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 x = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
+    Ik[4 * q] = x.x; Ik[4 * q + 1] = x.y; Ik[4 * q + 2] = x.z; Ik[4 * q + 3] = x.w;
+  }
+#pragma unroll
+  for (int i = 0; i < kWideRowsPerWave; ++i) {
+    const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+    if (r >= R) break;
+    Row16 o;
+    row16_core<false, G16, S16>(lut, n, g16, s16, active, jb.W + r * C + cl, jb.I + cl, va[i],
+                                vb[i], Ik, o);
+    const int64_t rc = r * C;
+    if (active)
+      store_row16<false>(o, jb.codes_out + (rc >> 3), jb.sel_out + (rc >> log2S), nullptr, s16,
+                         log2S, c0);
+    sh.sig[buf][grp][w + kWavesPerBlock * i][lane] = (uint8_t)o.sel;
+  }
+}
+
+// The accumulate side of one task: wave w of the accumulate waves adds rows w, w + 4, ... exactly
+// as the refine kernel's wave w does, with the selectors from LDS.
+template <int G16>
+__device__ __forceinline__ void fused_accumulate_task(const RefineBatch& b, const RefineJob& jb,
+                                                      int j, int64_t task, int w, int buf,
+                                                      int grp, FusedShared& sh) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t local = task - jb.geom.task_begin;
+  const int64_t rb = local / jb.geom.nslab;
+  const int slab = (int)(local - rb * jb.geom.nslab);
+  TaskRows16 t;
+  const int c0 = slab * kWideSlab + lane * kWideLane;
+  const int64_t R = jb.geom.R, C = jb.geom.C;
+  t.active = c0 < C;
+  const int cl = t.active ? c0 : 0;
+  t.job = j;
+  t.R = R;
+  t.r0 = rb * kWideRowsPerTask + w;
+#pragma unroll
+  for (int i = 0; i < kWideRowsPerWave; ++i) {
+    int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
+    r = r < R ? r : R - 1;
+    const int64_t base = r * C + cl;
+    t.va[i] = *reinterpret_cast<const uint4*>(jb.W + base);
+    t.vb[i] = *reinterpret_cast<const uint4*>(jb.W + base + 8);
+    t.cw[i] = *reinterpret_cast<const uint2*>(jb.codes_out + (base >> 3));
+    t.sb[i] = sh.sig[buf][grp][w + kWavesPerBlock * i][lane];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
+  accumulate_task16<G16, 8>(t, b.g / kWideLane, sh.rs, (int)threadIdx.x - kFusedAcc0);
+}
+
+}  // namespace
+
+template <int G16, int S16>
+__global__ __launch_bounds__(kFusedThreads, 1) void assign_refine_kernel(RefineBatch b) {
+  __shared__ FusedShared sh;
+  const int tid = threadIdx.x;
+  const int wave = wave_index();
+  const bool acc_wave = wave >= kFusedAssignWaves;
+  const int atid = tid - kFusedAcc0;                   // index among the accumulating threads
+  if (acc_wave) {
+#pragma unroll
+    for (int k = 0; k < kVals; ++k) sh.rs.bins[k >> 1][k & 1][atid] = 0.0;
+  }
+  const int64_t t_begin = task_lo(blockIdx.x, b.total_tasks, gridDim.x);
+  const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
+  int lut_job = -1, acc_job = -1;
+  int prev_job = -1;
+  int64_t prev_lo = 0, prev_hi = 0;                    // the step the accumulate waves take next
+  int buf = 0;
+  for (int64_t lo = t_begin;; buf ^= 1) {
+    int job = -1;
+    int64_t hi = lo;
+    if (lo < t_end) fused_step(b, lo, t_end, job, hi);
+    if (job < 0 && prev_job < 0) break;
+    // matrix changes, with every thread: the accumulate side finishes its matrix before it starts
+    // the next one; the assign side builds the lookup structure of its new matrix
+    if (prev_job >= 0 && prev_job != acc_job) {
+      if (acc_job >= 0) finish_job(b, acc_job, sh.rs, atid);
+      acc_job = prev_job;
+    }
+    if (job >= 0 && job != lut_job) {
+      __syncthreads();
+      build_lut(b.job[job].tables_in, b.n, sh.lut, sh.ls);
+      lut_job = job;
+    }
+    if (!acc_wave) {
+      const int grp = wave / kWavesPerBlock;
+      if (job >= 0 && lo + grp < hi)
+        fused_assign_task<G16, S16>(b, b.job[job], lo + grp, wave % kWavesPerBlock, buf, grp,
+                                    sh.lut, sh);
+    } else if (prev_job >= 0) {
+      // the codes of step s - 1 were written by this workgroup's assign waves before the last
+      // barrier (a workgroup-scope release and acquire: all waves share this CU's write-through
+      // cache, so a line cached earlier cannot hide them)
+      for (int64_t t = prev_lo; t < prev_hi; ++t)
+        fused_accumulate_task<G16>(b, b.job[prev_job], prev_job, t, wave - kFusedAssignWaves,
+                                   buf ^ 1, (int)(t - prev_lo), sh);
+    }
+    __syncthreads();
+    prev_job = job;
+    prev_lo = lo;
+    prev_hi = hi;
+    lo = hi;
+  }
+  if (acc_job >= 0) finish_job(b, acc_job, sh.rs, atid);
+}
+
+hipError_t launch_assign_refine(RefineBatch& b, hipStream_t stream) {
+  if (b.nblocks <= 0) return hipSuccess;
+  const dim3 grid(b.nblocks), block(kFusedThreads);
+  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane;
+  if (g16 == 8 && s16 == 8)
+    hipLaunchKernelGGL((assign_refine_kernel<8, 8>), grid, block, 0, stream, b);
+  else if (g16 == 8 && s16 == 1)
+    hipLaunchKernelGGL((assign_refine_kernel<8, 1>), grid, block, 0, stream, b);
+  else if (g16 == 1 && s16 == 1)
+    hipLaunchKernelGGL((assign_refine_kernel<1, 1>), grid, block, 0, stream, b);
+  else
+    hipLaunchKernelGGL((assign_refine_kernel<0, 0>), grid, block, 0, stream, b);
+  return hipGetLastError();
 }
 
 MatrixGeom refine_geom(int64_t R, int64_t C, int64_t task_begin, int S) {

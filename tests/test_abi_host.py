@@ -153,3 +153,15 @@ def test_awq_prescale_rejects_bad_arguments(lib):
              None) == INVALID                                                  # a misaligned
     assert f(FAKE, i64(4), i64(16), FAKE, FAKE, FAKE, None, None) == INVALID    # I without I_scaled
     assert b"I_scaled" in lib.aaac_last_error()
+
+
+def test_assign_refine_batch_rejects_bad_arguments(lib):
+    P = (ctypes.c_void_p * 1)(FAKE)
+    R = (i64 * 1)(64)
+    C = (i64 * 1)(1024)
+    f = lib.aaac_assign_refine_batch
+    need = lib.aaac_batch_workspace_bytes(OP_REFINE, 1, R, C, 128, 128, 16)
+    assert f(0, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(need), None) == INVALID
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 4, FAKE, ctypes.c_size_t(need), None) == INVALID
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(16), None) == WS_SMALL
+    assert f(1, P, R, C, 100, 100, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(need), None) == SHAPE
