@@ -9,7 +9,11 @@ from ._lib import (  # noqa: F401
     AAACError,
     aaac_assign,
     aaac_assign_batch,
+    aaac_assign_refine_batch,
+    aaac_awq_prescale,
     aaac_dequant,
+    aaac_gemv,
+    aaac_gemv_batch,
     aaac_importance,
     aaac_init_quantiles,
     aaac_pack,
@@ -17,4 +21,10 @@ from ._lib import (  # noqa: F401
     aaac_refine_batch,
     load,
 )
-from .quantize import QuantizedMatrix, importance, quantize_matrices, quantize_matrix  # noqa: F401
+from .quantize import (  # noqa: F401
+    QuantizedMatrix,
+    awq_prescale,
+    importance,
+    quantize_matrices,
+    quantize_matrix,
+)

@@ -36,6 +36,16 @@ class QuantizedMatrix:
                        self.g, self.S, self.n, out)
         return out
 
+    def gemv(self, x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """fp32 [B, R] = the packed weights times x (bf16 [B, C] or [C], B <= 4), decoded on the
+        fly (AAAC summary §1: the dequantized values are what inference uses)."""
+        x2 = x.reshape(-1, self.C).contiguous()
+        if out is None:
+            out = torch.empty(x2.shape[0], self.R, dtype=torch.float32, device=x.device)
+        L.aaac_gemv(self.codes, self.scales, self.bitmap, self.tables_bf16, self.R, self.C,
+                    self.g, self.S, self.n, x2, out)
+        return out
+
 
 def importance(chunks: Iterable[torch.Tensor], K: int, device) -> torch.Tensor:
     """fp32 [K] I_k = sum over all chunks of X[:, k]^2, accumulated in fp64 on the device."""
@@ -124,3 +134,12 @@ def quantize_matrix(W: torch.Tensor, I: torch.Tensor, g: int = 128, S: int = 128
                     iters: int = 10, tables=None) -> QuantizedMatrix:
     return quantize_matrices([W], [I], g, S, n, iters,
                              None if tables is None else [tables])[0]
+
+
+def awq_prescale(W: torch.Tensor, a: torch.Tensor, I: Optional[torch.Tensor] = None):
+    """Inputs for quantizing W diag(a) after AWQ-style weight scaling (AAAC summary §4):
+    (bf16(W * a), fp32(I / a^2) or None). The inference side then feeds x / a."""
+    Ws = torch.empty_like(W)
+    Is = None if I is None else torch.empty_like(I)
+    L.aaac_awq_prescale(W, a, Ws, I, Is)
+    return Ws, Is

@@ -306,6 +306,18 @@ def test_pack_and_dequant_bit_exact(R, C, g, S, n):
     assert np.array_equal(np.signbit(ref.bits_to_float(got)), np.signbit(want))
     # the final codes are the oracle's assign against the stored tables
     par.check_assign(W64, par.to_np64(I), tabs, g, S, codes, sel)
+    # decode GEMV on the quantized matrix (C % 32 == 0): within the fp32 bound of its sums
+    if C % 32 == 0:
+        x = torch.randn(2, C, device=DEV, generator=torch.Generator(device=DEV).manual_seed(C))
+        x = x.to(torch.bfloat16)
+        y = q.gemv(x)
+        torch.cuda.synchronize()
+        x64 = par.to_np64(x)
+        y_ref, a_ref = ref.gemv(p["codes"], p["scales"], p["bitmap"], p["tables"], R, C, g, S, x64)
+        nslab = -(-C // 2048)
+        gpl = 1 if g >= 32 else 32 // g
+        bound = (32 * nslab + gpl * nslab + 8) * 2.0 ** -24 * a_ref + 1e-30
+        assert np.all(np.abs(_np(y).astype(np.float64) - y_ref) <= bound)
 
 
 # ------------------------------------------------------------------ batch / determinism
