@@ -219,9 +219,9 @@ struct Row16 {
   float w[16];       // the weights
 };
 
-// LIMIT: interleave at most four weights' lookups (for kernels that run several waves per SIMD and
-// must keep registers low); without it the compiler may overlap all sixteen.
-template <bool WITH_ERR, int G16, int S16, bool LIMIT = true>
+// The compiler may interleave the lookups of all sixteen weights (the exact scan is out of line, so
+// the row stays within the register budget of four waves per SIMD).
+template <bool WITH_ERR, int G16, int S16>
 __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s16, bool active,
                                            const uint16_t* wsafe, const float* isafe,
                                            const uint4& va, const uint4& vb,
@@ -264,7 +264,6 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
       e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
       e1d = (q == 0) ? (double)a1 : e1d + (double)a1;
     }
-    if (LIMIT) __builtin_amdgcn_sched_barrier(0);
   }
   double D = block_sum_f64_t<S16>(accd, s16);
   double E0 = WITH_ERR ? block_sum_f64_t<S16>(e0d, s16) : 0.0;
