@@ -1,6 +1,6 @@
 """Comparison helpers for the GPU parity tests: HIP results against the fp64 oracle.
 
-Tolerances (derived in the design doc from the arithmetic of each kernel):
+Tolerances (each derived from the arithmetic of the kernel it checks):
   * codes: bit-exact, except a weight whose GPU entry is strictly farther than the oracle's nearest
     one by less than CODE_BAND (relative squared distance); equal distances must pick the lower
     index, so value ties are never exempt;
