@@ -68,7 +68,7 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
   const bool zero = (s == 0.0f);
   const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
   const float se = zero ? 1.0f : s;
-  const float Y = kLutScale * __builtin_amdgcn_rcpf(se);
+  const float Y = lut_y(se);
   const float nse = -se;
 
   float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
@@ -76,28 +76,7 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
   uint32_t Pw = 0, Qw = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const float t = __builtin_fmaf(w[k], Y, kLutMagic);
-    const uint32_t rho = __float_as_uint(t) & kLutMask;
-    const uint32_t cb = lut.code[rho];
-    const float2 p0 = *reinterpret_cast<const float2*>(
-        reinterpret_cast<const uint8_t*>(lut.pairs[0]) + lut.off0[rho]);
-    const float2 p1 = *reinterpret_cast<const float2*>(
-        reinterpret_cast<const uint8_t*>(lut.pairs[1]) + lut.off1[rho]);
-    const float r0a = __builtin_fmaf(nse, p0.x, w[k]);
-    const float r0b = __builtin_fmaf(nse, p0.y, w[k]);
-    const float r1a = __builtin_fmaf(nse, p1.x, w[k]);
-    const float r1b = __builtin_fmaf(nse, p1.y, w[k]);
-    const bool d0 = fabsf(r0b) < fabsf(r0a);
-    const bool d1 = fabsf(r1b) < fabsf(r1a);
-    const float m0 = fminf(fabsf(r0a), fabsf(r0b));
-    const float m1 = fminf(fabsf(r1a), fabsf(r1b));
-    const float e0 = m0 * m0;
-    acc = __builtin_fmaf(Ik[k], __builtin_fmaf(m1, m1, -e0), acc);
-    if (WITH_ERR) {
-      a0 = __builtin_fmaf(Ik[k], e0, a0);
-      a1 = __builtin_fmaf(Ik[k], m1 * m1, a1);
-    }
-    const uint32_t c = cb + (d0 ? 1u : 0u) + (d1 ? 16u : 0u);
+    const uint32_t c = lookup_weight<WITH_ERR>(w[k], Y, nse, lut, Ik[k], acc, a0, a1);
     if (k < 4) Pw |= c << (8 * k); else Qw |= c << (8 * (k - 4));
     if (k == 3 || k == 7) {
       accd += (double)acc;

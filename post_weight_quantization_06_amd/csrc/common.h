@@ -30,25 +30,28 @@ constexpr int kWideLane = 16;
 constexpr int kWideSlab = kWave * kWideLane;
 constexpr int kWideRowsPerWave = 4;
 constexpr int kWideRowsPerTask = kWideRowsPerWave * kWavesPerBlock;
+
 constexpr int kMaxJobs = 8;
 
 // ------------------------------------------------------------------------------------------------
 // Nearest-entry lookup structure (built in LDS by the assign kernel from the two tables).
-// u in [-1, 1] maps to record rho = bits(t) & kLutMask with
-//   t = fma(w, Y, kLutMagic),  Y = kLutScale / s,
-// t lies in [2^23, 2^24), so its low mantissa bits hold round(1 + kLutScale (u + 1)); record rho
+// u in [-1, 1] maps to record rho = round(kLutScale (u + 1)) + 1 through one fma,
+//   t = fma(w, Y, kLutMagic),  Y = kLutY / s,  kLutY = kLutScale * 2^-22,
+// which lands t in [2, 4), where the fp32 quantum is 2^-22: the low mantissa bits of t hold rho
+// (rounded to nearest even, as for any fp32 result), and the exponent field is 128, so shifting the
+// bit pattern left by two drops the exponent and leaves 4 rho, the record's byte offset. Record rho
 // covers u in [(rho - 1.5) / kLutScale - 1, (rho - 0.5) / kLutScale - 1]. For each table the record
 // holds the byte offset of a candidate pair {T[i], T[i+1]} in a small pair array (T[n] reads as
 // +inf), valid over that interval widened by kLutSlack: the nearest entry there is T[i], or T[i+1]
 // past the one midpoint the record contains. A record that would need other candidates points at a
-// NaN pair, which routes its group to the exact full scan. A third byte array holds the code base
-// i0 | i1 << 4. Three byte arrays and two 18-pair arrays: a few KB of LDS, and the pair reads hit at
-// most 18 distinct addresses per wave, so they never conflict.
+// NaN pair, which routes its group to the exact full scan. One 32-bit word per record (pair offsets
+// of both tables and the code base i0 | i1 << 4) and two 18-pair arrays: a few KB of LDS, and the
+// pair reads hit at most 18 distinct addresses per wave, so they never conflict.
 // ------------------------------------------------------------------------------------------------
 constexpr int kLutRecs = 1024;
-constexpr uint32_t kLutMask = kLutRecs - 1;
 constexpr float kLutScale = 0.5f * (kLutRecs - 2);                    // 511
-constexpr float kLutMagic = 8388608.0f + 1.0f + 0.5f * (kLutRecs - 2);
+constexpr float kLutY = 0x1p-22f * kLutScale;
+constexpr float kLutMagic = 2.0f + 0x1p-22f * (1.0f + kLutScale);     // 2 + 512 * 2^-22
 constexpr double kLutSlack = 0x1p-20;
 constexpr int kPairs = 18;                 // pair i < 17: {T[i], T[i + 1]}; pair 17: NaN
 constexpr int kNaNPair = 17;

@@ -32,12 +32,10 @@ struct LutScratch {
   int m[2];                 // distinct values (0: the table has a non-finite entry)
 };
 
-// The lookup structure in LDS: per record the byte offsets of the two candidate pairs and the code
-// base, and per table the pair arrays.
+// The lookup structure in LDS: per record one word, off0 | off1 << 8 | (i0 | i1 << 4) << 16 (byte
+// offsets of the two candidate pairs and the code base), and per table the pair arrays.
 struct Lut {
-  uint8_t off0[kLutRecs];
-  uint8_t off1[kLutRecs];
-  uint8_t code[kLutRecs];
+  uint32_t rec[kLutRecs];
   float2 pairs[2][kPairs];
   float tab[2][16];         // the raw tables, for the exact scan
 };
@@ -121,12 +119,13 @@ __device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScrat
       off[c] = (uint32_t)((single || pair) ? i0 : kNaNPair) * 8u;
       code |= (single || pair) ? ((uint32_t)i0 << (4 * c)) : 0u;
     }
-    lut.off0[rho] = (uint8_t)off[0];
-    lut.off1[rho] = (uint8_t)off[1];
-    lut.code[rho] = (uint8_t)code;
+    lut.rec[rho] = off[0] | (off[1] << 8) | (code << 16);
   }
   __syncthreads();
 }
+
+// Y for a group scale se > 0 (the lookup's u = w / se, scaled into the record index).
+__device__ __forceinline__ float lut_y(float se) { return kLutY * __builtin_amdgcn_rcpf(se); }
 
 // Nearest entries of one weight in both tables from the lookup structure (see the layout above):
 // returns the code byte q0 | q1 << 4 and accumulates I (m1^2 - m0^2) (and the two errors).
@@ -134,12 +133,13 @@ template <bool WITH_ERR>
 __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, const Lut& lut,
                                                   float Ik, float& acc, float& a0, float& a1) {
   const float t = __builtin_fmaf(w, Y, kLutMagic);
-  const uint32_t rho = __float_as_uint(t) & kLutMask;
-  const uint32_t cb = lut.code[rho];
+  const uint32_t rec = *reinterpret_cast<const uint32_t*>(
+      reinterpret_cast<const uint8_t*>(lut.rec) + (__float_as_uint(t) << 2));
+  const uint32_t cb = rec >> 16;
   const float2 p0 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[0]) + lut.off0[rho]);
+      reinterpret_cast<const uint8_t*>(lut.pairs[0]) + (rec & 0xFFu));
   const float2 p1 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[1]) + lut.off1[rho]);
+      reinterpret_cast<const uint8_t*>(lut.pairs[1]) + ((rec >> 8) & 0xFFu));
   const float r0a = __builtin_fmaf(nse, p0.x, w);
   const float r0b = __builtin_fmaf(nse, p0.y, w);
   const float r1a = __builtin_fmaf(nse, p1.x, w);
@@ -155,13 +155,6 @@ __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, c
     a1 = __builtin_fmaf(Ik, m1 * m1, a1);
   }
   return cb + (d0 ? 1u : 0u) + (d1 ? 16u : 0u);
-}
-
-// Keep the nibble of table `sel` from four code bytes (q0 | q1 << 4): bytes 0 and 2 of the result
-// hold two codes each.
-__device__ __forceinline__ uint32_t select_nibbles(uint32_t P, uint32_t sel) {
-  uint32_t p = (P >> (sel ? 4u : 0u)) & 0x0F0F0F0Fu;
-  return p | (p >> 4);
 }
 
 // Exact fallback for one lane of the wide mapping, reading its 16 weights and importances again
@@ -209,18 +202,20 @@ __device__ __noinline__ void slow_lane16(const uint16_t* __restrict__ wp,
 }
 
 // Codes, selection and errors of one row of the wide mapping (16 weights per lane); nothing is
-// stored. wsafe / isafe address the lane's 16 weights and importances in memory (in bounds also for
-// inactive lanes) for the exact fallback.
+// stored. The code bytes q0 | q1 << 4 are kept split by column parity so that the chosen nibbles
+// pack into code words with one bit-field insert: E[h] byte b belongs to weight 8h + 2b, O[h]
+// byte b to weight 8h + 2b + 1.
 struct Row16 {
-  uint32_t P[4];     // code bytes q0 | q1 << 4 of weights 4q .. 4q + 3
+  uint32_t E[2], O[2];
   uint32_t sel;      // 1 = T1
   double E0, E1;     // only with WITH_ERR
-  float s;           // the group scale
-  float w[16];       // the weights
 };
 
-// The compiler may interleave the lookups of all sixteen weights (the exact scan is out of line, so
-// the row stays within the register budget of four waves per SIMD).
+// One row: group scale, nearest entries of all sixteen weights, and the selection of each group.
+// G16 / S16 are the lanes per scale / selection group (0: the runtime g16 / s16). wsafe / isafe
+// address the lane's 16 weights and importances in memory (in bounds also for inactive lanes) for
+// the exact fallback. The compiler may interleave all sixteen lookups (the exact scan is out of
+// line, so the row stays within the register budget of four waves per SIMD).
 template <bool WITH_ERR, int G16, int S16>
 __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s16, bool active,
                                            const uint16_t* wsafe, const float* isafe,
@@ -228,8 +223,12 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
                                            const float (&Ik)[16], Row16& o) {
   const uint32_t amax = block_max_u32_t<G16>(lane_absmax16_bits(va, vb), g16);
   const float s = __uint_as_float(amax << 16);
-  o.s = s;
-  float* const w = o.w;
+  const bool zero = (s == 0.0f);
+  const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
+  const float se = zero ? 1.0f : s;
+  const float Y = lut_y(se);
+  const float nse = -se;
+  float w[16];
   {
     float wa[8], wb[8];
     unpack8(va, wa);
@@ -240,25 +239,21 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
       w[8 + k] = wb[k];
     }
   }
-  const bool zero = (s == 0.0f);
-  const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
-  const float se = zero ? 1.0f : s;
-  const float Y = kLutScale * __builtin_amdgcn_rcpf(se);
-  const float nse = -se;
 
+  uint32_t Ew[2] = {0u, 0u}, Ow[2] = {0u, 0u};
   double accd = 0.0, e0d = 0.0, e1d = 0.0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     // four weights per fp32 partial, then fp64
     float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
-    uint32_t word = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const uint32_t c = lookup_weight<WITH_ERR>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc,
                                                  a0, a1);
-      word |= c << (8 * k);
+      // weight 4q + k: word q / 2, byte 2 (q & 1) + k / 2 of its parity
+      const int sh = 8 * (2 * (q & 1) + (k >> 1));
+      if (k & 1) Ow[q >> 1] |= c << sh; else Ew[q >> 1] |= c << sh;
     }
-    o.P[q] = word;
     accd = (q == 0) ? (double)acc : accd + (double)acc;
     if (WITH_ERR) {
       e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
@@ -288,29 +283,39 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
       D = sD;
       E0 = sE0;
       E1 = sE1;
-      o.P[0] = (uint32_t)clo;
-      o.P[1] = (uint32_t)(clo >> 32);
-      o.P[2] = (uint32_t)chi;
-      o.P[3] = (uint32_t)(chi >> 32);
+      // byte k of (clo, chi) is weight k
+      const uint32_t l0 = (uint32_t)clo, l1 = (uint32_t)(clo >> 32);
+      const uint32_t h0 = (uint32_t)chi, h1 = (uint32_t)(chi >> 32);
+      Ew[0] = __builtin_amdgcn_perm(l1, l0, 0x06040200u);
+      Ow[0] = __builtin_amdgcn_perm(l1, l0, 0x07050301u);
+      Ew[1] = __builtin_amdgcn_perm(h1, h0, 0x06040200u);
+      Ow[1] = __builtin_amdgcn_perm(h1, h0, 0x07050301u);
     }
   }
+  o.E[0] = Ew[0]; o.E[1] = Ew[1];
+  o.O[0] = Ow[0]; o.O[1] = Ow[1];
   o.sel = (D < 0.0) ? 1u : 0u;
   o.E0 = E0;
   o.E1 = E1;
 }
 
 // Store the selected codes (8 bytes), and once per selection group the selector (and errors).
-template <bool WITH_ERR>
 // codes_row, sel_row and err_row point at the row's first code word, selector and error pair
 // (wave-uniform); c0 is the lane's first column. Rows start on a selection-group boundary, so the
 // lane's offsets within the row follow from c0 alone.
+template <bool WITH_ERR>
 __device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes_row, uint8_t* sel_row,
                                             double* err_row, int s16, int log2S, int c0) {
-  const uint32_t lo = __builtin_amdgcn_perm(select_nibbles(o.P[1], o.sel),
-                                            select_nibbles(o.P[0], o.sel), 0x06040200u);
-  const uint32_t hi = __builtin_amdgcn_perm(select_nibbles(o.P[3], o.sel),
-                                            select_nibbles(o.P[2], o.sel), 0x06040200u);
-  *reinterpret_cast<uint2*>(codes_row + (c0 >> 3)) = make_uint2(lo, hi);
+  const uint32_t sh = o.sel ? 4u : 0u;
+  uint32_t out[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    // low nibble: the chosen code of the even column, high nibble: of the odd column
+    const uint32_t lo = o.E[k] >> sh;
+    const uint32_t hi = o.O[k] << (4u - sh);
+    out[k] = (lo & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);
+  }
+  *reinterpret_cast<uint2*>(codes_row + (c0 >> 3)) = make_uint2(out[0], out[1]);
   if (((c0 >> 4) & (s16 - 1)) == 0) {
     const int h = c0 >> log2S;
     sel_row[h] = (uint8_t)o.sel;
