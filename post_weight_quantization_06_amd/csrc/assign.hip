@@ -76,7 +76,8 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
   uint32_t Pw = 0, Qw = 0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const uint32_t c = lookup_weight<WITH_ERR>(w[k], Y, nse, lut, Ik[k], acc, a0, a1);
+    // byte 0 of the lookup's result is the code byte
+    const uint32_t c = lookup_weight<WITH_ERR>(w[k], Y, nse, lut, Ik[k], acc, a0, a1) & 0xFFu;
     if (k < 4) Pw |= c << (8 * k); else Qw |= c << (8 * (k - 4));
     if (k == 3 || k == 7) {
       accd += (double)acc;

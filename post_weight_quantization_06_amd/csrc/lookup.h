@@ -32,8 +32,8 @@ struct LutScratch {
   int m[2];                 // distinct values (0: the table has a non-finite entry)
 };
 
-// The lookup structure in LDS: per record one word, off0 | off1 << 8 | (i0 | i1 << 4) << 16 (byte
-// offsets of the two candidate pairs and the code base), and per table the pair arrays.
+// The lookup structure in LDS: per record one word, (i0 | i1 << 4) | off0 << 8 | off1 << 16 (the
+// code base and the byte offsets of the two candidate pairs), and per table the pair arrays.
 struct Lut {
   uint32_t rec[kLutRecs];
   float2 pairs[2][kPairs];
@@ -119,7 +119,7 @@ __device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScrat
       off[c] = (uint32_t)((single || pair) ? i0 : kNaNPair) * 8u;
       code |= (single || pair) ? ((uint32_t)i0 << (4 * c)) : 0u;
     }
-    lut.rec[rho] = off[0] | (off[1] << 8) | (code << 16);
+    lut.rec[rho] = code | (off[0] << 8) | (off[1] << 16);
   }
   __syncthreads();
 }
@@ -128,18 +128,20 @@ __device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScrat
 __device__ __forceinline__ float lut_y(float se) { return kLutY * __builtin_amdgcn_rcpf(se); }
 
 // Nearest entries of one weight in both tables from the lookup structure (see the layout above):
-// returns the code byte q0 | q1 << 4 and accumulates I (m1^2 - m0^2) (and the two errors).
+// returns the record word with the code byte q0 | q1 << 4 in byte 0 (the increments never carry out
+// of a nibble: a pair whose second entry is past the table or NaN is never taken), and accumulates
+// I (m1^2 - m0^2) (and the two errors).
 template <bool WITH_ERR>
 __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, const Lut& lut,
                                                   float Ik, float& acc, float& a0, float& a1) {
   const float t = __builtin_fmaf(w, Y, kLutMagic);
+  const uint32_t ra = __float_as_uint(t) << 2;
   const uint32_t rec = *reinterpret_cast<const uint32_t*>(
-      reinterpret_cast<const uint8_t*>(lut.rec) + (__float_as_uint(t) << 2));
-  const uint32_t cb = rec >> 16;
+      reinterpret_cast<const uint8_t*>(lut.rec) + ra);
   const float2 p0 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[0]) + (rec & 0xFFu));
+      reinterpret_cast<const uint8_t*>(lut.pairs[0]) + ((rec >> 8) & 0xFFu));
   const float2 p1 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[1]) + ((rec >> 8) & 0xFFu));
+      reinterpret_cast<const uint8_t*>(lut.pairs[1]) + (rec >> 16));
   const float r0a = __builtin_fmaf(nse, p0.x, w);
   const float r0b = __builtin_fmaf(nse, p0.y, w);
   const float r1a = __builtin_fmaf(nse, p1.x, w);
@@ -154,7 +156,7 @@ __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, c
     a0 = __builtin_fmaf(Ik, e0, a0);
     a1 = __builtin_fmaf(Ik, m1 * m1, a1);
   }
-  return cb + (d0 ? 1u : 0u) + (d1 ? 16u : 0u);
+  return rec + (d0 ? 1u : 0u) + (d1 ? 16u : 0u);   // byte 0: the code byte
 }
 
 // Exact fallback for one lane of the wide mapping, reading its 16 weights and importances again
@@ -202,7 +204,7 @@ __device__ __noinline__ void slow_lane16(const uint16_t* __restrict__ wp,
 }
 
 // Codes, selection and errors of one row of the wide mapping (16 weights per lane); nothing is
-// stored. The code bytes q0 | q1 << 4 are kept split by column parity so that the chosen nibbles
+// stored. The code bytes q0 | q1 << 4 are gathered by column parity so that the chosen nibbles
 // pack into code words with one bit-field insert: E[h] byte b belongs to weight 8h + 2b, O[h]
 // byte b to weight 8h + 2b + 1.
 struct Row16 {
@@ -240,25 +242,33 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
     }
   }
 
-  uint32_t Ew[2] = {0u, 0u}, Ow[2] = {0u, 0u};
+  uint32_t c[16];
   double accd = 0.0, e0d = 0.0, e1d = 0.0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     // four weights per fp32 partial, then fp64
     float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t c = lookup_weight<WITH_ERR>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc,
-                                                 a0, a1);
-      // weight 4q + k: word q / 2, byte 2 (q & 1) + k / 2 of its parity
-      const int sh = 8 * (2 * (q & 1) + (k >> 1));
-      if (k & 1) Ow[q >> 1] |= c << sh; else Ew[q >> 1] |= c << sh;
-    }
+    for (int k = 0; k < 4; ++k)
+      c[4 * q + k] = lookup_weight<WITH_ERR>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc, a0,
+                                             a1);
     accd = (q == 0) ? (double)acc : accd + (double)acc;
     if (WITH_ERR) {
       e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
       e1d = (q == 0) ? (double)a1 : e1d + (double)a1;
     }
+  }
+  // byte 0 of c[k] is weight k's code byte; gather them by column parity
+  uint32_t Ew[2], Ow[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t* ch = c + 8 * h;
+    const uint32_t e01 = __builtin_amdgcn_perm(ch[2], ch[0], 0x0c0c0400u);
+    const uint32_t e23 = __builtin_amdgcn_perm(ch[6], ch[4], 0x0c0c0400u);
+    Ew[h] = __builtin_amdgcn_perm(e23, e01, 0x05040100u);
+    const uint32_t o01 = __builtin_amdgcn_perm(ch[3], ch[1], 0x0c0c0400u);
+    const uint32_t o23 = __builtin_amdgcn_perm(ch[7], ch[5], 0x0c0c0400u);
+    Ow[h] = __builtin_amdgcn_perm(o23, o01, 0x05040100u);
   }
   double D = block_sum_f64_t<S16>(accd, s16);
   double E0 = WITH_ERR ? block_sum_f64_t<S16>(e0d, s16) : 0.0;
