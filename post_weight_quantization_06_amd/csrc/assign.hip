@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
     const AssignJob& jb = b.job[j];
     if (j != cur) {
       __syncthreads();
-      build_lut(jb.tables, n, lut, ls);
+      build_lut<kBlock>(jb.tables, n, lut, ls);
       cur = j;
     }
     const int64_t local = task - jb.geom.task_begin;
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
     const AssignJob& jb = b.job[j];
     if (j != cur) {
       __syncthreads();
-      build_lut(jb.tables, n, lut, ls);
+      build_lut<kBlock>(jb.tables, n, lut, ls);
       cur = j;
     }
     const int64_t local = task - jb.geom.task_begin;

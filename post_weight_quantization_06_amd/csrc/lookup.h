@@ -27,9 +27,8 @@ struct LutScratch {
   int first[2][16];
   float sv[2][16];          // distinct values, ascending
   int six[2][16];           // lowest index holding each distinct value
-  int mlo[2][16];           // midpoint i lies in record rho iff mlo[i] <= rho <= mhi[i]
-  int mhi[2][16];           // and lies below record rho iff mhi[i] < rho
   int m[2];                 // distinct values (0: the table has a non-finite entry)
+  uint32_t wsum[16];        // per-wave totals of the record scan
 };
 
 // The lookup structure in LDS: per record one word, (i0 | i1 << 4) | off0 << 8 | off1 << 16 (the
@@ -40,9 +39,21 @@ struct Lut {
   float tab[2][16];         // the raw tables, for the exact scan
 };
 
-// Build the lookup structure for tables T (fp32 [2][n], global) with all threads of the block.
-// Must be called by every thread; ends with a barrier.
-__device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScratch& ls) {
+// Build the lookup structure for tables T (fp32 [2][n], global) with all NT threads of the block
+// (NT = blockDim.x, a power of two from 64 to 1024). Must be called by every thread; ends with a
+// barrier.
+//
+// Midpoint i of a table (between its distinct values i and i + 1) lies in the records
+// [mlo_i, mhi_i] and below every record past mhi_i. Per record, "below" (midpoints below it) and
+// "inside" (midpoints in it) decide the candidates. They are counted with a difference array: each
+// midpoint adds +1 to below at mhi_i + 1, +1 to inside at mlo_i and -1 at mhi_i + 1, one byte per
+// count in a packed word (below_0, inside_0, below_1, inside_1; every count is at most 15, so the
+// packed prefix sums are exact). The array lives in the record words themselves, and one prefix
+// scan over the 1024 records turns it into the counts, which each thread then replaces by its
+// records' final words.
+template <int NT>
+__device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScratch& ls) {
+  static_assert(NT >= kWave && NT <= kLutRecs && (NT & (NT - 1)) == 0, "block size");
   const int tid = threadIdx.x;
   const float qnan = __uint_as_float(0x7fc00000u);
   if (tid < 32) {
@@ -51,6 +62,9 @@ __device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScrat
     ls.raw[c][j] = x;
     lut.tab[c][j] = x;
   }
+  constexpr int kPer = kLutRecs / NT;       // records per thread
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) lut.rec[tid + NT * k] = 0u;
   __syncthreads();
   if (tid < 32) {
     const int c = tid >> 4, j = tid & 15;
@@ -92,22 +106,47 @@ __device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScrat
       const double S = (double)kLutScale;
       const double hi = floor((M + 1.0 + kLutSlack) * S + 1.5);
       const double lo = ceil((M + 1.0 - kLutSlack) * S + 0.5);
-      ls.mhi[c][i] = (int)fmin(fmax(hi, -1.0), 4096.0);
-      ls.mlo[c][i] = (int)fmin(fmax(lo, -1.0), 4096.0);
+      // hi >= lo always; both clamped to [-1, 4096]
+      const int mhi = (int)fmin(fmax(hi, -1.0), 4096.0);
+      const int mlo = (int)fmin(fmax(lo, -1.0), 4096.0);
+      const int end = mhi + 1;                           // >= 0
+      const bool in_range = mhi >= 0 && mlo < kLutRecs;  // the midpoint lies in some record
+      const uint32_t in1 = 1u << (16 * c + 8);
+      if (end < kLutRecs) atomicAdd(&lut.rec[end], (1u << (16 * c)) - (in_range ? in1 : 0u));
+      if (in_range) atomicAdd(&lut.rec[mlo > 0 ? mlo : 0], in1);
     }
   }
   __syncthreads();
-  for (int rho = tid; rho < kLutRecs; rho += (int)blockDim.x) {
+  // prefix sums: thread t owns the run of kPer consecutive records starting at t * kPer
+  const int r0 = tid * kPer;
+  uint32_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) tot += lut.rec[r0 + k];
+  // inclusive scan of the thread totals within the wave, then across the waves
+  const int lane = tid & (kWave - 1);
+  uint32_t incl = tot;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) ls.wsum[tid / kWave] = incl;
+  __syncthreads();
+  uint32_t P = incl - tot;
+  const int wv = tid / kWave;
+#pragma unroll
+  for (int w = 0; w < NT / kWave - 1; ++w) P += (w < wv) ? ls.wsum[w] : 0u;
+  // each record is read (its difference) before this thread overwrites it with the final word
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    P += lut.rec[r0 + k];
     uint32_t off[2];
     uint32_t code = 0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int m = ls.m[c];
-      int below = 0, inside = 0;
-      for (int i = 0; i + 1 < m; ++i) {
-        below += (ls.mhi[c][i] < rho) ? 1 : 0;
-        inside += (ls.mlo[c][i] <= rho && rho <= ls.mhi[c][i]) ? 1 : 0;
-      }
+      const int below = (int)((P >> (16 * c)) & 0xFFu);
+      const int inside = (int)((P >> (16 * c + 8)) & 0xFFu);
       // clamped indices keep every read inside the arrays whatever the branch
       const int j0 = below < 15 ? below : 15;
       const int j1 = below + 1 < 15 ? below + 1 : 15;
@@ -119,7 +158,7 @@ __device__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScrat
       off[c] = (uint32_t)((single || pair) ? i0 : kNaNPair) * 8u;
       code |= (single || pair) ? ((uint32_t)i0 << (4 * c)) : 0u;
     }
-    lut.rec[rho] = code | (off[0] << 8) | (off[1] << 16);
+    lut.rec[r0 + k] = code | (off[0] << 8) | (off[1] << 16);
   }
   __syncthreads();
 }

@@ -548,7 +548,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void assign_refine_kernel(RefineB
     }
     if (job >= 0 && job != lut_job) {
       __syncthreads();
-      build_lut(b.job[job].tables_in, b.n, sh.lut, sh.ls);
+      build_lut<kFusedThreads>(b.job[job].tables_in, b.n, sh.lut, sh.ls);
       lut_job = job;
     }
     if (!acc_wave) {
