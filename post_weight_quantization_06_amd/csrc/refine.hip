@@ -134,14 +134,17 @@ __device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, Refin
   const float If[8] = {t.I0.x, t.I0.y, t.I0.z, t.I0.w, t.I1.x, t.I1.y, t.I1.z, t.I1.w};
   double Id[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) Id[k] = t.active ? (double)If[k] : 0.0;
+  for (int k = 0; k < 8; ++k) Id[k] = (double)If[k];
   char* const lds = reinterpret_cast<char*>(&sh.bins[0][0][0]) + tid * sizeof(double);
-  // the scales of all rows first: eight independent lane reductions (an inactive lane reads a
-  // group of its own matrix, so its scale is finite and its zero importance drops its terms)
+  // the scales of all rows first: eight independent lane reductions. A lane past the last column
+  // reads a group of its own matrix and gets scale 0, so its terms are zero (whole scale groups are
+  // inactive together, so no active group sees the zero).
   float s[kRowsPerWave];
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i)
-    s[i] = __uint_as_float(block_max_u32_t<G8>(lane_absmax_bits(t.v[i]), g8) << 16);
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const float si = __uint_as_float(block_max_u32_t<G8>(lane_absmax_bits(t.v[i]), g8) << 16);
+    s[i] = t.active ? si : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     // rows past the end of the matrix are the same for the whole wave
@@ -211,11 +214,14 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
                         t.I[1].z, t.I[1].w, t.I[2].x, t.I[2].y, t.I[2].z, t.I[2].w,
                         t.I[3].x, t.I[3].y, t.I[3].z, t.I[3].w};
   char* const lds = reinterpret_cast<char*>(&sh.bins[0][0][0]) + tid * sizeof(double);
+  // a lane past the last column gets scale 0, so its terms are zero (see accumulate_task)
   float s[kWideRowsPerWave];
 #pragma unroll
-  for (int i = 0; i < kWideRowsPerWave; ++i)
-    s[i] = __uint_as_float(block_max_u32_t<G16>(lane_absmax16_bits(t.va[i], t.vb[i]), g16)
-                           << 16);
+  for (int i = 0; i < kWideRowsPerWave; ++i) {
+    const float si = __uint_as_float(
+        block_max_u32_t<G16>(lane_absmax16_bits(t.va[i], t.vb[i]), g16) << 16);
+    s[i] = t.active ? si : 0.0f;
+  }
 #pragma unroll
   for (int i = 0; i < kWideRowsPerWave; ++i) {
     if (t.r0 + (int64_t)kWavesPerBlock * i >= t.R) break;
@@ -236,7 +242,7 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
         const uint32_t word = k < 8 ? t.cw[i].x : t.cw[i].y;
         const uint32_t q = (word >> (4 * (k & 7))) & 15u;
         p[u] = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
-        const double Id = t.active ? (double)If[k] : 0.0;
+        const double Id = (double)If[k];
         num[u] = Id * (double)(s[i] * w[k]);       // s w is exact in fp32
         den[u] = Id * s2;
       }
