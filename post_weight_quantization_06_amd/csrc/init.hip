@@ -57,7 +57,7 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 
 __device__ __forceinline__ void flush_hist(const uint32_t* lds, unsigned long long* hist, int bins) {
-  for (int i = threadIdx.x; i < bins; i += kBlock)
+  for (int i = threadIdx.x; i < bins; i += (int)blockDim.x)
     if (lds[i]) atomicAdd(hist + i, (unsigned long long)lds[i]);
 }
 
@@ -116,49 +116,48 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __res
 // Passes 2-4: histogram of byte `pass` (0-based from the top) of keys whose higher bytes match an
 // active prefix. The active prefixes (at most 32, sorted) are found through a 256-slot table
 // indexed by the prefix's low byte; a slot holds one prefix, and a slot that would need more sends
-// its keys to a binary search of the sorted list.
-__global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __restrict__ keys, int64_t N,
+// its keys to a binary search of the sorted list. One workgroup of 1024 threads per CU: the fixed
+// work of a workgroup (clearing the rows in use, the slot table, flushing its histogram with
+// global atomics) is paid once per CU, and 64 KB of loads stay in flight per CU.
+constexpr int kPassThreads = 1024;
+constexpr int kSlots = 4096;
+__global__ __launch_bounds__(kPassThreads) void init_pass_kernel(const uint32_t* __restrict__ keys, int64_t N,
                                                            int pass, const InitState* state,
                                                            unsigned long long* hist) {
   __shared__ uint32_t h[kTargets * kDigits];
   __shared__ uint32_t act[kTargets];
-  // slot entry: (prefix, position in the list); position -1 = no prefix, -2 = several prefixes
-  // (those keys use a binary search of the sorted list)
-  __shared__ uint2 slot[kDigits];
+  // slot entry, indexed by the low 12 bits of a prefix: (prefix, position in the list); position
+  // -1 = no prefix, -2 = several prefixes (those keys use a binary search of the sorted list).
+  // With at most 32 prefixes in 4096 slots a shared slot is rare and holds 1/4096 of the keys.
+  __shared__ uint2 slot[kSlots];
+  __shared__ uint32_t cnt[kSlots];
   __shared__ uint32_t nact;
   const int tid = threadIdx.x;
-  for (int i = tid; i < kTargets * kDigits; i += kBlock) h[i] = 0;
   if (tid < kTargets) act[tid] = state->active[tid];
   if (tid == 0) nact = state->nactive;
+  for (int i = tid; i < kSlots; i += kPassThreads) {
+    slot[i] = make_uint2(0u, (uint32_t)-1);
+    cnt[i] = 0u;
+  }
   __syncthreads();
   const int na = (int)nact;
-  {
-    // thread = slot: the active prefixes whose low byte is this slot
-    int m = 0;
-    uint32_t pfx = 0;
-    int at = -1;
-    for (int t = 0; t < na; ++t) {
-      if ((act[t] & 255u) != (uint32_t)tid) continue;
-      if (m == 0) {
-        pfx = act[t];
-        at = t;
-      } else {
-        at = -2;
-      }
-      ++m;
-    }
-    slot[tid] = make_uint2(pfx, (uint32_t)at);
+  for (int i = tid; i < na * kDigits; i += kPassThreads) h[i] = 0;   // the rows in use
+  if (tid < na) atomicAdd(&cnt[act[tid] & (kSlots - 1)], 1u);
+  __syncthreads();
+  if (tid < na) {
+    const uint32_t sl = act[tid] & (kSlots - 1);
+    slot[sl] = cnt[sl] == 1u ? make_uint2(act[tid], (uint32_t)tid) : make_uint2(0u, (uint32_t)-2);
   }
   __syncthreads();
   const int pshift = 32 - 8 * pass;       // prefix = key >> pshift
   const int dshift = 24 - 8 * pass;       // digit = (key >> dshift) & 255
   const int64_t n4 = N / 4;
   const uint4* k4 = reinterpret_cast<const uint4*>(keys);
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  const int64_t stride = (int64_t)gridDim.x * kPassThreads;
   // four 16-byte loads in flight per thread: unconditional at clamped indices, the out-of-range
   // ones then ignored
   constexpr int kUnroll = 4;
-  for (int64_t i0 = (int64_t)blockIdx.x * kBlock + tid; i0 < n4; i0 += kUnroll * stride) {
+  for (int64_t i0 = (int64_t)blockIdx.x * kPassThreads + tid; i0 < n4; i0 += kUnroll * stride) {
     uint4 qs[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -173,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __res
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t pre = kk[e] >> pshift;
-      const uint2 en = slot[pre & 255u];
+      const uint2 en = slot[pre & (kSlots - 1)];
       const int i0 = (int)en.y;
       int hit = (i0 >= 0 && en.x == pre) ? i0 : -1;
       if (i0 == -2) {
@@ -192,15 +191,18 @@ __global__ __launch_bounds__(kBlock) void init_pass_kernel(const uint32_t* __res
   flush_hist(h, hist, na * kDigits);
 }
 
-// One workgroup: move every target one byte down, rebuild the active prefix list, clear the
-// histogram; after the last pass write the tables. The histogram rows are first copied to LDS with
-// all threads (one coalesced read each) so that each target walks its row there.
-__global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N, int n,
-                                                             InitState* state,
-                                                             unsigned long long* hist,
-                                                             float* tables) {
+// One workgroup of 1024 threads (a target or two per wave): move every target one byte down,
+// rebuild the active prefix list, clear the histogram rows used; after the last pass write the
+// tables. The rows in use are first copied to LDS (one coalesced read per thread and row) so that
+// each target walks its row there.
+constexpr int kSelectThreads = 1024;
+__global__ __launch_bounds__(kSelectThreads) void init_select_kernel(int pass, int64_t N, int n,
+                                                                     InitState* state,
+                                                                     unsigned long long* hist,
+                                                                     float* tables) {
   const int tid = threadIdx.x;
   const int nt = 2 * n;
+  constexpr int kWaves = kSelectThreads / kWave;
   __shared__ uint32_t newp[kTargets];
   __shared__ unsigned long long hl[kTargets * kDigits];
   __shared__ uint32_t first[kTargets];
@@ -229,28 +231,38 @@ __global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N
   }
   __syncthreads();
   const int rows = rows_s;
+  // the rows in use and the (zero) row after them, read by a target without a row of its own,
+  // which the construction of the active list rules out
+  const int copy = rows < kTargets ? rows + 1 : kTargets;
   {
-    // the whole histogram region (always allocated) in one round of loads: a thread issues all of
-    // its 32 loads before it stores any
-    unsigned long long v[kTargets];
+    // thread t reads digit t & 255 of rows t / 256, t / 256 + 4, ...: all its loads before any
+    // store
+    constexpr int kPer = kTargets * kDigits / kSelectThreads;
+    unsigned long long v[kPer];
 #pragma unroll
-    for (int r = 0; r < kTargets; ++r) v[r] = hist[r * kDigits + tid];
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kSelectThreads;
+      v[k] = i < copy * kDigits ? hist[i] : 0ull;
+    }
 #pragma unroll
-    for (int r = 0; r < kTargets; ++r) hl[r * kDigits + tid] = v[r];
+    for (int k = 0; k < kPer; ++k) {
+      const int i = tid + k * kSelectThreads;
+      if (i < copy * kDigits) hl[i] = v[k];
+    }
   }
   __syncthreads();
   {
-    // wave w resolves targets w, w + 4, ...: lane l holds the count of digits 4l .. 4l + 3 of the
+    // wave w resolves targets w and w + 16: lane l holds the count of digits 4l .. 4l + 3 of the
     // target's row, an inclusive scan over the wave finds the lane whose digits hold the rank,
     // and that lane walks its four digits
     const int lane = tid & (kWave - 1), wave = tid / kWave;
-    for (int t = wave; t < nt; t += kWavesPerBlock) {
+    for (int t = wave; t < nt; t += kWaves) {
       const uint32_t pre = pre_s[t];
       int slot = 0;
       if (pass > 0) {
         // the row of this target's prefix: one compare per lane, first match
         const unsigned long long m = __ballot(lane < rows && act_s[lane & (kTargets - 1)] == pre);
-        slot = m ? __builtin_ctzll(m) : rows;
+        slot = m ? __builtin_ctzll(m) : copy - 1;
       }
       const uint64_t rank = rank_s[t];
       const unsigned long long* row = hl + slot * kDigits + 4 * lane;
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(kBlock) void init_select_kernel(int pass, int64_t N
     }
   }
   __syncthreads();
-  for (int i = tid; i < kTargets * kDigits; i += kBlock) hist[i] = 0ull;
+  for (int i = tid; i < rows * kDigits; i += kSelectThreads) hist[i] = 0ull;
   if (tid < nt) {
     state->prefix[tid] = newp[tid];
     // first occurrence of this prefix among the targets
@@ -318,19 +330,19 @@ hipError_t launch_init(const uint16_t* W, int64_t R, int64_t C, int g, int n, fl
                      l.hist);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kBlock), 0, stream, 0, N, n, l.state,
+  hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, 0, N, n, l.state,
                      l.hist, tables);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t n4 = N / 4;
-  int64_t grid = (n4 + kBlock - 1) / kBlock;
-  const int64_t cap = (int64_t)device_cu_count() * 4;
+  int64_t grid = (n4 + kPassThreads - 1) / kPassThreads;
+  const int64_t cap = (int64_t)device_cu_count();
   if (grid > cap) grid = cap;
   if (grid < 1) grid = 1;
   for (int pass = 1; pass < 4; ++pass) {
-    hipLaunchKernelGGL(init_pass_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, l.keys, N,
-                       pass, l.state, l.hist);
+    hipLaunchKernelGGL(init_pass_kernel, dim3((unsigned)grid), dim3(kPassThreads), 0, stream, l.keys,
+                       N, pass, l.state, l.hist);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kBlock), 0, stream, pass, N, n, l.state,
+    hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, pass, N, n, l.state,
                        l.hist, tables);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
