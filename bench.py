@@ -186,13 +186,20 @@ def main():
         e.record(stream)
         return e
 
+    # init reads only W and importance only X, so init runs on a second stream (default priority,
+    # like every stream here) beside importance; the loop waits for both
+    side = torch.cuda.Stream(device=dev)
+
     def step(record):
         marks = {"a": [], "r": []}
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i, W in enumerate(Ws):
+                L.aaac_init_quantiles(W, g, n, tabs[i], ws_init)
         for xid, K in streams:
             acc[xid].zero_()
             L.aaac_importance(Xs[xid], acc[xid], Iv[xid], ws_imp[xid])
-        for i, W in enumerate(Ws):
-            L.aaac_init_quantiles(W, g, n, tabs[i], ws_init)
+        stream.wait_stream(side)
         loop0 = ev()
         for it in range(iters):
             flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
