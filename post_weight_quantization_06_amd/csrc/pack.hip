@@ -9,28 +9,41 @@
 
 namespace aaac {
 
+// The scale word of every scale group: lane mapping of the 8-weight assign (a lane holds 8
+// consecutive weights of a row, a group spans g / 8 lanes). The rows of a task are all loaded first
+// (unconditional loads at clamped in-bounds addresses), so a wave keeps eight rows in flight.
 __global__ __launch_bounds__(kBlock) void pack_scales_kernel(const uint16_t* __restrict__ W,
                                                              MatrixGeom geom, int g, int S,
                                                              const uint8_t* __restrict__ sel,
                                                              uint16_t* __restrict__ scales) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = g / kPerLane;
+  const int log2g = 31 - __builtin_clz((unsigned)g), log2S = 31 - __builtin_clz((unsigned)S);
+  const int64_t R = geom.R, C = geom.C;
   for (int64_t task = blockIdx.x; task < geom.ntasks; task += gridDim.x) {
     const int64_t rb = task / geom.nslab;
     const int slab = (int)(task - rb * geom.nslab);
     const int c0 = slab * kSlab + lane * kPerLane;
-    const bool active = c0 < geom.C;
+    const bool active = c0 < C;
+    const int cl = active ? c0 : 0;
+    const int64_t r0 = rb * kRowsPerTask + wave;
+    uint4 v[kRowsPerWave];
+#pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-      const int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
-      if (r >= geom.R) break;
-      const int64_t base = r * (int64_t)geom.C + c0;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (active) v = *reinterpret_cast<const uint4*>(W + base);
-      const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
+      int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+      r = r < R ? r : R - 1;
+      v[i] = *reinterpret_cast<const uint4*>(W + r * C + cl);
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
+      if (r >= R) break;                              // the same for the whole wave
+      const uint32_t amax = block_max_u32(lane_absmax_bits(v[i]), g8);
       if (active && ((c0 >> 3) & (g8 - 1)) == 0) {
+        const int64_t base = r * C + c0;
         uint32_t word = amax;
-        if (S == g) word |= (sel[base / S] ? 1u : 0u) << 15;
-        scales[base / g] = (uint16_t)word;
+        if (S == g) word |= (sel[base >> log2S] ? 1u : 0u) << 15;
+        scales[base >> log2g] = (uint16_t)word;
       }
     }
   }
@@ -85,6 +98,7 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
   return bits;
 }
 
+// A thread dequantizes 8 weights (one code word) per step, four steps with their loads in flight.
 __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint32_t* __restrict__ codes,
                                                          const uint16_t* __restrict__ scales,
                                                          const uint8_t* __restrict__ bitmap,
@@ -95,33 +109,45 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint32_t* __restr
   if (threadIdx.x < 2 * n)
     tab[threadIdx.x / n][threadIdx.x % n] = __uint_as_float((uint32_t)tables_bf16[threadIdx.x] << 16);
   __syncthreads();
+  const int log2g = 31 - __builtin_clz((unsigned)g), log2S = 31 - __builtin_clz((unsigned)S);
   const int64_t nvec = R * C / 8;
-  for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < nvec;
-       i += (int64_t)gridDim.x * kBlock) {
-    const int64_t base = i * 8;
-    const uint32_t cw = codes[i];
-    const uint32_t word = scales[base / g];
-    uint32_t sg;
-    if (bitmap == nullptr) {
-      sg = word >> 15;
-    } else {
-      const int64_t h = base / S;
-      sg = (bitmap[h >> 3] >> (h & 7)) & 1u;
-    }
-    const float s = __uint_as_float((word & 0x7fffu) << 16);
-    uint32_t o[8];
+  const int64_t stride = (int64_t)gridDim.x * kBlock;
+  constexpr int kSteps = 4;
+  for (int64_t i0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; i0 < nvec; i0 += kSteps * stride) {
+    uint32_t cw[kSteps], word[kSteps], sg[kSteps];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const uint32_t q = (cw >> (4 * k)) & 15u;
-      const float t = tab[sg][q < (uint32_t)n ? q : 0];
-      const float p = s * t;
-      // exact in fp32 unless the product is a nonzero subnormal
-      o[k] = (s == 0.0f || t == 0.0f || fabsf(p) >= 0x1p-126f)
-                 ? f32_to_bf16_rne(p)
-                 : f64_to_bf16_bits((double)s * (double)t);
+    for (int u = 0; u < kSteps; ++u) {
+      int64_t i = i0 + u * stride;
+      i = i < nvec ? i : nvec - 1;                    // in bounds; the result is not stored
+      const int64_t base = i * 8;
+      cw[u] = codes[i];
+      word[u] = scales[base >> log2g];
+      if (bitmap == nullptr) {
+        sg[u] = word[u] >> 15;
+      } else {
+        const int64_t h = base >> log2S;
+        sg[u] = (bitmap[h >> 3] >> (h & 7)) & 1u;
+      }
     }
-    out[i] = make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
-                        o[6] | (o[7] << 16));
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i >= nvec) break;
+      const float s = __uint_as_float((word[u] & 0x7fffu) << 16);
+      uint32_t o[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t q = (cw[u] >> (4 * k)) & 15u;
+        const float t = tab[sg[u]][q < (uint32_t)n ? q : 0];
+        const float p = s * t;
+        // exact in fp32 unless the product is a nonzero subnormal
+        o[k] = (s == 0.0f || t == 0.0f || fabsf(p) >= 0x1p-126f)
+                   ? f32_to_bf16_rne(p)
+                   : f64_to_bf16_bits((double)s * (double)t);
+      }
+      out[i] = make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
+                          o[6] | (o[7] << 16));
+    }
   }
 }
 
