@@ -129,6 +129,8 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--one-stream", action="store_true",
+                    help="run init after importance on one stream (for per-kernel profiles)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this implementation has no multi-GPU path "
@@ -188,7 +190,7 @@ def main():
 
     # init reads only W and importance only X, so init runs on a second stream (default priority,
     # like every stream here) beside importance; the loop waits for both
-    side = torch.cuda.Stream(device=dev)
+    side = stream if args.one_stream else torch.cuda.Stream(device=dev)
 
     def step(record):
         marks = {"a": [], "r": []}

@@ -4,7 +4,7 @@ Turns the raw rocprofv3 output of the runs below (one counter group per run, all
 one folder RAW) into the short Markdown summaries kept beside the traffic JSON:
 
     rocprofv3 --kernel-trace --stats --output-format csv -d RAW/prof_c2 -o run -- \\
-        python -u bench.py --steps 2 --warmup 1 --no-cpu
+        python -u bench.py --steps 2 --warmup 1 --no-cpu --one-stream
     rocprofv3 --pmc FETCH_SIZE ... -d RAW/pmc_fetch ...      (the same bench command, 1 step)
     rocprofv3 --pmc WRITE_SIZE ... -d RAW/pmc_write ...
     rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU ... -d RAW/pmc_sq ...
@@ -36,7 +36,7 @@ X_BYTES = 4 * 262144 * (3 * 4096 + 14336)            # the four activation strea
 PEAK = 8e12
 
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {raw}/prof_c2 -o run "
-             "-- python -u bench.py --steps 2 --warmup 1 --no-cpu")
+             "-- python -u bench.py --steps 2 --warmup 1 --no-cpu --one-stream")
 SQ1 = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
        "SQ_WAIT_INST_ANY SQ_INSTS_VMEM_RD")
 SQ2 = ("SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
@@ -47,7 +47,7 @@ WRITTEN_BY = ("Summary written by `python -m post_weight_quantization_06_amd.pro
 
 def _pmc_cmd(counters, out, raw):
     return ("rocprofv3 --pmc %s --output-format csv -d %s/%s -o run -- python -u bench.py "
-            "--steps 1 --warmup 1 --no-cpu" % (counters, raw, out))
+            "--steps 1 --warmup 1 --no-cpu --one-stream" % (counters, raw, out))
 
 
 def _rows(path):
