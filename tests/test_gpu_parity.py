@@ -154,6 +154,26 @@ def test_init_quantiles_zero_groups_and_ties():
     assert np.array_equal(_np(tables), np.concatenate([T0, T1]).astype(np.float32))
 
 
+def test_init_quantiles_prefix_slot_collisions():
+    """Targets at +-0.75 and +-0.75 * 2^-32: their key prefixes differ (exponents 32 apart) but
+    share the low 12 bits the prefix table is indexed by, so the search for shared slots runs in
+    every pass."""
+    _say("init prefix slot collisions")
+    R, C, g, n = 64, 1024, 128, 16
+    group = np.concatenate([[1.0], np.full(31, 0.75), np.full(32, 0.75 * 2.0 ** -32),
+                            np.full(32, -0.75 * 2.0 ** -32), np.full(32, -0.75)])
+    rng = np.random.default_rng(11)
+    rows = [np.concatenate([rng.permutation(group) for _ in range(C // g)]) for _ in range(R)]
+    W = torch.from_numpy(np.stack(rows).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    tables = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(W, g, n, tables)
+    torch.cuda.synchronize()
+    T0, T1 = ref.init_tables(par.to_np64(W), g, n)
+    want = np.concatenate([T0, T1]).astype(np.float32)
+    assert set(np.abs(want).tolist()) >= {0.75, 0.75 * 2.0 ** -32}
+    assert np.array_equal(_np(tables), want), (_np(tables), want)
+
+
 # ------------------------------------------------------------------ assign
 
 ASSIGN_CASES = [
