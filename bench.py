@@ -169,8 +169,7 @@ def main():
     Iv = {xid: torch.empty(K, dtype=torch.float32, device=dev) for xid, K in streams}
     ws_imp = {xid: L.workspace(L.workspace_bytes(L.OP_IMPORTANCE, cfg.tokens, K), dev)
               for xid, K in streams}
-    ws_init = L.workspace(max(L.workspace_bytes(L.OP_INIT, R, C, g, S, n)
-                              for R, C in zip(Rs, Cs)), dev)
+    ws_init = L.workspace(L.batch_workspace_bytes(L.OP_INIT, Rs, Cs, g, 8, n), dev)
     ws_r = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), dev)
     Is = [Iv[m.x_id] for m in mats]
     tabs = [torch.empty(2 * n, dtype=torch.float32, device=dev) for _ in mats]
@@ -196,8 +195,7 @@ def main():
         marks = {"a": [], "r": []}
         side.wait_stream(stream)
         with torch.cuda.stream(side):
-            for i, W in enumerate(Ws):
-                L.aaac_init_quantiles(W, g, n, tabs[i], ws_init)
+            L.aaac_init_quantiles_batch(Ws, g, n, tabs, ws_init)
         for xid, K in streams:
             acc[xid].zero_()
             L.aaac_importance(Xs[xid], acc[xid], Iv[xid], ws_imp[xid])

@@ -215,6 +215,17 @@ aaac_status aaac_awq_prescale(const uint16_t* W, int64_t R, int64_t C, const flo
 size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int64_t* C, int g,
                                   int S, int n);
 
+/*
+ * Init for up to AAAC_MAX_BATCH matrices sharing g and n, in one set of launches (8 in all, not 8
+ * per matrix): tables[i] as aaac_init_quantiles gives for matrix i, bit for bit. The workspace
+ * holds aaac_batch_workspace_bytes(AAAC_OP_INIT, count, R, C, g, 8, n) bytes (fixed headers of
+ * histograms, then the keys of every matrix), zero-filled before its first use; every call leaves
+ * the headers zero again, so one workspace serves any later batch that fits in it.
+ */
+aaac_status aaac_init_quantiles_batch(int count, const uint16_t* const* W, const int64_t* R,
+                                      const int64_t* C, int g, int n, float* const* tables,
+                                      void* ws, size_t ws_bytes, void* stream);
+
 aaac_status aaac_assign_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,
                               const float* const* tables, uint8_t* const* codes,

@@ -31,7 +31,7 @@ EXPORTED = (
     "aaac_status_string", "aaac_last_error", "aaac_workspace_bytes", "aaac_importance",
     "aaac_init_quantiles", "aaac_assign", "aaac_refine", "aaac_pack", "aaac_dequant",
     "aaac_batch_workspace_bytes", "aaac_assign_batch", "aaac_refine_batch", "aaac_awq_prescale",
-    "aaac_gemv", "aaac_gemv_batch", "aaac_assign_refine_batch",
+    "aaac_gemv", "aaac_gemv_batch", "aaac_assign_refine_batch", "aaac_init_quantiles_batch",
 )
 
 
@@ -77,6 +77,8 @@ def load(path: str = LIB_PATH):
                               c_vp, c_vp]),
         "aaac_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
                                  c_vp]),
+        "aaac_init_quantiles_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
+                                              P(c_vp), c_vp, c_size, c_vp]),
         "aaac_assign_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
                                       P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp]),
         "aaac_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
@@ -258,6 +260,25 @@ def aaac_dequant(codes: torch.Tensor, scales: torch.Tensor, bitmap: Optional[tor
 
 def _arr(ctype, values):
     return (ctype * len(values))(*values)
+
+
+def aaac_init_quantiles_batch(Ws: Sequence[torch.Tensor], g: int, n: int,
+                              tables: Sequence[torch.Tensor], ws: Optional[torch.Tensor] = None,
+                              stream=None):
+    """Init tables of up to MAX_BATCH matrices in one set of launches (see aaac.h)."""
+    lib = load()
+    k = len(Ws)
+    Rs = [W.shape[0] for W in Ws]
+    Cs = [W.shape[1] for W in Ws]
+    for i in range(k):
+        _need(Ws[i], "W[%d]" % i, torch.bfloat16)
+        _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
+    if ws is None:
+        ws = workspace(batch_workspace_bytes(OP_INIT, Rs, Cs, g, 8, n), Ws[0].device)
+    st = lib.aaac_init_quantiles_batch(
+        k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, n,
+        _arr(c_vp, [t.data_ptr() for t in tables]), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "aaac_init_quantiles_batch")
 
 
 def aaac_assign_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,

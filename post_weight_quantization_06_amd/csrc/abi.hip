@@ -265,6 +265,26 @@ aaac_status do_gemv(int count, const uint8_t* const* codes, const uint16_t* cons
   return hip_status(launch_gemv(b, static_cast<hipStream_t>(stream)), who);
 }
 
+aaac_status do_init(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                    int g, int n, float* const* tables, void* ws, size_t ws_bytes, void* stream,
+                    const char* who) {
+  if (count < 1 || count > AAAC_MAX_BATCH)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: count=%d (need 1..%d)", who, count, AAAC_MAX_BATCH);
+  if (!W || !R || !C || !tables) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    aaac_status st = check_shape(R[i], C[i], g, 8, n, false, who);
+    if (st != AAAC_OK) return st;
+    if (!W[i] || !aligned(W[i], 16) || !tables[i] || !aligned(tables[i], 4))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: W or tables null or misaligned", who, i);
+  }
+  const size_t need = init_workspace_bytes(count, R, C);
+  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
+  if (ws_bytes < need)
+    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
+  return hip_status(launch_init(count, W, R, C, g, n, tables, ws, static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -291,7 +311,7 @@ size_t aaac_workspace_bytes(int op, int64_t R, int64_t C, int g, int S, int n) {
     }
     case AAAC_OP_INIT:
       if (check_shape(R, C, g, 8, n, false, "aaac_workspace_bytes") != AAAC_OK) return 0;
-      return init_workspace_bytes(R, C, n);
+      return init_workspace_bytes(1, &R, &C);
     case AAAC_OP_ASSIGN:
       return 0;
     case AAAC_OP_REFINE:
@@ -305,9 +325,12 @@ size_t aaac_workspace_bytes(int op, int64_t R, int64_t C, int g, int S, int n) {
 size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int64_t* C, int g,
                                   int S, int n) {
   if (count < 1 || count > AAAC_MAX_BATCH || !R || !C) return 0;
+  const bool init = op == AAAC_OP_INIT;
   for (int i = 0; i < count; ++i)
-    if (check_shape(R[i], C[i], g, S, n, true, "aaac_batch_workspace_bytes") != AAAC_OK) return 0;
+    if (check_shape(R[i], C[i], g, init ? 8 : S, n, !init, "aaac_batch_workspace_bytes") != AAAC_OK)
+      return 0;
   if (op == AAAC_OP_REFINE) return refine_ws_bytes(count);
+  if (init) return init_workspace_bytes(count, R, C);
   return 0;
 }
 
@@ -333,16 +356,13 @@ aaac_status aaac_importance(const float* X, int64_t T, int64_t K, int64_t ldx, d
 
 aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, int n,
                                 float* tables, void* ws, size_t ws_bytes, void* stream) {
-  const char* who = "aaac_init_quantiles";
-  aaac_status st = check_shape(R, C, g, 8, n, false, who);
-  if (st != AAAC_OK) return st;
-  if (!W || !aligned(W, 16) || !tables || !aligned(tables, 4))
-    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
-  const size_t need = init_workspace_bytes(R, C, n);
-  if (!ws || !aligned(ws, 256)) return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned", who);
-  if (ws_bytes < need)
-    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes, need);
-  return hip_status(launch_init(W, R, C, g, n, tables, ws, static_cast<hipStream_t>(stream)), who);
+  return do_init(1, &W, &R, &C, g, n, &tables, ws, ws_bytes, stream, "aaac_init_quantiles");
+}
+
+aaac_status aaac_init_quantiles_batch(int count, const uint16_t* const* W, const int64_t* R,
+                                      const int64_t* C, int g, int n, float* const* tables,
+                                      void* ws, size_t ws_bytes, void* stream) {
+  return do_init(count, W, R, C, g, n, tables, ws, ws_bytes, stream, "aaac_init_quantiles_batch");
 }
 
 aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,

@@ -255,9 +255,9 @@ hipError_t launch_importance(const float* X, int64_t T, int64_t K, int64_t ldx, 
                              float* I_out, double* partials, int nsplit, hipStream_t stream);
 int importance_splits(int64_t T, int64_t K);
 
-size_t init_workspace_bytes(int64_t R, int64_t C, int n);
-hipError_t launch_init(const uint16_t* W, int64_t R, int64_t C, int g, int n, float* tables,
-                       void* ws, hipStream_t stream);
+size_t init_workspace_bytes(int count, const int64_t* R, const int64_t* C);
+hipError_t launch_init(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                       int g, int n, float* const* tables, void* ws, hipStream_t stream);
 
 hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                        const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,

@@ -1,16 +1,17 @@
 // Table initialization (AAAC summary §2 mechanism 4): equally spaced quantiles of the normalized
-// weights, T1 half a step above T0, found by an exact radix select.
+// weights, T1 half a step above T0, found by an exact radix select, for up to kMaxJobs matrices in
+// one set of launches.
 //
 // u = fl32(w / s) (IEEE division; u = +0 when s = 0) is mapped to an order-preserving 32-bit key
 // (flip all bits of negatives, set the sign bit of non-negatives). The 2n target ranks are resolved
 // one byte at a time, most significant first: pass 1 histograms the top byte of every key; after
-// each pass a single workgroup walks the histogram of every target's current prefix to the byte
-// that holds its residual rank; passes 2-4 histogram the next byte of the keys whose prefix is one
-// of the (at most 2n) active prefixes. Integer counts make every step exact and order-free.
+// each pass one workgroup per matrix walks the histogram of every target's current prefix to the
+// byte that holds its residual rank; passes 2-4 histogram the next byte of the keys whose prefix is
+// one of the (at most 2n) active prefixes. Integer counts make every step exact and order-free.
 //
-// Workspace: hist u64 [32][256] | state (see InitState) | keys u32 [N]. The histogram and the state
-// sit at fixed offsets, so a workspace reused for a matrix of another size still starts from the
-// zero histogram the previous call left behind.
+// Workspace: kMaxJobs headers of (hist u64 [32][256] | state), then the keys u32 [N_i] of every
+// matrix. The headers sit at fixed offsets, so a workspace reused for other matrices (or another
+// count of them) still starts from the zero histograms the previous call left behind.
 #include "common.h"
 
 namespace aaac {
@@ -28,24 +29,29 @@ struct InitState {
   uint32_t pad[3];
 };
 
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+constexpr size_t kHistBytes = align256(sizeof(unsigned long long) * kTargets * kDigits);
+constexpr size_t kHeaderBytes = kHistBytes + align256(sizeof(InitState));
+constexpr size_t kHeadersBytes = kMaxJobs * kHeaderBytes;
 
-struct InitLayout {
-  uint32_t* keys;
-  unsigned long long* hist;
+// One matrix of an init batch.
+struct InitJob {
+  const uint16_t* W;
+  int64_t R, C, N;
+  int64_t nslab;                 // 512-column slabs per row
+  uint32_t* keys;                // [N]
+  unsigned long long* hist;      // [32][256], zero between calls
   InitState* state;
+  float* tables;                 // [2][n]
+  int64_t task_begin;            // first keys task (kRowsPerTask rows of one slab)
+  int64_t chunk_begin;           // first pass chunk (kChunkVecs 16-byte vectors of keys)
 };
 
-InitLayout layout(void* ws) {
-  char* p = static_cast<char*>(ws);
-  InitLayout l;
-  l.hist = reinterpret_cast<unsigned long long*>(p);
-  p += align256(sizeof(unsigned long long) * kTargets * kDigits);
-  l.state = reinterpret_cast<InitState*>(p);
-  p += align256(sizeof(InitState));
-  l.keys = reinterpret_cast<uint32_t*>(p);
-  return l;
-}
+struct InitBatch {
+  InitJob job[kMaxJobs];
+  int njobs, g, n;
+  int64_t total_tasks, total_chunks;
+};
 
 __device__ __forceinline__ uint32_t order_key(float u) {
   const uint32_t b = __float_as_uint(u);
@@ -63,11 +69,10 @@ __device__ __forceinline__ void flush_hist(const uint32_t* lds, unsigned long lo
 
 }  // namespace
 
-// Pass 1: keys of all weights (same lane mapping as assign) and the histogram of their top byte.
-__global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __restrict__ W,
-                                                           MatrixGeom geom, int g,
-                                                           uint32_t* __restrict__ keys,
-                                                           unsigned long long* hist) {
+// Keys of all weights (same lane mapping as assign's 8-weight mapping) and the histogram of their
+// top byte. A workgroup walks a contiguous range of tasks; its LDS histogram goes to a matrix's
+// histogram when the workgroup leaves that matrix.
+__global__ __launch_bounds__(kBlock) void init_keys_kernel(InitBatch b) {
   // eight copies of the histogram, by lane & 7: most keys share a few top bytes, and adds to one
   // address from many lanes of an instruction are serialized
   constexpr int kCopies = 8;
@@ -76,18 +81,39 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __res
 #pragma unroll
   for (int c = 0; c < kCopies; ++c) h[c][tid] = 0;
   __syncthreads();
-  const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = g / kPerLane;
-  for (int64_t task = blockIdx.x; task < geom.ntasks; task += gridDim.x) {
-    const int64_t rb = task / geom.nslab;
-    const int slab = (int)(task - rb * geom.nslab);
+  const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = b.g / kPerLane;
+  const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
+  int cur = -1;
+  auto flush = [&](int j) {
+    __syncthreads();
+    uint32_t tot = 0;
+#pragma unroll
+    for (int c = 0; c < kCopies; ++c) {
+      tot += h[c][tid];
+      h[c][tid] = 0;
+    }
+    if (tot) atomicAdd(b.job[j].hist + tid, (unsigned long long)tot);
+    __syncthreads();
+  };
+  for (int64_t task = task_lo(blockIdx.x, b.total_tasks, gridDim.x); task < t_end; ++task) {
+    int j = cur < 0 ? 0 : cur;
+    while (j + 1 < b.njobs && task >= b.job[j + 1].task_begin) ++j;
+    if (j != cur) {
+      if (cur >= 0) flush(cur);
+      cur = j;
+    }
+    const InitJob& jb = b.job[j];
+    const int64_t local = task - jb.task_begin;
+    const int64_t rb = local / jb.nslab;
+    const int slab = (int)(local - rb * jb.nslab);
     const int c0 = slab * kSlab + lane * kPerLane;
-    const bool active = c0 < geom.C;
+    const bool active = c0 < jb.C;
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
-      if (r >= geom.R) break;
-      const int64_t base = r * (int64_t)geom.C + c0;
+      if (r >= jb.R) break;
+      const int64_t base = r * jb.C + c0;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (active) v = *reinterpret_cast<const uint4*>(W + base);
+      if (active) v = *reinterpret_cast<const uint4*>(jb.W + base);
       const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
       if (!active) continue;
       const float s = __uint_as_float(amax << 16);
@@ -101,105 +127,121 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(const uint16_t* __res
         k[e] = order_key(u);
         atomicAdd(&h[tid & (kCopies - 1)][k[e] >> 24], 1u);
       }
-      uint4* dst = reinterpret_cast<uint4*>(keys + base);
+      uint4* dst = reinterpret_cast<uint4*>(jb.keys + base);
       dst[0] = make_uint4(k[0], k[1], k[2], k[3]);
       dst[1] = make_uint4(k[4], k[5], k[6], k[7]);
     }
   }
-  __syncthreads();
-  uint32_t tot = 0;
-#pragma unroll
-  for (int c = 0; c < kCopies; ++c) tot += h[c][tid];
-  if (tot) atomicAdd(hist + tid, (unsigned long long)tot);
+  if (cur >= 0) flush(cur);
 }
 
 // Passes 2-4: histogram of byte `pass` (0-based from the top) of keys whose higher bytes match an
-// active prefix. The active prefixes (at most 32, sorted) are found through a 256-slot table
-// indexed by the prefix's low byte; a slot holds one prefix, and a slot that would need more sends
-// its keys to a binary search of the sorted list. One workgroup of 1024 threads per CU: the fixed
-// work of a workgroup (clearing the rows in use, the slot table, flushing its histogram with
-// global atomics) is paid once per CU, and 64 KB of loads stay in flight per CU.
+// active prefix of their matrix. The active prefixes (at most 32, sorted) are found through a
+// 4096-slot table on their low 12 bits; a slot holds one prefix, and a slot that would need more
+// sends its keys to a binary search of the sorted list (with 32 prefixes in 4096 slots a shared
+// slot is rare and holds 1/4096 of the keys). One workgroup of 1024 threads per CU walks a
+// contiguous range of chunks: its fixed work (clearing the histogram rows in use, the prefix
+// table, flushing its histogram with global atomics) is paid once per CU and matrix, and each
+// thread keeps four 16-byte loads in flight.
 constexpr int kPassThreads = 1024;
 constexpr int kSlots = 4096;
-__global__ __launch_bounds__(kPassThreads) void init_pass_kernel(const uint32_t* __restrict__ keys, int64_t N,
-                                                           int pass, const InitState* state,
-                                                           unsigned long long* hist) {
+constexpr int kPassUnroll = 4;
+constexpr int64_t kChunkVecs = (int64_t)kPassThreads * kPassUnroll;
+
+__global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, int pass) {
   __shared__ uint32_t h[kTargets * kDigits];
   __shared__ uint32_t act[kTargets];
-  // slot entry, indexed by the low 12 bits of a prefix: (prefix, position in the list); position
-  // -1 = no prefix, -2 = several prefixes (those keys use a binary search of the sorted list).
-  // With at most 32 prefixes in 4096 slots a shared slot is rare and holds 1/4096 of the keys.
+  // slot entry: (prefix, position in the list); position -1 = no prefix, -2 = several prefixes
   __shared__ uint2 slot[kSlots];
   __shared__ uint32_t cnt[kSlots];
   __shared__ uint32_t nact;
   const int tid = threadIdx.x;
-  if (tid < kTargets) act[tid] = state->active[tid];
-  if (tid == 0) nact = state->nactive;
-  for (int i = tid; i < kSlots; i += kPassThreads) {
-    slot[i] = make_uint2(0u, (uint32_t)-1);
-    cnt[i] = 0u;
-  }
-  __syncthreads();
-  const int na = (int)nact;
-  for (int i = tid; i < na * kDigits; i += kPassThreads) h[i] = 0;   // the rows in use
-  if (tid < na) atomicAdd(&cnt[act[tid] & (kSlots - 1)], 1u);
-  __syncthreads();
-  if (tid < na) {
-    const uint32_t sl = act[tid] & (kSlots - 1);
-    slot[sl] = cnt[sl] == 1u ? make_uint2(act[tid], (uint32_t)tid) : make_uint2(0u, (uint32_t)-2);
-  }
-  __syncthreads();
   const int pshift = 32 - 8 * pass;       // prefix = key >> pshift
   const int dshift = 24 - 8 * pass;       // digit = (key >> dshift) & 255
-  const int64_t n4 = N / 4;
-  const uint4* k4 = reinterpret_cast<const uint4*>(keys);
-  const int64_t stride = (int64_t)gridDim.x * kPassThreads;
-  // four 16-byte loads in flight per thread: unconditional at clamped indices, the out-of-range
-  // ones then ignored
-  constexpr int kUnroll = 4;
-  for (int64_t i0 = (int64_t)blockIdx.x * kPassThreads + tid; i0 < n4; i0 += kUnroll * stride) {
-    uint4 qs[kUnroll];
+  const int64_t c_end = task_lo(blockIdx.x + 1, b.total_chunks, gridDim.x);
+  int cur = -1;
+  int na = 0;
+  for (int64_t chunk = task_lo(blockIdx.x, b.total_chunks, gridDim.x); chunk < c_end; ++chunk) {
+    int j = cur < 0 ? 0 : cur;
+    while (j + 1 < b.njobs && chunk >= b.job[j + 1].chunk_begin) ++j;
+    if (j != cur) {
+      if (cur >= 0) {
+        __syncthreads();
+        flush_hist(h, b.job[cur].hist, na * kDigits);
+      }
+      // this matrix's active prefixes and their slots
+      __syncthreads();
+      if (tid < kTargets) act[tid] = b.job[j].state->active[tid];
+      if (tid == 0) nact = b.job[j].state->nactive;
+      for (int i = tid; i < kSlots; i += kPassThreads) {
+        slot[i] = make_uint2(0u, (uint32_t)-1);
+        cnt[i] = 0u;
+      }
+      __syncthreads();
+      na = (int)nact;
+      for (int i = tid; i < na * kDigits; i += kPassThreads) h[i] = 0;   // the rows in use
+      if (tid < na) atomicAdd(&cnt[act[tid] & (kSlots - 1)], 1u);
+      __syncthreads();
+      if (tid < na) {
+        const uint32_t sl = act[tid] & (kSlots - 1);
+        slot[sl] = cnt[sl] == 1u ? make_uint2(act[tid], (uint32_t)tid)
+                                 : make_uint2(0u, (uint32_t)-2);
+      }
+      __syncthreads();
+      cur = j;
+    }
+    const InitJob& jb = b.job[j];
+    const int64_t n4 = jb.N / 4;
+    const uint4* k4 = reinterpret_cast<const uint4*>(jb.keys);
+    const int64_t v0 = (chunk - jb.chunk_begin) * kChunkVecs + tid;
+    // four 16-byte loads in flight per thread: unconditional at clamped indices, the out-of-range
+    // ones then ignored
+    uint4 qs[kPassUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t i = i0 + u * stride;
+    for (int u = 0; u < kPassUnroll; ++u) {
+      const int64_t i = v0 + (int64_t)u * kPassThreads;
       qs[u] = k4[i < n4 ? i : n4 - 1];
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-    if (i0 + u * stride >= n4) break;
-    const uint4 q = qs[u];
-    const uint32_t kk[4] = {q.x, q.y, q.z, q.w};
+    for (int u = 0; u < kPassUnroll; ++u) {
+      if (v0 + (int64_t)u * kPassThreads >= n4) break;
+      const uint32_t kk[4] = {qs[u].x, qs[u].y, qs[u].z, qs[u].w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t pre = kk[e] >> pshift;
-      const uint2 en = slot[pre & (kSlots - 1)];
-      const int i0 = (int)en.y;
-      int hit = (i0 >= 0 && en.x == pre) ? i0 : -1;
-      if (i0 == -2) {
-        int lo = 0, hi = na;               // first active prefix >= pre
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (act[mid] < pre) lo = mid + 1; else hi = mid;
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t pre = kk[e] >> pshift;
+        const uint2 en = slot[pre & (kSlots - 1)];
+        const int i0 = (int)en.y;
+        int hit = (i0 >= 0 && en.x == pre) ? i0 : -1;
+        if (i0 == -2) {
+          int lo = 0, hi = na;               // first active prefix >= pre
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (act[mid] < pre) lo = mid + 1; else hi = mid;
+          }
+          if (lo < na && act[lo] == pre) hit = lo;
         }
-        if (lo < na && act[lo] == pre) hit = lo;
+        if (hit >= 0) atomicAdd(&h[hit * kDigits + ((kk[e] >> dshift) & 255u)], 1u);
       }
-      if (hit >= 0) atomicAdd(&h[hit * kDigits + ((kk[e] >> dshift) & 255u)], 1u);
-    }
     }
   }
-  __syncthreads();
-  flush_hist(h, hist, na * kDigits);
+  if (cur >= 0) {
+    __syncthreads();
+    flush_hist(h, b.job[cur].hist, na * kDigits);
+  }
 }
 
-// One workgroup of 1024 threads (a target or two per wave): move every target one byte down,
-// rebuild the active prefix list, clear the histogram rows used; after the last pass write the
-// tables. The rows in use are first copied to LDS (one coalesced read per thread and row) so that
-// each target walks its row there.
+// One workgroup of 1024 threads per matrix (a target or two per wave): move every target one byte
+// down, rebuild the active prefix list, clear the histogram rows used; after the last pass write
+// the tables. The rows in use are first copied to LDS (one coalesced read per thread and row) so
+// that each target walks its row there.
 constexpr int kSelectThreads = 1024;
-__global__ __launch_bounds__(kSelectThreads) void init_select_kernel(int pass, int64_t N, int n,
-                                                                     InitState* state,
-                                                                     unsigned long long* hist,
-                                                                     float* tables) {
+__global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b, int pass) {
+  const InitJob& jb = b.job[blockIdx.x];
+  const int64_t N = jb.N;
+  const int n = b.n;
+  InitState* const state = jb.state;
+  unsigned long long* const hist = jb.hist;
+  float* const tables = jb.tables;
   const int tid = threadIdx.x;
   const int nt = 2 * n;
   constexpr int kWaves = kSelectThreads / kWave;
@@ -313,37 +355,53 @@ __global__ __launch_bounds__(kSelectThreads) void init_select_kernel(int pass, i
   if (pass == 3 && tid < nt) tables[tid] = key_value(newp[tid]);
 }
 
-size_t init_workspace_bytes(int64_t R, int64_t C, int n) {
-  (void)n;
-  return align256((size_t)R * C * 4) + align256(sizeof(unsigned long long) * kTargets * kDigits) +
-         align256(sizeof(InitState));
+size_t init_workspace_bytes(int count, const int64_t* R, const int64_t* C) {
+  size_t bytes = kHeadersBytes;
+  for (int i = 0; i < count; ++i) bytes += align256((size_t)R[i] * (size_t)C[i] * 4);
+  return bytes;
 }
 
-hipError_t launch_init(const uint16_t* W, int64_t R, int64_t C, int g, int n, float* tables,
-                       void* ws, hipStream_t stream) {
-  const int64_t N = R * C;
-  InitLayout l = layout(ws);
-  const MatrixGeom geom = make_geom(R, C, 0);
-  const int64_t want = (int64_t)device_cu_count() * 4;
-  const int grid1 = (int)(geom.ntasks < want ? geom.ntasks : want);
-  hipLaunchKernelGGL(init_keys_kernel, dim3(grid1), dim3(kBlock), 0, stream, W, geom, g, l.keys,
-                     l.hist);
+hipError_t launch_init(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                       int g, int n, float* const* tables, void* ws, hipStream_t stream) {
+  InitBatch b{};
+  b.njobs = count;
+  b.g = g;
+  b.n = n;
+  char* const base = static_cast<char*>(ws);
+  char* keys = base + kHeadersBytes;
+  int64_t tb = 0, cb = 0;
+  for (int i = 0; i < count; ++i) {
+    InitJob& j = b.job[i];
+    const MatrixGeom geom = make_geom(R[i], C[i], tb);
+    j.W = W[i];
+    j.R = R[i];
+    j.C = C[i];
+    j.N = R[i] * C[i];
+    j.nslab = geom.nslab;
+    j.hist = reinterpret_cast<unsigned long long*>(base + (size_t)i * kHeaderBytes);
+    j.state = reinterpret_cast<InitState*>(base + (size_t)i * kHeaderBytes + kHistBytes);
+    j.keys = reinterpret_cast<uint32_t*>(keys);
+    keys += align256((size_t)j.N * 4);
+    j.tables = tables[i];
+    j.task_begin = tb;
+    tb += geom.ntasks;
+    j.chunk_begin = cb;
+    cb += (j.N / 4 + kChunkVecs - 1) / kChunkVecs;
+  }
+  b.total_tasks = tb;
+  b.total_chunks = cb;
+  const int64_t cus = device_cu_count();
+  const int grid1 = (int)(tb < cus * 4 ? tb : cus * 4);
+  hipLaunchKernelGGL(init_keys_kernel, dim3(grid1), dim3(kBlock), 0, stream, b);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, 0, N, n, l.state,
-                     l.hist, tables);
+  hipLaunchKernelGGL(init_select_kernel, dim3(count), dim3(kSelectThreads), 0, stream, b, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t n4 = N / 4;
-  int64_t grid = (n4 + kPassThreads - 1) / kPassThreads;
-  const int64_t cap = (int64_t)device_cu_count();
-  if (grid > cap) grid = cap;
-  if (grid < 1) grid = 1;
+  const int grid = (int)(cb < cus ? cb : cus);
   for (int pass = 1; pass < 4; ++pass) {
-    hipLaunchKernelGGL(init_pass_kernel, dim3((unsigned)grid), dim3(kPassThreads), 0, stream, l.keys,
-                       N, pass, l.state, l.hist);
+    hipLaunchKernelGGL(init_pass_kernel, dim3(grid), dim3(kPassThreads), 0, stream, b, pass);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(init_select_kernel, dim3(1), dim3(kSelectThreads), 0, stream, pass, N, n, l.state,
-                       l.hist, tables);
+    hipLaunchKernelGGL(init_select_kernel, dim3(count), dim3(kSelectThreads), 0, stream, b, pass);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

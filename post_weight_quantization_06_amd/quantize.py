@@ -99,9 +99,10 @@ def quantize_matrices(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], g:
     sels = [torch.empty(R * C // S, dtype=torch.uint8, device=dev) for R, C in zip(Rs, Cs)]
     if tables is None:
         tabs = [torch.empty(2 * n, dtype=torch.float32, device=dev) for _ in range(k)]
-        for i in range(k):
-            need = L.workspace_bytes(L.OP_INIT, Rs[i], Cs[i], g, S, n)
-            L.aaac_init_quantiles(Ws[i], g, n, tabs[i], wsp.get("init", need))
+        for b0, group in _batches(list(range(k))):
+            sl = slice(b0, b0 + len(group))
+            need = L.batch_workspace_bytes(L.OP_INIT, Rs[sl], Cs[sl], g, 8, n)
+            L.aaac_init_quantiles_batch(Ws[sl], g, n, tabs[sl], wsp.get("init", need))
     else:
         tabs = [t.reshape(-1).to(torch.float32).clone() for t in tables]
     for it in range(iters):

@@ -41,7 +41,7 @@ def lib():
 def test_header_declares_the_six_operations_and_the_batch_calls():
     names = declared_functions()
     for op in ("importance", "init_quantiles", "assign", "refine", "pack", "dequant",
-               "assign_batch", "refine_batch"):
+               "init_quantiles_batch", "assign_batch", "refine_batch"):
         assert "aaac_" + op in names
 
 
@@ -165,3 +165,26 @@ def test_assign_refine_batch_rejects_bad_arguments(lib):
     assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 4, FAKE, ctypes.c_size_t(need), None) == INVALID
     assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(16), None) == WS_SMALL
     assert f(1, P, R, C, 100, 100, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(need), None) == SHAPE
+
+
+def test_init_batch_workspace_and_arguments(lib):
+    R1 = (i64 * 1)(64)
+    C1 = (i64 * 1)(1024)
+    R2 = (i64 * 2)(64, 128)
+    C2 = (i64 * 2)(1024, 2048)
+    one = lib.aaac_batch_workspace_bytes(OP_INIT, 1, R1, C1, 128, 8, 16)
+    two = lib.aaac_batch_workspace_bytes(OP_INIT, 2, R2, C2, 128, 8, 16)
+    # the single call and a batch of one need the same workspace; keys add 4 bytes per weight
+    assert one == lib.aaac_workspace_bytes(OP_INIT, 64, 1024, 128, 0, 16)
+    assert two - one >= 128 * 2048 * 4
+    assert lib.aaac_batch_workspace_bytes(OP_INIT, 1, R1, (i64 * 1)(1000), 128, 8, 16) == 0
+    f = lib.aaac_init_quantiles_batch
+    P = (ctypes.c_void_p * 1)(FAKE)
+    assert f(0, P, R1, C1, 128, 16, P, FAKE, ctypes.c_size_t(one), None) == INVALID
+    assert f(9, P, R1, C1, 128, 16, P, FAKE, ctypes.c_size_t(one), None) == INVALID
+    assert f(1, None, R1, C1, 128, 16, P, FAKE, ctypes.c_size_t(one), None) == INVALID
+    assert f(1, P, R1, C1, 128, 16, P, FAKE, ctypes.c_size_t(one - 1), None) == WS_SMALL
+    assert f(1, P, R1, (i64 * 1)(1000), 128, 16, P, FAKE, ctypes.c_size_t(one), None) == SHAPE
+    assert f(1, P, R1, C1, 128, 17, P, FAKE, ctypes.c_size_t(one), None) == SHAPE
+    bad = (ctypes.c_void_p * 1)((1 << 20) + 2)
+    assert f(1, bad, R1, C1, 128, 16, P, FAKE, ctypes.c_size_t(one), None) == INVALID

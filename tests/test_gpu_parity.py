@@ -154,6 +154,32 @@ def test_init_quantiles_zero_groups_and_ties():
     assert np.array_equal(_np(tables), np.concatenate([T0, T1]).astype(np.float32))
 
 
+def test_init_batch_equals_single_calls():
+    """One batched init equals the per-matrix calls bit for bit; the same workspace then serves a
+    smaller batch of other sizes (every call leaves the histogram headers zero)."""
+    _say("init batch")
+    for g, n, shapes in ((128, 16, [(512, 4096), (128, 4096), (64, 1024), (700, 2048), (33, 640)]),
+                         (16, 15, [(96, 1024), (40, 4096), (7, 8192)])):
+        Ws = [_weight(R, C, 300 + 7 * i + g) for i, (R, C) in enumerate(shapes)]
+        Rs = [R for R, _ in shapes]
+        Cs = [C for _, C in shapes]
+        ws = L.workspace(L.batch_workspace_bytes(L.OP_INIT, Rs, Cs, g, 8, n), DEV)
+        got = [torch.empty(2 * n, dtype=torch.float32, device=DEV) for _ in shapes]
+        L.aaac_init_quantiles_batch(Ws, g, n, got, ws)
+        again = [torch.empty(2 * n, dtype=torch.float32, device=DEV) for _ in shapes[1:]]
+        L.aaac_init_quantiles_batch(Ws[:0:-1], g, n, again[::-1], ws)   # reversed, one fewer
+        want = [torch.empty(2 * n, dtype=torch.float32, device=DEV) for _ in shapes]
+        for W, t in zip(Ws, want):
+            L.aaac_init_quantiles(W, g, n, t)
+        torch.cuda.synchronize()
+        for i in range(len(shapes)):
+            assert torch.equal(got[i], want[i]), (g, shapes[i])
+        for i in range(1, len(shapes)):
+            assert torch.equal(again[i - 1], want[i]), (g, shapes[i])
+        T0, T1 = ref.init_tables(par.to_np64(Ws[-1]), g, n)
+        assert np.array_equal(_np(got[-1]), np.concatenate([T0, T1]).astype(np.float32))
+
+
 def test_init_quantiles_prefix_slot_collisions():
     """Targets at +-0.75 and +-0.75 * 2^-32: their key prefixes differ (exponents 32 apart) but
     share the low 12 bits the prefix table is indexed by, so the search for shared slots runs in
