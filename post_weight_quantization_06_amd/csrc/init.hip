@@ -26,7 +26,8 @@ struct InitState {
   uint64_t rank[kTargets];       // residual rank inside that prefix
   uint32_t active[kTargets];     // sorted distinct prefixes of the current pass
   uint32_t nactive;
-  uint32_t pad[3];
+  uint32_t fold;                 // shift of the prefix table's slot hash for the next pass
+  uint32_t pad[2];
 };
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -137,9 +138,10 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(InitBatch b) {
 
 // Passes 2-4: histogram of byte `pass` (0-based from the top) of keys whose higher bytes match an
 // active prefix of their matrix. The active prefixes (at most 32, sorted) are found through a
-// 4096-slot table on their low 12 bits; a slot holds one prefix, and a slot that would need more
-// sends its keys to a binary search of the sorted list (with 32 prefixes in 4096 slots a shared
-// slot is rare and holds 1/4096 of the keys). One workgroup of 1024 threads per CU walks a
+// 4096-slot table indexed by slot_of(prefix, fold); a slot holds one prefix, and a slot that would
+// need more sends its keys to a binary search of the sorted list. The select kernel picks, per
+// matrix and pass, the first fold shift that gives every active prefix a slot of its own, so the
+// search is only taken when no candidate does. One workgroup of 1024 threads per CU walks a
 // contiguous range of chunks: its fixed work (clearing the histogram rows in use, the prefix
 // table, flushing its histogram with global atomics) is paid once per CU and matrix, and each
 // thread keeps four 16-byte loads in flight.
@@ -148,19 +150,29 @@ constexpr int kSlots = 4096;
 constexpr int kPassUnroll = 4;
 constexpr int64_t kChunkVecs = (int64_t)kPassThreads * kPassUnroll;
 
+// Slot of a prefix: its low 12 bits with its bits from `fold` up xored in. Quotients of two bf16
+// values have short mantissas, so the low bits alone would be mostly zero and the keys' slot reads
+// would pile onto a few LDS banks; the fold spreads them.
+__device__ __forceinline__ uint32_t slot_of(uint32_t pre, uint32_t fold) {
+  return (pre ^ (pre >> fold)) & (kSlots - 1);
+}
+constexpr int kFolds = 8;
+__constant__ const uint32_t kFoldShift[kFolds] = {12, 11, 13, 10, 14, 9, 15, 8};
+
 __global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, int pass) {
   __shared__ uint32_t h[kTargets * kDigits];
   __shared__ uint32_t act[kTargets];
   // slot entry: (prefix, position in the list); position -1 = no prefix, -2 = several prefixes
   __shared__ uint2 slot[kSlots];
   __shared__ uint32_t cnt[kSlots];
-  __shared__ uint32_t nact;
+  __shared__ uint32_t nact, fold_s;
   const int tid = threadIdx.x;
   const int pshift = 32 - 8 * pass;       // prefix = key >> pshift
   const int dshift = 24 - 8 * pass;       // digit = (key >> dshift) & 255
   const int64_t c_end = task_lo(blockIdx.x + 1, b.total_chunks, gridDim.x);
   int cur = -1;
   int na = 0;
+  uint32_t fold = kFoldShift[0];
   for (int64_t chunk = task_lo(blockIdx.x, b.total_chunks, gridDim.x); chunk < c_end; ++chunk) {
     int j = cur < 0 ? 0 : cur;
     while (j + 1 < b.njobs && chunk >= b.job[j + 1].chunk_begin) ++j;
@@ -172,18 +184,22 @@ __global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, in
       // this matrix's active prefixes and their slots
       __syncthreads();
       if (tid < kTargets) act[tid] = b.job[j].state->active[tid];
-      if (tid == 0) nact = b.job[j].state->nactive;
+      if (tid == 0) {
+        nact = b.job[j].state->nactive;
+        fold_s = b.job[j].state->fold;
+      }
       for (int i = tid; i < kSlots; i += kPassThreads) {
         slot[i] = make_uint2(0u, (uint32_t)-1);
         cnt[i] = 0u;
       }
       __syncthreads();
       na = (int)nact;
+      fold = fold_s;
       for (int i = tid; i < na * kDigits; i += kPassThreads) h[i] = 0;   // the rows in use
-      if (tid < na) atomicAdd(&cnt[act[tid] & (kSlots - 1)], 1u);
+      if (tid < na) atomicAdd(&cnt[slot_of(act[tid], fold)], 1u);
       __syncthreads();
       if (tid < na) {
-        const uint32_t sl = act[tid] & (kSlots - 1);
+        const uint32_t sl = slot_of(act[tid], fold);
         slot[sl] = cnt[sl] == 1u ? make_uint2(act[tid], (uint32_t)tid)
                                  : make_uint2(0u, (uint32_t)-2);
       }
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, in
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t pre = kk[e] >> pshift;
-        const uint2 en = slot[pre & (kSlots - 1)];
+        const uint2 en = slot[slot_of(pre, fold)];
         const int i0 = (int)en.y;
         int hit = (i0 >= 0 && en.x == pre) ? i0 : -1;
         if (i0 == -2) {
@@ -352,7 +368,33 @@ __global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b
     for (int t = 0; t < nt; ++t) m += first[t];
     state->nactive = m;
   }
-  if (pass == 3 && tid < nt) tables[tid] = key_value(newp[tid]);
+  if (pass == 3) {
+    if (tid < nt) tables[tid] = key_value(newp[tid]);
+    return;
+  }
+  // the slot hash of the next pass: wave w tries fold candidate w; lane t holds target t's slot
+  // (or a value no slot takes when t repeats an earlier target's prefix) and looks for an equal
+  // slot on a lower lane
+  __shared__ uint32_t fold_ok[kFolds];
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  if (wave < kFolds) {
+    const uint32_t f = kFoldShift[wave];
+    const uint32_t mine =
+        (lane < nt && first[lane]) ? slot_of(newp[lane], f) : (uint32_t)(kSlots + lane);
+    bool clash = false;
+    for (int t = 0; t < kTargets; ++t) {
+      const uint32_t other = (uint32_t)__shfl((int)mine, t);
+      clash = clash || (t < lane && other == mine);
+    }
+    const unsigned long long any = __ballot(clash);
+    if (lane == 0) fold_ok[wave] = any ? 0u : 1u;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t f = kFoldShift[0];
+    for (int c = kFolds - 1; c >= 0; --c) f = fold_ok[c] ? kFoldShift[c] : f;
+    state->fold = f;
+  }
 }
 
 size_t init_workspace_bytes(int count, const int64_t* R, const int64_t* C) {

@@ -200,6 +200,59 @@ def test_init_quantiles_prefix_slot_collisions():
     assert np.array_equal(_np(tables), want), (_np(tables), want)
 
 
+# shifts the init passes try, in order, for the prefix table's slot hash (p ^ p >> f) & 4095
+INIT_FOLDS = (12, 11, 13, 10, 14, 9, 15, 8)
+
+
+def _fold_collision_weights(s_bits):
+    """16 bf16 weights below the group maximum s whose quotients' 24-bit key prefixes form 8 pairs,
+    pair k sharing a slot under fold INIT_FOLDS[k]: every fold the last pass can choose leaves two
+    active prefixes in one slot."""
+    s32 = np.array([s_bits << 16], np.uint32).view(np.float32)[0]
+    wb = np.arange(0x0080, s_bits, dtype=np.uint32)
+    u = (wb << 16).view(np.float32) / s32
+    keep = u >= np.float32(2.0 ** -20)
+    wb, u = wb[keep], u[keep]
+    pre = (u.view(np.uint32) | np.uint32(0x80000000)) >> np.uint32(8)
+    used = {int((np.float32(1.0).view(np.uint32) | 0x80000000) >> 8)}
+    chosen = []
+    for f in INIT_FOLDS:
+        sl = (pre ^ (pre >> np.uint32(f))) & np.uint32(4095)
+        order = np.argsort(sl, kind="stable")
+        for a in range(len(order) - 1):
+            i, j = int(order[a]), int(order[a + 1])
+            if sl[i] == sl[j] and pre[i] != pre[j] and not {int(pre[i]), int(pre[j])} & used:
+                chosen += [int(wb[i]), int(wb[j])]
+                used |= {int(pre[i]), int(pre[j])}
+                break
+        else:
+            raise AssertionError("no pair for fold %d" % f)
+    return chosen
+
+
+def test_init_quantiles_every_fold_collides():
+    """Groups of 128: 8 copies of each of 16 weights (7 of the largest) and the group maximum.
+    Every target lands on one of the 17 values, and every slot hash the last pass can pick puts
+    two of their prefixes in one slot, so that pass resolves them through the sorted-list search."""
+    _say("init every fold collides")
+    R, C, g, n = 32, 1024, 128, 16
+    s_bits = 0x3CF5
+    vals = sorted(_fold_collision_weights(s_bits),
+                  key=lambda b: np.array([b << 16], np.uint32).view(np.float32)[0])
+    assert len(set(vals)) == 16
+    group = np.array(sum(([b] * 8 for b in vals[:15]), []) + [vals[15]] * 7 + [s_bits], np.uint16)
+    rng = np.random.default_rng(12)
+    rows = [np.concatenate([rng.permutation(group) for _ in range(C // g)]) for _ in range(R)]
+    W = torch.from_numpy(np.stack(rows).view(np.int16)).view(torch.bfloat16).to(DEV)
+    tables = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(W, g, n, tables)
+    torch.cuda.synchronize()
+    T0, T1 = ref.init_tables(par.to_np64(W), g, n)
+    want = np.concatenate([T0, T1]).astype(np.float32)
+    assert len(set(want.tolist())) == 17
+    assert np.array_equal(_np(tables), want), (_np(tables), want)
+
+
 # ------------------------------------------------------------------ assign
 
 ASSIGN_CASES = [
