@@ -4,12 +4,13 @@
 //
 // u = fl32(w / s) (IEEE division; u = +0 when s = 0) is mapped to an order-preserving 32-bit key
 // (flip all bits of negatives, set the sign bit of non-negatives). The 2n target ranks are resolved
-// one byte at a time, most significant first: pass 1 histograms the top byte of every key; after
-// each pass one workgroup per matrix walks the histogram of every target's current prefix to the
-// byte that holds its residual rank; passes 2-4 histogram the next byte of the keys whose prefix is
-// one of the (at most 2n) active prefixes. Integer counts make every step exact and order-free.
+// in three digits, most significant first: 12 bits, then 10, then 10. The keys kernel histograms
+// the top 12 bits of every key; after each histogram one workgroup per matrix walks the histogram
+// row of every target's current prefix to the digit that holds its residual rank; two passes then
+// histogram the next 10 bits of the keys whose prefix is one of the (at most 2n) active prefixes.
+// Integer counts make every step exact and order-free.
 //
-// Workspace: kMaxJobs headers of (hist u64 [32][256] | state), then the keys u32 [N_i] of every
+// Workspace: kMaxJobs headers of (hist u64 [32][1024] | state), then the keys u32 [N_i] of every
 // matrix. The headers sit at fixed offsets, so a workspace reused for other matrices (or another
 // count of them) still starts from the zero histograms the previous call left behind.
 #include "common.h"
@@ -19,19 +20,28 @@ namespace aaac {
 namespace {
 
 constexpr int kTargets = 32;
-constexpr int kDigits = 256;
+// digits: step 0 (the keys kernel) takes the top kTopBits of a key, steps 1 and 2 (the passes)
+// kLowBits each
+constexpr int kTopBits = 12;
+constexpr int kTopDigits = 1 << kTopBits;
+constexpr int kLowBits = 10;
+constexpr int kLowDigits = 1 << kLowBits;
+constexpr int kSteps = 3;
+constexpr int kHistBins = kTargets * kLowDigits;      // [target row][digit]; step 0 uses row 0..3
+static_assert(kTopBits + (kSteps - 1) * kLowBits == 32, "the digits cover the key");
+static_assert(kTopDigits <= kHistBins, "the top digit's histogram fits the rows");
 
 struct InitState {
   uint32_t prefix[kTargets];     // resolved high bytes of each target's key
   uint64_t rank[kTargets];       // residual rank inside that prefix
-  uint32_t active[kTargets];     // sorted distinct prefixes of the current pass
+  uint32_t active[kTargets];     // sorted distinct prefixes of the next step
   uint32_t nactive;
-  uint32_t fold;                 // shift of the prefix table's slot hash for the next pass
+  uint32_t hash;                 // multiplier of the prefix table's slot hash for the next step
   uint32_t pad[2];
 };
 
 constexpr size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-constexpr size_t kHistBytes = align256(sizeof(unsigned long long) * kTargets * kDigits);
+constexpr size_t kHistBytes = align256(sizeof(unsigned long long) * kHistBins);
 constexpr size_t kHeaderBytes = kHistBytes + align256(sizeof(InitState));
 constexpr size_t kHeadersBytes = kMaxJobs * kHeaderBytes;
 
@@ -41,7 +51,7 @@ struct InitJob {
   int64_t R, C, N;
   int64_t nslab;                 // 512-column slabs per row
   uint32_t* keys;                // [N]
-  unsigned long long* hist;      // [32][256], zero between calls
+  unsigned long long* hist;      // [32][1024], zero between calls
   InitState* state;
   float* tables;                 // [2][n]
   int64_t task_begin;            // first keys task (kRowsPerTask rows of one slab)
@@ -71,29 +81,30 @@ __device__ __forceinline__ void flush_hist(const uint32_t* lds, unsigned long lo
 }  // namespace
 
 // Keys of all weights (same lane mapping as assign's 8-weight mapping) and the histogram of their
-// top byte. A workgroup walks a contiguous range of tasks; its LDS histogram goes to a matrix's
+// top 12 bits. A workgroup walks a contiguous range of tasks; its LDS histogram goes to a matrix's
 // histogram when the workgroup leaves that matrix.
 __global__ __launch_bounds__(kBlock) void init_keys_kernel(InitBatch b) {
-  // eight copies of the histogram, by lane & 7: most keys share a few top bytes, and adds to one
-  // address from many lanes of an instruction are serialized
-  constexpr int kCopies = 8;
-  __shared__ uint32_t h[kCopies][kDigits];
+  // two copies of the histogram, by lane parity: the busiest bins hold a few percent of the keys,
+  // and adds to one address from several lanes of an instruction are serialized
+  constexpr int kCopies = 2;
+  __shared__ uint32_t h[kCopies][kTopDigits];
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int c = 0; c < kCopies; ++c) h[c][tid] = 0;
+  for (int i = tid; i < kCopies * kTopDigits; i += kBlock) (&h[0][0])[i] = 0;
   __syncthreads();
   const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = b.g / kPerLane;
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
   int cur = -1;
   auto flush = [&](int j) {
     __syncthreads();
-    uint32_t tot = 0;
+    for (int i = tid; i < kTopDigits; i += kBlock) {
+      uint32_t tot = 0;
 #pragma unroll
-    for (int c = 0; c < kCopies; ++c) {
-      tot += h[c][tid];
-      h[c][tid] = 0;
+      for (int c = 0; c < kCopies; ++c) {
+        tot += h[c][i];
+        h[c][i] = 0;
+      }
+      if (tot) atomicAdd(b.job[j].hist + i, (unsigned long long)tot);
     }
-    if (tot) atomicAdd(b.job[j].hist + tid, (unsigned long long)tot);
     __syncthreads();
   };
   for (int64_t task = task_lo(blockIdx.x, b.total_tasks, gridDim.x); task < t_end; ++task) {
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(InitBatch b) {
         float u = s > 0.0f ? w[e] / s : 0.0f;
         if (u == 0.0f) u = 0.0f;            // zero is unsigned
         k[e] = order_key(u);
-        atomicAdd(&h[tid & (kCopies - 1)][k[e] >> 24], 1u);
+        atomicAdd(&h[tid & (kCopies - 1)][k[e] >> (32 - kTopBits)], 1u);
       }
       uint4* dst = reinterpret_cast<uint4*>(jb.keys + base);
       dst[0] = make_uint4(k[0], k[1], k[2], k[3]);
@@ -136,72 +147,79 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(InitBatch b) {
   if (cur >= 0) flush(cur);
 }
 
-// Passes 2-4: histogram of byte `pass` (0-based from the top) of keys whose higher bytes match an
-// active prefix of their matrix. The active prefixes (at most 32, sorted) are found through a
-// 4096-slot table indexed by slot_of(prefix, fold); a slot holds one prefix, and a slot that would
-// need more sends its keys to a binary search of the sorted list. The select kernel picks, per
-// matrix and pass, the first fold shift that gives every active prefix a slot of its own, so the
-// search is only taken when no candidate does. One workgroup of 1024 threads per CU walks a
-// contiguous range of chunks: its fixed work (clearing the histogram rows in use, the prefix
-// table, flushing its histogram with global atomics) is paid once per CU and matrix, and each
-// thread keeps four 16-byte loads in flight.
+// Steps 1 and 2: histogram of the next 10 bits of the keys whose higher bits match an active prefix
+// of their matrix. The active prefixes (at most 32, sorted) are found through a 2048-slot table
+// indexed by slot_of(prefix, hash); a slot holds one prefix, and a slot that would need more sends
+// its keys to a binary search of the sorted list. The select kernel picks, per matrix and step,
+// the first hash multiplier that gives every active prefix a slot of its own, so the search is
+// only taken when no candidate does. One workgroup of 1024 threads per CU walks a contiguous range
+// of chunks: its fixed work (clearing the histogram rows in use, the prefix table, flushing its
+// histogram with global atomics) is paid once per CU and matrix, and each thread keeps four
+// 16-byte loads in flight.
 constexpr int kPassThreads = 1024;
-constexpr int kSlots = 4096;
+constexpr int kSlotBits = 11;
+constexpr int kSlots = 1 << kSlotBits;
 constexpr int kPassUnroll = 4;
 constexpr int64_t kChunkVecs = (int64_t)kPassThreads * kPassUnroll;
+// slot entry: prefix << 5 | position in the sorted list, or one of two markers (neither equals a
+// 22-bit prefix once shifted down by 5)
+constexpr uint32_t kSlotEmpty = 0xFFFFFFFFu;
+constexpr uint32_t kSlotShared = 0xFFFFFFFEu;
+static_assert(kTopBits + kLowBits + 5 <= 32, "a slot entry holds a prefix and a position");
 
-// Slot of a prefix: its low 12 bits with its bits from `fold` up xored in. Quotients of two bf16
-// values have short mantissas, so the low bits alone would be mostly zero and the keys' slot reads
-// would pile onto a few LDS banks; the fold spreads them.
-__device__ __forceinline__ uint32_t slot_of(uint32_t pre, uint32_t fold) {
-  return (pre ^ (pre >> fold)) & (kSlots - 1);
+// Slot of a prefix (at most 22 bits): the top 11 bits of the low 32 bits of prefix x hash, a
+// 24-bit odd multiplier (one full-rate 24-bit multiply). Quotients of two bf16 values have short
+// mantissas, so the prefixes' low bits are mostly zero; the product mixes every bit of the prefix
+// into the slot, which also spreads the keys' slot reads over the LDS banks.
+__device__ __forceinline__ uint32_t slot_of(uint32_t pre, uint32_t hash) {
+  // HIP's __umul24 returns int: the shift must see the product as unsigned
+  return static_cast<uint32_t>(__umul24(pre, hash)) >> (32 - kSlotBits);
 }
-constexpr int kFolds = 8;
-__constant__ const uint32_t kFoldShift[kFolds] = {12, 11, 13, 10, 14, 9, 15, 8};
+constexpr int kHashes = 8;
+__constant__ const uint32_t kHashMul[kHashes] = {0x9E3779u, 0x85EBCBu, 0xC2B2AFu, 0x27D4EBu,
+                                                 0x165667u, 0xB55A4Fu, 0x7FEB35u, 0x61C887u};
 
-__global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, int pass) {
-  __shared__ uint32_t h[kTargets * kDigits];
+__global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, int step) {
+  __shared__ uint32_t h[kHistBins];
   __shared__ uint32_t act[kTargets];
-  // slot entry: (prefix, position in the list); position -1 = no prefix, -2 = several prefixes
-  __shared__ uint2 slot[kSlots];
+  __shared__ uint32_t slot[kSlots];
   __shared__ uint32_t cnt[kSlots];
-  __shared__ uint32_t nact, fold_s;
+  __shared__ uint32_t nact, hash_s;
   const int tid = threadIdx.x;
-  const int pshift = 32 - 8 * pass;       // prefix = key >> pshift
-  const int dshift = 24 - 8 * pass;       // digit = (key >> dshift) & 255
+  const int pshift = 32 - kTopBits - kLowBits * (step - 1);   // prefix = key >> pshift
+  const int dshift = pshift - kLowBits;                        // digit = (key >> dshift) & 1023
   const int64_t c_end = task_lo(blockIdx.x + 1, b.total_chunks, gridDim.x);
   int cur = -1;
   int na = 0;
-  uint32_t fold = kFoldShift[0];
+  uint32_t hash = kHashMul[0];
   for (int64_t chunk = task_lo(blockIdx.x, b.total_chunks, gridDim.x); chunk < c_end; ++chunk) {
     int j = cur < 0 ? 0 : cur;
     while (j + 1 < b.njobs && chunk >= b.job[j + 1].chunk_begin) ++j;
     if (j != cur) {
       if (cur >= 0) {
         __syncthreads();
-        flush_hist(h, b.job[cur].hist, na * kDigits);
+        flush_hist(h, b.job[cur].hist, na * kLowDigits);
       }
       // this matrix's active prefixes and their slots
       __syncthreads();
       if (tid < kTargets) act[tid] = b.job[j].state->active[tid];
       if (tid == 0) {
         nact = b.job[j].state->nactive;
-        fold_s = b.job[j].state->fold;
+        hash_s = b.job[j].state->hash;
       }
       for (int i = tid; i < kSlots; i += kPassThreads) {
-        slot[i] = make_uint2(0u, (uint32_t)-1);
+        slot[i] = kSlotEmpty;
         cnt[i] = 0u;
       }
       __syncthreads();
       na = (int)nact;
-      fold = fold_s;
-      for (int i = tid; i < na * kDigits; i += kPassThreads) h[i] = 0;   // the rows in use
-      if (tid < na) atomicAdd(&cnt[slot_of(act[tid], fold)], 1u);
+      hash = hash_s;
+      for (int i = tid; i < na * kLowDigits; i += kPassThreads) h[i] = 0;   // the rows in use
+      if (tid < na) atomicAdd(&cnt[slot_of(act[tid], hash)], 1u);
       __syncthreads();
       if (tid < na) {
-        const uint32_t sl = slot_of(act[tid], fold);
-        slot[sl] = cnt[sl] == 1u ? make_uint2(act[tid], (uint32_t)tid)
-                                 : make_uint2(0u, (uint32_t)-2);
+        const uint32_t sl = slot_of(act[tid], hash);
+        slot[sl] = cnt[sl] == 1u ? (act[tid] << 5) | (uint32_t)tid : kSlotShared;
       }
       __syncthreads();
       cur = j;
@@ -218,40 +236,105 @@ __global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, in
       const int64_t i = v0 + (int64_t)u * kPassThreads;
       qs[u] = k4[i < n4 ? i : n4 - 1];
     }
+    // all 16 slot reads, then the hits, then all 16 adds: a search between them would make every
+    // key wait for the LDS operations in flight, the previous key's add included, and adds to
+    // the one bin of u = 1 or u = -1 are slow when every group has its maximum there
+    constexpr int kKeys = 4 * kPassUnroll;
+    uint32_t kk[kKeys], en[kKeys];
 #pragma unroll
     for (int u = 0; u < kPassUnroll; ++u) {
-      if (v0 + (int64_t)u * kPassThreads >= n4) break;
-      const uint32_t kk[4] = {qs[u].x, qs[u].y, qs[u].z, qs[u].w};
+      kk[4 * u] = qs[u].x;
+      kk[4 * u + 1] = qs[u].y;
+      kk[4 * u + 2] = qs[u].z;
+      kk[4 * u + 3] = qs[u].w;
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t pre = kk[e] >> pshift;
-        const uint2 en = slot[slot_of(pre, fold)];
-        const int i0 = (int)en.y;
-        int hit = (i0 >= 0 && en.x == pre) ? i0 : -1;
-        if (i0 == -2) {
+    for (int i = 0; i < kKeys; ++i) en[i] = slot[slot_of(kk[i] >> pshift, hash)];
+    int hit[kKeys];
+    bool shared = false;
+#pragma unroll
+    for (int i = 0; i < kKeys; ++i) {
+      const uint32_t pre = kk[i] >> pshift;
+      const bool valid = v0 + (int64_t)(i / 4) * kPassThreads < n4;
+      hit[i] = (valid && (en[i] >> 5) == pre) ? (int)(en[i] & 31u) : -1;
+      shared = shared || (valid && en[i] == kSlotShared);
+    }
+    if (__ballot(shared)) {
+      for (int i = 0; i < kKeys; ++i) {
+        const uint32_t pre = kk[i] >> pshift;
+        const bool valid = v0 + (int64_t)(i / 4) * kPassThreads < n4;
+        if (valid && en[i] == kSlotShared) {
           int lo = 0, hi = na;               // first active prefix >= pre
           while (lo < hi) {
             const int mid = (lo + hi) >> 1;
             if (act[mid] < pre) lo = mid + 1; else hi = mid;
           }
-          if (lo < na && act[lo] == pre) hit = lo;
+          if (lo < na && act[lo] == pre) hit[i] = lo;
         }
-        if (hit >= 0) atomicAdd(&h[hit * kDigits + ((kk[e] >> dshift) & 255u)], 1u);
       }
     }
+#pragma unroll
+    for (int i = 0; i < kKeys; ++i)
+      if (hit[i] >= 0)
+        atomicAdd(&h[hit[i] * kLowDigits + ((kk[i] >> dshift) & (kLowDigits - 1))], 1u);
   }
   if (cur >= 0) {
     __syncthreads();
-    flush_hist(h, b.job[cur].hist, na * kDigits);
+    flush_hist(h, b.job[cur].hist, na * kLowDigits);
   }
 }
 
-// One workgroup of 1024 threads per matrix (a target or two per wave): move every target one byte
-// down, rebuild the active prefix list, clear the histogram rows used; after the last pass write
-// the tables. The rows in use are first copied to LDS (one coalesced read per thread and row) so
-// that each target walks its row there.
+// One workgroup of 1024 threads per matrix (a target or two per wave): move every target one digit
+// down, rebuild the active prefix list, clear the histogram rows used; after the last step write
+// the tables. A wave finds its target's digit in two rounds over the row, which sits in L2 after
+// the histogram kernel's atomics: lane l first sums digits [l P, (l + 1) P) (P = 64 or 16), an
+// inclusive scan over the wave and a ballot find the lane whose block holds the rank, then lane j
+// reads digit j of that block and a second scan and ballot find the digit.
 constexpr int kSelectThreads = 1024;
-__global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b, int pass) {
+
+struct DigitPick {
+  uint32_t digit;   // the digit whose count range holds the rank
+  uint64_t rest;    // the rank's residual inside that digit
+};
+
+__device__ __forceinline__ uint64_t wave_incl_scan(uint64_t v, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint64_t other = (uint64_t)__shfl_up((unsigned long long)v, d);
+    if (lane >= d) v += other;
+  }
+  return v;
+}
+
+// A histogram row staged in LDS: one u64 of padding after every 32 digits, so that lanes reading
+// blocks of 16 or 64 consecutive digits start on different banks.
+__device__ __forceinline__ int padded(int d) { return d + (d >> 5); }
+constexpr int kPaddedLow = kLowDigits + kLowDigits / 32;
+constexpr int kPaddedTop = kTopDigits + kTopDigits / 32;
+
+// The digit of a staged histogram row (kPer * 64 bins) that holds `rank`, the same on every lane.
+template <int kPer>
+__device__ __forceinline__ DigitPick pick_digit(const unsigned long long* row, uint64_t rank,
+                                                int lane) {
+  // round 1: lane l sums digits [l kPer, (l + 1) kPer)
+  uint64_t mine = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) mine += row[padded(lane * kPer + k)];
+  const uint64_t incl = wave_incl_scan(mine, lane);
+  // the first lane whose inclusive count exceeds the rank (the last lane if none does)
+  const unsigned long long hit = __ballot(rank < incl);
+  const int owner = hit ? __builtin_ctzll(hit) : kWave - 1;
+  const uint64_t base = (uint64_t)__shfl((unsigned long long)(incl - mine), owner);
+  // round 2: lane j < kPer takes digit j of the owner's block
+  const uint64_t c = lane < kPer ? (uint64_t)row[padded(owner * kPer + lane)] : 0ull;
+  const uint64_t incl2 = base + wave_incl_scan(c, lane);
+  const unsigned long long hit2 = __ballot(lane < kPer && rank < incl2);
+  const int dl = hit2 ? __builtin_ctzll(hit2) : kPer - 1;
+  const uint64_t below = (uint64_t)__shfl((unsigned long long)(incl2 - c), dl);
+  return DigitPick{(uint32_t)(owner * kPer + dl), rank - below};
+}
+
+__global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b, int step) {
   const InitJob& jb = b.job[blockIdx.x];
   const int64_t N = jb.N;
   const int n = b.n;
@@ -259,12 +342,12 @@ __global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b
   unsigned long long* const hist = jb.hist;
   float* const tables = jb.tables;
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
   const int nt = 2 * n;
   constexpr int kWaves = kSelectThreads / kWave;
   __shared__ uint32_t newp[kTargets];
-  __shared__ unsigned long long hl[kTargets * kDigits];
   __shared__ uint32_t first[kTargets];
-  if (pass == 0 && tid < nt) {
+  if (step == 0 && tid < nt) {
     // target ranks of reading: T0[j] at floor((2j+1) N / 2n), T1[j] at min(N-1, floor((j+1) N / n))
     const int j = tid % n;
     uint64_t r;
@@ -281,7 +364,7 @@ __global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b
   __shared__ uint32_t act_s[kTargets], pre_s[kTargets];
   __shared__ uint64_t rank_s[kTargets];
   __shared__ int rows_s;
-  if (tid == 0) rows_s = pass == 0 ? 1 : (int)state->nactive;
+  if (tid == 0) rows_s = step == 0 ? 1 : (int)state->nactive;
   if (tid < kTargets) {
     act_s[tid] = state->active[tid];
     pre_s[tid] = state->prefix[tid];
@@ -289,66 +372,45 @@ __global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b
   }
   __syncthreads();
   const int rows = rows_s;
-  // the rows in use and the (zero) row after them, read by a target without a row of its own,
-  // which the construction of the active list rules out
-  const int copy = rows < kTargets ? rows + 1 : kTargets;
-  {
-    // thread t reads digit t & 255 of rows t / 256, t / 256 + 4, ...: all its loads before any
-    // store
-    constexpr int kPer = kTargets * kDigits / kSelectThreads;
-    unsigned long long v[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kSelectThreads;
-      v[k] = i < copy * kDigits ? hist[i] : 0ull;
-    }
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int i = tid + k * kSelectThreads;
-      if (i < copy * kDigits) hl[i] = v[k];
-    }
+  const int dbits = step == 0 ? kTopBits : kLowBits;
+  // staged rows: the top digit's one row for every wave, or one row per wave
+  static_assert(kWaves * kPaddedLow >= kPaddedTop, "the top digit's row fits the staging area");
+  __shared__ unsigned long long rowbuf[kWaves * kPaddedLow];
+  if (step == 0) {
+    for (int i = tid; i < kTopDigits; i += kSelectThreads) rowbuf[padded(i)] = hist[i];
   }
   __syncthreads();
-  {
-    // wave w resolves targets w and w + 16: lane l holds the count of digits 4l .. 4l + 3 of the
-    // target's row, an inclusive scan over the wave finds the lane whose digits hold the rank,
-    // and that lane walks its four digits
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    for (int t = wave; t < nt; t += kWaves) {
-      const uint32_t pre = pre_s[t];
-      int slot = 0;
-      if (pass > 0) {
-        // the row of this target's prefix: one compare per lane, first match
-        const unsigned long long m = __ballot(lane < rows && act_s[lane & (kTargets - 1)] == pre);
-        slot = m ? __builtin_ctzll(m) : copy - 1;
-      }
-      const uint64_t rank = rank_s[t];
-      const unsigned long long* row = hl + slot * kDigits + 4 * lane;
-      const uint64_t c0 = row[0], c1 = row[1], c2 = row[2], c3 = row[3];
-      const uint64_t mine = c0 + c1 + c2 + c3;
-      uint64_t incl = mine;
+  // every wave runs the same number of rounds, so the block barriers match
+  static_assert(kTargets % kWaves == 0, "targets per wave");
+  for (int r = 0; r < kTargets / kWaves; ++r) {
+    const int t = wave + r * kWaves;
+    const bool mine = t < nt;
+    const uint32_t pre = pre_s[t];
+    unsigned long long* const wrow = rowbuf + wave * kPaddedLow;
+    if (step > 0 && mine) {
+      // the row of this target's prefix: one compare per lane, first match (the construction of
+      // the active list gives every target one; the fallback is a zero row or the last row)
+      const unsigned long long m = __ballot(lane < rows && act_s[lane & (kTargets - 1)] == pre);
+      const int row = m ? __builtin_ctzll(m) : (rows < kTargets ? rows : kTargets - 1);
+      const unsigned long long* const hrow = hist + (size_t)row * kLowDigits;
 #pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) {
-        const uint64_t other = (uint64_t)__shfl_up((unsigned long long)incl, d);
-        if (lane >= d) incl += other;
-      }
-      const uint64_t excl = incl - mine;
-      // the first lane whose inclusive count exceeds the rank (the last lane if none does)
-      const unsigned long long hit = __ballot(rank < incl);
-      const int owner = hit ? __builtin_ctzll(hit) : kWave - 1;
-      if (lane == owner) {
-        uint64_t cum = excl;
-        int d = 4 * lane;
-        if (rank >= cum + c0 && d < kDigits - 1) { cum += c0; ++d;
-          if (rank >= cum + c1 && d < kDigits - 1) { cum += c1; ++d;
-            if (rank >= cum + c2 && d < kDigits - 1) { cum += c2; ++d; } } }
-        newp[t] = (pre << 8) | (uint32_t)d;
-        state->rank[t] = rank - cum;
+      for (int k = 0; k < kLowDigits / kWave; ++k)
+        wrow[padded(k * kWave + lane)] = hrow[k * kWave + lane];
+    }
+    __syncthreads();
+    if (mine) {
+      const DigitPick pk = step == 0 ? pick_digit<kTopDigits / kWave>(rowbuf, rank_s[t], lane)
+                                     : pick_digit<kLowDigits / kWave>(wrow, rank_s[t], lane);
+      if (lane == 0) {
+        newp[t] = (pre << dbits) | pk.digit;
+        state->rank[t] = pk.rest;
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int i = tid; i < rows * kDigits; i += kSelectThreads) hist[i] = 0ull;
+  // clear what this step's histogram used: the top digit's 4096 bins, or the rows in use
+  const int used = step == 0 ? kTopDigits : rows * kLowDigits;
+  for (int i = tid; i < used; i += kSelectThreads) hist[i] = 0ull;
   if (tid < nt) {
     state->prefix[tid] = newp[tid];
     // first occurrence of this prefix among the targets
@@ -368,17 +430,16 @@ __global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b
     for (int t = 0; t < nt; ++t) m += first[t];
     state->nactive = m;
   }
-  if (pass == 3) {
+  if (step == kSteps - 1) {
     if (tid < nt) tables[tid] = key_value(newp[tid]);
     return;
   }
-  // the slot hash of the next pass: wave w tries fold candidate w; lane t holds target t's slot
-  // (or a value no slot takes when t repeats an earlier target's prefix) and looks for an equal
-  // slot on a lower lane
-  __shared__ uint32_t fold_ok[kFolds];
-  const int lane = tid & (kWave - 1), wave = tid / kWave;
-  if (wave < kFolds) {
-    const uint32_t f = kFoldShift[wave];
+  // the slot hash of the next step: wave w tries multiplier w; lane t holds target t's slot (or a
+  // value no slot takes when t repeats an earlier target's prefix) and looks for an equal slot on
+  // a lower lane
+  __shared__ uint32_t hash_ok[kHashes];
+  if (wave < kHashes) {
+    const uint32_t f = kHashMul[wave];
     const uint32_t mine =
         (lane < nt && first[lane]) ? slot_of(newp[lane], f) : (uint32_t)(kSlots + lane);
     bool clash = false;
@@ -387,13 +448,13 @@ __global__ __launch_bounds__(kSelectThreads) void init_select_kernel(InitBatch b
       clash = clash || (t < lane && other == mine);
     }
     const unsigned long long any = __ballot(clash);
-    if (lane == 0) fold_ok[wave] = any ? 0u : 1u;
+    if (lane == 0) hash_ok[wave] = any ? 0u : 1u;
   }
   __syncthreads();
   if (tid == 0) {
-    uint32_t f = kFoldShift[0];
-    for (int c = kFolds - 1; c >= 0; --c) f = fold_ok[c] ? kFoldShift[c] : f;
-    state->fold = f;
+    uint32_t f = kHashMul[0];
+    for (int c = kHashes - 1; c >= 0; --c) f = hash_ok[c] ? kHashMul[c] : f;
+    state->hash = f;
   }
 }
 
@@ -440,10 +501,10 @@ hipError_t launch_init(int count, const uint16_t* const* W, const int64_t* R, co
   hipLaunchKernelGGL(init_select_kernel, dim3(count), dim3(kSelectThreads), 0, stream, b, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int grid = (int)(cb < cus ? cb : cus);
-  for (int pass = 1; pass < 4; ++pass) {
-    hipLaunchKernelGGL(init_pass_kernel, dim3(grid), dim3(kPassThreads), 0, stream, b, pass);
+  for (int step = 1; step < kSteps; ++step) {
+    hipLaunchKernelGGL(init_pass_kernel, dim3(grid), dim3(kPassThreads), 0, stream, b, step);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(init_select_kernel, dim3(count), dim3(kSelectThreads), 0, stream, b, pass);
+    hipLaunchKernelGGL(init_select_kernel, dim3(count), dim3(kSelectThreads), 0, stream, b, step);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -181,9 +181,8 @@ def test_init_batch_equals_single_calls():
 
 
 def test_init_quantiles_prefix_slot_collisions():
-    """Targets at +-0.75 and +-0.75 * 2^-32: their key prefixes differ (exponents 32 apart) but
-    share the low 12 bits the prefix table is indexed by, so the search for shared slots runs in
-    every pass."""
+    """Targets at +-0.75 and +-0.75 * 2^-32: key prefixes that differ only in the exponent (32
+    apart), on both sides of zero."""
     _say("init prefix slot collisions")
     R, C, g, n = 64, 1024, 128, 16
     group = np.concatenate([[1.0], np.full(31, 0.75), np.full(32, 0.75 * 2.0 ** -32),
@@ -200,24 +199,31 @@ def test_init_quantiles_prefix_slot_collisions():
     assert np.array_equal(_np(tables), want), (_np(tables), want)
 
 
-# shifts the init passes try, in order, for the prefix table's slot hash (p ^ p >> f) & 4095
-INIT_FOLDS = (12, 11, 13, 10, 14, 9, 15, 8)
+# the init passes' prefix table: 2048 slots, slot = low 32 bits of (p x M) >> 21 with the first of
+# these multipliers that separates all active prefixes; the last pass's prefixes are the top 22
+# key bits
+INIT_HASHES = (0x9E3779, 0x85EBCB, 0xC2B2AF, 0x27D4EB, 0x165667, 0xB55A4F, 0x7FEB35, 0x61C887)
+INIT_LAST_SHIFT = 10
+
+
+def _init_slot(p, m):
+    return ((p.astype(np.uint64) * np.uint64(m)) & np.uint64(0xFFFFFFFF)) >> np.uint64(21)
 
 
 def _fold_collision_weights(s_bits):
-    """16 bf16 weights below the group maximum s whose quotients' 24-bit key prefixes form 8 pairs,
-    pair k sharing a slot under fold INIT_FOLDS[k]: every fold the last pass can choose leaves two
-    active prefixes in one slot."""
+    """16 bf16 weights below the group maximum s whose quotients' 22-bit key prefixes form 8 pairs,
+    pair k sharing a slot under multiplier INIT_HASHES[k]: every hash the last pass can choose
+    leaves two active prefixes in one slot."""
     s32 = np.array([s_bits << 16], np.uint32).view(np.float32)[0]
     wb = np.arange(0x0080, s_bits, dtype=np.uint32)
     u = (wb << 16).view(np.float32) / s32
     keep = u >= np.float32(2.0 ** -20)
     wb, u = wb[keep], u[keep]
-    pre = (u.view(np.uint32) | np.uint32(0x80000000)) >> np.uint32(8)
-    used = {int((np.float32(1.0).view(np.uint32) | 0x80000000) >> 8)}
+    pre = (u.view(np.uint32) | np.uint32(0x80000000)) >> np.uint32(INIT_LAST_SHIFT)
+    used = {int((np.float32(1.0).view(np.uint32) | 0x80000000) >> INIT_LAST_SHIFT)}
     chosen = []
-    for f in INIT_FOLDS:
-        sl = (pre ^ (pre >> np.uint32(f))) & np.uint32(4095)
+    for f in INIT_HASHES:
+        sl = _init_slot(pre, f)
         order = np.argsort(sl, kind="stable")
         for a in range(len(order) - 1):
             i, j = int(order[a]), int(order[a + 1])
@@ -226,15 +232,15 @@ def _fold_collision_weights(s_bits):
                 used |= {int(pre[i]), int(pre[j])}
                 break
         else:
-            raise AssertionError("no pair for fold %d" % f)
+            raise AssertionError("no pair for multiplier %#x" % f)
     return chosen
 
 
-def test_init_quantiles_every_fold_collides():
+def test_init_quantiles_every_slot_hash_collides():
     """Groups of 128: 8 copies of each of 16 weights (7 of the largest) and the group maximum.
     Every target lands on one of the 17 values, and every slot hash the last pass can pick puts
     two of their prefixes in one slot, so that pass resolves them through the sorted-list search."""
-    _say("init every fold collides")
+    _say("init every slot hash collides")
     R, C, g, n = 32, 1024, 128, 16
     s_bits = 0x3CF5
     vals = sorted(_fold_collision_weights(s_bits),
