@@ -15,8 +15,14 @@ namespace aaac {
 __global__ __launch_bounds__(kBlock) void pack_scales_kernel(const uint16_t* __restrict__ W,
                                                              MatrixGeom geom, int g, int S,
                                                              const uint8_t* __restrict__ sel,
-                                                             uint16_t* __restrict__ scales) {
+                                                             uint16_t* __restrict__ scales,
+                                                             const float* __restrict__ tables,
+                                                             int n,
+                                                             uint16_t* __restrict__ tables_bf16) {
   const int tid = threadIdx.x;
+  // the tables, when no bitmap kernel follows to convert them
+  if (tables_bf16 != nullptr && blockIdx.x == 0 && tid < 2 * n)
+    tables_bf16[tid] = (uint16_t)f32_to_bf16_rne(tables[tid]);
   const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = g / kPerLane;
   const int log2g = 31 - __builtin_clz((unsigned)g), log2S = 31 - __builtin_clz((unsigned)S);
   const int64_t R = geom.R, C = geom.C;
@@ -71,19 +77,33 @@ hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, in
                        const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
                        uint16_t* tables_bf16, hipStream_t stream) {
   const MatrixGeom geom = make_geom(R, C, 0);
-  const int64_t want = (int64_t)device_cu_count() * 4;
+  // one task per workgroup (up to 2^20, then a grid-stride loop): the dispatcher balances the
+  // tail, where a grid of a few workgroups per CU looping over the tasks left its last round
+  // partly empty
+  const int64_t want = 1 << 20;
   const int grid = (int)(geom.ntasks < want ? geom.ntasks : want);
+  // with the selection bit in the scale's sign there is no bitmap, and the scales kernel converts
+  // the tables itself: one launch instead of two
+  const bool bits = S < g;
   hipLaunchKernelGGL(pack_scales_kernel, dim3(grid), dim3(kBlock), 0, stream, W, geom, g, S, sel,
-                     scales);
+                     scales, tables, n, bits ? nullptr : tables_bf16);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !bits) return e;
   const int64_t ngroups = R * C / S;
-  int64_t items = bitmap ? (ngroups + 7) / 8 : 0;
+  int64_t items = (ngroups + 7) / 8;
   if (items < 2 * n) items = 2 * n;
   hipLaunchKernelGGL(pack_bits_kernel, dim3((unsigned)((items + kBlock - 1) / kBlock)),
-                     dim3(kBlock), 0, stream, sel, ngroups, S < g ? bitmap : nullptr, tables, n,
-                     tables_bf16);
+                     dim3(kBlock), 0, stream, sel, ngroups, bitmap, tables, n, tables_bf16);
   return hipGetLastError();
+}
+
+// Two finite fp32 values rounded to bf16 (ties to even) and packed, lo in the low half: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // fp64 value -> bf16 bits, ties to even, by exact scaling to the binade's quantum.
@@ -134,19 +154,31 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint32_t* __restr
       const int64_t i = i0 + u * stride;
       if (i >= nvec) break;
       const float s = __uint_as_float((word[u] & 0x7fffu) << 16);
-      uint32_t o[8];
+      float t[8], p[8];
+      bool tiny = false;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const uint32_t q = (cw[u] >> (4 * k)) & 15u;
-        const float t = tab[sg[u]][q < (uint32_t)n ? q : 0];
-        const float p = s * t;
-        // exact in fp32 unless the product is a nonzero subnormal
-        o[k] = (s == 0.0f || t == 0.0f || fabsf(p) >= 0x1p-126f)
-                   ? f32_to_bf16_rne(p)
-                   : f64_to_bf16_bits((double)s * (double)t);
+        t[k] = tab[sg[u]][q < (uint32_t)n ? q : 0];
+        p[k] = s * t[k];
+        // exact in fp32 unless the product is a nonzero subnormal (or underflows to zero)
+        tiny = tiny || (fabsf(p[k]) < 0x1p-126f && s != 0.0f && t[k] != 0.0f);
       }
-      out[i] = make_uint4(o[0] | (o[1] << 16), o[2] | (o[3] << 16), o[4] | (o[5] << 16),
-                          o[6] | (o[7] << 16));
+      // pairs of exact products rounded to bf16 (ties to even) by the conversion instruction
+      uint32_t o[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
+      if (tiny) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (fabsf(p[k]) < 0x1p-126f && s != 0.0f && t[k] != 0.0f) {
+            const uint32_t b = f64_to_bf16_bits((double)s * (double)t[k]);
+            const int sh = 16 * (k & 1);
+            o[k >> 1] = (o[k >> 1] & ~(0xffffu << sh)) | (b << sh);
+          }
+        }
+      }
+      out[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }

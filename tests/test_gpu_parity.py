@@ -425,6 +425,45 @@ def test_pack_and_dequant_bit_exact(R, C, g, S, n):
         assert np.all(np.abs(_np(y).astype(np.float64) - y_ref) <= bound)
 
 
+def test_dequant_rounding_edges():
+    """Dequant of crafted packed inputs against the oracle, bit for bit: products whose 16
+    significant bits tie at the bf16 rounding point, nonzero subnormal products, products below
+    half the smallest bf16 subnormal, zero scales and entries (and their signs), negative entries,
+    and products that round past the largest finite bf16 value."""
+    _say("dequant rounding edges")
+    R, C, g, S, n = 32, 512, 16, 16, 16
+    rng = np.random.default_rng(23)
+    codes = rng.integers(0, 256, size=(R, C // 2), dtype=np.uint8)
+    # scale magnitudes (bf16 bits): ordinary, full-mantissa, smallest normal and subnormal,
+    # tiny subnormals, huge, zero; the sign bit is the selector
+    mags = np.array([0x3F80, 0x3FFF, 0x3C0F, 0x0080, 0x0001, 0x0013, 0x0101, 0x7F7F, 0x7E81, 0x0000,
+                     0x3A55, 0x4123], np.uint16)
+    scales = mags[rng.integers(0, len(mags), size=R * C // g)] | (
+        rng.integers(0, 2, size=R * C // g).astype(np.uint16) << 15)
+    tables = np.array([[0x3F80, 0xBF80, 0x0000, 0x8000, 0x3FFF, 0xBFFF, 0x3F81, 0x0080,
+                        0x0001, 0x8013, 0x7F7F, 0x3E55, 0xBD2B, 0x4001, 0x3F01, 0x0100],
+                       [0x3FC1, 0xBFC3, 0x3C81, 0x3AFF, 0x0081, 0x8001, 0x4780, 0xC2AB,
+                        0x3F7F, 0x3FC0, 0x3FA0, 0xBE81, 0x0000, 0x3F03, 0x3F05, 0x7F00]], np.uint16)
+    want = ref.dequant(codes, scales, None, tables, R, C, g, S)
+    # the crafted values reach every case the kernel treats apart
+    prod = ref.decoded_weights(codes, scales, None, tables, R, C, g, S)
+    tiny = (np.abs(prod) < 2.0 ** -126) & (prod != 0)
+    assert tiny.any() and np.isinf(want).any() and (want == 0).any()
+    assert (np.abs(prod[tiny]) < 2.0 ** -134).any()
+    ties = (prod != 0) & np.isfinite(prod) & (np.abs(prod) >= 2.0 ** -126)
+    _, e = np.frexp(np.abs(prod[ties]))          # |p| in [2^(e-1), 2^e): bf16 quantum 2^(e-8)
+    halves = np.abs(prod[ties]) / np.ldexp(1.0, e - 9)
+    assert ((halves == np.floor(halves)) & (halves % 2 == 1)).any()   # exactly half a quantum off
+    W_hat = torch.empty(R, C, dtype=torch.bfloat16, device=DEV)
+    L.aaac_dequant(torch.from_numpy(codes.reshape(-1)).to(DEV),
+                   torch.from_numpy(scales.view(np.int16)).to(DEV), None,
+                   torch.from_numpy(tables.reshape(-1).view(np.int16)).to(DEV), R, C, g, S, n, W_hat)
+    torch.cuda.synchronize()
+    got = ref.bits_to_float(_np(W_hat.view(torch.int16)).view(np.uint16))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
 # ------------------------------------------------------------------ batch / determinism
 
 def test_batch_equals_single_calls_and_is_deterministic():
