@@ -5,7 +5,8 @@ calibration activations at their real token count, streamed in chunks), runs the
 bench.py does (batched assign and refine over all matrices of the layer), and checks against the
 oracle what it can compute at that size:
   - importance on sampled columns (all tokens);
-  - init tables, bit-exact, on the smallest and one large matrix;
+  - init tables (one batched call over the layer, as the benchmark runs it), bit-exact, on the
+    smallest and one large matrix, and equal to the single-matrix call;
   - assign on sampled rows of every matrix, at the first and the last iteration;
   - refine tables of two matrices from full-matrix sums (the GPU's codes and selectors as data);
   - pack and dequant on sampled rows of every matrix after the final assign.
@@ -100,13 +101,17 @@ def _run_layer(cfg_id, layer, init_check, refine_check):
     W64s = [par.to_np64(W) for W in Ws]
     Is64 = [par.to_np64(I) for I in Is]
 
-    ws_init = L.workspace(max(L.workspace_bytes(L.OP_INIT, R, C, g, S, n)
-                              for R, C in zip(Rs, Cs)), DEV)
     ws_r = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), DEV)
     tabs = [torch.empty(2 * n, dtype=torch.float32, device=DEV) for _ in mats]
-    for i, W in enumerate(Ws):
-        L.aaac_init_quantiles(W, g, n, tabs[i], ws_init)
+    # init as the benchmark runs it: one batched call over the layer's matrices (at most 8)
+    assert len(mats) <= 8
+    ws_init = L.workspace(L.batch_workspace_bytes(L.OP_INIT, Rs, Cs, g, 8, n), DEV)
+    L.aaac_init_quantiles_batch(Ws, g, n, tabs, ws_init)
+    # and the single call on the first checked matrix, bit for bit the same
+    single = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(Ws[init_check[0]], g, n, single)
     torch.cuda.synchronize()
+    assert torch.equal(single, tabs[init_check[0]])
     for i in init_check:
         T0, T1 = ref.init_tables(W64s[i], g, n)
         want = np.concatenate([T0, T1]).astype(np.float32)

@@ -154,6 +154,36 @@ def test_init_quantiles_zero_groups_and_ties():
     assert np.array_equal(_np(tables), np.concatenate([T0, T1]).astype(np.float32))
 
 
+def test_init_quantiles_extreme_scales():
+    """Groups at the edges of fp32 quotients: bf16-subnormal scales, scales of 2^126 and 2^127,
+    weights 2^-120 under a group maximum of 2^10 (subnormal quotients), a lone smallest
+    subnormal, tiny weights with normal quotients; the tables are the oracle's bit for bit."""
+    _say("init extreme scales")
+    R, C, g, n = 64, 512, 128, 16
+    W = syn.make_weight(R, C, 31, "cpu").float()
+    for r, top in ((0, 1e-38), (1, 2.0 ** 127), (2, 2.0 ** 126)):
+        W[r, :g] = W[r, :g] / W[r, :g].abs().max() * top  # scales 1e-38 (subnormal), 2^127, 2^126
+    W[3, :g] = 2.0 ** -120
+    W[3, 0] = 2.0 ** 10                                 # quotients 2^-130: subnormal
+    W[4, :g] = 0
+    W[4, 5] = -(2.0 ** -133)                            # smallest bf16 subnormal, alone
+    W[5, g:2 * g] *= 2.0 ** -100                        # tiny weights, normal quotients
+    Wb = W.to(torch.bfloat16).to(DEV)
+    tables = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(Wb, g, n, tables)
+    torch.cuda.synchronize()
+    T0, T1 = ref.init_tables(par.to_np64(Wb), g, n)
+    want = np.concatenate([T0, T1]).astype(np.float32)
+    assert np.array_equal(_np(tables), want), (_np(tables), want)
+    # the same groups drawn on as targets: one matrix of only the extreme rows
+    Wx = Wb[:6].contiguous()
+    tx = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(Wx, g, n, tx)
+    torch.cuda.synchronize()
+    T0, T1 = ref.init_tables(par.to_np64(Wx), g, n)
+    assert np.array_equal(_np(tx), np.concatenate([T0, T1]).astype(np.float32))
+
+
 def test_init_batch_equals_single_calls():
     """One batched init equals the per-matrix calls bit for bit; the same workspace then serves a
     smaller batch of other sizes (every call leaves the histogram headers zero)."""
