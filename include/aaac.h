@@ -216,7 +216,7 @@ size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int
                                   int S, int n);
 
 /*
- * Init for up to AAAC_MAX_BATCH matrices sharing g and n, in one set of launches (8 in all, not 8
+ * Init for up to AAAC_MAX_BATCH matrices sharing g and n, in one set of launches (6 in all, not 6
  * per matrix): tables[i] as aaac_init_quantiles gives for matrix i, bit for bit. The workspace
  * holds aaac_batch_workspace_bytes(AAAC_OP_INIT, count, R, C, g, 8, n) bytes (fixed headers of
  * histograms, then the keys of every matrix), zero-filled before its first use; every call leaves
