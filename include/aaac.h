@@ -158,6 +158,24 @@ aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uin
                          uint16_t* W_hat, void* stream);
 
 /*
+ * Pack and dequantize up to AAAC_MAX_BATCH matrices that share g, S and n, in one set of launches
+ * (pack: 1, or 2 with bitmaps; dequant: 1): every output as aaac_pack / aaac_dequant give for
+ * matrix i, bit for bit. Arrays of count per-matrix arguments, laid out and owned as in the
+ * single calls; bitmap may be NULL when S == g (else it and every bitmap[i] must be given).
+ * Errors: AAAC_ERR_INVALID_ARG for count outside [1, AAAC_MAX_BATCH], a null array, or any matrix
+ * the single call would reject (nothing is launched then).
+ */
+aaac_status aaac_pack_batch(int count, const uint16_t* const* W, const int64_t* R,
+                            const int64_t* C, int g, int S, int n, const uint8_t* const* sel,
+                            const float* const* tables, uint16_t* const* scales,
+                            uint8_t* const* bitmap, uint16_t* const* tables_bf16, void* stream);
+aaac_status aaac_dequant_batch(int count, const uint8_t* const* codes,
+                               const uint16_t* const* scales, const uint8_t* const* bitmap,
+                               const uint16_t* const* tables_bf16, const int64_t* R,
+                               const int64_t* C, int g, int S, int n, uint16_t* const* W_hat,
+                               void* stream);
+
+/*
  * Decode GEMV on the packed format, AAAC summary §1 (4-bit weights with 16-bit activations, W4A16;
  * the dequantized values are the weights inference uses) and §2 mechanism 3 (the stored format):
  *   y[b, r] = sum_c |s(r, c)| * T~_sel(r, c)[q(r, c)] * x[b, c]      for b < B

@@ -32,6 +32,7 @@ EXPORTED = (
     "aaac_init_quantiles", "aaac_assign", "aaac_refine", "aaac_pack", "aaac_dequant",
     "aaac_batch_workspace_bytes", "aaac_assign_batch", "aaac_refine_batch", "aaac_awq_prescale",
     "aaac_gemv", "aaac_gemv_batch", "aaac_assign_refine_batch", "aaac_init_quantiles_batch",
+    "aaac_pack_batch", "aaac_dequant_batch",
 )
 
 
@@ -79,6 +80,10 @@ def load(path: str = LIB_PATH):
                                  c_vp]),
         "aaac_init_quantiles_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
                                               P(c_vp), c_vp, c_size, c_vp]),
+        "aaac_pack_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
+                                    P(c_vp), P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp]),
+        "aaac_dequant_batch": (c_int, [c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), P(c_i64),
+                                       P(c_i64), c_int, c_int, c_int, P(c_vp), c_vp]),
         "aaac_assign_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
                                       P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp]),
         "aaac_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
@@ -256,6 +261,59 @@ def aaac_dequant(codes: torch.Tensor, scales: torch.Tensor, bitmap: Optional[tor
     st = lib.aaac_dequant(_ptr(codes), _ptr(scales), _ptr(bitmap), _ptr(tables_bf16), R, C, g, S,
                           n, _ptr(W_hat), _stream(stream))
     _check(st, "aaac_dequant")
+
+
+def aaac_pack_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
+                    sels: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
+                    scales: Sequence[torch.Tensor], bitmaps: Optional[Sequence[torch.Tensor]],
+                    tables_bf16: Sequence[torch.Tensor], stream=None):
+    """aaac_pack for up to MAX_BATCH matrices in one set of launches (see aaac.h); bitmaps is None
+    when S == g."""
+    lib = load()
+    k = len(Ws)
+    Rs = [W.shape[0] for W in Ws]
+    Cs = [W.shape[1] for W in Ws]
+    for i in range(k):
+        R, C = Rs[i], Cs[i]
+        _need(Ws[i], "W[%d]" % i, torch.bfloat16)
+        _need(sels[i], "sel[%d]" % i, torch.uint8, R * C // S)
+        _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
+        _need(scales[i], "scales[%d]" % i, torch.int16, R * C // g)
+        _need(tables_bf16[i], "tables_bf16[%d]" % i, torch.int16, 2 * n)
+        if bitmaps is not None:
+            _need(bitmaps[i], "bitmap[%d]" % i, torch.uint8, (R * C // S + 7) // 8)
+    st = lib.aaac_pack_batch(
+        k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
+        _arr(c_vp, [t.data_ptr() for t in sels]), _arr(c_vp, [t.data_ptr() for t in tables]),
+        _arr(c_vp, [t.data_ptr() for t in scales]),
+        None if bitmaps is None else _arr(c_vp, [t.data_ptr() for t in bitmaps]),
+        _arr(c_vp, [t.data_ptr() for t in tables_bf16]), _stream(stream))
+    _check(st, "aaac_pack_batch")
+
+
+def aaac_dequant_batch(codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor],
+                       bitmaps: Optional[Sequence[torch.Tensor]],
+                       tables_bf16: Sequence[torch.Tensor], Rs: Sequence[int], Cs: Sequence[int],
+                       g: int, S: int, n: int, W_hats: Sequence[torch.Tensor], stream=None):
+    """aaac_dequant for up to MAX_BATCH matrices in one launch (see aaac.h); bitmaps is None when
+    S == g."""
+    lib = load()
+    k = len(codes)
+    for i in range(k):
+        R, C = Rs[i], Cs[i]
+        _need(codes[i], "codes[%d]" % i, torch.uint8, R * C // 2)
+        _need(scales[i], "scales[%d]" % i, torch.int16, R * C // g)
+        _need(tables_bf16[i], "tables_bf16[%d]" % i, torch.int16, 2 * n)
+        _need(W_hats[i], "W_hat[%d]" % i, torch.bfloat16, R * C)
+        if bitmaps is not None:
+            _need(bitmaps[i], "bitmap[%d]" % i, torch.uint8, (R * C // S + 7) // 8)
+    st = lib.aaac_dequant_batch(
+        k, _arr(c_vp, [t.data_ptr() for t in codes]), _arr(c_vp, [t.data_ptr() for t in scales]),
+        None if bitmaps is None else _arr(c_vp, [t.data_ptr() for t in bitmaps]),
+        _arr(c_vp, [t.data_ptr() for t in tables_bf16]), _arr(c_i64, list(Rs)),
+        _arr(c_i64, list(Cs)), g, S, n, _arr(c_vp, [t.data_ptr() for t in W_hats]),
+        _stream(stream))
+    _check(st, "aaac_dequant_batch")
 
 
 def _arr(ctype, values):

@@ -285,6 +285,53 @@ aaac_status do_init(int count, const uint16_t* const* W, const int64_t* R, const
                     who);
 }
 
+
+aaac_status do_pack(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C, int g,
+                    int S, int n, const uint8_t* const* sel, const float* const* tables,
+                    uint16_t* const* scales, uint8_t* const* bitmap, uint16_t* const* tables_bf16,
+                    void* stream, const char* who) {
+  if (count < 1 || count > AAAC_MAX_BATCH)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: count %d outside [1, %d]", who, count, AAAC_MAX_BATCH);
+  if (!W || !R || !C || !sel || !tables || !scales || !tables_bf16)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    aaac_status st = check_shape(R[i], C[i], g, S, n, true, who);
+    if (st != AAAC_OK) return st;
+    if (!W[i] || !aligned(W[i], 16) || !sel[i] || !tables[i] || !aligned(tables[i], 4) ||
+        !scales[i] || !aligned(scales[i], 2) || !tables_bf16[i] || !aligned(tables_bf16[i], 2))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer (matrix %d)", who, i);
+    const uint8_t* bm = bitmap ? bitmap[i] : nullptr;
+    if ((S < g) != (bm != nullptr))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: bitmap must be given exactly when S < g", who);
+  }
+  return hip_status(launch_pack(count, W, R, C, g, S, n, sel, tables, scales, bitmap, tables_bf16,
+                                static_cast<hipStream_t>(stream)),
+                    who);
+}
+
+aaac_status do_dequant(int count, const uint8_t* const* codes, const uint16_t* const* scales,
+                       const uint8_t* const* bitmap, const uint16_t* const* tables_bf16,
+                       const int64_t* R, const int64_t* C, int g, int S, int n,
+                       uint16_t* const* W_hat, void* stream, const char* who) {
+  if (count < 1 || count > AAAC_MAX_BATCH)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: count %d outside [1, %d]", who, count, AAAC_MAX_BATCH);
+  if (!codes || !scales || !tables_bf16 || !R || !C || !W_hat)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  for (int i = 0; i < count; ++i) {
+    aaac_status st = check_shape(R[i], C[i], g, S, n, true, who);
+    if (st != AAAC_OK) return st;
+    if (!codes[i] || !aligned(codes[i], 4) || !scales[i] || !aligned(scales[i], 2) ||
+        !tables_bf16[i] || !aligned(tables_bf16[i], 2) || !W_hat[i] || !aligned(W_hat[i], 16))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer (matrix %d)", who, i);
+    const uint8_t* bm = bitmap ? bitmap[i] : nullptr;
+    if ((S < g) != (bm != nullptr))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: bitmap must be given exactly when S < g", who);
+  }
+  return hip_status(launch_dequant(count, codes, scales, bitmap, tables_bf16, R, C, g, S, n,
+                                   W_hat, static_cast<hipStream_t>(stream)),
+                    who);
+}
+
 }  // namespace
 
 extern "C" {
@@ -403,33 +450,34 @@ aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t
 aaac_status aaac_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                       const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
                       uint16_t* tables_bf16, void* stream) {
-  const char* who = "aaac_pack";
-  aaac_status st = check_shape(R, C, g, S, n, true, who);
-  if (st != AAAC_OK) return st;
-  if (!W || !aligned(W, 16) || !sel || !tables || !aligned(tables, 4) || !scales ||
-      !aligned(scales, 2) || !tables_bf16 || !aligned(tables_bf16, 2))
-    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
-  if ((S < g) != (bitmap != nullptr))
-    return fail(AAAC_ERR_INVALID_ARG, "%s: bitmap must be given exactly when S < g", who);
-  return hip_status(launch_pack(W, R, C, g, S, n, sel, tables, scales, bitmap, tables_bf16,
-                                static_cast<hipStream_t>(stream)),
-                    who);
+  uint8_t* const bm[1] = {bitmap};
+  return do_pack(1, &W, &R, &C, g, S, n, &sel, &tables, &scales, bm, &tables_bf16, stream,
+                 "aaac_pack");
+}
+
+aaac_status aaac_pack_batch(int count, const uint16_t* const* W, const int64_t* R,
+                            const int64_t* C, int g, int S, int n, const uint8_t* const* sel,
+                            const float* const* tables, uint16_t* const* scales,
+                            uint8_t* const* bitmap, uint16_t* const* tables_bf16, void* stream) {
+  return do_pack(count, W, R, C, g, S, n, sel, tables, scales, bitmap, tables_bf16, stream,
+                 "aaac_pack_batch");
 }
 
 aaac_status aaac_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
                          const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
                          uint16_t* W_hat, void* stream) {
-  const char* who = "aaac_dequant";
-  aaac_status st = check_shape(R, C, g, S, n, true, who);
-  if (st != AAAC_OK) return st;
-  if (!codes || !aligned(codes, 4) || !scales || !aligned(scales, 2) || !tables_bf16 ||
-      !aligned(tables_bf16, 2) || !W_hat || !aligned(W_hat, 16))
-    return fail(AAAC_ERR_INVALID_ARG, "%s: null or misaligned pointer", who);
-  if ((S < g) != (bitmap != nullptr))
-    return fail(AAAC_ERR_INVALID_ARG, "%s: bitmap must be given exactly when S < g", who);
-  return hip_status(launch_dequant(codes, scales, bitmap, tables_bf16, R, C, g, S, n, W_hat,
-                                   static_cast<hipStream_t>(stream)),
-                    who);
+  const uint8_t* const bm[1] = {bitmap};
+  return do_dequant(1, &codes, &scales, bm, &tables_bf16, &R, &C, g, S, n, &W_hat, stream,
+                    "aaac_dequant");
+}
+
+aaac_status aaac_dequant_batch(int count, const uint8_t* const* codes,
+                               const uint16_t* const* scales, const uint8_t* const* bitmap,
+                               const uint16_t* const* tables_bf16, const int64_t* R,
+                               const int64_t* C, int g, int S, int n, uint16_t* const* W_hat,
+                               void* stream) {
+  return do_dequant(count, codes, scales, bitmap, tables_bf16, R, C, g, S, n, W_hat, stream,
+                    "aaac_dequant_batch");
 }
 
 aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const int64_t* R,

@@ -259,12 +259,14 @@ size_t init_workspace_bytes(int count, const int64_t* R, const int64_t* C);
 hipError_t launch_init(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
                        int g, int n, float* const* tables, void* ws, hipStream_t stream);
 
-hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
-                       const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
-                       uint16_t* tables_bf16, hipStream_t stream);
-hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
-                          const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
-                          uint16_t* W_hat, hipStream_t stream);
+hipError_t launch_pack(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                       int g, int S, int n, const uint8_t* const* sel, const float* const* tables,
+                       uint16_t* const* scales, uint8_t* const* bitmap,
+                       uint16_t* const* tables_bf16, hipStream_t stream);
+hipError_t launch_dequant(int count, const uint8_t* const* codes, const uint16_t* const* scales,
+                          const uint8_t* const* bitmap, const uint16_t* const* tables_bf16,
+                          const int64_t* R, const int64_t* C, int g, int S, int n,
+                          uint16_t* const* W_hat, hipStream_t stream);
 // Decode GEMV over up to kMaxJobs packed matrices that share g, S, n and the batch size B.
 struct GemvJob {
   const uint8_t* codes;      // [R, C / 2]

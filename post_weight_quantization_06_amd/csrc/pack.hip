@@ -9,26 +9,63 @@
 
 namespace aaac {
 
+// Up to kMaxJobs matrices that share g, S and n; a single call is a batch of one.
+struct PackJob {
+  const uint16_t* W;
+  MatrixGeom geom;              // task numbering shared by the batch (32 rows x 512 columns)
+  const uint8_t* sel;
+  uint16_t* scales;
+  uint8_t* bitmap;              // S < g, else null
+  const float* tables;
+  uint16_t* tables_bf16;
+  int64_t byte_begin;           // first bitmap byte (or table item) of this job, batch-wide
+  int64_t nbytes;               // bitmap bytes of this job (0 when S == g)
+};
+
+struct PackBatch {
+  PackJob job[kMaxJobs];
+  int njobs, g, S, n;
+  int64_t total_tasks, total_items;
+};
+
+constexpr int kDequantSteps = 4;
+constexpr int64_t kDequantTaskVecs = (int64_t)kBlock * kDequantSteps;
+
+struct DequantJob {
+  const uint32_t* codes;        // one word per 8 weights
+  const uint16_t* scales;
+  const uint8_t* bitmap;        // S < g, else null
+  const uint16_t* tables_bf16;
+  uint4* out;                   // 8 bf16 per vector
+  int64_t task_begin;           // first task (kDequantTaskVecs vectors) of this job, batch-wide
+  int64_t nvec;
+};
+
+struct DequantBatch {
+  DequantJob job[kMaxJobs];
+  int njobs, g, S, n;
+  int64_t total_tasks;
+};
+
 // The scale word of every scale group: lane mapping of the 8-weight assign (a lane holds 8
-// consecutive weights of a row, a group spans g / 8 lanes). The rows of a task are all loaded first
-// (unconditional loads at clamped in-bounds addresses), so a wave keeps eight rows in flight.
-__global__ __launch_bounds__(kBlock) void pack_scales_kernel(const uint16_t* __restrict__ W,
-                                                             MatrixGeom geom, int g, int S,
-                                                             const uint8_t* __restrict__ sel,
-                                                             uint16_t* __restrict__ scales,
-                                                             const float* __restrict__ tables,
-                                                             int n,
-                                                             uint16_t* __restrict__ tables_bf16) {
+// consecutive weights of a row, a group spans g / 8 lanes). One workgroup per task; the rows of a
+// task are all loaded first (unconditional loads at clamped in-bounds addresses), so a wave keeps
+// eight rows in flight. With the selector in the sign bit (S == g) the first workgroup of each
+// matrix also converts its tables; with a bitmap the bits kernel does.
+__global__ __launch_bounds__(kBlock) void pack_scales_kernel(PackBatch b) {
   const int tid = threadIdx.x;
-  // the tables, when no bitmap kernel follows to convert them
-  if (tables_bf16 != nullptr && blockIdx.x == 0 && tid < 2 * n)
-    tables_bf16[tid] = (uint16_t)f32_to_bf16_rne(tables[tid]);
-  const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = g / kPerLane;
-  const int log2g = 31 - __builtin_clz((unsigned)g), log2S = 31 - __builtin_clz((unsigned)S);
-  const int64_t R = geom.R, C = geom.C;
-  for (int64_t task = blockIdx.x; task < geom.ntasks; task += gridDim.x) {
-    const int64_t rb = task / geom.nslab;
-    const int slab = (int)(task - rb * geom.nslab);
+  const int lane = tid & (kWave - 1), wave = tid / kWave, g8 = b.g / kPerLane;
+  const int log2g = 31 - __builtin_clz((unsigned)b.g), log2S = 31 - __builtin_clz((unsigned)b.S);
+  for (int64_t task = blockIdx.x; task < b.total_tasks; task += gridDim.x) {
+    int j = 0;
+    while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
+    const PackJob& jb = b.job[j];
+    if (jb.bitmap == nullptr && task == jb.geom.task_begin && tid < 2 * b.n)
+      jb.tables_bf16[tid] = (uint16_t)f32_to_bf16_rne(jb.tables[tid]);
+    const int64_t R = jb.geom.R, C = jb.geom.C;
+    const int64_t local = task - jb.geom.task_begin;
+    const int64_t rb = local / jb.geom.nslab;
+    const int slab = (int)(local - rb * jb.geom.nslab);
     const int c0 = slab * kSlab + lane * kPerLane;
     const bool active = c0 < C;
     const int cl = active ? c0 : 0;
@@ -38,7 +75,7 @@ __global__ __launch_bounds__(kBlock) void pack_scales_kernel(const uint16_t* __r
     for (int i = 0; i < kRowsPerWave; ++i) {
       int64_t r = r0 + (int64_t)kWavesPerBlock * i;
       r = r < R ? r : R - 1;
-      v[i] = *reinterpret_cast<const uint4*>(W + r * C + cl);
+      v[i] = *reinterpret_cast<const uint4*>(jb.W + r * C + cl);
     }
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
@@ -48,53 +85,31 @@ __global__ __launch_bounds__(kBlock) void pack_scales_kernel(const uint16_t* __r
       if (active && ((c0 >> 3) & (g8 - 1)) == 0) {
         const int64_t base = r * C + c0;
         uint32_t word = amax;
-        if (S == g) word |= (sel[base >> log2S] ? 1u : 0u) << 15;
-        scales[base >> log2g] = (uint16_t)word;
+        if (b.S == b.g) word |= (jb.sel[base >> log2S] ? 1u : 0u) << 15;
+        jb.scales[base >> log2g] = (uint16_t)word;
       }
     }
   }
 }
 
-__global__ __launch_bounds__(kBlock) void pack_bits_kernel(const uint8_t* __restrict__ sel,
-                                                           int64_t ngroups,
-                                                           uint8_t* __restrict__ bitmap,
-                                                           const float* __restrict__ tables,
-                                                           int n, uint16_t* __restrict__ tables_bf16) {
+// S < g: the selector bitmap, one byte (8 selection groups) per thread over the batch's bytes,
+// and the tables (the first 2n items of each matrix).
+__global__ __launch_bounds__(kBlock) void pack_bits_kernel(PackBatch b) {
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i < 2 * n) tables_bf16[i] = (uint16_t)f32_to_bf16_rne(tables[i]);
-  if (bitmap == nullptr) return;
-  const int64_t nbytes = (ngroups + 7) / 8;
-  if (i >= nbytes) return;
-  uint32_t b = 0;
+  if (i >= b.total_items) return;
+  int j = 0;
+  while (j + 1 < b.njobs && i >= b.job[j + 1].byte_begin) ++j;
+  const PackJob& jb = b.job[j];
+  const int64_t local = i - jb.byte_begin;
+  if (local < 2 * b.n) jb.tables_bf16[local] = (uint16_t)f32_to_bf16_rne(jb.tables[local]);
+  if (local >= jb.nbytes) return;
+  const int64_t ngroups = jb.geom.R * jb.geom.C / b.S;
+  uint32_t bits = 0;
   for (int k = 0; k < 8; ++k) {
-    const int64_t h = i * 8 + k;
-    if (h < ngroups && sel[h]) b |= 1u << k;
+    const int64_t h = local * 8 + k;
+    if (h < ngroups && jb.sel[h]) bits |= 1u << k;
   }
-  bitmap[i] = (uint8_t)b;
-}
-
-hipError_t launch_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
-                       const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
-                       uint16_t* tables_bf16, hipStream_t stream) {
-  const MatrixGeom geom = make_geom(R, C, 0);
-  // one task per workgroup (up to 2^20, then a grid-stride loop): the dispatcher balances the
-  // tail, where a grid of a few workgroups per CU looping over the tasks left its last round
-  // partly empty
-  const int64_t want = 1 << 20;
-  const int grid = (int)(geom.ntasks < want ? geom.ntasks : want);
-  // with the selection bit in the scale's sign there is no bitmap, and the scales kernel converts
-  // the tables itself: one launch instead of two
-  const bool bits = S < g;
-  hipLaunchKernelGGL(pack_scales_kernel, dim3(grid), dim3(kBlock), 0, stream, W, geom, g, S, sel,
-                     scales, tables, n, bits ? nullptr : tables_bf16);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !bits) return e;
-  const int64_t ngroups = R * C / S;
-  int64_t items = (ngroups + 7) / 8;
-  if (items < 2 * n) items = 2 * n;
-  hipLaunchKernelGGL(pack_bits_kernel, dim3((unsigned)((items + kBlock - 1) / kBlock)),
-                     dim3(kBlock), 0, stream, sel, ngroups, bitmap, tables, n, tables_bf16);
-  return hipGetLastError();
+  jb.bitmap[local] = (uint8_t)bits;
 }
 
 // Two finite fp32 values rounded to bf16 (ties to even) and packed, lo in the low half: one
@@ -118,40 +133,46 @@ __device__ __forceinline__ uint32_t f64_to_bf16_bits(double x) {
   return bits;
 }
 
-// A thread dequantizes 8 weights (one code word) per step, four steps with their loads in flight.
-__global__ __launch_bounds__(kBlock) void dequant_kernel(const uint32_t* __restrict__ codes,
-                                                         const uint16_t* __restrict__ scales,
-                                                         const uint8_t* __restrict__ bitmap,
-                                                         const uint16_t* __restrict__ tables_bf16,
-                                                         int64_t R, int64_t C, int g, int S, int n,
-                                                         uint4* __restrict__ out) {
+// A thread dequantizes 8 weights (one code word) per step, four steps with their loads in flight;
+// a workgroup takes tasks of 1024 vectors of one matrix, so the matrix's fields are uniform and
+// every step reads 256 consecutive code words and writes 4 KB in one piece.
+__global__ __launch_bounds__(kBlock) void dequant_kernel(DequantBatch b) {
   __shared__ float tab[2][16];
-  if (threadIdx.x < 2 * n)
-    tab[threadIdx.x / n][threadIdx.x % n] = __uint_as_float((uint32_t)tables_bf16[threadIdx.x] << 16);
-  __syncthreads();
-  const int log2g = 31 - __builtin_clz((unsigned)g), log2S = 31 - __builtin_clz((unsigned)S);
-  const int64_t nvec = R * C / 8;
-  const int64_t stride = (int64_t)gridDim.x * kBlock;
-  constexpr int kSteps = 4;
-  for (int64_t i0 = (int64_t)blockIdx.x * kBlock + threadIdx.x; i0 < nvec; i0 += kSteps * stride) {
-    uint32_t cw[kSteps], word[kSteps], sg[kSteps];
+  const int n = b.n;
+  const int log2g = 31 - __builtin_clz((unsigned)b.g), log2S = 31 - __builtin_clz((unsigned)b.S);
+  int cur = -1;
+  for (int64_t task = blockIdx.x; task < b.total_tasks; task += gridDim.x) {
+    int j = 0;
+    while (j + 1 < b.njobs && task >= b.job[j + 1].task_begin) ++j;
+    const DequantJob& jb = b.job[j];
+    if (j != cur) {
+      __syncthreads();
+      if (threadIdx.x < 2 * n)
+        tab[threadIdx.x / n][threadIdx.x % n] =
+            __uint_as_float((uint32_t)jb.tables_bf16[threadIdx.x] << 16);
+      __syncthreads();
+      cur = j;
+    }
+    const int64_t nvec = jb.nvec;
+    const int64_t i0 = (task - jb.task_begin) * kDequantTaskVecs + threadIdx.x;
+    uint32_t cw[kDequantSteps], word[kDequantSteps], sg[kDequantSteps];
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-      int64_t i = i0 + u * stride;
+    for (int u = 0; u < kDequantSteps; ++u) {
+      int64_t i = i0 + (int64_t)u * kBlock;
       i = i < nvec ? i : nvec - 1;                    // in bounds; the result is not stored
       const int64_t base = i * 8;
-      cw[u] = codes[i];
-      word[u] = scales[base >> log2g];
-      if (bitmap == nullptr) {
+      cw[u] = jb.codes[i];
+      word[u] = jb.scales[base >> log2g];
+      if (jb.bitmap == nullptr) {
         sg[u] = word[u] >> 15;
       } else {
         const int64_t h = base >> log2S;
-        sg[u] = (bitmap[h >> 3] >> (h & 7)) & 1u;
+        sg[u] = (jb.bitmap[h >> 3] >> (h & 7)) & 1u;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kSteps; ++u) {
-      const int64_t i = i0 + u * stride;
+    for (int u = 0; u < kDequantSteps; ++u) {
+      const int64_t i = i0 + (int64_t)u * kBlock;
       if (i >= nvec) break;
       const float s = __uint_as_float((word[u] & 0x7fffu) << 16);
       float t[8], p[8];
@@ -172,28 +193,85 @@ __global__ __launch_bounds__(kBlock) void dequant_kernel(const uint32_t* __restr
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           if (fabsf(p[k]) < 0x1p-126f && s != 0.0f && t[k] != 0.0f) {
-            const uint32_t b = f64_to_bf16_bits((double)s * (double)t[k]);
+            const uint32_t bits = f64_to_bf16_bits((double)s * (double)t[k]);
             const int sh = 16 * (k & 1);
-            o[k >> 1] = (o[k >> 1] & ~(0xffffu << sh)) | (b << sh);
+            o[k >> 1] = (o[k >> 1] & ~(0xffffu << sh)) | (bits << sh);
           }
         }
       }
-      out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+      jb.out[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
 
-hipError_t launch_dequant(const uint8_t* codes, const uint16_t* scales, const uint8_t* bitmap,
-                          const uint16_t* tables_bf16, int64_t R, int64_t C, int g, int S, int n,
-                          uint16_t* W_hat, hipStream_t stream) {
-  const int64_t nvec = R * C / 8;
-  int64_t grid = (nvec + kBlock - 1) / kBlock;
+hipError_t launch_pack(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                       int g, int S, int n, const uint8_t* const* sel, const float* const* tables,
+                       uint16_t* const* scales, uint8_t* const* bitmap,
+                       uint16_t* const* tables_bf16, hipStream_t stream) {
+  PackBatch b{};
+  b.njobs = count;
+  b.g = g;
+  b.S = S;
+  b.n = n;
+  const bool bits = S < g;
+  int64_t tb = 0, items = 0;
+  for (int i = 0; i < count; ++i) {
+    PackJob& j = b.job[i];
+    j.W = W[i];
+    j.geom = make_geom(R[i], C[i], tb);
+    tb += j.geom.ntasks;
+    j.sel = sel[i];
+    j.scales = scales[i];
+    j.bitmap = bits ? bitmap[i] : nullptr;
+    j.tables = tables[i];
+    j.tables_bf16 = tables_bf16[i];
+    j.nbytes = bits ? (R[i] * C[i] / S + 7) / 8 : 0;
+    j.byte_begin = items;
+    items += j.nbytes > 2 * n ? j.nbytes : 2 * n;
+  }
+  b.total_tasks = tb;
+  b.total_items = items;
+  // one task per workgroup (up to 2^20, then a grid-stride loop): the dispatcher balances the
+  // tail, where a grid of a few workgroups per CU looping over the tasks left its last round
+  // partly empty
+  const int64_t want = 1 << 20;
+  const int grid = (int)(tb < want ? tb : want);
+  hipLaunchKernelGGL(pack_scales_kernel, dim3(grid > 0 ? grid : 1), dim3(kBlock), 0, stream, b);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !bits) return e;
+  hipLaunchKernelGGL(pack_bits_kernel, dim3((unsigned)((items + kBlock - 1) / kBlock)),
+                     dim3(kBlock), 0, stream, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(int count, const uint8_t* const* codes, const uint16_t* const* scales,
+                          const uint8_t* const* bitmap, const uint16_t* const* tables_bf16,
+                          const int64_t* R, const int64_t* C, int g, int S, int n,
+                          uint16_t* const* W_hat, hipStream_t stream) {
+  DequantBatch b{};
+  b.njobs = count;
+  b.g = g;
+  b.S = S;
+  b.n = n;
+  int64_t tasks = 0;
+  for (int i = 0; i < count; ++i) {
+    DequantJob& j = b.job[i];
+    j.codes = reinterpret_cast<const uint32_t*>(codes[i]);
+    j.scales = scales[i];
+    j.bitmap = S < g ? bitmap[i] : nullptr;
+    j.tables_bf16 = tables_bf16[i];
+    j.out = reinterpret_cast<uint4*>(W_hat[i]);
+    j.task_begin = tasks;
+    j.nvec = R[i] * C[i] / 8;
+    tasks += (j.nvec + kDequantTaskVecs - 1) / kDequantTaskVecs;
+  }
+  b.total_tasks = tasks;
+  // up to 8 workgroups per CU walking the tasks: a workgroup per task paid its table load and
+  // barriers for every 1024 vectors
   const int64_t cap = (int64_t)device_cu_count() * 8;
-  if (grid > cap) grid = cap;
+  int64_t grid = tasks < cap ? tasks : cap;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream,
-                     reinterpret_cast<const uint32_t*>(codes), scales, S < g ? bitmap : nullptr,
-                     tables_bf16, R, C, g, S, n, reinterpret_cast<uint4*>(W_hat));
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream, b);
   return hipGetLastError();
 }
 

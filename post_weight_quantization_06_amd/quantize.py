@@ -117,17 +117,22 @@ def quantize_matrices(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], g:
     for b0, group in _batches(list(range(k))):
         sl = slice(b0, b0 + len(group))
         L.aaac_assign_batch(Ws[sl], g, S, n, Is[sl], tabs[sl], codes[sl], sels[sl])
+    scales = [torch.empty(R * C // g, dtype=torch.int16, device=dev) for R, C in zip(Rs, Cs)]
+    bitmaps = ([torch.empty((R * C // S + 7) // 8, dtype=torch.uint8, device=dev)
+                for R, C in zip(Rs, Cs)] if S < g else None)
+    tbs = [torch.empty(2 * n, dtype=torch.int16, device=dev) for _ in range(k)]
+    for b0, group in _batches(list(range(k))):
+        sl = slice(b0, b0 + len(group))
+        L.aaac_pack_batch(Ws[sl], g, S, n, sels[sl], tabs[sl], scales[sl],
+                          bitmaps[sl] if bitmaps is not None else None, tbs[sl])
     out = []
     for i in range(k):
         R, C = Rs[i], Cs[i]
-        scales = torch.empty(R * C // g, dtype=torch.int16, device=dev)
-        bitmap = (torch.empty((R * C // S + 7) // 8, dtype=torch.uint8, device=dev)
-                  if S < g else None)
-        tb = torch.empty(2 * n, dtype=torch.int16, device=dev)
-        L.aaac_pack(Ws[i], g, S, n, sels[i], tabs[i], scales, bitmap, tb)
         out.append(QuantizedMatrix(R, C, g, S, n, codes[i].view(R, C // 2),
                                    sels[i].view(R, C // S), tabs[i].view(2, n),
-                                   scales.view(R, C // g), bitmap, tb.view(2, n)))
+                                   scales[i].view(R, C // g),
+                                   bitmaps[i] if bitmaps is not None else None,
+                                   tbs[i].view(2, n)))
     return out
 
 

@@ -41,7 +41,8 @@ def lib():
 def test_header_declares_the_six_operations_and_the_batch_calls():
     names = declared_functions()
     for op in ("importance", "init_quantiles", "assign", "refine", "pack", "dequant",
-               "init_quantiles_batch", "assign_batch", "refine_batch"):
+               "init_quantiles_batch", "assign_batch", "refine_batch", "pack_batch",
+               "dequant_batch"):
         assert "aaac_" + op in names
 
 
@@ -188,3 +189,25 @@ def test_init_batch_workspace_and_arguments(lib):
     assert f(1, P, R1, C1, 128, 17, P, FAKE, ctypes.c_size_t(one), None) == SHAPE
     bad = (ctypes.c_void_p * 1)((1 << 20) + 2)
     assert f(1, bad, R1, C1, 128, 16, P, FAKE, ctypes.c_size_t(one), None) == INVALID
+
+
+def test_pack_and_dequant_batches_reject_bad_arguments(lib):
+    """Argument checks of the batched pack and dequant run on the host: nothing is launched."""
+    R1 = (i64 * 1)(64)
+    C1 = (i64 * 1)(1024)
+    P = (ctypes.c_void_p * 1)(FAKE)
+    bad = (ctypes.c_void_p * 1)((1 << 20) + 2)
+    pk = lib.aaac_pack_batch
+    assert pk(0, P, R1, C1, 128, 128, 16, P, P, P, None, P, None) == INVALID      # count 0
+    assert pk(9, P, R1, C1, 128, 128, 16, P, P, P, None, P, None) == INVALID      # count > 8
+    assert pk(1, None, R1, C1, 128, 128, 16, P, P, P, None, P, None) == INVALID   # null array
+    assert pk(1, P, R1, C1, 128, 128, 16, P, P, P, P, P, None) == INVALID         # bitmap, S == g
+    assert pk(1, P, R1, C1, 128, 16, 16, P, P, P, None, P, None) == INVALID       # none, S < g
+    assert pk(1, bad, R1, C1, 128, 128, 16, P, P, P, None, P, None) == INVALID    # misaligned W
+    assert pk(1, P, R1, (i64 * 1)(1000), 128, 128, 16, P, P, P, None, P, None) == SHAPE
+    dq = lib.aaac_dequant_batch
+    assert dq(0, P, P, None, P, R1, C1, 128, 128, 16, P, None) == INVALID
+    assert dq(1, P, P, None, None, R1, C1, 128, 128, 16, P, None) == INVALID     # null tables
+    assert dq(1, P, P, None, P, R1, C1, 128, 16, 16, P, None) == INVALID         # S < g, no bitmap
+    assert dq(1, P, P, None, P, R1, C1, 128, 128, 16, bad, None) == INVALID      # misaligned out
+    assert dq(1, P, P, None, P, R1, C1, 128, 128, 17, P, None) == SHAPE

@@ -455,6 +455,50 @@ def test_pack_and_dequant_bit_exact(R, C, g, S, n):
         assert np.all(np.abs(_np(y).astype(np.float64) - y_ref) <= bound)
 
 
+def test_pack_and_dequant_batches_equal_single_calls():
+    """One batched pack and one batched dequant over matrices of several shapes give the single
+    calls' outputs bit for bit: selector in the scale sign bit, separate bitmaps, NVFP4-style
+    groups, ragged row counts and widths."""
+    for g, S, n, shapes in ((128, 128, 16, [(64, 1024), (33, 640), (7, 4096)]),
+                            (128, 16, 16, [(40, 1024), (3, 384), (96, 256)]),
+                            (16, 16, 15, [(40, 256), (5, 48), (1, 16)])):
+        _say("pack/dequant batch", g, S, n)
+        Ws = [_weight(R, C, 500 + R + C) for R, C in shapes]
+        Is = [_importance(C, 32, 600 + C)[2] for _, C in shapes]
+        Rs = [R for R, _ in shapes]
+        Cs = [C for _, C in shapes]
+        tabs = [torch.empty(2 * n, dtype=torch.float32, device=DEV) for _ in shapes]
+        L.aaac_init_quantiles_batch(Ws, g, n, tabs)
+        codes = [torch.empty(R * C // 2, dtype=torch.uint8, device=DEV) for R, C in shapes]
+        sels = [torch.empty(R * C // S, dtype=torch.uint8, device=DEV) for R, C in shapes]
+        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
+
+        def outputs():
+            sc = [torch.empty(R * C // g, dtype=torch.int16, device=DEV) for R, C in shapes]
+            bm = ([torch.empty((R * C // S + 7) // 8, dtype=torch.uint8, device=DEV)
+                   for R, C in shapes] if S < g else None)
+            tb = [torch.empty(2 * n, dtype=torch.int16, device=DEV) for _ in shapes]
+            wh = [torch.empty(R, C, dtype=torch.bfloat16, device=DEV) for R, C in shapes]
+            return sc, bm, tb, wh
+
+        one, many = outputs(), outputs()
+        for i in range(len(shapes)):
+            bmi = one[1][i] if S < g else None
+            L.aaac_pack(Ws[i], g, S, n, sels[i], tabs[i], one[0][i], bmi, one[2][i])
+            L.aaac_dequant(codes[i], one[0][i], bmi, one[2][i], Rs[i], Cs[i], g, S, n, one[3][i])
+        L.aaac_pack_batch(Ws, g, S, n, sels, tabs, many[0], many[1], many[2])
+        L.aaac_dequant_batch(codes, many[0], many[1], many[2], Rs, Cs, g, S, n, many[3])
+        torch.cuda.synchronize()
+        for k in (0, 1, 2, 3):
+            if one[k] is None:
+                continue
+            for i in range(len(shapes)):
+                a, b = one[k][i], many[k][i]
+                if a.dtype == torch.bfloat16:
+                    a, b = a.view(torch.int16), b.view(torch.int16)
+                assert torch.equal(a, b), (g, S, n, shapes[i], k)
+
+
 def test_dequant_rounding_edges():
     """Dequant of crafted packed inputs against the oracle, bit for bit: products whose 16
     significant bits tie at the bf16 rounding point, nonzero subnormal products, products below
