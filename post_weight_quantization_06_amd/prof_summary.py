@@ -64,7 +64,7 @@ def kernel_stats(raw, prof, out_md):
            "```\n%s\n```\n" % TRACE_CMD.format(raw=raw),
            "Source: `run_kernel_stats.csv`. One bench step runs importance on the 4 activation "
            "streams, a batched init of the 7 matrices, 10 x (batched assign, batched refine), a final batched "
-           "assign, then pack and dequant per matrix; 3 steps (1 warmup + 2 timed) are traced, then "
+           "assign, then one batched pack and one batched dequant; 3 steps (1 warmup + 2 timed) are traced, then "
            "the decode GEMV (9 launches) and the AWQ pre-scale (3 rounds of 7 launches) on the "
            "packed layer. Only this library's kernels are listed (input generation and copies "
            "omitted); \"per step\" is the total divided by 3.\n",
