@@ -120,12 +120,22 @@ __global__ __launch_bounds__(kBlock) void init_keys_kernel(InitBatch b) {
     const int slab = (int)(local - rb * jb.nslab);
     const int c0 = slab * kSlab + lane * kPerLane;
     const bool active = c0 < jb.C;
+    // all rows of the task loaded before any is used (clamped in-bounds rows; a lane past the
+    // last column holds zeros)
+    uint4 vr[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
+      r = r < jb.R ? r : jb.R - 1;
+      vr[i] = active ? *reinterpret_cast<const uint4*>(jb.W + r * jb.C + c0)
+                     : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int64_t r = rb * kRowsPerTask + wave + (int64_t)kWavesPerBlock * i;
-      if (r >= jb.R) break;
+      if (r >= jb.R) break;                              // the same for the whole wave
       const int64_t base = r * jb.C + c0;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (active) v = *reinterpret_cast<const uint4*>(jb.W + base);
+      const uint4 v = vr[i];
       const uint32_t amax = block_max_u32(lane_absmax_bits(v), g8);
       if (!active) continue;
       const float s = __uint_as_float(amax << 16);
