@@ -296,7 +296,7 @@ __global__ __launch_bounds__(kPassThreads) void init_pass_kernel(InitBatch b, in
 
 // One workgroup of 1024 threads per matrix (a target or two per wave): move every target one digit
 // down, rebuild the active prefix list, clear the histogram rows used; after the last step write
-// the tables. A wave finds its target's digit in two rounds over the row, which sits in L2 after
+// the tables. A wave finds its target's digit in two steps over the row, which sits in L2 after
 // the histogram kernel's atomics: lane l first sums digits [l P, (l + 1) P) (P = 64 or 16), an
 // inclusive scan over the wave and a ballot find the lane whose block holds the rank, then lane j
 // reads digit j of that block and a second scan and ballot find the digit.
@@ -326,7 +326,7 @@ constexpr int kPaddedTop = kTopDigits + kTopDigits / 32;
 template <int kPer>
 __device__ __forceinline__ DigitPick pick_digit(const unsigned long long* row, uint64_t rank,
                                                 int lane) {
-  // round 1: lane l sums digits [l kPer, (l + 1) kPer)
+  // first: lane l sums digits [l kPer, (l + 1) kPer)
   uint64_t mine = 0;
 #pragma unroll
   for (int k = 0; k < kPer; ++k) mine += row[padded(lane * kPer + k)];
@@ -335,7 +335,7 @@ __device__ __forceinline__ DigitPick pick_digit(const unsigned long long* row, u
   const unsigned long long hit = __ballot(rank < incl);
   const int owner = hit ? __builtin_ctzll(hit) : kWave - 1;
   const uint64_t base = (uint64_t)__shfl((unsigned long long)(incl - mine), owner);
-  // round 2: lane j < kPer takes digit j of the owner's block
+  // then: lane j < kPer takes digit j of the owner's block
   const uint64_t c = lane < kPer ? (uint64_t)row[padded(owner * kPer + lane)] : 0ull;
   const uint64_t incl2 = base + wave_incl_scan(c, lane);
   const unsigned long long hit2 = __ballot(lane < kPer && rank < incl2);
