@@ -1,20 +1,25 @@
 """Throughput of the dual-codebook quantization loop on one MI355X.
 
-A step is one pass of the whole path over one synthetic decoder layer whose inputs are resident
-in HBM: importance of every activation stream, quantile init of every matrix, `iters` x (batched
-assign, batched refine) with bf16 tables on the last refine, the final assign, pack and dequant.
+A step is one pass of the whole path over one synthetic workload whose inputs are resident in HBM.
+Per decoder layer: importance of every activation stream, quantile init of every matrix (beside the
+importance, on a second stream), `iters` x (batched assign with its error totals, batched refine)
+with bf16 tables on the last refine, the final assign, pack and dequant. The default workload is the
+32B-shaped model: 64 layers, every layer's weights resident (62.4 GB of bf16), quantized one layer
+after another.
 
 Metric (value): bf16 weight bytes quantized per second per assign+refine iteration,
-2 * numel * iters / t_loop, with t_loop the HIP-event time of the loop region of a step.
+2 * numel * iters / t_loop, with t_loop the HIP-event time of the loop regions of a step (summed
+over the layers).
 roofline: the dominant of the two loop kernels (assign, refine); achieved = its algorithmic bytes
 per launch / its mean launch duration (HIP events on the launch stream); traffic = its HBM bytes per
-launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary (scaled by a plain copy), or null
-when that summary was taken on other kernel sources or on another workload.
-cpu_baseline: the fp64 oracle, assign + refine on a sample matrix, timed on the host.
-inference: after the timed steps, the decode GEMV over the packed layer and the AWQ pre-scale of
-the layer, each against the HBM peak (outside the metric).
+launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of this workload (scaled by a
+plain copy), or null when that summary was taken on other kernel sources.
+cpu_baseline: the fp64 oracle (assign + refine iterations) on a sample of the workload's matrices,
+one single-threaded worker process per matrix, timed on the host.
+inference: after the timed steps, the decode GEMV over one packed layer and the AWQ pre-scale of
+that layer, each against the HBM peak (outside the metric).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--no-cpu]
 """
 
 import argparse
@@ -28,7 +33,10 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "hbm_traffic_assign_refine_llama8b_layer.json")
+TRAFFIC_SUMMARY = {
+    2: os.path.join(ROOT, "profiles", "hbm_traffic_assign_refine_llama8b_layer.json"),
+    5: os.path.join(ROOT, "profiles", "hbm_traffic_assign_refine_32b_model.json"),
+}
 
 
 def algorithmic_bytes(numel, S):
@@ -37,14 +45,20 @@ def algorithmic_bytes(numel, S):
     return numel * (2.0 + 0.5 + 1.0 / S)
 
 
-def cpu_baseline(W, I, g, S, n, budget_s=15.0):
-    """Oracle assign+refine iterations on one matrix (host copy), until about budget_s seconds."""
+# ------------------------------------------------------------------------------------------------
+# CPU baseline: the oracle in worker processes (test infrastructure, timed beside the GPU)
+# ------------------------------------------------------------------------------------------------
+
+def _oracle_worker(args):
+    """One worker: oracle init, then assign + refine iterations on one matrix until the budget is
+    spent. Runs in a fresh process with one BLAS/OpenMP thread."""
+    bits, R, C, I32, g, S, n, budget = args
     import numpy as np
 
     from oracle import aaac_ref as ref
 
-    W64 = W.float().cpu().numpy().astype(np.float64)
-    I64 = I.cpu().numpy().astype(np.float64)
+    W64 = ref.bits_to_float(np.frombuffer(bits, dtype=np.uint16).reshape(R, C))
+    I64 = np.frombuffer(I32, dtype=np.float32).astype(np.float64)
     T0, T1 = ref.init_tables(W64, g, n)
     its = 0
     t0 = time.perf_counter()
@@ -53,28 +67,98 @@ def cpu_baseline(W, I, g, S, n, budget_s=15.0):
         T0, T1 = ref.refine(W64, I64, a["codes"], a["sel"], T0, T1, g, S)
         its += 1
         el = time.perf_counter() - t0
-        if el >= budget_s or its >= 50:
+        if el >= budget:
             break
-    return {"value": round(2.0 * W64.size * its / el / 1e9, 6), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": "%d oracle assign+refine iterations (fp64 NumPy, one thread) on the "
-                      "%dx%d matrix of the layer, %.1f s" % (its, W64.shape[0], W64.shape[1], el)}
+    return its, el, R * C
 
 
-def inference_side(L, torch, dev, stream, mats, codes, scales, bitmaps, tb16, Ws, Is, g, S, n,
-                   reps=8):
-    """The two entry points around the loop, timed on this layer after the quantization steps:
-    the decode GEMV over every packed matrix in one launch (batch 1), with 512 MB read between
-    launches so that the packed weights come from HBM and not from the 256 MB last-level cache,
-    and the AWQ pre-scale of every matrix (read W, write W_scaled)."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _worker_ready(_):
+    import numpy  # noqa: F401  (loaded before the GPU is touched in the parent)
+
+    from oracle import aaac_ref  # noqa: F401
+    return os.getpid()
+
+
+def start_cpu_pool(workers):
+    """Worker processes for the CPU baseline, started before the parent touches the GPU (each
+    child is a fresh interpreter with one BLAS/OpenMP thread)."""
+    import concurrent.futures
+    import multiprocessing as mp
+
+    env_keys = ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")
+    saved = {k: os.environ.get(k) for k in env_keys}
+    for k in env_keys:
+        os.environ[k] = "1"
+    try:
+        ex = concurrent.futures.ProcessPoolExecutor(max_workers=workers,
+                                                    mp_context=mp.get_context("spawn"))
+        pids = set(ex.map(_worker_ready, range(4 * workers)))
+    finally:
+        for k, v in saved.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+    return ex, len(pids)
+
+
+def cpu_baseline(pool, jobs, g, S, n, budget_s, workers):
+    """jobs: list of (name, W bf16 tensor, I fp32 tensor), one per worker process of pool; the rate
+    is the summed weight bytes per iteration over the longest worker's time."""
+    import numpy as np
+    import torch
+
+    payload = []
+    for _, W, I in jobs:
+        bits = W.view(torch.int16).cpu().numpy().view(np.uint16).tobytes()
+        payload.append((bits, W.shape[0], W.shape[1],
+                        I.float().cpu().numpy().tobytes(), g, S, n, budget_s))
+    t0 = time.perf_counter()
+    res = list(pool.map(_oracle_worker, payload))
+    wall = time.perf_counter() - t0
+    weight_bytes = sum(2.0 * numel * its for its, _, numel in res)
+    busy = max(el for _, el, _ in res)
+    names = sorted({name for name, _, _ in jobs})
+    shapes = sorted({"%dx%d" % tuple(W.shape) for _, W, _ in jobs})
+    return {"value": round(weight_bytes / busy / 1e9, 6), "unit": "GB/s",
+            "cores": workers, "kind": "oracle",
+            "sample": "%d matrices (%s, %s) of the workload, each in its own single-threaded "
+                      "worker process (fp64 NumPy oracle: init, then assign + refine iterations "
+                      "for about %.0f s; %d iterations in all; pool wall %.1f s)"
+                      % (len(jobs), ", ".join(names), "/".join(shapes), budget_s,
+                         sum(its for its, _, _ in res), wall),
+            "host": {"cpu": _cpu_model(), "os_cpu_count": os.cpu_count(),
+                     "workers": workers}}
+
+
+# ------------------------------------------------------------------------------------------------
+# Inference side (outside the metric)
+# ------------------------------------------------------------------------------------------------
+
+def inference_side(L, torch, dev, stream, shapes, buf, Ws, Is, g, S, n, reps=8):
+    """The two entry points around the loop, timed on one layer after the quantization steps:
+    the decode GEMV over every packed matrix of the layer in one launch (batch 1), with 512 MB read
+    between launches so that the packed weights come from HBM and not from the 256 MB last-level
+    cache, and the AWQ pre-scale of every matrix (read W, write W_scaled)."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
-    Rs = [m.rows for m in mats]
-    Cs = [m.cols for m in mats]
+    Rs = [R for R, _ in shapes]
+    Cs = [C for _, C in shapes]
     xs = [torch.randn(1, C, device=dev, generator=gen).to(torch.bfloat16) for C in Cs]
     ys = [torch.empty(R, device=dev) for R in Rs]
     flush = torch.ones(1 << 27, dtype=torch.float32, device=dev)
-    bms = None if S == g else bitmaps
+    bms = None if S == g else buf.bitmaps
     gemv_bytes = sum(R * C // 2 + 2 * (R * C // g) + ((R * C // S + 7) // 8 if S < g else 0)
                      + 2 * C + 4 * R for R, C in zip(Rs, Cs))
     ts = []
@@ -83,7 +167,7 @@ def inference_side(L, torch, dev, stream, mats, codes, scales, bitmaps, tb16, Ws
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        L.aaac_gemv_batch(codes, scales, bms, tb16, Rs, Cs, g, S, n, xs, ys)
+        L.aaac_gemv_batch(buf.codes, buf.scales, bms, buf.tables_bf16, Rs, Cs, g, S, n, xs, ys)
         e1.record(stream)
         torch.cuda.synchronize()
         if r:
@@ -108,12 +192,12 @@ def inference_side(L, torch, dev, stream, mats, codes, scales, bitmaps, tb16, Ws
     gb = gemv_bytes / (gemv_ms * 1e-3) / 1e9
     ab = awq_bytes / (awq_ms * 1e-3) / 1e9
     return {
-        "gemv": {"workload": "decode GEMV, batch 1, every linear of the layer in one launch, "
+        "gemv": {"workload": "decode GEMV, batch 1, every linear of one layer in one launch, "
                              "packed weights cold in HBM",
                  "us_per_launch": round(gemv_ms * 1e3, 2), "bytes_per_launch": gemv_bytes,
                  "achieved": round(gb, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                  "frac": round(gb / HBM_PEAK_GBS, 4)},
-        "awq_prescale": {"workload": "W diag(a) and I / a^2 for every linear of the layer, "
+        "awq_prescale": {"workload": "W diag(a) and I / a^2 for every linear of one layer, "
                                      "one launch per matrix",
                          "us_per_layer": round(awq_ms * 1e3, 2), "bytes": awq_bytes,
                          "achieved": round(ab, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -121,14 +205,19 @@ def inference_side(L, torch, dev, stream, mats, codes, scales, bitmaps, tb16, Ws
     }
 
 
+# ------------------------------------------------------------------------------------------------
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-inference", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="oracle worker processes (capped by the host's CPU count)")
     ap.add_argument("--one-stream", action="store_true",
                     help="run init after importance on one stream (for per-kernel profiles)")
     args = ap.parse_args()
@@ -136,6 +225,11 @@ def main():
         print("bench.py measures one GPU only: this implementation has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    pool = None
+    if not args.no_cpu:
+        pool, started = start_cpu_pool(max(1, min(args.cpu_workers, os.cpu_count() or 1)))
+        print("[bench] %d oracle worker processes started" % started, file=sys.stderr,
+              flush=True)
 
     import torch
 
@@ -148,38 +242,36 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = syn.config(args.config)
-    if cfg.layers != 1:
-        raise SystemExit("bench.py times one resident layer; config %d streams %d layers"
-                         % (args.config, cfg.layers))
     g, S, n, iters = cfg.g, cfg.S, cfg.n, cfg.iters
     mats = cfg.matrices
-    print("[bench] generating %s" % cfg.name, file=sys.stderr, flush=True)
-    Ws = [syn.make_weight(m.rows, m.cols, syn.seed_for(cfg.cfg_id, 0, m.tensor_id), dev)
-          for m in mats]
+    nl = cfg.layers
+    shapes = [(m.rows, m.cols) for m in mats]
+    print("[bench] generating %s (%d layer%s)" % (cfg.name, nl, "s" if nl > 1 else ""),
+          file=sys.stderr, flush=True)
+    Ws = [[syn.make_weight(m.rows, m.cols, syn.seed_for(cfg.cfg_id, l, m.tensor_id), dev)
+           for m in mats] for l in range(nl)]
+    # the activation streams of one layer, resident; every layer of a multi-layer model reads this
+    # one set (each layer's own activations would come from running the previous layers on
+    # calibration text; synthesizing 90 GB per layer is input generation, not the path)
     streams = cfg.x_streams()
     Xs = {xid: syn.make_activations(cfg.tokens, K, syn.seed_for(cfg.cfg_id, 0, xid), dev)
           for xid, K in streams}
     torch.cuda.synchronize()
-    numel = sum(m.numel for m in mats)
-    Rs = [m.rows for m in mats]
-    Cs = [m.cols for m in mats]
+    numel_layer = sum(m.numel for m in mats)
+    numel = numel_layer * nl
+    Rs = [R for R, _ in shapes]
+    Cs = [C for _, C in shapes]
+    print("[bench] %d weights resident, %.1f GB of activations" % (
+        numel, sum(X.numel() * 4 for X in Xs.values()) / 1e9), file=sys.stderr, flush=True)
 
     # buffers and workspaces (allocated once)
+    wsp = pkg.Workspaces(dev)
     acc = {xid: torch.zeros(K, dtype=torch.float64, device=dev) for xid, K in streams}
     Iv = {xid: torch.empty(K, dtype=torch.float32, device=dev) for xid, K in streams}
-    ws_imp = {xid: L.workspace(L.workspace_bytes(L.OP_IMPORTANCE, cfg.tokens, K), dev)
-              for xid, K in streams}
     ws_init = L.workspace(L.batch_workspace_bytes(L.OP_INIT, Rs, Cs, g, 8, n), dev)
-    ws_r = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), dev)
     Is = [Iv[m.x_id] for m in mats]
-    tabs = [torch.empty(2 * n, dtype=torch.float32, device=dev) for _ in mats]
-    codes = [torch.empty(m.numel // 2, dtype=torch.uint8, device=dev) for m in mats]
-    sels = [torch.empty(m.numel // S, dtype=torch.uint8, device=dev) for m in mats]
-    scales = [torch.empty(m.numel // g, dtype=torch.int16, device=dev) for m in mats]
-    bitmaps = [torch.empty((m.numel // S + 7) // 8, dtype=torch.uint8, device=dev)
-               if S < g else None for m in mats]
-    tb16 = [torch.empty(2 * n, dtype=torch.int16, device=dev) for _ in mats]
-    W_hat = [torch.empty_like(W) for W in Ws]
+    bufs = [pkg.LayerBuffers(shapes, g, S, n, iters, dev) for _ in range(nl)]
+    W_hat = [torch.empty(R, C, dtype=torch.bfloat16, device=dev) for R, C in shapes]
     stream = torch.cuda.current_stream()
 
     def ev():
@@ -187,43 +279,65 @@ def main():
         e.record(stream)
         return e
 
+    class Timing(pkg.Probe):
+        """HIP events around the launches of two of the iterations of every layer (rotating with
+        the layer and step), and around each layer's whole loop."""
+
+        def __init__(self, probe_its):
+            self.probe_its = probe_its
+            self.a, self.r, self.loops = [], [], []
+            self._e = None
+
+        def loop_begin(self):
+            self._l0 = ev()
+
+        def loop_end(self):
+            self.loops.append((self._l0, ev()))
+
+        def before_assign(self, it):
+            self._e = ev() if it in self.probe_its else None
+
+        def before_refine(self, it):
+            if self._e is not None:
+                e1 = ev()
+                self.a.append((self._e, e1))
+                self._e = e1
+
+        def after_refine(self, it):
+            if self._e is not None:
+                self.r.append((self._e, ev()))
+                self._e = None
+
     # init reads only W and importance only X, so init runs on a second stream (default priority,
     # like every stream here) beside importance; the loop waits for both
     side = stream if args.one_stream else torch.cuda.Stream(device=dev)
 
     def step(idx):
-        # HIP events around the launches of two of the iterations (rotating with the step index)
-        # time assign and refine live; an event record between every pair of launches would add
-        # about 110 us to the 3.1 ms loop
-        marks = {"a": [], "r": []}
-        probe = set() if idx < 0 else {idx % iters, (idx + iters // 2) % iters}
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            L.aaac_init_quantiles_batch(Ws, g, n, tabs, ws_init)
-        for xid, K in streams:
-            acc[xid].zero_()
-            L.aaac_importance(Xs[xid], acc[xid], Iv[xid], ws_imp[xid])
-        stream.wait_stream(side)
-        loop0 = ev()
-        for it in range(iters):
-            flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
-            if it not in probe:
-                L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
-                L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, tabs, flags, ws_r)
-                continue
-            e0 = ev()
-            L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
-            e1 = ev()
-            L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, tabs, flags, ws_r)
-            e2 = ev()
-            marks["a"].append((e0, e1))
-            marks["r"].append((e1, e2))
-        loop1 = ev()
-        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
-        bms = bitmaps if S < g else None
-        L.aaac_pack_batch(Ws, g, S, n, sels, tabs, scales, bms, tb16)
-        L.aaac_dequant_batch(codes, scales, bms, tb16, Rs, Cs, g, S, n, W_hat)
-        return loop0, loop1, marks
+        timing = None
+        for l in range(nl):
+            probe = (set() if idx < 0 else
+                     {(idx + l) % iters, (idx + l + iters // 2) % iters})
+            t = Timing(probe)
+            buf = bufs[l]
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                L.aaac_init_quantiles_batch(Ws[l], g, n, buf.tables, ws_init)
+            for xid, K in streams:
+                acc[xid].zero_()
+                L.aaac_importance(Xs[xid], acc[xid], Iv[xid],
+                                  wsp.get(("importance", xid), L.workspace_bytes(
+                                      L.OP_IMPORTANCE, Xs[xid].shape[0], K)))
+            stream.wait_stream(side)
+            pkg.run_loop(Ws[l], Is, buf, wsp, init=False, probe=t)
+            L.aaac_dequant_batch(buf.codes, buf.scales, buf.bitmaps, buf.tables_bf16, Rs, Cs,
+                                 g, S, n, W_hat)
+            if timing is None:
+                timing = t
+            else:
+                timing.a += t.a
+                timing.r += t.r
+                timing.loops += t.loops
+        return timing
 
     # one plain device-to-device copy of 1 GiB, outside the timed region: the reference launch that
     # HBM byte counters (FETCH_SIZE / WRITE_SIZE) are scaled by
@@ -238,17 +352,21 @@ def main():
     print("[bench] warmup done", file=sys.stderr, flush=True)
     t_start = time.perf_counter()
     s0 = ev()
-    recs = [step(i) for i in range(args.steps)]
+    recs = []
+    for i in range(args.steps):
+        recs.append(step(i))
+        if nl > 1:
+            print("[bench] step %d enqueued" % i, file=sys.stderr, flush=True)
     s1 = ev()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     step_ms = s0.elapsed_time(s1) / args.steps
-    loop_ms = sum(a.elapsed_time(b) for a, b, _ in recs) / args.steps
-    a_ms = [x.elapsed_time(y) for _, _, m in recs for x, y in m["a"]]
-    r_ms = [x.elapsed_time(y) for _, _, m in recs for x, y in m["r"]]
+    loop_ms = sum(a.elapsed_time(b) for t in recs for a, b in t.loops) / args.steps
+    a_ms = [x.elapsed_time(y) for t in recs for x, y in t.a]
+    r_ms = [x.elapsed_time(y) for t in recs for x, y in t.r]
     a_avg = sum(a_ms) / len(a_ms)
     r_avg = sum(r_ms) / len(r_ms)
-    bytes_launch = algorithmic_bytes(numel, S)
+    bytes_launch = algorithmic_bytes(numel_layer, S)
     dom, dom_ms = ("assign", a_avg) if a_avg >= r_avg else ("refine", r_avg)
     achieved = bytes_launch / (dom_ms * 1e-3) / 1e9
     value = 2.0 * numel * iters / (loop_ms * 1e-3) / 1e9
@@ -257,21 +375,35 @@ def main():
                                         bytes_launch / a_avg / 1e6, r_avg * 1e3,
                                         bytes_launch / r_avg / 1e6, wall),
           file=sys.stderr, flush=True)
+    # the error totals of the last step: non-increasing over the iterations of every matrix
+    for l in range(nl):
+        pkg.check_history(bufs[l].err, w2=bufs[l].w2)
+    last = bufs[nl - 1].err[:, 0].cpu().tolist()
+    print("[bench] error history, last layer, first matrix: %s" % ", ".join(
+        "%.6g" % x for x in last), file=sys.stderr, flush=True)
     traffic = None
-    if args.config == 2:
-        t = pmc_traffic.load_traffic(TRAFFIC_SUMMARY, dom)
+    if args.config in TRAFFIC_SUMMARY:
+        t = pmc_traffic.load_traffic(TRAFFIC_SUMMARY[args.config], dom)
         traffic = None if t is None else int(round(t))
-    inference = inference_side(L, torch, dev, stream, mats, codes, scales, bitmaps, tb16, Ws, Is,
-                               g, S, n)
-    print("[bench] gemv %.1f us (%.0f GB/s), awq prescale %.1f us (%.0f GB/s)" % (
-        inference["gemv"]["us_per_launch"], inference["gemv"]["achieved"],
-        inference["awq_prescale"]["us_per_layer"], inference["awq_prescale"]["achieved"]),
-        file=sys.stderr, flush=True)
+    inference = None
+    if not args.no_inference:
+        inference = inference_side(L, torch, dev, stream, shapes, bufs[0], Ws[0], Is, g, S, n)
+        print("[bench] gemv %.1f us (%.0f GB/s), awq prescale %.1f us (%.0f GB/s)" % (
+            inference["gemv"]["us_per_launch"], inference["gemv"]["achieved"],
+            inference["awq_prescale"]["us_per_layer"], inference["awq_prescale"]["achieved"]),
+            file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu:
-        k = min(range(len(mats)), key=lambda i: mats[i].numel)
-        print("[bench] cpu baseline on %s" % mats[k].name, file=sys.stderr, flush=True)
-        cpu = cpu_baseline(Ws[k], Is[k], g, S, n, args.cpu_budget)
+        # the two smallest matrices (by size) of evenly spaced layers, one per worker
+        workers = max(1, min(args.cpu_workers, os.cpu_count() or 1))
+        order = sorted(range(len(mats)), key=lambda i: mats[i].numel)[:2]
+        nsample = max(1, workers // len(order))
+        layers = sorted({round(k * (nl - 1) / max(1, nsample - 1)) for k in range(nsample)})
+        jobs = [(mats[i].name, Ws[l][i], Is[i]) for l in layers for i in order][:workers]
+        print("[bench] cpu baseline: %d oracle workers" % len(jobs), file=sys.stderr, flush=True)
+        cpu = cpu_baseline(pool, jobs, g, S, n, args.cpu_budget, len(jobs))
+        cpu["sample"] += "; layers %s" % layers
+        pool.shutdown()
     out = {
         "metric": "bf16 weights quantized/sec per assign+refine iter (GB/s) and % of HBM peak",
         "value": round(value, 3),
@@ -285,7 +417,7 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32",
         "data": "synthetic",
-        "config": {"workload": cfg.name, "matrices": [[m.rows, m.cols] for m in mats],
+        "config": {"workload": cfg.name, "layers": nl, "matrices": [list(s) for s in shapes],
                    "numel": numel, "g": g, "S": S, "n": n, "iters": iters,
                    "calib_tokens": cfg.tokens},
         "loop_ms_per_step": round(loop_ms, 4),

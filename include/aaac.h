@@ -55,6 +55,7 @@ typedef int32_t aaac_status;
 
 /* Flags of aaac_refine. */
 #define AAAC_REFINE_ROUND_BF16 1        /* round the new tables to bf16 (ties to even), stored as fp32 */
+#define AAAC_REFINE_W2_KNOWN 2          /* *w2 already holds sum I w^2 of this matrix (see err) */
 
 /* Static description of a status code. Never NULL. */
 const char* aaac_status_string(aaac_status status);
@@ -105,11 +106,17 @@ aaac_status aaac_init_quantiles(const uint16_t* W, int64_t R, int64_t C, int g, 
  * codes   [R * C / 2] bytes, two codes per byte, the low nibble holds the even column.
  * sel     [R * C / S] bytes, 0 = T0, 1 = T1, one per selection group in row-major order.
  * err     NULL, or fp64 [R * C / S][2] receiving (E_0, E_1) per selection group (for checking).
- * One kernel; it needs no workspace (the lookup structure lives in LDS).
+ * err_total  NULL, or one fp64 receiving the total weighted error of the assignment,
+ *         sum over H of E_sel(H) (the k-means objective that the alternation never increases, §2
+ *         mechanism 4). Summed in a fixed order (lanes in row order, then waves, then workgroups
+ *         in order; no floating-point atomics), so it is reproducible call after call. Needs ws.
+ * ws      with err_total: aaac_workspace_bytes(AAAC_OP_ASSIGN, R, C, g, S, n) bytes, same
+ *         zero-fill rule as the other workspaces; otherwise ignored (may be NULL, ws_bytes 0).
+ * One kernel (the lookup structure lives in LDS).
  */
 aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
-                        double* err, void* stream);
+                        double* err, double* err_total, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Refine, AAAC summary §2 mechanism 4 (activation-weighted k-means). For every table c and entry j,
@@ -124,14 +131,24 @@ aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, i
  *
  * codes, sel   as written by aaac_assign.
  * tables_in    fp32 [2][n];  tables_out fp32 [2][n], may equal tables_in.
- * flags        0 or AAAC_REFINE_ROUND_BF16 (round the new entries to bf16; used on the last
- *              iteration so that the final assign runs against the stored tables).
+ * flags        0, or AAAC_REFINE_ROUND_BF16 (round the new entries to bf16; used on the last
+ *              iteration so that the final assign runs against the stored tables) and/or
+ *              AAAC_REFINE_W2_KNOWN (see w2; needs err).
+ * err          NULL, or one fp64 receiving the total weighted error of the incoming assignment
+ *              (the codes and selectors under tables_in: the quantity aaac_assign's err_total
+ *              reports), formed from the cell sums as E = W2 - 2 sum_cells T num +
+ *              sum_cells T^2 den with W2 = sum I_k w_k^2 (sums of exact fp64 terms). Its absolute
+ *              accuracy is about 1e-15 W2, far below E except for matrices quantized almost
+ *              exactly (aaac_assign's err_total has no such limit).
+ * w2           with err: one fp64. Without AAAC_REFINE_W2_KNOWN the kernel sums W2 (one more fp64
+ *              fma per weight) and writes it here; with the flag it reads W2 from here (the value
+ *              an earlier call on the same W and I wrote), at no cost per weight. NULL without err.
  * ws           aaac_workspace_bytes(AAAC_OP_REFINE, R, C, g, S, n) bytes.
  */
 aaac_status aaac_refine(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const uint8_t* codes, const uint8_t* sel,
-                        const float* tables_in, float* tables_out, int flags, void* ws,
-                        size_t ws_bytes, void* stream);
+                        const float* tables_in, float* tables_out, int flags, double* err,
+                        double* w2, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Pack, AAAC summary §2 mechanism 3 and §4: the stored format.
@@ -223,10 +240,14 @@ aaac_status aaac_awq_prescale(const uint16_t* W, int64_t R, int64_t C, const flo
  * Batched assign / refine over up to AAAC_MAX_BATCH matrices that share g, S and n (for example
  * the seven linears of one decoder layer) in one launch each. Element i of every array describes
  * matrix i exactly as the single-matrix call does; the results are bitwise identical to calling
- * the single-matrix entry points one matrix at a time. refine updates tables[i] in place.
- * The host arrays are read during the call only. The refine workspace holds
+ * the single-matrix entry points one matrix at a time, except where a sum's rounding depends on
+ * how the rows are split over workgroups (the refine sums and err_total: the same call gives the
+ * same bits every time; against single calls they agree to rounding). refine updates tables[i] in
+ * place. The host arrays are read during the call only. The refine workspace holds
  * aaac_batch_workspace_bytes(AAAC_OP_REFINE, count, R, C, g, S, n) bytes, same zero-fill rule as
- * above; assign needs none.
+ * above. assign: err_total is NULL or fp64 [count] (the total of matrix i in err_total[i]), with
+ * a workspace of aaac_batch_workspace_bytes(AAAC_OP_ASSIGN, count, R, C, g, S, n) bytes.
+ * refine: err and w2 are NULL or fp64 [count] each (matrix i's at index i, as in aaac_refine).
  */
 #define AAAC_MAX_BATCH 8
 
@@ -247,13 +268,14 @@ aaac_status aaac_init_quantiles_batch(int count, const uint16_t* const* W, const
 aaac_status aaac_assign_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,
                               const float* const* tables, uint8_t* const* codes,
-                              uint8_t* const* sel, void* stream);
+                              uint8_t* const* sel, double* err_total, void* ws, size_t ws_bytes,
+                              void* stream);
 
 aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,
                               const uint8_t* const* codes, const uint8_t* const* sel,
-                              float* const* tables, int flags, void* ws, size_t ws_bytes,
-                              void* stream);
+                              float* const* tables, int flags, double* err, double* w2, void* ws,
+                              size_t ws_bytes, void* stream);
 
 /*
  * One iteration of the alternation (AAAC summary §2 mechanism 4) in one launch: the batched assign

@@ -22,9 +22,17 @@ from ._lib import (  # noqa: F401
     load,
 )
 from .quantize import (  # noqa: F401
+    Layer,
+    LayerBuffers,
+    Probe,
     QuantizedMatrix,
+    Workspaces,
     awq_prescale,
+    check_history,
     importance,
+    quantize_layer,
     quantize_matrices,
     quantize_matrix,
+    quantize_model,
+    run_loop,
 )

@@ -25,6 +25,7 @@ AAAC_ERR_HIP = 4
 
 OP_IMPORTANCE, OP_INIT, OP_ASSIGN, OP_REFINE = 0, 1, 2, 3
 REFINE_ROUND_BF16 = 1
+REFINE_W2_KNOWN = 2
 MAX_BATCH = 8
 
 EXPORTED = (
@@ -71,9 +72,9 @@ def load(path: str = LIB_PATH):
         "aaac_init_quantiles": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_vp, c_vp, c_size,
                                         c_vp]),
         "aaac_assign": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
-                                c_vp, c_vp]),
+                                c_vp, c_vp, c_vp, c_size, c_vp]),
         "aaac_refine": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
-                                c_vp, c_int, c_vp, c_size, c_vp]),
+                                c_vp, c_int, c_vp, c_vp, c_vp, c_size, c_vp]),
         "aaac_pack": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
                               c_vp, c_vp]),
         "aaac_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
@@ -85,10 +86,11 @@ def load(path: str = LIB_PATH):
         "aaac_dequant_batch": (c_int, [c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), P(c_i64),
                                        P(c_i64), c_int, c_int, c_int, P(c_vp), c_vp]),
         "aaac_assign_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
-                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp]),
-        "aaac_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
-                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int, c_vp, c_size,
+                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_vp, c_vp, c_size,
                                       c_vp]),
+        "aaac_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int, c_int,
+                                      P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int, c_vp, c_vp,
+                                      c_vp, c_size, c_vp]),
         "aaac_awq_prescale": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
         "aaac_assign_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
                                              c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int,
@@ -197,7 +199,10 @@ def aaac_init_quantiles(W: torch.Tensor, g: int, n: int, tables: torch.Tensor,
 
 def aaac_assign(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, tables: torch.Tensor,
                 codes: torch.Tensor, sel: torch.Tensor, err: Optional[torch.Tensor] = None,
+                err_total: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                 stream=None):
+    """err: fp64 [R*C/S*2] (E0, E1) per selection group or None; err_total: fp64 [1] receiving
+    the sum of the chosen errors, or None (then ws is not needed)."""
     lib = load()
     R, C = W.shape
     _need(W, "W", torch.bfloat16)
@@ -207,14 +212,22 @@ def aaac_assign(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, tables
     _need(sel, "sel", torch.uint8, R * C // S)
     if err is not None:
         _need(err, "err", torch.float64, 2 * (R * C // S))
+    if err_total is not None:
+        _need(err_total, "err_total", torch.float64, 1)
+        if ws is None:
+            ws = workspace(lib.aaac_workspace_bytes(OP_ASSIGN, R, C, g, S, n), W.device)
     st = lib.aaac_assign(_ptr(W), R, C, g, S, n, _ptr(I), _ptr(tables), _ptr(codes), _ptr(sel),
-                         _ptr(err), _stream(stream))
+                         _ptr(err), _ptr(err_total), _ptr(ws), 0 if ws is None else ws.numel(),
+                         _stream(stream))
     _check(st, "aaac_assign")
 
 
 def aaac_refine(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, codes: torch.Tensor,
                 sel: torch.Tensor, tables_in: torch.Tensor, tables_out: torch.Tensor,
-                flags: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
+                flags: int = 0, ws: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
+                w2: Optional[torch.Tensor] = None, stream=None):
+    """err: fp64 [1] receiving the error of the incoming assignment, with w2 fp64 [1] (sum I w^2:
+    written, or read with REFINE_W2_KNOWN), or both None."""
     lib = load()
     R, C = W.shape
     _need(W, "W", torch.bfloat16)
@@ -223,11 +236,15 @@ def aaac_refine(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, codes:
     _need(sel, "sel", torch.uint8, R * C // S)
     _need(tables_in, "tables_in", torch.float32, 2 * n)
     _need(tables_out, "tables_out", torch.float32, 2 * n)
+    if err is not None:
+        _need(err, "err", torch.float64, 1)
+    if w2 is not None:
+        _need(w2, "w2", torch.float64, 1)
     if ws is None:
         ws = workspace(lib.aaac_workspace_bytes(OP_REFINE, R, C, g, S, n), W.device)
     st = lib.aaac_refine(_ptr(W), R, C, g, S, n, _ptr(I), _ptr(codes), _ptr(sel),
-                         _ptr(tables_in), _ptr(tables_out), flags, _ptr(ws), ws.numel(),
-                         _stream(stream))
+                         _ptr(tables_in), _ptr(tables_out), flags, _ptr(err), _ptr(w2),
+                         _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "aaac_refine")
 
 
@@ -342,7 +359,9 @@ def aaac_init_quantiles_batch(Ws: Sequence[torch.Tensor], g: int, n: int,
 def aaac_assign_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
                       Is: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
                       codes: Sequence[torch.Tensor], sels: Sequence[torch.Tensor],
+                      err_total: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                       stream=None):
+    """err_total: fp64 [len(Ws)] receiving each matrix's sum of chosen errors, or None."""
     lib = load()
     k = len(Ws)
     Rs = [W.shape[0] for W in Ws]
@@ -353,18 +372,26 @@ def aaac_assign_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
         _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
         _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
+    if err_total is not None:
+        _need(err_total, "err_total", torch.float64, k)
+        if ws is None:
+            ws = workspace(batch_workspace_bytes(OP_ASSIGN, Rs, Cs, g, S, n), Ws[0].device)
     st = lib.aaac_assign_batch(
         k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
         _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in tables]),
         _arr(c_vp, [t.data_ptr() for t in codes]), _arr(c_vp, [t.data_ptr() for t in sels]),
-        _stream(stream))
+        _ptr(err_total), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
     _check(st, "aaac_assign_batch")
 
 
 def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
                       Is: Sequence[torch.Tensor], codes: Sequence[torch.Tensor],
                       sels: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
-                      flags: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
+                      flags: int = 0, ws: Optional[torch.Tensor] = None,
+                      err: Optional[torch.Tensor] = None, w2: Optional[torch.Tensor] = None,
+                      stream=None):
+    """err, w2: fp64 [len(Ws)] each (the incoming assignment's error per matrix, and sum I w^2 per
+    matrix: written, or read with REFINE_W2_KNOWN), or both None."""
     lib = load()
     k = len(Ws)
     Rs = [W.shape[0] for W in Ws]
@@ -375,13 +402,17 @@ def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
         _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
         _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
+    if err is not None:
+        _need(err, "err", torch.float64, k)
+    if w2 is not None:
+        _need(w2, "w2", torch.float64, k)
     if ws is None:
         ws = workspace(batch_workspace_bytes(OP_REFINE, Rs, Cs, g, S, n), Ws[0].device)
     st = lib.aaac_refine_batch(
         k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
         _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in codes]),
         _arr(c_vp, [t.data_ptr() for t in sels]), _arr(c_vp, [t.data_ptr() for t in tables]),
-        flags, _ptr(ws), ws.numel(), _stream(stream))
+        flags, _ptr(err), _ptr(w2), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "aaac_refine_batch")
 
 

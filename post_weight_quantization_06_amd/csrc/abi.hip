@@ -72,9 +72,9 @@ aaac_status check_shape(int64_t R, int64_t C, int g, int S, int n, bool need_S, 
   return AAAC_OK;
 }
 
-// refine workspace: job counters (256 bytes), then fp64 partials [count][64][kMaxRefineBlocks]
+// refine workspace: job counters (256 bytes), then fp64 partials [count][kPartVals][kMaxRefineBlocks]
 size_t refine_ws_bytes(int count) {
-  return 256 + (size_t)count * 64 * kMaxRefineBlocks * sizeof(double);
+  return 256 + (size_t)count * kPartVals * kMaxRefineBlocks * sizeof(double);
 }
 
 aaac_status check_batch(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
@@ -91,10 +91,16 @@ aaac_status check_batch(int count, const uint16_t* const* W, const int64_t* R, c
   return AAAC_OK;
 }
 
+// assign workspace (only with error totals): job counters (256 bytes), then fp64 partials
+// [count][kMaxAssignBlocks]
+size_t assign_ws_bytes(int count) {
+  return 256 + (size_t)count * kMaxAssignBlocks * sizeof(double);
+}
+
 aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
                       int g, int S, int n, const float* const* I, const float* const* tables,
-                      uint8_t* const* codes, uint8_t* const* sel, double* err, void* stream,
-                      const char* who) {
+                      uint8_t* const* codes, uint8_t* const* sel, double* err, double* err_total,
+                      void* ws, size_t ws_bytes, void* stream, const char* who) {
   aaac_status st = check_batch(count, W, R, C, g, S, n, who);
   if (st != AAAC_OK) return st;
   if (!I || !tables || !codes || !sel) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
@@ -106,6 +112,16 @@ aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, con
                   "bytes)", who, i);
   }
   if (err && !aligned(err, 8)) return fail(AAAC_ERR_INVALID_ARG, "%s: err misaligned", who);
+  if (err_total) {
+    if (!aligned(err_total, 8))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: err_total misaligned", who);
+    if (!ws || !aligned(ws, 256))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned (needed with err_total)",
+                  who);
+    if (ws_bytes < assign_ws_bytes(count))
+      return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes,
+                  assign_ws_bytes(count));
+  }
   AssignBatch b{};
   b.njobs = count;
   b.g = g;
@@ -122,8 +138,14 @@ aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, con
     j.codes = reinterpret_cast<uint32_t*>(codes[i]);
     j.sel = sel[i];
     j.err = err;
+    j.err_total = err_total ? err_total + i : nullptr;
   }
   b.total_tasks = tb;
+  if (err_total) {
+    b.totals = 1;
+    b.counters = static_cast<uint32_t*>(ws);
+    b.partials = reinterpret_cast<double*>(static_cast<char*>(ws) + 256);
+  }
   return hip_status(launch_assign(b, err != nullptr, static_cast<hipStream_t>(stream)), who);
 }
 
@@ -150,24 +172,7 @@ void build_refine_batch(RefineBatch& b, int count, const uint16_t* const* W, con
   if (nb > kMaxRefineBlocks) nb = kMaxRefineBlocks;
   b.nblocks = (int32_t)nb;
   // workgroup b owns tasks [task_lo(b), task_lo(b + 1)); record which workgroups meet each job
-  auto owner = [&](int64_t t) {
-    int64_t lo = 0, hi = nb - 1;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi + 1) / 2;
-      if (task_lo(mid, tb, nb) <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-  };
-  int32_t slots = 1;
-  for (int i = 0; i < count; ++i) {
-    RefineJob& j = b.job[i];
-    const int64_t w0 = owner(j.geom.task_begin);
-    const int64_t w1 = owner(j.geom.task_begin + j.geom.ntasks - 1);
-    j.wg_lo = (int32_t)w0;
-    j.wg_count = (int32_t)(w1 - w0 + 1);
-    if (j.wg_count > slots) slots = j.wg_count;
-  }
-  b.slots = slots;
+  b.slots = job_slots(b.job, count, tb, nb);
   b.counters = static_cast<uint32_t*>(ws);
   b.partials = reinterpret_cast<double*>(static_cast<char*>(ws) + 256);
 }
@@ -183,10 +188,12 @@ aaac_status check_refine_ws(int count, void* ws, size_t ws_bytes, const char* wh
 aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
                       int g, int S, int n, const float* const* I, const uint8_t* const* codes,
                       const uint8_t* const* sel, const float* const* tin, float* const* tout,
-                      int flags, void* ws, size_t ws_bytes, void* stream, const char* who) {
+                      int flags, double* err, double* w2, void* ws, size_t ws_bytes, void* stream,
+                      const char* who) {
   aaac_status st = check_batch(count, W, R, C, g, S, n, who);
   if (st != AAAC_OK) return st;
-  if (flags & ~AAAC_REFINE_ROUND_BF16) return fail(AAAC_ERR_INVALID_ARG, "%s: unknown flags %d", who, flags);
+  if (flags & ~(AAAC_REFINE_ROUND_BF16 | AAAC_REFINE_W2_KNOWN))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: unknown flags %d", who, flags);
   if (!I || !codes || !sel || !tin || !tout) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
   for (int i = 0; i < count; ++i) {
     if (!I[i] || !aligned(I[i], 16) || !codes[i] || !aligned(codes[i], 16) || !sel[i] || !tin[i] ||
@@ -195,14 +202,21 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
   }
   st = check_refine_ws(count, ws, ws_bytes, who);
   if (st != AAAC_OK) return st;
+  if (err && (!aligned(err, 8) || !w2 || !aligned(w2, 8)))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: err and w2 must be given together, 8-byte aligned", who);
+  if (!err && (flags & AAAC_REFINE_W2_KNOWN))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: AAAC_REFINE_W2_KNOWN without err and w2", who);
   RefineBatch b{};
   build_refine_batch(b, count, W, R, C, g, S, n, I, flags, ws);
+  b.errs = err ? 1 : 0;
   for (int i = 0; i < count; ++i) {
     RefineJob& j = b.job[i];
     j.codes = reinterpret_cast<const uint32_t*>(codes[i]);
     j.sel = sel[i];
     j.tables_in = tin[i];
     j.tables_out = tout[i];
+    j.err_out = err ? err + i : nullptr;
+    j.w2 = err ? w2 + i : nullptr;
   }
   return hip_status(launch_refine(b, static_cast<hipStream_t>(stream)), who);
 }
@@ -360,7 +374,8 @@ size_t aaac_workspace_bytes(int op, int64_t R, int64_t C, int g, int S, int n) {
       if (check_shape(R, C, g, 8, n, false, "aaac_workspace_bytes") != AAAC_OK) return 0;
       return init_workspace_bytes(1, &R, &C);
     case AAAC_OP_ASSIGN:
-      return 0;
+      if (check_shape(R, C, g, S, n, true, "aaac_workspace_bytes") != AAAC_OK) return 0;
+      return assign_ws_bytes(1);
     case AAAC_OP_REFINE:
       if (check_shape(R, C, g, S, n, true, "aaac_workspace_bytes") != AAAC_OK) return 0;
       return refine_ws_bytes(1);
@@ -377,6 +392,7 @@ size_t aaac_batch_workspace_bytes(int op, int count, const int64_t* R, const int
     if (check_shape(R[i], C[i], g, init ? 8 : S, n, !init, "aaac_batch_workspace_bytes") != AAAC_OK)
       return 0;
   if (op == AAAC_OP_REFINE) return refine_ws_bytes(count);
+  if (op == AAAC_OP_ASSIGN) return assign_ws_bytes(count);
   if (init) return init_workspace_bytes(count, R, C);
   return 0;
 }
@@ -414,37 +430,39 @@ aaac_status aaac_init_quantiles_batch(int count, const uint16_t* const* W, const
 
 aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const float* tables, uint8_t* codes, uint8_t* sel,
-                        double* err, void* stream) {
-  return do_assign(1, &W, &R, &C, g, S, n, &I, &tables, &codes, &sel, err, stream, "aaac_assign");
+                        double* err, double* err_total, void* ws, size_t ws_bytes, void* stream) {
+  return do_assign(1, &W, &R, &C, g, S, n, &I, &tables, &codes, &sel, err, err_total, ws, ws_bytes,
+                   stream, "aaac_assign");
 }
 
 aaac_status aaac_assign_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,
                               const float* const* tables, uint8_t* const* codes,
-                              uint8_t* const* sel, void* stream) {
-  return do_assign(count, W, R, C, g, S, n, I, tables, codes, sel, nullptr, stream,
-                   "aaac_assign_batch");
+                              uint8_t* const* sel, double* err_total, void* ws, size_t ws_bytes,
+                              void* stream) {
+  return do_assign(count, W, R, C, g, S, n, I, tables, codes, sel, nullptr, err_total, ws,
+                   ws_bytes, stream, "aaac_assign_batch");
 }
 
 aaac_status aaac_refine(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
                         const float* I, const uint8_t* codes, const uint8_t* sel,
-                        const float* tables_in, float* tables_out, int flags, void* ws,
-                        size_t ws_bytes, void* stream) {
-  return do_refine(1, &W, &R, &C, g, S, n, &I, &codes, &sel, &tables_in, &tables_out, flags, ws,
-                   ws_bytes, stream, "aaac_refine");
+                        const float* tables_in, float* tables_out, int flags, double* err,
+                        double* w2, void* ws, size_t ws_bytes, void* stream) {
+  return do_refine(1, &W, &R, &C, g, S, n, &I, &codes, &sel, &tables_in, &tables_out, flags, err,
+                   w2, ws, ws_bytes, stream, "aaac_refine");
 }
 
 aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t* R,
                               const int64_t* C, int g, int S, int n, const float* const* I,
                               const uint8_t* const* codes, const uint8_t* const* sel,
-                              float* const* tables, int flags, void* ws, size_t ws_bytes,
-                              void* stream) {
+                              float* const* tables, int flags, double* err, double* w2, void* ws,
+                              size_t ws_bytes, void* stream) {
   if (!tables) return fail(AAAC_ERR_INVALID_ARG, "aaac_refine_batch: null tables array");
   const float* tin[AAAC_MAX_BATCH];
   const int m = count < AAAC_MAX_BATCH ? (count > 0 ? count : 0) : AAAC_MAX_BATCH;
   for (int i = 0; i < m; ++i) tin[i] = tables[i];
-  return do_refine(count, W, R, C, g, S, n, I, codes, sel, tin, tables, flags, ws, ws_bytes, stream,
-                   "aaac_refine_batch");
+  return do_refine(count, W, R, C, g, S, n, I, codes, sel, tin, tables, flags, err, w2, ws,
+                   ws_bytes, stream, "aaac_refine_batch");
 }
 
 aaac_status aaac_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
@@ -502,7 +520,8 @@ aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const 
     // 8-weight selection groups: the two launches
     const float* tin[AAAC_MAX_BATCH];
     for (int i = 0; i < count; ++i) tin[i] = tables[i];
-    st = do_assign(count, W, R, C, g, S, n, I, tin, codes, sel, nullptr, stream, who);
+    st = do_assign(count, W, R, C, g, S, n, I, tin, codes, sel, nullptr, nullptr, nullptr, 0,
+                   stream, who);
     if (st != AAAC_OK) return st;
     const uint8_t* cc[AAAC_MAX_BATCH];
     const uint8_t* sc[AAAC_MAX_BATCH];
@@ -510,8 +529,8 @@ aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const 
       cc[i] = codes[i];
       sc[i] = sel[i];
     }
-    return do_refine(count, W, R, C, g, S, n, I, cc, sc, tin, tables, flags, ws, ws_bytes, stream,
-                     who);
+    return do_refine(count, W, R, C, g, S, n, I, cc, sc, tin, tables, flags, nullptr, nullptr, ws,
+                     ws_bytes, stream, who);
   }
   RefineBatch b{};
   build_refine_batch(b, count, W, R, C, g, S, n, I, flags, ws);

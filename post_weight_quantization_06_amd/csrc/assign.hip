@@ -14,7 +14,7 @@ namespace {
 
 struct RowOut {
   double D;         // E_1 - E_0 of the lane's selection group (after the butterfly)
-  double E0, E1;    // only with err output
+  double E0, E1;    // E0 with kErrTotal and kErrFull, E1 with kErrFull
   uint32_t P, Q;    // code bytes (q0 | q1 << 4) of weights 0-3 and 4-7
 };
 
@@ -57,10 +57,13 @@ __device__ __forceinline__ void slow_lane(const float* w, uint32_t amax, const f
   o.Q = Qw;
 }
 
-template <bool WITH_ERR, int G8, int S8>
-__device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, int n, int g8,
-                                           int s8, int log2S, int64_t base, bool active,
-                                           const uint4& v, const float (&Ik)[8]) {
+// One row of the 8-weight mapping: codes, selection, stores. Returns this lane's share of the
+// row's chosen error (its own error sum for the table its group chose; 0 for inactive lanes and
+// with kErrNone).
+template <int EM, int G8, int S8>
+__device__ __forceinline__ double assign_row(const AssignJob& jb, const Lut& lut, int n, int g8,
+                                             int s8, int log2S, int64_t base, bool active,
+                                             const uint4& v, const float (&Ik)[8]) {
   const uint32_t amax = block_max_u32_t<G8>(lane_absmax_bits(v), g8);
   const float s = __uint_as_float(amax << 16);
   float w[8];
@@ -77,12 +80,12 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     // byte 0 of the lookup's result is the code byte
-    const uint32_t c = lookup_weight<WITH_ERR>(w[k], Y, nse, lut, Ik[k], acc, a0, a1) & 0xFFu;
+    const uint32_t c = lookup_weight<EM>(w[k], Y, nse, lut, Ik[k], acc, a0, a1) & 0xFFu;
     if (k < 4) Pw |= c << (8 * k); else Qw |= c << (8 * (k - 4));
     if (k == 3 || k == 7) {
       accd += (double)acc;
       acc = 0.0f;
-      if (WITH_ERR) {
+      if (EM >= kErrTotal) {
         e0d += (double)a0;
         e1d += (double)a1;
         a0 = 0.0f;
@@ -92,25 +95,33 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
   }
   RowOut o;
   o.D = block_sum_f64_t<S8>(accd, s8);
-  o.E0 = WITH_ERR ? block_sum_f64_t<S8>(e0d, s8) : 0.0;
-  o.E1 = WITH_ERR ? block_sum_f64_t<S8>(e1d, s8) : 0.0;
+  o.E0 = EM == kErrFull ? block_sum_f64_t<S8>(e0d, s8) : 0.0;
+  o.E1 = EM == kErrFull ? block_sum_f64_t<S8>(e1d, s8) : 0.0;
   o.P = Pw;
   o.Q = Qw;
+  double L0 = e0d, L1 = e1d;     // the lane's own error sums
   if (zero) {
     o.D = 0.0;
     o.E0 = 0.0;
     o.E1 = 0.0;
+    L0 = 0.0;
+    L1 = 0.0;
   }
   const bool bad = active && (!fast_scale || !(fabs(o.D) < __builtin_inf()));
   if (__any(bad)) {
     RowOut so;
-    slow_lane<WITH_ERR>(w, amax, Ik, lut.tab, n, so);
+    slow_lane<(EM >= kErrTotal)>(w, amax, Ik, lut.tab, n, so);
+    const double l0 = so.E0, l1 = so.E1;
     so.D = block_sum_f64_t<S8>(so.D, s8);
-    if (WITH_ERR) {
+    if (EM == kErrFull) {
       so.E0 = block_sum_f64_t<S8>(so.E0, s8);
       so.E1 = block_sum_f64_t<S8>(so.E1, s8);
     }
-    if (bad) o = so;
+    if (bad) {
+      o = so;
+      L0 = l0;
+      L1 = l1;
+    }
   }
   const uint32_t sel = (o.D < 0.0) ? 1u : 0u;
   const uint32_t sh = sel ? 4u : 0u;
@@ -119,36 +130,78 @@ __device__ __forceinline__ void assign_row(const AssignJob& jb, const Lut& lut, 
   p |= p >> 4;
   q |= q >> 4;
   const uint32_t packed = __builtin_amdgcn_perm(q, p, 0x06040200u);
+  const bool leader = active && ((base >> 3) & (s8 - 1)) == 0;
   if (active) {
     jb.codes[base >> 3] = packed;
-    if (((base >> 3) & (s8 - 1)) == 0) {
+    if (leader) {
       const int64_t h = base >> log2S;
       jb.sel[h] = (uint8_t)sel;
-      if (WITH_ERR) {
+      if (EM == kErrFull && jb.err) {
         jb.err[2 * h] = o.E0;
         jb.err[2 * h + 1] = o.E1;
       }
     }
   }
+  if (EM == kErrNone || !active) return 0.0;
+  return sel ? L1 : L0;
+}
+
+// Sum of this workgroup's chosen errors over job j, then (last workgroup of the job, by an integer
+// ticket) the job's total: each lane's running sum in row order, the lanes of a wave by butterfly,
+// the waves in order, the workgroups' partials in workgroup order. Every order is fixed, so the
+// total is reproducible for a given call. Called by every thread of the workgroup (barriers).
+__device__ void finish_err_total(const AssignBatch& b, int j, double lane_sum) {
+  __shared__ double wsum[kWavesPerBlock];
+  __shared__ uint32_t ticket;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const AssignJob& jb = b.job[j];
+  double* part = b.partials + (size_t)j * b.slots;
+  const double ws = block_sum_f64_t<kWave>(lane_sum, kWave);
+  __syncthreads();
+  if (lane == 0) wsum[wave] = ws;
+  __syncthreads();
+  if (tid == 0) {
+    part[(int)blockIdx.x - jb.wg_lo] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    __threadfence();
+    ticket = atomicAdd(b.counters + j, 1u);
+  }
+  __syncthreads();
+  if (ticket != (uint32_t)(jb.wg_count - 1)) return;
+  // last workgroup of this job: every partial is visible after the fence
+  __threadfence();
+  const int cnt = jb.wg_count;
+  const int s0 = (tid * cnt) / kBlock, s1 = ((tid + 1) * cnt) / kBlock;
+  double acc = 0.0;
+  for (int i = s0; i < s1; ++i) acc += part[i];
+  const double t = block_sum_f64_t<kWave>(acc, kWave);
+  __syncthreads();
+  if (lane == 0) wsum[wave] = t;
+  __syncthreads();
+  if (tid == 0) {
+    *jb.err_total = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+    b.counters[j] = 0u;
+  }
 }
 
 }  // namespace
 
-template <bool WITH_ERR, int G16, int S16>
-__device__ __forceinline__ void assign_row16(const AssignJob& jb, const Lut& lut, int n, int g16,
-                                             int s16, int log2S, int64_t r, int c0,
-                                             bool active, const uint16_t* wsafe,
-                                             const float* isafe, const uint4& va,
-                                             const uint4& vb, const float (&Ik)[16]) {
+template <int EM, int G16, int S16>
+__device__ __forceinline__ double assign_row16(const AssignJob& jb, const Lut& lut, int n,
+                                               int g16, int s16, int log2S, int64_t r, int c0,
+                                               bool active, const uint16_t* wsafe,
+                                               const float* isafe, const uint4& va,
+                                               const uint4& vb, const float (&Ik)[16]) {
   Row16 o;
-  row16_core<WITH_ERR, G16, S16>(lut, n, g16, s16, active, wsafe, isafe, va, vb, Ik, o);
+  row16_core<EM, G16, S16>(lut, n, g16, s16, active, wsafe, isafe, va, vb, Ik, o);
   const int64_t rc = r * jb.geom.C;          // wave-uniform; a multiple of S
   if (active)
-    store_row16<WITH_ERR>(o, jb.codes + (rc >> 3), jb.sel + (rc >> log2S),
-                          WITH_ERR ? jb.err + 2 * (rc >> log2S) : nullptr, s16, log2S, c0);
+    store_row16<EM>(o, jb.codes + (rc >> 3), jb.sel + (rc >> log2S),
+                    (EM == kErrFull && jb.err) ? jb.err + 2 * (rc >> log2S) : nullptr, s16, log2S,
+                    c0);
+  return (EM != kErrNone && active) ? o.Esel : 0.0;
 }
 
-template <bool WITH_ERR, int G16, int S16>
+template <int EM, int G16, int S16>
 __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
   __shared__ Lut lut;
   __shared__ LutScratch ls;
@@ -156,13 +209,19 @@ __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
   const int wave = wave_index();
   const int g16 = b.g / kWideLane, s16 = b.S / kWideLane, n = b.n;
   const int log2S = 31 - __builtin_clz((unsigned)b.S);
+  const bool totals = EM == kErrTotal || (EM == kErrFull && b.totals);
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
   int cur = -1;
+  double etot = 0.0;
   for (int64_t task = task_lo(blockIdx.x, b.total_tasks, gridDim.x); task < t_end; ++task) {
     int j = 0;
     while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
     const AssignJob& jb = b.job[j];
     if (j != cur) {
+      if (EM != kErrNone && totals && cur >= 0) {
+        finish_err_total(b, cur, etot);
+        etot = 0.0;
+      }
       __syncthreads();
       build_lut<kBlock>(jb.tables, n, lut, ls);
       cur = j;
@@ -196,13 +255,15 @@ __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
     for (int i = 0; i < kWideRowsPerWave; ++i) {
       const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
       if (r >= R) break;
-      assign_row16<WITH_ERR, G16, S16>(jb, lut, n, g16, s16, log2S, r, c0, active,
-                                        jb.W + r * C + cl, jb.I + cl, va[i], vb[i], Ik);
+      const double e = assign_row16<EM, G16, S16>(jb, lut, n, g16, s16, log2S, r, c0, active,
+                                                  jb.W + r * C + cl, jb.I + cl, va[i], vb[i], Ik);
+      if (EM != kErrNone) etot += e;
     }
   }
+  if (EM != kErrNone && totals && cur >= 0) finish_err_total(b, cur, etot);
 }
 
-template <bool WITH_ERR, int G8, int S8>
+template <int EM, int G8, int S8>
 __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
   __shared__ Lut lut;
   __shared__ LutScratch ls;
@@ -211,13 +272,19 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
   const int wave = tid / kWave;
   const int g8 = b.g / kPerLane, s8 = b.S / kPerLane, n = b.n;
   const int log2S = 31 - __builtin_clz((unsigned)b.S);
+  const bool totals = EM == kErrTotal || (EM == kErrFull && b.totals);
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
   int cur = -1;
+  double etot = 0.0;
   for (int64_t task = task_lo(blockIdx.x, b.total_tasks, gridDim.x); task < t_end; ++task) {
     int j = 0;
     while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
     const AssignJob& jb = b.job[j];
     if (j != cur) {
+      if (EM != kErrNone && totals && cur >= 0) {
+        finish_err_total(b, cur, etot);
+        etot = 0.0;
+      }
       __syncthreads();
       build_lut<kBlock>(jb.tables, n, lut, ls);
       cur = j;
@@ -250,46 +317,48 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
-      if (r < R)
-        assign_row<WITH_ERR, G8, S8>(jb, lut, n, g8, s8, log2S, r * C + c0, active, v[i], Ik);
+      if (r < R) {
+        const double e =
+            assign_row<EM, G8, S8>(jb, lut, n, g8, s8, log2S, r * C + c0, active, v[i], Ik);
+        if (EM != kErrNone) etot += e;
+      }
     }
   }
+  if (EM != kErrNone && totals && cur >= 0) finish_err_total(b, cur, etot);
 }
 
-template <bool WITH_ERR, int G8, int S8>
+// Grid of a launch: enough workgroups to fill every CU at the kernel's occupancy, at most one per
+// task and at most kMaxAssignBlocks. With totals, the jobs' workgroup ranges are recorded first.
+template <class K>
+hipError_t launch_with_grid(K kernel, const AssignBatch& b0, int& occ, hipStream_t stream) {
+  if (occ <= 0) {
+    int blocks = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, kBlock, 0);
+    occ = (e == hipSuccess && blocks > 0) ? blocks : 2;
+  }
+  int64_t want = (int64_t)device_cu_count() * occ;
+  if (want > kMaxAssignBlocks) want = kMaxAssignBlocks;
+  const int grid = (int)(b0.total_tasks < want ? b0.total_tasks : want);
+  if (grid <= 0) return hipSuccess;
+  AssignBatch b = b0;
+  if (b.totals) b.slots = job_slots(b.job, b.njobs, b.total_tasks, grid);
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(kBlock), 0, stream, b);
+  return hipGetLastError();
+}
+
+template <int EM, int G8, int S8>
 hipError_t launch_assign_t(const AssignBatch& b, hipStream_t stream) {
   static int occ = 0;
-  if (occ <= 0) {
-    int blocks = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &blocks, assign_kernel<WITH_ERR, G8, S8>, kBlock, 0);
-    occ = (e == hipSuccess && blocks > 0) ? blocks : 2;
-  }
-  const int64_t want = (int64_t)device_cu_count() * occ;
-  const int grid = (int)(b.total_tasks < want ? b.total_tasks : want);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((assign_kernel<WITH_ERR, G8, S8>), dim3(grid), dim3(kBlock), 0, stream, b);
-  return hipGetLastError();
+  return launch_with_grid(assign_kernel<EM, G8, S8>, b, occ, stream);
 }
 
-template <bool WITH_ERR, int G16, int S16>
+template <int EM, int G16, int S16>
 hipError_t launch_assign_wide_t(const AssignBatch& b, hipStream_t stream) {
   static int occ = 0;
-  if (occ <= 0) {
-    int blocks = 0;
-    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &blocks, assign_wide_kernel<WITH_ERR, G16, S16>, kBlock, 0);
-    occ = (e == hipSuccess && blocks > 0) ? blocks : 2;
-  }
-  const int64_t want = (int64_t)device_cu_count() * occ;
-  const int grid = (int)(b.total_tasks < want ? b.total_tasks : want);
-  if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL((assign_wide_kernel<WITH_ERR, G16, S16>), dim3(grid), dim3(kBlock), 0, stream,
-                     b);
-  return hipGetLastError();
+  return launch_with_grid(assign_wide_kernel<EM, G16, S16>, b, occ, stream);
 }
 
-template <bool WITH_ERR>
+template <int EM>
 hipError_t launch_assign_g(const AssignBatch& b, hipStream_t stream) {
   if (b.S >= kWideLane) {
     // same jobs, task numbering of the wide mapping
@@ -302,18 +371,19 @@ hipError_t launch_assign_g(const AssignBatch& b, hipStream_t stream) {
     }
     w.total_tasks = tb;
     const int g16 = b.g / kWideLane, s16 = b.S / kWideLane;
-    if (g16 == 8 && s16 == 8) return launch_assign_wide_t<WITH_ERR, 8, 8>(w, stream);   // 128/128
-    if (g16 == 8 && s16 == 1) return launch_assign_wide_t<WITH_ERR, 8, 1>(w, stream);   // 128/16
-    if (g16 == 1 && s16 == 1) return launch_assign_wide_t<WITH_ERR, 1, 1>(w, stream);   // 16/16
-    return launch_assign_wide_t<WITH_ERR, 0, 0>(w, stream);
+    if (g16 == 8 && s16 == 8) return launch_assign_wide_t<EM, 8, 8>(w, stream);   // 128/128
+    if (g16 == 8 && s16 == 1) return launch_assign_wide_t<EM, 8, 1>(w, stream);   // 128/16
+    if (g16 == 1 && s16 == 1) return launch_assign_wide_t<EM, 1, 1>(w, stream);   // 16/16
+    return launch_assign_wide_t<EM, 0, 0>(w, stream);
   }
   const int g8 = b.g / kPerLane, s8 = b.S / kPerLane;
-  if (g8 == 16 && s8 == 16) return launch_assign_t<WITH_ERR, 16, 16>(b, stream);
-  return launch_assign_t<WITH_ERR, 0, 0>(b, stream);
+  if (g8 == 16 && s8 == 16) return launch_assign_t<EM, 16, 16>(b, stream);
+  return launch_assign_t<EM, 0, 0>(b, stream);
 }
 
 hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream) {
-  return with_err ? launch_assign_g<true>(b, stream) : launch_assign_g<false>(b, stream);
+  if (with_err) return launch_assign_g<kErrFull>(b, stream);
+  return b.totals ? launch_assign_g<kErrTotal>(b, stream) : launch_assign_g<kErrNone>(b, stream);
 }
 
 }  // namespace aaac

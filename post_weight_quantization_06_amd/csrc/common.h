@@ -202,6 +202,9 @@ struct AssignJob {
   uint32_t* codes;          // [R * C / 8] dwords, 8 nibbles each
   uint8_t* sel;             // [R * C / S]
   double* err;              // nullable, [R * C / S][2]
+  double* err_total;        // nullable, one fp64: sum of the chosen errors over the matrix
+  int32_t wg_lo;            // first workgroup whose task range meets this job (totals only)
+  int32_t wg_count;         // number of such workgroups
 };
 
 struct AssignBatch {
@@ -209,7 +212,37 @@ struct AssignBatch {
   int32_t njobs;
   int32_t g, S, n;
   int64_t total_tasks;
+  int32_t totals;           // 1: every job's err_total is written (partials/counters given)
+  int32_t slots;            // largest wg_count of the batch
+  double* partials;         // [njobs][slots] per-workgroup sums of the chosen errors
+  uint32_t* counters;       // [njobs], zero between calls
 };
+
+// Workgroup b of a grid of nb owns tasks [task_lo(b), task_lo(b + 1)). Records in each job which
+// workgroups meet its tasks (wg_lo, wg_count) and returns the largest count.
+template <class Job>
+inline int32_t job_slots(Job* jobs, int njobs, int64_t total_tasks, int64_t nb) {
+  auto owner = [&](int64_t t) {
+    int64_t lo = 0, hi = nb - 1;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) / 2;
+      if (task_lo(mid, total_tasks, nb) <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  int32_t slots = 1;
+  for (int i = 0; i < njobs; ++i) {
+    const int64_t w0 = owner(jobs[i].geom.task_begin);
+    const int64_t w1 = owner(jobs[i].geom.task_begin + jobs[i].geom.ntasks - 1);
+    jobs[i].wg_lo = (int32_t)w0;
+    jobs[i].wg_count = (int32_t)(w1 - w0 + 1);
+    if (jobs[i].wg_count > slots) slots = jobs[i].wg_count;
+  }
+  return slots;
+}
+
+// Largest assign grid; the error-total workspace holds this many partials per matrix.
+constexpr int kMaxAssignBlocks = 4096;
 
 struct RefineJob {
   MatrixGeom geom;
@@ -221,20 +254,26 @@ struct RefineJob {
   float* tables_out;
   uint32_t* codes_out;      // fused assign + accumulate only: where the assign step writes
   uint8_t* sel_out;
+  double* err_out;          // nullable: error of the incoming assignment
+  double* w2;               // with err_out: sum I w^2 (output, or input with the W2-known flag)
   int32_t wg_lo;            // first workgroup whose task range meets this job
   int32_t wg_count;         // number of such workgroups
 };
+
+// Per-workgroup partial values of a refine: 64 cell sums (num, den of 32 cells), sum I w^2, pad.
+constexpr int kPartVals = 66;
 
 struct RefineBatch {
   RefineJob job[kMaxJobs];
   int32_t njobs;
   int32_t g, S, n;
   int64_t total_tasks;
-  double* partials;         // [njobs][64][slots]
+  double* partials;         // [njobs][kPartVals][slots]
   uint32_t* counters;       // [njobs], zero between calls
   int32_t nblocks;          // grid size
   int32_t slots;            // largest wg_count of the batch
-  int32_t flags;
+  int32_t flags;            // bit 0: round to bf16; bit 1: W2 given
+  int32_t errs;             // 1: the jobs have err_out
 };
 
 // ------------------------------------------------------------------------------------------------
@@ -242,6 +281,7 @@ struct RefineBatch {
 // ------------------------------------------------------------------------------------------------
 int device_cu_count();
 
+// with_err: the per-group error array (kErrFull); b.totals: the per-matrix totals.
 hipError_t launch_assign(const AssignBatch& b, bool with_err, hipStream_t stream);
 hipError_t launch_refine(RefineBatch& b, hipStream_t stream);
 int refine_grid(int64_t total_tasks);

@@ -14,12 +14,23 @@
 // magnitude: fp32 over four weights, then fp64. The selection is D < 0 (ties keep T0). Its
 // rounding error is below 8 * 2^-24 (E_0 + E_1), so a selection can only differ from the exact one
 // when |E_1 - E_0| < 1e-6 max(E_0, E_1).
+//
+// Error outputs (template parameter EM): kErrNone computes only D. kErrTotal also sums I m_0^2 and
+// I m_1^2 over each lane's weights (fp32 over four weights, then fp64; no reduction across lanes):
+// once the group's selection is known, each lane's share of the chosen error is its own sum for
+// the chosen table, so a matrix's total is the sum of every lane's share (no cancellation). kErrFull
+// also reduces E_0 and E_1 over each group for the error array.
 #ifndef AAAC_LOOKUP_H
 #define AAAC_LOOKUP_H
 
 #include "common.h"
 
 namespace aaac {
+
+constexpr int kErrNone = 0;
+constexpr int kErrTotal = 1;
+constexpr int kErrFull = 2;
+
 namespace {
 
 struct LutScratch {
@@ -169,8 +180,8 @@ __device__ __forceinline__ float lut_y(float se) { return kLutY * __builtin_amdg
 // Nearest entries of one weight in both tables from the lookup structure (see the layout above):
 // returns the record word with the code byte q0 | q1 << 4 in byte 0 (the increments never carry out
 // of a nibble: a pair whose second entry is past the table or NaN is never taken), and accumulates
-// I (m1^2 - m0^2) (and the two errors).
-template <bool WITH_ERR>
+// I (m1^2 - m0^2) (and I m0^2, I m1^2 as EM asks).
+template <int EM>
 __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, const Lut& lut,
                                                   float Ik, float& acc, float& a0, float& a1) {
   const float t = __builtin_fmaf(w, Y, kLutMagic);
@@ -191,7 +202,7 @@ __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, c
   const float m1 = fminf(fabsf(r1a), fabsf(r1b));
   const float e0 = m0 * m0;
   acc = __builtin_fmaf(Ik, __builtin_fmaf(m1, m1, -e0), acc);
-  if (WITH_ERR) {
+  if (EM >= kErrTotal) {
     a0 = __builtin_fmaf(Ik, e0, a0);
     a1 = __builtin_fmaf(Ik, m1 * m1, a1);
   }
@@ -249,7 +260,8 @@ __device__ __noinline__ void slow_lane16(const uint16_t* __restrict__ wp,
 struct Row16 {
   uint32_t E[2], O[2];
   uint32_t sel;      // 1 = T1
-  double E0, E1;     // only with WITH_ERR
+  double E0, E1;     // group errors (kErrFull)
+  double Esel;       // this lane's share of the row's chosen error (kErrTotal, kErrFull)
 };
 
 // One row: group scale, nearest entries of all sixteen weights, and the selection of each group.
@@ -257,7 +269,7 @@ struct Row16 {
 // address the lane's 16 weights and importances in memory (in bounds also for inactive lanes) for
 // the exact fallback. The compiler may interleave all sixteen lookups (the exact scan is out of
 // line, so the row stays within the register budget of four waves per SIMD).
-template <bool WITH_ERR, int G16, int S16>
+template <int EM, int G16, int S16>
 __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s16, bool active,
                                            const uint16_t* wsafe, const float* isafe,
                                            const uint4& va, const uint4& vb,
@@ -289,10 +301,9 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
     float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      c[4 * q + k] = lookup_weight<WITH_ERR>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc, a0,
-                                             a1);
+      c[4 * q + k] = lookup_weight<EM>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc, a0, a1);
     accd = (q == 0) ? (double)acc : accd + (double)acc;
-    if (WITH_ERR) {
+    if (EM >= kErrTotal) {
       e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
       e1d = (q == 0) ? (double)a1 : e1d + (double)a1;
     }
@@ -310,21 +321,25 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
     Ow[h] = __builtin_amdgcn_perm(o23, o01, 0x05040100u);
   }
   double D = block_sum_f64_t<S16>(accd, s16);
-  double E0 = WITH_ERR ? block_sum_f64_t<S16>(e0d, s16) : 0.0;
-  double E1 = WITH_ERR ? block_sum_f64_t<S16>(e1d, s16) : 0.0;
+  // the lane's own error sums (kErrTotal, kErrFull); kErrFull also reduces them over the group
+  double L0 = e0d, L1 = e1d;
+  double E0 = EM == kErrFull ? block_sum_f64_t<S16>(e0d, s16) : 0.0;
+  double E1 = EM == kErrFull ? block_sum_f64_t<S16>(e1d, s16) : 0.0;
   if (zero) {
     D = 0.0;
     E0 = 0.0;
     E1 = 0.0;
+    L0 = 0.0;
+    L1 = 0.0;
   }
   const bool bad = active && (!fast_scale || !(fabs(D) < __builtin_inf()));
   if (__any(bad)) {
     double lD, lE0, lE1;
     uint64_t clo, chi;
-    slow_lane16<WITH_ERR>(wsafe, isafe, amax, lut.tab, n, lD, lE0, lE1, clo, chi);
+    slow_lane16<(EM >= kErrTotal)>(wsafe, isafe, amax, lut.tab, n, lD, lE0, lE1, clo, chi);
     const double sD = block_sum_f64_t<S16>(lD, s16);
     double sE0 = 0.0, sE1 = 0.0;
-    if (WITH_ERR) {
+    if (EM == kErrFull) {
       sE0 = block_sum_f64_t<S16>(lE0, s16);
       sE1 = block_sum_f64_t<S16>(lE1, s16);
     }
@@ -332,6 +347,8 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
       D = sD;
       E0 = sE0;
       E1 = sE1;
+      L0 = lE0;
+      L1 = lE1;
       // byte k of (clo, chi) is weight k
       const uint32_t l0 = (uint32_t)clo, l1 = (uint32_t)(clo >> 32);
       const uint32_t h0 = (uint32_t)chi, h1 = (uint32_t)(chi >> 32);
@@ -346,13 +363,14 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
   o.sel = (D < 0.0) ? 1u : 0u;
   o.E0 = E0;
   o.E1 = E1;
+  o.Esel = o.sel ? L1 : L0;
 }
 
 // Store the selected codes (8 bytes), and once per selection group the selector (and errors).
 // codes_row, sel_row and err_row point at the row's first code word, selector and error pair
 // (wave-uniform); c0 is the lane's first column. Rows start on a selection-group boundary, so the
 // lane's offsets within the row follow from c0 alone.
-template <bool WITH_ERR>
+template <int EM>
 __device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes_row, uint8_t* sel_row,
                                             double* err_row, int s16, int log2S, int c0) {
   const uint32_t sh = o.sel ? 4u : 0u;
@@ -368,7 +386,7 @@ __device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes_row,
   if (((c0 >> 4) & (s16 - 1)) == 0) {
     const int h = c0 >> log2S;
     sel_row[h] = (uint8_t)o.sel;
-    if (WITH_ERR) {
+    if (EM == kErrFull && err_row) {
       err_row[2 * h] = o.E0;
       err_row[2 * h + 1] = o.E1;
     }

@@ -4,8 +4,9 @@
 // the weights whose selection group chose c and whose code is j; the new entry is num / den (the
 // minimizer of sum I (w - s t)^2), or the old entry if the cell is empty.
 //
-// Accumulation: each term is exact in fp64 (s w and s^2 have at most 16 significant bits, times
-// the 24-bit I), and every thread adds its terms into a private column of 64 fp64 bins in LDS
+// Accumulation: each term is exact in fp64 for every finite input (s w and s^2 are products of two
+// bf16 values, at most 16 significant bits, formed in fp64, times the 24-bit I; the exponents stay
+// far inside the fp64 range), and every thread adds its terms into a private column of 64 fp64 bins in LDS
 // (32 cells x {num, den}, laid out [bin][thread]) with ds_add_f64. When a workgroup leaves a matrix
 // it reduces its 256 columns in a fixed order and writes one fp64 partial per (bin, workgroup); the
 // last workgroup to finish that matrix (an integer ticket) adds the partials in workgroup order and
@@ -13,6 +14,13 @@
 //
 // The bins take 128 KB, one workgroup per CU; to keep enough bytes in flight each wave loads the
 // rows of its next task before it accumulates the current one.
+//
+// Error of the incoming assignment (optional). With the cell sums, the total weighted error of the
+// codes and selectors under the tables they were chosen with is
+//   E = sum I (w - s T_c[q])^2 = W2 - 2 sum_cells T num + sum_cells T^2 den,   W2 = sum I w^2,
+// formed by the last workgroup of the matrix before it writes the new tables. W2 depends only on
+// W and I: the caller either has it from an earlier call (then it costs nothing), or every thread
+// sums I w^2 over its weights in a register (exact fp64 terms), one more fp64 fma per weight.
 #include <type_traits>
 
 #include "common.h"
@@ -24,6 +32,7 @@ namespace {
 
 constexpr int kCells = 32;   // 2 tables x 16 entries
 constexpr int kVals = 64;    // value v = 2 cell + {0: num, 1: den}
+constexpr int kW2 = 64;      // partial value 64: sum I w^2 (with error output)
 
 // bins[cell][sum][thread]: a thread's num and den of one cell are 2 KB apart (one immediate
 // offset), and the 64 lanes of a wave touch 64 consecutive doubles (no bank conflicts).
@@ -128,8 +137,9 @@ __device__ __forceinline__ void load_task(const TaskCursor& c, int log2S, TaskRo
   t.I1 = *reinterpret_cast<const float4*>(c.I + cl + 4);
 }
 
-template <int G8>
-__device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, RefineShared& sh) {
+template <int G8, bool ERRS>
+__device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, RefineShared& sh,
+                                                double& w2) {
   const int tid = threadIdx.x;
   const float If[8] = {t.I0.x, t.I0.y, t.I0.z, t.I0.w, t.I1.x, t.I1.y, t.I1.z, t.I1.w};
   double Id[8];
@@ -149,7 +159,10 @@ __device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, Refin
   for (int i = 0; i < kRowsPerWave; ++i) {
     // rows past the end of the matrix are the same for the whole wave
     if (t.r0 + (int64_t)kWavesPerBlock * i >= t.R) break;
-    const double s2 = (double)(s[i] * s[i]);     // exact: s has 8 significant bits
+    // s w and s^2 are formed in fp64: products of two bf16 values (16 significant bits) are
+    // exact there for every finite bf16 scale, and so are their products with the fp32 I
+    const double sd = (double)s[i];
+    const double s2 = sd * sd;
     float w[8];
     unpack8(t.v[i], w);
     char* const row = lds + (t.sb[i] ? 16 * sizeof(sh.bins[0]) : 0);
@@ -157,8 +170,10 @@ __device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, Refin
     for (int k = 0; k < 8; ++k) {
       const uint32_t q = (t.cw[i] >> (4 * k)) & 15u;
       double* const p = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
-      atomicAdd(p, Id[k] * (double)(s[i] * w[k]));    // s w is exact in fp32
+      const double wd = (double)w[k];
+      atomicAdd(p, Id[k] * (sd * wd));
       atomicAdd(p + kBlock, Id[k] * s2);
+      if (ERRS) w2 = __builtin_fma(Id[k] * (t.active ? 1.0 : 0.0), wd * wd, w2);
     }
     // one row at a time: interleaving rows would push the live registers past the 256 a lane can
     // address and spill loaded values that are still in flight
@@ -206,9 +221,9 @@ __device__ __forceinline__ void load_task16(const TaskCursor& c, int log2S, Task
 // col: this thread's column of bins (its index among the accumulating threads). PART: weights
 // whose terms are formed before their adds are issued (16: the whole row; 8: half a row, for
 // kernels that must keep registers low). The adds go out in the same order either way.
-template <int G16, int PART = 16>
+template <int G16, int PART = 16, bool ERRS = false>
 __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, RefineShared& sh,
-                                                  int col) {
+                                                  int col, double& w2) {
   const int tid = col;
   const float If[16] = {t.I[0].x, t.I[0].y, t.I[0].z, t.I[0].w, t.I[1].x, t.I[1].y,
                         t.I[1].z, t.I[1].w, t.I[2].x, t.I[2].y, t.I[2].z, t.I[2].w,
@@ -225,7 +240,8 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
 #pragma unroll
   for (int i = 0; i < kWideRowsPerWave; ++i) {
     if (t.r0 + (int64_t)kWavesPerBlock * i >= t.R) break;
-    const double s2 = (double)(s[i] * s[i]);     // exact: s has 8 significant bits
+    const double sd = (double)s[i];               // fp64 terms: exact for every bf16 scale
+    const double s2 = sd * sd;
     float w[16];
     unpack8(t.va[i], *reinterpret_cast<float(*)[8]>(&w[0]));
     unpack8(t.vb[i], *reinterpret_cast<float(*)[8]>(&w[8]));
@@ -243,8 +259,11 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
         const uint32_t q = (word >> (4 * (k & 7))) & 15u;
         p[u] = reinterpret_cast<double*>(row + q * sizeof(sh.bins[0]));
         const double Id = (double)If[k];
-        num[u] = Id * (double)(s[i] * w[k]);       // s w is exact in fp32
+        const double wd = (double)w[k];
+        num[u] = Id * (sd * wd);
         den[u] = Id * s2;
+        // a lane past the last column reads a weight of its own matrix: it adds nothing
+        if (ERRS) w2 = __builtin_fma(t.active ? Id : 0.0, wd * wd, w2);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -264,13 +283,15 @@ __device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, TaskRo
 __device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, TaskRows16& t) {
   load_task16(c, log2S, t);
 }
-template <int GL>
-__device__ __forceinline__ void accumulate_rows(const TaskRows& t, int gl, RefineShared& sh) {
-  accumulate_task<GL>(t, gl, sh);
+template <int GL, bool ERRS>
+__device__ __forceinline__ void accumulate_rows(const TaskRows& t, int gl, RefineShared& sh,
+                                                double& w2) {
+  accumulate_task<GL, ERRS>(t, gl, sh, w2);
 }
-template <int GL>
-__device__ __forceinline__ void accumulate_rows(const TaskRows16& t, int gl, RefineShared& sh) {
-  accumulate_task16<GL>(t, gl, sh, threadIdx.x);
+template <int GL, bool ERRS>
+__device__ __forceinline__ void accumulate_rows(const TaskRows16& t, int gl, RefineShared& sh,
+                                                double& w2) {
+  accumulate_task16<GL, 16, ERRS>(t, gl, sh, threadIdx.x, w2);
 }
 
 // Round a finite fp64 value to bf16 (ties to even) directly, without an intermediate fp32
@@ -287,14 +308,24 @@ __device__ __forceinline__ float f64_to_bf16_value(double x) {
 }
 
 // Publish this workgroup's partial of job j (and zero the bins); the last workgroup of the job adds
-// all partials and writes the tables. Every thread of the workgroup calls it (it holds barriers);
-// tid is the caller's index among the kBlock accumulating threads, and threads outside [0, kBlock)
-// only take part in the barriers.
-__device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int tid) {
+// all partials and writes the tables (and with ERRS the error of the incoming assignment; w2 is the
+// caller's running sum of I w^2, reset here). Every thread of the workgroup calls it (it holds
+// barriers); tid is the caller's index among the kBlock accumulating threads, and threads outside
+// [0, kBlock) only take part in the barriers.
+template <bool ERRS>
+__device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int tid, double& w2) {
+  // ERRS: this call summed I w^2 (w2); b.errs alone: W2 comes from the caller
   const bool act = tid >= 0 && tid < kBlock;
   const RefineJob& jb = b.job[j];
   __shared__ double part4[4][kVals];
+  __shared__ double w2s[kWavesPerBlock + 1];
   __shared__ uint32_t ticket;
+  if (ERRS) {
+    // this workgroup's sum of I w^2: lanes by butterfly, waves in order
+    const double ws = block_sum_f64_t<kWave>(act ? w2 : 0.0, kWave);
+    w2 = 0.0;
+    if (act && (tid & (kWave - 1)) == 0) w2s[tid / kWave] = ws;
+  }
   __syncthreads();
   if (act) {
     // value v = tid & 63 over the 64 columns of quarter q = tid >> 6: four interleaved sums over a
@@ -312,11 +343,15 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
 #pragma unroll
     for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
   }
-  double* part = b.partials + (size_t)j * kVals * b.slots;
+  double* part = b.partials + (size_t)j * kPartVals * b.slots;
   const int slot = (int)blockIdx.x - jb.wg_lo;
   if (act && tid < kVals) {
     const double tot = ((part4[0][tid] + part4[1][tid]) + part4[2][tid]) + part4[3][tid];
     part[(size_t)tid * b.slots + slot] = tot;
+    __threadfence();
+  }
+  if (ERRS && act && tid == kVals) {
+    part[(size_t)kW2 * b.slots + slot] = ((w2s[0] + w2s[1]) + w2s[2]) + w2s[3];
     __threadfence();
   }
   __syncthreads();
@@ -344,16 +379,41 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
     for (; i < s1; ++i) s += pv[i];
     part4[q][v] = s;
   }
+  if (ERRS && act && (tid & 63) == 0) {
+    // the I w^2 partials, quarter q of the workgroups per thread, in workgroup order
+    const int q = tid >> 6;
+    const int cnt = jb.wg_count;
+    const double* pv = part + (size_t)kW2 * b.slots;
+    double s = 0.0;
+    for (int i = (q * cnt) / 4; i < ((q + 1) * cnt) / 4; ++i) s += pv[i];
+    w2s[q] = s;
+  }
   __syncthreads();
+  __shared__ double eterm[kCells];
   if (act && tid < kCells) {
     const int c = tid >> 4, idx = tid & 15;
     const int vn = 2 * tid, vd = 2 * tid + 1;
     const double nsum = ((part4[0][vn] + part4[1][vn]) + part4[2][vn]) + part4[3][vn];
     const double dsum = ((part4[0][vd] + part4[1][vd]) + part4[2][vd]) + part4[3][vd];
+    double et = 0.0;
     if (idx < b.n) {
       const float old = jb.tables_in[c * b.n + idx];
       const double val = dsum > 0.0 ? nsum / dsum : (double)old;
+      // this cell's part of the incoming error: T^2 den - 2 T num with the old entry T
+      const double T = (double)old;
+      et = T * (T * dsum - 2.0 * nsum);
       jb.tables_out[c * b.n + idx] = (b.flags & 1) ? f64_to_bf16_value(val) : (float)val;
+    }
+    if (b.errs) eterm[tid] = et;
+  }
+  if (b.errs) {
+    __syncthreads();
+    if (tid == 0 && jb.err_out) {
+      const double W2 = ERRS ? ((w2s[0] + w2s[1]) + w2s[2]) + w2s[3] : *jb.w2;
+      double x = 0.0;
+      for (int k = 0; k < kCells; ++k) x += eterm[k];
+      jb.err_out[0] = W2 + x;
+      if (ERRS) *jb.w2 = W2;
     }
   }
   if (tid == 0) b.counters[j] = 0u;
@@ -362,7 +422,7 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
 
 }  // namespace
 
-template <bool WIDE, int GL>
+template <bool WIDE, int GL, bool ERRS>
 __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
   __shared__ RefineShared sh;
   const int tid = threadIdx.x;
@@ -376,6 +436,7 @@ __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
   typedef typename std::conditional<WIDE, TaskRows16, TaskRows>::type Rows;
   Rows A, B;
   int cur = -1;
+  double w2 = 0.0;
   if (t_begin >= t_end) return;
   // the cursor stops at the last task: past the end a buffer reloads that task and is never used
   TaskCursor c;
@@ -386,20 +447,20 @@ __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
     load_rows(c, log2S, B);
     cursor_next(b, c);
     if (A.job != cur) {
-      if (cur >= 0) finish_job(b, cur, sh, threadIdx.x);
+      if (cur >= 0) finish_job<ERRS>(b, cur, sh, threadIdx.x, w2);
       cur = A.job;
     }
-    accumulate_rows<GL>(A, gl, sh);
+    accumulate_rows<GL, ERRS>(A, gl, sh, w2);
     if (task + 1 >= t_end) break;
     load_rows(c, log2S, A);
     cursor_next(b, c);
     if (B.job != cur) {
-      finish_job(b, cur, sh, threadIdx.x);
+      finish_job<ERRS>(b, cur, sh, threadIdx.x, w2);
       cur = B.job;
     }
-    accumulate_rows<GL>(B, gl, sh);
+    accumulate_rows<GL, ERRS>(B, gl, sh, w2);
   }
-  if (cur >= 0) finish_job(b, cur, sh, threadIdx.x);
+  if (cur >= 0) finish_job<ERRS>(b, cur, sh, threadIdx.x, w2);
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -479,11 +540,11 @@ __device__ __forceinline__ void fused_assign_task(const RefineBatch& b, const Re
     const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
     if (r >= R) break;
     Row16 o;
-    row16_core<false, G16, S16>(lut, n, g16, s16, active, jb.W + r * C + cl, jb.I + cl, va[i],
+    row16_core<kErrNone, G16, S16>(lut, n, g16, s16, active, jb.W + r * C + cl, jb.I + cl, va[i],
                                 vb[i], Ik, o);
     const int64_t rc = r * C;
     if (active)
-      store_row16<false>(o, jb.codes_out + (rc >> 3), jb.sel_out + (rc >> log2S), nullptr, s16,
+      store_row16<kErrNone>(o, jb.codes_out + (rc >> 3), jb.sel_out + (rc >> log2S), nullptr, s16,
                          log2S, c0);
     sh.sig[buf][grp][w + kWavesPerBlock * i][lane] = (uint8_t)o.sel;
   }
@@ -519,7 +580,8 @@ __device__ __forceinline__ void fused_accumulate_task(const RefineBatch& b, cons
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
-  accumulate_task16<G16, 8>(t, b.g / kWideLane, sh.rs, (int)threadIdx.x - kFusedAcc0);
+  double w2 = 0.0;
+  accumulate_task16<G16, 8>(t, b.g / kWideLane, sh.rs, (int)threadIdx.x - kFusedAcc0, w2);
 }
 
 }  // namespace
@@ -538,6 +600,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void assign_refine_kernel(RefineB
   const int64_t t_begin = task_lo(blockIdx.x, b.total_tasks, gridDim.x);
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
   int lut_job = -1, acc_job = -1;
+  double w2_unused = 0.0;
   int prev_job = -1;
   int64_t prev_lo = 0, prev_hi = 0;                    // the step the accumulate waves take next
   int buf = 0;
@@ -549,7 +612,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void assign_refine_kernel(RefineB
     // matrix changes, with every thread: the accumulate side finishes its matrix before it starts
     // the next one; the assign side builds the lookup structure of its new matrix
     if (prev_job >= 0 && prev_job != acc_job) {
-      if (acc_job >= 0) finish_job(b, acc_job, sh.rs, atid);
+      if (acc_job >= 0) finish_job<false>(b, acc_job, sh.rs, atid, w2_unused);
       acc_job = prev_job;
     }
     if (job >= 0 && job != lut_job) {
@@ -576,7 +639,7 @@ __global__ __launch_bounds__(kFusedThreads, 1) void assign_refine_kernel(RefineB
     prev_hi = hi;
     lo = hi;
   }
-  if (acc_job >= 0) finish_job(b, acc_job, sh.rs, atid);
+  if (acc_job >= 0) finish_job<false>(b, acc_job, sh.rs, atid, w2_unused);
 }
 
 hipError_t launch_assign_refine(RefineBatch& b, hipStream_t stream) {
@@ -605,21 +668,28 @@ int refine_grid(int64_t total_tasks) {
   return (int)(total_tasks < want ? total_tasks : want);
 }
 
-hipError_t launch_refine(RefineBatch& b, hipStream_t stream) {
-  if (b.nblocks <= 0) return hipSuccess;
+template <bool ERRS>
+hipError_t launch_refine_t(RefineBatch& b, hipStream_t stream) {
   const dim3 grid(b.nblocks), block(kBlock);
   if (b.S >= kWideLane) {
     const int g16 = b.g / kWideLane;
     if (g16 == 8)
-      hipLaunchKernelGGL((refine_kernel<true, 8>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((refine_kernel<true, 8, ERRS>), grid, block, 0, stream, b);
     else if (g16 == 1)
-      hipLaunchKernelGGL((refine_kernel<true, 1>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((refine_kernel<true, 1, ERRS>), grid, block, 0, stream, b);
     else
-      hipLaunchKernelGGL((refine_kernel<true, 0>), grid, block, 0, stream, b);
+      hipLaunchKernelGGL((refine_kernel<true, 0, ERRS>), grid, block, 0, stream, b);
   } else {
-    hipLaunchKernelGGL((refine_kernel<false, 0>), grid, block, 0, stream, b);
+    hipLaunchKernelGGL((refine_kernel<false, 0, ERRS>), grid, block, 0, stream, b);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_refine(RefineBatch& b, hipStream_t stream) {
+  if (b.nblocks <= 0) return hipSuccess;
+  // the I w^2 sum only when the caller does not have it
+  if (b.errs && !(b.flags & 2)) return launch_refine_t<true>(b, stream);
+  return launch_refine_t<false>(b, stream);
 }
 
 }  // namespace aaac

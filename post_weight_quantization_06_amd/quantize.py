@@ -1,18 +1,30 @@
-"""Loop driver over the C ABI (AAAC summary §2 mechanism 4): init, iters x (assign, refine), bf16
-tables, final assign, pack.
+"""Loop driver over the C ABI (AAAC summary §2 mechanism 4): importance, init, iters x (assign,
+refine), bf16 tables, final assign, pack -- for a set of matrices, a decoder layer, or a whole model
+streamed layer by layer (§4: models up to 32B; every layer is quantized on its own, from its own
+activations).
 
 Control flow only: every step is one library call enqueued on the current stream; the host does not
 synchronize inside the loop. Device buffers come from torch.
+
+The total weighted error of every assignment is kept on the device in a history
+[iters + 1, matrices]: row t is the error of iteration t's assignment, reported by the refine that
+consumes it (from its cell sums, at the cost of one register sum per thread), and the last row is
+the final assign's own err_total against the bf16 tables. The alternation is a k-means descent, so
+rows 0 .. iters-1 never increase; `check_history` verifies that after the loop (one host read).
 """
 
 from __future__ import annotations
 
 import dataclasses
-from typing import Iterable, List, Optional, Sequence
+from typing import Callable, Dict, Iterable, List, Optional, Sequence, Tuple
 
 import torch
 
 from . import _lib as L
+
+# relative slack of the monotonicity check: the error totals are fp64 sums of fp32-rounded terms
+# (relative error below 2.4e-7), and decisions inside the 1e-6 tie band may go either way
+MONOTONE_RTOL = 1e-6
 
 
 @dataclasses.dataclass
@@ -28,6 +40,7 @@ class QuantizedMatrix:
     scales: torch.Tensor         # int16 [R, C/g] bf16 bits, sign bit = selector when S == g
     bitmap: Optional[torch.Tensor]  # uint8 [ceil(R C / S / 8)] when S < g
     tables_bf16: torch.Tensor    # int16 [2, n] bf16 bits
+    err_history: Optional[torch.Tensor] = None   # fp64 [iters + 1] total error per assign
 
     def dequant(self, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         if out is None:
@@ -47,25 +60,9 @@ class QuantizedMatrix:
         return out
 
 
-def importance(chunks: Iterable[torch.Tensor], K: int, device) -> torch.Tensor:
-    """fp32 [K] I_k = sum over all chunks of X[:, k]^2, accumulated in fp64 on the device."""
-    acc = torch.zeros(K, dtype=torch.float64, device=device)
-    out = torch.empty(K, dtype=torch.float32, device=device)
-    ws = None
-    any_chunk = False
-    for X in chunks:
-        need = L.workspace_bytes(L.OP_IMPORTANCE, X.shape[0], K)
-        if ws is None or ws.numel() < need:
-            ws = L.workspace(need, device)
-        L.aaac_importance(X, acc, out, ws)
-        any_chunk = True
-    if not any_chunk:
-        L.aaac_importance(torch.empty(0, K, dtype=torch.float32, device=device), acc, out)
-    return out
-
-
 class Workspaces:
-    """Zero-filled workspaces reused across the calls of one quantization run."""
+    """Zero-filled workspaces reused across the calls of one quantization run (each call leaves its
+    counters zero again, so a workspace serves any later call it is large enough for)."""
 
     def __init__(self, device):
         self.device = device
@@ -79,67 +76,233 @@ class Workspaces:
         return t
 
 
-def _batches(seq, k=L.MAX_BATCH):
-    for i in range(0, len(seq), k):
-        yield i, seq[i:i + k]
+def importance(chunks: Iterable[torch.Tensor], K: int, device,
+               workspaces: Optional[Workspaces] = None, acc: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """fp32 [K] I_k = sum over all chunks of X[:, k]^2, accumulated in fp64 on the device (AAAC
+    summary §2 mechanism 2). chunks: fp32 [T_i, K] tensors (one resident tensor is one chunk)."""
+    wsp = workspaces or Workspaces(device)
+    acc = torch.zeros(K, dtype=torch.float64, device=device) if acc is None else acc.zero_()
+    out = torch.empty(K, dtype=torch.float32, device=device) if out is None else out
+    any_chunk = False
+    for X in chunks:
+        L.aaac_importance(X, acc, out, wsp.get(("importance", K),
+                                               L.workspace_bytes(L.OP_IMPORTANCE, X.shape[0], K)))
+        any_chunk = True
+    if not any_chunk:
+        L.aaac_importance(torch.empty(0, K, dtype=torch.float32, device=device), acc, out)
+    return out
+
+
+def _batches(k, size=L.MAX_BATCH):
+    for b0 in range(0, k, size):
+        yield slice(b0, min(k, b0 + size))
+
+
+class LayerBuffers:
+    """Device outputs of one set of matrices that share (g, S, n): codes, selectors, fp32 and bf16
+    tables, scales, bitmaps and the error history. Allocated once; a run overwrites them."""
+
+    def __init__(self, shapes: Sequence[Tuple[int, int]], g: int, S: int, n: int, iters: int,
+                 device):
+        self.shapes = [tuple(s) for s in shapes]
+        self.g, self.S, self.n, self.iters = g, S, n, iters
+        self.device = device
+        dev = device
+        self.codes = [torch.empty(R * C // 2, dtype=torch.uint8, device=dev) for R, C in shapes]
+        self.sels = [torch.empty(R * C // S, dtype=torch.uint8, device=dev) for R, C in shapes]
+        self.tables = [torch.empty(2 * n, dtype=torch.float32, device=dev) for _ in shapes]
+        self.scales = [torch.empty(R * C // g, dtype=torch.int16, device=dev) for R, C in shapes]
+        self.bitmaps = ([torch.empty((R * C // S + 7) // 8, dtype=torch.uint8, device=dev)
+                         for R, C in shapes] if S < g else None)
+        self.tables_bf16 = [torch.empty(2 * n, dtype=torch.int16, device=dev) for _ in shapes]
+        # error history: err[t, i] = total error of iteration t's assignment of matrix i (rows
+        # 0 .. iters-1 from the refine that consumes it, the last row from the final assign);
+        # w2[i] = sum I w^2 of matrix i (summed by the first refine, read by the others)
+        self.err = torch.zeros(iters + 1, len(shapes), dtype=torch.float64, device=dev)
+        self.w2 = torch.zeros(len(shapes), dtype=torch.float64, device=dev)
+
+    def results(self) -> List[QuantizedMatrix]:
+        out = []
+        for i, (R, C) in enumerate(self.shapes):
+            out.append(QuantizedMatrix(
+                R, C, self.g, self.S, self.n, self.codes[i].view(R, C // 2),
+                self.sels[i].view(R, C // self.S), self.tables[i].view(2, self.n),
+                self.scales[i].view(R, C // self.g),
+                self.bitmaps[i] if self.bitmaps is not None else None,
+                self.tables_bf16[i].view(2, self.n), self.err[:, i]))
+        return out
+
+
+class Probe:
+    """Hooks the loop calls on the host as it enqueues work (for timing with stream events).
+    The default does nothing."""
+
+    def loop_begin(self):
+        pass
+
+    def before_assign(self, it):
+        pass
+
+    def before_refine(self, it):
+        pass
+
+    def after_refine(self, it):
+        pass
+
+    def loop_end(self):
+        pass
+
+
+def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerBuffers,
+             wsp: Workspaces, init: bool = True, pack: bool = True,
+             probe: Optional[Probe] = None, totals: bool = True) -> LayerBuffers:
+    """Enqueue the quantization of matrices Ws (bf16 [R_i, C_i]) with importances Is (fp32 [C_i])
+    into buf: batched init (unless init is False: then buf.tables hold the starting tables),
+    buf.iters x (batched assign, batched refine; the last refine rounds the tables to bf16), the
+    final assign, and pack. With totals, every refine reports the error of the assignment it
+    consumes and the final assign its own (buf.err), and the first refine sums buf.w2."""
+    g, S, n, iters = buf.g, buf.S, buf.n, buf.iters
+    if iters < 1:
+        raise ValueError("iters must be >= 1 (the last refine rounds the tables to bf16)")
+    k = len(Ws)
+    Rs = [W.shape[0] for W in Ws]
+    Cs = [W.shape[1] for W in Ws]
+    if [tuple(W.shape) for W in Ws] != buf.shapes:
+        raise ValueError("matrix shapes do not match the buffers")
+    pr = probe or Probe()
+    sl = list(_batches(k))
+    if init:
+        for b in sl:
+            need = L.batch_workspace_bytes(L.OP_INIT, Rs[b], Cs[b], g, 8, n)
+            L.aaac_init_quantiles_batch(Ws[b], g, n, buf.tables[b], wsp.get("init", need))
+
+    pr.loop_begin()
+    for it in range(iters):
+        flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
+        pr.before_assign(it)
+        for b in sl:
+            L.aaac_assign_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b], buf.sels[b])
+        pr.before_refine(it)
+        for b in sl:
+            ws_r = wsp.get(("refine", b.start), L.batch_workspace_bytes(
+                L.OP_REFINE, Rs[b], Cs[b], g, S, n))
+            if totals and it > 0:
+                flags |= L.REFINE_W2_KNOWN
+            L.aaac_refine_batch(Ws[b], g, S, n, Is[b], buf.codes[b], buf.sels[b], buf.tables[b],
+                                flags, ws_r, buf.err[it, b] if totals else None,
+                                buf.w2[b] if totals else None)
+        pr.after_refine(it)
+    pr.loop_end()
+    for b in sl:
+        ws_a = (wsp.get(("assign", b.start), L.batch_workspace_bytes(L.OP_ASSIGN, Rs[b], Cs[b],
+                                                                        g, S, n))
+                if totals else None)
+        L.aaac_assign_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b], buf.sels[b],
+                            buf.err[iters, b] if totals else None, ws_a)
+    if pack:
+        for b in sl:
+            L.aaac_pack_batch(Ws[b], g, S, n, buf.sels[b], buf.tables[b], buf.scales[b],
+                              buf.bitmaps[b] if buf.bitmaps is not None else None,
+                              buf.tables_bf16[b])
+    return buf
+
+
+def check_history(err: torch.Tensor, rtol: float = MONOTONE_RTOL,
+                  w2: Optional[torch.Tensor] = None):
+    """Raise if the total error of some matrix increased from one iteration's assignment to the
+    next (rows 0 .. iters-1 of the history; the last row, against the bf16-rounded tables, is not
+    comparable). w2 (sum I w^2 per matrix, or None) widens the slack by the 1e-15 W2 accuracy of
+    the errors refine reports. Reads the history from the device (synchronizes)."""
+    h = err.detach().double().cpu()
+    if h.dim() == 1:
+        h = h[:, None]
+    body = h[:-1]
+    if body.shape[0] >= 2:
+        slack = body[:-1] * rtol
+        if w2 is not None:
+            slack = slack + 1e-13 * w2.detach().double().cpu().reshape(1, -1)
+        bad = body[1:] > body[:-1] + slack
+        if bool(bad.any()):
+            t, m = [int(x) for x in bad.nonzero()[0]]
+            raise RuntimeError("total error increased for matrix %d from iteration %d to %d: "
+                               "%.17g -> %.17g" % (m, t, t + 1, float(body[t, m]),
+                                                   float(body[t + 1, m])))
+    return h
 
 
 def quantize_matrices(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], g: int, S: int,
                       n: int, iters: int, tables: Optional[Sequence[torch.Tensor]] = None,
-                      workspaces: Optional[Workspaces] = None) -> List[QuantizedMatrix]:
-    """Quantize matrices that share (g, S, n); matrix i uses importance Is[i] (fp32 [C_i])."""
-    if iters < 1:
-        raise ValueError("iters must be >= 1 (the last refine rounds the tables to bf16)")
+                      workspaces: Optional[Workspaces] = None,
+                      check: bool = True) -> List[QuantizedMatrix]:
+    """Quantize matrices that share (g, S, n); matrix i uses importance Is[i] (fp32 [C_i]).
+    With check, the error history is verified to be non-increasing (one synchronization)."""
     dev = Ws[0].device
     wsp = workspaces or Workspaces(dev)
-    k = len(Ws)
-    Rs = [W.shape[0] for W in Ws]
-    Cs = [W.shape[1] for W in Ws]
-    codes = [torch.empty(R * C // 2, dtype=torch.uint8, device=dev) for R, C in zip(Rs, Cs)]
-    sels = [torch.empty(R * C // S, dtype=torch.uint8, device=dev) for R, C in zip(Rs, Cs)]
-    if tables is None:
-        tabs = [torch.empty(2 * n, dtype=torch.float32, device=dev) for _ in range(k)]
-        for b0, group in _batches(list(range(k))):
-            sl = slice(b0, b0 + len(group))
-            need = L.batch_workspace_bytes(L.OP_INIT, Rs[sl], Cs[sl], g, 8, n)
-            L.aaac_init_quantiles_batch(Ws[sl], g, n, tabs[sl], wsp.get("init", need))
-    else:
-        tabs = [t.reshape(-1).to(torch.float32).clone() for t in tables]
-    for it in range(iters):
-        flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
-        for b0, group in _batches(list(range(k))):
-            sl = slice(b0, b0 + len(group))
-            Wb, Ib = Ws[sl], Is[sl]
-            L.aaac_assign_batch(Wb, g, S, n, Ib, tabs[sl], codes[sl], sels[sl])
-            ws_r = wsp.get(("refine", b0), L.batch_workspace_bytes(
-                L.OP_REFINE, Rs[sl], Cs[sl], g, S, n))
-            L.aaac_refine_batch(Wb, g, S, n, Ib, codes[sl], sels[sl], tabs[sl], flags, ws_r)
-    for b0, group in _batches(list(range(k))):
-        sl = slice(b0, b0 + len(group))
-        L.aaac_assign_batch(Ws[sl], g, S, n, Is[sl], tabs[sl], codes[sl], sels[sl])
-    scales = [torch.empty(R * C // g, dtype=torch.int16, device=dev) for R, C in zip(Rs, Cs)]
-    bitmaps = ([torch.empty((R * C // S + 7) // 8, dtype=torch.uint8, device=dev)
-                for R, C in zip(Rs, Cs)] if S < g else None)
-    tbs = [torch.empty(2 * n, dtype=torch.int16, device=dev) for _ in range(k)]
-    for b0, group in _batches(list(range(k))):
-        sl = slice(b0, b0 + len(group))
-        L.aaac_pack_batch(Ws[sl], g, S, n, sels[sl], tabs[sl], scales[sl],
-                          bitmaps[sl] if bitmaps is not None else None, tbs[sl])
-    out = []
-    for i in range(k):
-        R, C = Rs[i], Cs[i]
-        out.append(QuantizedMatrix(R, C, g, S, n, codes[i].view(R, C // 2),
-                                   sels[i].view(R, C // S), tabs[i].view(2, n),
-                                   scales[i].view(R, C // g),
-                                   bitmaps[i] if bitmaps is not None else None,
-                                   tbs[i].view(2, n)))
-    return out
+    buf = LayerBuffers([tuple(W.shape) for W in Ws], g, S, n, iters, dev)
+    if tables is not None:
+        for t, src in zip(buf.tables, tables):
+            t.copy_(src.reshape(-1).to(torch.float32))
+    run_loop(Ws, Is, buf, wsp, init=tables is None)
+    if check:
+        check_history(buf.err, w2=buf.w2)
+    return buf.results()
 
 
 def quantize_matrix(W: torch.Tensor, I: torch.Tensor, g: int = 128, S: int = 128, n: int = 16,
                     iters: int = 10, tables=None) -> QuantizedMatrix:
     return quantize_matrices([W], [I], g, S, n, iters,
                              None if tables is None else [tables])[0]
+
+
+@dataclasses.dataclass
+class Layer:
+    """One decoder layer to quantize: its matrices, and for each matrix the id of the activation
+    stream that feeds it (matrices that read the same input share a stream); streams maps each id
+    to an iterable of fp32 [T_i, K] chunks of that input over the calibration tokens (or to one
+    resident tensor)."""
+    Ws: Sequence[torch.Tensor]
+    stream_of: Sequence[int]
+    streams: Dict[int, object]
+
+
+def quantize_layer(layer: Layer, g: int, S: int, n: int, iters: int,
+                   workspaces: Optional[Workspaces] = None,
+                   buffers: Optional[LayerBuffers] = None,
+                   probe: Optional[Probe] = None) -> LayerBuffers:
+    """Importance of every activation stream of the layer, then run_loop over its matrices."""
+    dev = layer.Ws[0].device
+    wsp = workspaces or Workspaces(dev)
+    Is_by = {}
+    for sid, src in layer.streams.items():
+        chunks = [src] if isinstance(src, torch.Tensor) else src
+        K = next(W.shape[1] for W, s in zip(layer.Ws, layer.stream_of) if s == sid)
+        Is_by[sid] = importance(chunks, K, dev, wsp)
+    Is = [Is_by[s] for s in layer.stream_of]
+    buf = buffers or LayerBuffers([tuple(W.shape) for W in layer.Ws], g, S, n, iters, dev)
+    return run_loop(layer.Ws, Is, buf, wsp, probe=probe)
+
+
+def quantize_model(layers: Iterable[Layer], g: int, S: int, n: int, iters: int,
+                   on_layer: Optional[Callable[[int, List[QuantizedMatrix]], None]] = None,
+                   check: bool = True) -> List[List[QuantizedMatrix]]:
+    """Quantize a model layer after layer (AAAC summary §4: models up to 32B; §2 mechanism 4: each
+    layer needs only its own activations, so layers are independent). The weights of every layer
+    stay where the caller keeps them; the layers' outputs are kept and returned in order. One
+    workspace set serves all layers. on_layer(i, results) runs after layer i is enqueued."""
+    wsp = None
+    out = []
+    for i, layer in enumerate(layers):
+        if wsp is None:
+            wsp = Workspaces(layer.Ws[0].device)
+        buf = quantize_layer(layer, g, S, n, iters, wsp)
+        if check:
+            check_history(buf.err, w2=buf.w2)
+        res = buf.results()
+        out.append(res)
+        if on_layer is not None:
+            on_layer(i, res)
+    return out
 
 
 def awq_prescale(W: torch.Tensor, a: torch.Tensor, I: Optional[torch.Tensor] = None):

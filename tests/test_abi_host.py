@@ -59,7 +59,9 @@ def test_status_strings(lib):
 
 def test_workspace_queries_are_host_only(lib):
     ws = lib.aaac_workspace_bytes
-    assert ws(OP_ASSIGN, 64, 1024, 128, 128, 16) == 0          # assign needs no workspace
+    # assign needs a workspace only for its error totals: counters and per-workgroup partials
+    assert ws(OP_ASSIGN, 64, 1024, 128, 128, 16) > 256
+    assert ws(OP_ASSIGN, 64, 1000, 128, 128, 16) == 0          # C not a multiple of g
     assert ws(OP_REFINE, 64, 1024, 128, 128, 16) > 0
     assert ws(OP_INIT, 64, 1024, 128, 0, 16) >= 64 * 1024 * 4  # one 32-bit key per weight
     assert ws(OP_REFINE, 64, 1000, 128, 128, 16) == 0          # C not a multiple of g
@@ -81,8 +83,10 @@ def test_batch_workspace_grows_with_count(lib):
     assert lib.aaac_batch_workspace_bytes(OP_REFINE, 9, R2, C2, 128, 128, 16) == 0
 
 
-def _assign(lib, R, C, g, S, n, W=FAKE, I=FAKE, T=FAKE, codes=FAKE, sel=FAKE, err=None):
-    return lib.aaac_assign(W, i64(R), i64(C), g, S, n, I, T, codes, sel, err, None)
+def _assign(lib, R, C, g, S, n, W=FAKE, I=FAKE, T=FAKE, codes=FAKE, sel=FAKE, err=None,
+            err_total=None, ws=None, ws_bytes=0):
+    return lib.aaac_assign(W, i64(R), i64(C), g, S, n, I, T, codes, sel, err, err_total, ws,
+                           ctypes.c_size_t(ws_bytes), None)
 
 
 def test_assign_rejects_bad_shapes_and_pointers_before_launch(lib):
@@ -100,15 +104,42 @@ def test_assign_rejects_bad_shapes_and_pointers_before_launch(lib):
     assert len(lib.aaac_last_error()) > 0
 
 
+def test_assign_error_total_needs_its_workspace(lib):
+    need = lib.aaac_workspace_bytes(OP_ASSIGN, 64, 1024, 128, 128, 16)
+    assert _assign(lib, 64, 1024, 128, 128, 16, err_total=FAKE) == INVALID          # no ws
+    assert b"err_total" in lib.aaac_last_error()
+    assert _assign(lib, 64, 1024, 128, 128, 16, err_total=FAKE, ws=FAKE,
+                   ws_bytes=need - 1) == WS_SMALL
+    assert _assign(lib, 64, 1024, 128, 128, 16, err_total=ctypes.c_void_p((1 << 20) + 4), ws=FAKE,
+                   ws_bytes=need) == INVALID                                         # misaligned
+    assert _assign(lib, 64, 1024, 128, 128, 16, err_total=FAKE,
+                   ws=ctypes.c_void_p((1 << 20) + 128), ws_bytes=need) == INVALID    # ws alignment
+    R2 = (i64 * 2)(64, 128)
+    C2 = (i64 * 2)(1024, 2048)
+    two = lib.aaac_batch_workspace_bytes(OP_ASSIGN, 2, R2, C2, 128, 128, 16)
+    assert two > need
+    P = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    f = lib.aaac_assign_batch
+    assert f(2, P, R2, C2, 128, 128, 16, P, P, P, P, FAKE, FAKE, ctypes.c_size_t(need),
+             None) == WS_SMALL
+
+
 def test_refine_rejects_small_workspace_and_unknown_flags(lib):
     need = lib.aaac_workspace_bytes(OP_REFINE, 64, 1024, 128, 128, 16)
     args = (FAKE, i64(64), i64(1024), 128, 128, 16, FAKE, FAKE, FAKE, FAKE, FAKE)
-    assert lib.aaac_refine(*args, 0, FAKE, ctypes.c_size_t(need - 1), None) == WS_SMALL
+    n_ = ctypes.c_size_t(need)
+    assert lib.aaac_refine(*args, 0, None, None, FAKE, ctypes.c_size_t(need - 1), None) == WS_SMALL
     assert b"workspace" in lib.aaac_last_error()
-    assert lib.aaac_refine(*args, 2, FAKE, ctypes.c_size_t(need), None) == INVALID
-    assert lib.aaac_refine(*args, 0, None, ctypes.c_size_t(need), None) == INVALID
-    assert lib.aaac_refine(*args, 0, ctypes.c_void_p((1 << 20) + 128), ctypes.c_size_t(need),
+    assert lib.aaac_refine(*args, 4, None, None, FAKE, n_, None) == INVALID       # unknown flag
+    assert lib.aaac_refine(*args, 0, None, None, None, n_, None) == INVALID
+    assert lib.aaac_refine(*args, 0, None, None, ctypes.c_void_p((1 << 20) + 128), n_,
                            None) == INVALID
+    # the optional error output: 8-byte aligned, with its w2 partner, and the W2-known flag only
+    # with them
+    assert lib.aaac_refine(*args, 0, ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, n_,
+                           None) == INVALID
+    assert lib.aaac_refine(*args, 0, FAKE, None, FAKE, n_, None) == INVALID
+    assert lib.aaac_refine(*args, 2, None, None, FAKE, n_, None) == INVALID
 
 
 def test_pack_and_dequant_bitmap_rule(lib):
@@ -138,9 +169,12 @@ def test_batch_calls_reject_bad_counts(lib):
     P = (ctypes.c_void_p * 1)(FAKE)
     R = (i64 * 1)(64)
     C = (i64 * 1)(1024)
-    assert lib.aaac_assign_batch(0, P, R, C, 128, 128, 16, P, P, P, P, None) == INVALID
-    assert lib.aaac_assign_batch(9, P, R, C, 128, 128, 16, P, P, P, P, None) == INVALID
-    assert lib.aaac_refine_batch(1, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE,
+    z = ctypes.c_size_t(0)
+    assert lib.aaac_assign_batch(0, P, R, C, 128, 128, 16, P, P, P, P, None, None, z,
+                                 None) == INVALID
+    assert lib.aaac_assign_batch(9, P, R, C, 128, 128, 16, P, P, P, P, None, None, z,
+                                 None) == INVALID
+    assert lib.aaac_refine_batch(1, P, R, C, 128, 128, 16, P, P, P, P, 0, None, None, FAKE,
                                  ctypes.c_size_t(16), None) == WS_SMALL
 
 

@@ -9,6 +9,9 @@ oracle what it can compute at that size:
     smallest and one large matrix, and equal to the single-matrix call;
   - assign on sampled rows of every matrix, at the first and the last iteration;
   - refine tables of two matrices from full-matrix sums (the GPU's codes and selectors as data);
+  - the error totals that every assign returns (as the loop driver runs it): on the refine-checked
+    matrices against the oracle's total error of the GPU's assignment, and non-increasing over the
+    iterations for every matrix;
   - pack and dequant on sampled rows of every matrix after the final assign.
 """
 
@@ -119,33 +122,57 @@ def _run_layer(cfg_id, layer, init_check, refine_check):
 
     codes = [torch.empty(R * C // 2, dtype=torch.uint8, device=DEV) for R, C in zip(Rs, Cs)]
     sels = [torch.empty(R * C // S, dtype=torch.uint8, device=DEV) for R, C in zip(Rs, Cs)]
+    hist = torch.zeros(iters + 1, len(mats), dtype=torch.float64, device=DEV)
+    ws_a = L.workspace(L.batch_workspace_bytes(L.OP_ASSIGN, Rs, Cs, g, S, n), DEV)
     for it in range(iters):
         flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
         checked = it in (0, iters - 1)
         T_in = [_np(t).astype(np.float64).reshape(2, n) for t in tabs] if checked else None
-        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
+        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels, hist[it], ws_a)
         if checked:
             torch.cuda.synchronize()
             _check_assign_rows(W64s, Is64, tabs, g, S, codes, sels, rows)
-        L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, tabs, flags, ws_r)
+            e_want = {}
+            for i in refine_check:
+                R, C = Rs[i], Cs[i]
+                want = par.total_error_rows(W64s[i], Is64[i], ref.unpack_codes(_np(codes[i]), R, C),
+                                            _np(sels[i]).reshape(R, C // S), T_in[i], g, S)
+                got = float(hist[it, i].item())
+                assert abs(got - want) <= 1e-6 * want, (mats[i].name, it, got, want)
+                e_want[i] = want
+        # as the loop driver runs it: the first refine sums I w^2, the later ones read it
+        rerr = torch.zeros(len(mats), dtype=torch.float64, device=DEV)
+        if it == 0:
+            w2 = torch.zeros(len(mats), dtype=torch.float64, device=DEV)
+        L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, tabs,
+                            flags | (L.REFINE_W2_KNOWN if it else 0), ws_r, rerr, w2)
         if checked:
             torch.cuda.synchronize()
+            for i in refine_check:
+                # the refine reports the error of the assignment it consumed, and sum I w^2
+                e_r, w2_r = float(rerr[i].item()), float(w2[i].item())
+                w2_o = float(np.sum(Is64[i][None, :] * W64s[i] ** 2))
+                assert abs(w2_r - w2_o) <= 1e-12 * w2_o, (mats[i].name, w2_r, w2_o)
+                assert abs(e_r - e_want[i]) <= 1e-6 * e_want[i] + 1e-13 * w2_o, (
+                    mats[i].name, it, e_r, e_want[i])
             for i in refine_check:
                 R, C = Rs[i], Cs[i]
                 q = ref.unpack_codes(_np(codes[i]), R, C)
                 s = _np(sels[i]).reshape(R, C // S)
-                want, _, _ = par.oracle_refine(W64s[i], Is64[i], q, s, T_in[i], g, S)
+                want, _, _, bound = par.oracle_refine(W64s[i], Is64[i], q, s, T_in[i], g, S)
                 got = _np(tabs[i]).astype(np.float64).reshape(2, n)
                 if flags:
-                    par.check_tables_bf16(got, want)
+                    par.check_tables_bf16(got, want, bound)
                 else:
-                    par.check_tables(got, want)
+                    par.check_tables(got, want, bound)
             _say("iter", it, "checked")
 
     # final assign against the bf16 tables, then pack and dequant
-    L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
+    L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels, hist[iters], ws_a)
     torch.cuda.synchronize()
     _check_assign_rows(W64s, Is64, tabs, g, S, codes, sels, rows)
+    h = P.check_history(hist, w2=w2)
+    _say("error history (first matrix)", h[:, 0].tolist())
     for i, W in enumerate(Ws):
         R, C = Rs[i], Cs[i]
         scales = torch.empty(R * C // g, dtype=torch.int16, device=DEV)
@@ -198,6 +225,8 @@ def test_full_size_13b_mlp_selection_bitmap():
 
 
 @pytest.mark.timeout(600)
-def test_full_size_32b_model_last_layer():
-    # one of the 64 streamed layers (the last one), every matrix at its real shape
-    _run_layer(5, 63, init_check=(1,), refine_check=(1, 3))
+@pytest.mark.parametrize("layer", [0, 21, 42, 63])
+def test_full_size_32b_model_layers(layer):
+    # four of the 64 streamed layers (the first, two inner ones, the last), every matrix at its
+    # real shape with the layer's own seeds
+    _run_layer(5, layer, init_check=(1,), refine_check=(1, 3))

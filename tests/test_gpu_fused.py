@@ -107,8 +107,8 @@ def test_fused_step_parity_with_oracle():
             q = par.unpack_gpu_codes(codes[i], R, C)
             s = _np(sels[i]).reshape(R, C // S)
             par.check_assign(W64, I64, T_in[i], g, S, q, s)
-            want, _, _ = par.oracle_refine(W64, I64, q, s, T_in[i], g, S)
-            par.check_tables(_np(tabs[i]).astype(np.float64).reshape(2, n), want)
+            want, _, _, bound = par.oracle_refine(W64, I64, q, s, T_in[i], g, S)
+            par.check_tables(_np(tabs[i]).astype(np.float64).reshape(2, n), want, bound)
 
 
 @pytest.mark.timeout(300)

@@ -315,6 +315,29 @@ def test_assign_matches_oracle(R, C, g, S, n):
     res = par.check_assign(par.to_np64(W), par.to_np64(I), _np(tables).reshape(2, n), g, S,
                            par.unpack_gpu_codes(codes, R, C), _np(sel), _np(err))
     _say("exempt", res["sel_exempt"], res["code_exempt"])
+    _check_err_total(W, I, tables, g, S, n, codes, sel)
+
+
+def _check_err_total(W, I, tables, g, S, n, codes, sel):
+    """err_total of the plain and the err-array variant: the same codes and selectors, and within
+    1e-6 of the oracle's total error of the GPU's assignment."""
+    R, C = W.shape
+    ws = L.workspace(L.workspace_bytes(L.OP_ASSIGN, R, C, g, S, n), DEV)
+    tots = []
+    for with_err in (False, True):
+        tot = torch.full((1,), -1.0, dtype=torch.float64, device=DEV)
+        c2, s2 = torch.empty_like(codes), torch.empty_like(sel)
+        e = torch.empty(2 * (R * C // S), dtype=torch.float64, device=DEV) if with_err else None
+        L.aaac_assign(W, g, S, n, I, tables, c2, s2, e, tot, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(c2, codes) and torch.equal(s2, sel)
+        tots.append(float(tot.item()))
+    T = _np(tables).astype(np.float64).reshape(2, n)
+    want = ref.total_error(par.to_np64(W), par.to_np64(I), par.unpack_gpu_codes(codes, R, C),
+                           _np(sel).reshape(R, C // S), T[0], T[1], g, S)
+    for got in tots:
+        assert abs(got - want) <= 1e-6 * abs(want) + 1e-300, (got, want)
+    return tots[0]
 
 
 def test_assign_edge_inputs():
@@ -392,21 +415,105 @@ def test_refine_matches_oracle(R, C, g, S, n):
     out = torch.empty_like(tables)
     L.aaac_refine(W, g, S, n, I, codes, sel, tables, out)
     torch.cuda.synchronize()
-    want, num, den = par.oracle_refine(par.to_np64(W), par.to_np64(I),
-                                       par.unpack_gpu_codes(codes, R, C),
-                                       _np(sel).reshape(R, C // S), _np(tables).reshape(2, n)
-                                       .astype(np.float64), g, S)
-    rel = par.check_tables(_np(out), want)
+    want, num, den, bound = par.oracle_refine(par.to_np64(W), par.to_np64(I),
+                                              par.unpack_gpu_codes(codes, R, C),
+                                              _np(sel).reshape(R, C // S),
+                                              _np(tables).reshape(2, n).astype(np.float64), g, S)
+    rel = par.check_tables(_np(out), want, bound)
     _say("refine max rel", rel)
     # in place, with bf16 rounding: equals bf16 of the fp64 update unless that sits within the
     # table tolerance of a bf16 rounding boundary
     L.aaac_refine(W, g, S, n, I, codes, sel, tables, tables, L.REFINE_ROUND_BF16)
     torch.cuda.synchronize()
-    got = _np(tables).astype(np.float64).reshape(2, n)
-    wb = ref.bf16_round(want)
-    lo = ref.bf16_round(want * (1 - par.TABLE_RTOL))
-    hi = ref.bf16_round(want * (1 + par.TABLE_RTOL))
-    assert np.all((got == wb) | (got == lo) | (got == hi)), (got, wb)
+    par.check_tables_bf16(_np(tables), want, bound)
+
+
+def _edge_matrix(kind, R, C):
+    """Matrices whose group scales leave the fast range: zero groups, bf16-subnormal and 3e30
+    scales mixed with ordinary groups ("edge"), or every group scaled by 2^100 or 2^-100 (exact in
+    bf16: a power of two only moves the exponent)."""
+    W = _weight(R, C, 71)
+    if kind == "edge":
+        W[0] = 0
+        W[1, :128] = 1e-39
+        W[1, 5] = -3e-39
+        W[2, 128:256] = 3e30
+        W[2, 130] = -1e29
+        W[5, 256:384] = 2e36
+        W[6] = W[6] * 2.0 ** -120
+    elif kind == "up":
+        W = (W.float() * 2.0 ** 100).to(torch.bfloat16)
+    else:
+        W = (W.float() * 2.0 ** -100).to(torch.bfloat16)
+    return W
+
+
+@pytest.mark.parametrize("kind", ["edge", "up", "down"])
+def test_refine_and_loop_extreme_group_scales(kind):
+    """Three iterations of the loop on matrices with group scales far outside [2^-30, 2^30]: every
+    assign and refine step against the oracle (tables within tolerance, never NaN), the error
+    totals within 1e-6 of the oracle's. Refine forms s w and s^2 in fp64, so its terms are exact
+    for every finite bf16 scale."""
+    _say("extreme scales", kind)
+    R, C, g, S, n, iters = 64, 512, 128, 128, 16, 3
+    W = _edge_matrix(kind, R, C)
+    _, _, I = _importance(C, 64, 73)
+    if kind == "edge":
+        I[:32] = 0
+        I[100:104] = 1e20
+    W64, I64 = par.to_np64(W), par.to_np64(I)
+    assert np.all(np.isfinite(W64))
+    tables = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(W, g, n, tables)
+    torch.cuda.synchronize()
+    T0, T1 = ref.init_tables(W64, g, n)
+    assert np.array_equal(_np(tables), np.concatenate([T0, T1]).astype(np.float32))
+    for it in range(iters):
+        T_in = _np(tables).astype(np.float64).reshape(2, n)
+        codes, sel, err = _assign(W, I, tables, g, S, n)
+        cq = par.unpack_gpu_codes(codes, R, C)
+        sq = _np(sel).reshape(R, C // S)
+        par.check_assign(W64, I64, T_in, g, S, cq, _np(sel), _np(err))
+        _check_err_total(W, I, tables, g, S, n, codes, sel)
+        flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
+        rerr = torch.zeros(1, dtype=torch.float64, device=DEV)
+        w2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+        L.aaac_refine(W, g, S, n, I, codes, sel, tables, tables, flags, err=rerr, w2=w2)
+        torch.cuda.synchronize()
+        got = _np(tables).astype(np.float64).reshape(2, n)
+        assert np.all(np.isfinite(got)), got
+        # the refine's error report: W2 exact to rounding, E within its stated 1e-15 W2 accuracy
+        e_r, w2_r = float(rerr.item()), float(w2.item())
+        w2_o = float(np.sum(I64[None, :] * W64 ** 2))
+        e_o = ref.total_error(W64, I64, cq, sq, T_in[0], T_in[1], g, S)
+        assert abs(w2_r - w2_o) <= 1e-12 * w2_o
+        assert abs(e_r - e_o) <= 1e-6 * e_o + 1e-13 * w2_o, (e_r, e_o, w2_o)
+        want, _, _, bound = par.oracle_refine(W64, I64, cq, sq, T_in, g, S)
+        if flags:
+            par.check_tables_bf16(got, want, bound)
+        else:
+            par.check_tables(got, want, bound)
+
+
+def test_scaling_by_a_power_of_two_changes_nothing():
+    """u = w / s does not change when W is multiplied by 2^100: the loop on the scaled matrix gives
+    the tables of the unscaled one (the scaled one runs the exact scan, the other the lookup, so
+    decisions may differ only inside the tie band; with none, the tables are bitwise equal)."""
+    _say("power-of-two invariance")
+    R, C, g, S, n = 64, 512, 128, 128, 16
+    W = _weight(R, C, 75)
+    Wup = (W.float() * 2.0 ** 100).to(torch.bfloat16)
+    _, _, I = _importance(C, 64, 76)
+    outs = []
+    for M in (W, Wup):
+        q = P.quantize_matrix(M, I, g, S, n, iters=3)
+        torch.cuda.synchronize()
+        outs.append(q)
+    a, b = outs
+    if torch.equal(a.codes, b.codes) and torch.equal(a.sel, b.sel):
+        assert torch.equal(a.tables, b.tables)
+    else:
+        par.check_tables(_np(b.tables), _np(a.tables).astype(np.float64), None, rtol=1e-4)
 
 
 # ------------------------------------------------------------------ pack / dequant
@@ -572,6 +679,37 @@ def test_batch_equals_single_calls_and_is_deterministic():
         assert torch.equal(out, runs[0][2][i])
 
 
+def test_batch_error_totals():
+    """aaac_assign_batch with err_total: one total per matrix, equal to the single call's within
+    rounding (the rows are split over workgroups differently), within 1e-6 of the oracle, and
+    bitwise the same on a second call; the codes are those of the call without totals."""
+    _say("batch err totals")
+    for g, S, n, shapes in ((128, 128, 16, [(256, 1024), (64, 1024), (300, 2048)]),
+                            (16, 16, 15, [(40, 256), (5, 48), (96, 512)]),
+                            (128, 8, 16, [(33, 384), (70, 128)])):
+        Ws = [_weight(R, C, 5200 + R + C) for R, C in shapes]
+        Is = [_importance(C, 64, 5300 + C)[2] for _, C in shapes]
+        tabs = [torch.empty(2 * n, dtype=torch.float32, device=DEV) for _ in shapes]
+        L.aaac_init_quantiles_batch(Ws, g, n, tabs)
+        codes = [torch.empty(W.numel() // 2, dtype=torch.uint8, device=DEV) for W in Ws]
+        sels = [torch.empty(W.numel() // S, dtype=torch.uint8, device=DEV) for W in Ws]
+        L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
+        runs = []
+        for _ in range(2):
+            c2 = [torch.empty_like(c) for c in codes]
+            s2 = [torch.empty_like(x) for x in sels]
+            tot = torch.full((len(Ws),), -1.0, dtype=torch.float64, device=DEV)
+            L.aaac_assign_batch(Ws, g, S, n, Is, tabs, c2, s2, tot)
+            torch.cuda.synchronize()
+            for i in range(len(Ws)):
+                assert torch.equal(c2[i], codes[i]) and torch.equal(s2[i], sels[i])
+            runs.append(_np(tot).copy())
+        assert np.array_equal(runs[0], runs[1])
+        for i, W in enumerate(Ws):
+            single = _check_err_total(W, Is[i], tabs[i], g, S, n, codes[i], sels[i])
+            assert abs(runs[0][i] - single) <= 1e-12 * abs(single) + 1e-300, (g, S, i)
+
+
 # ------------------------------------------------------------------ the loop
 
 @pytest.mark.timeout(900)
@@ -589,25 +727,51 @@ def test_loop_single_layer_against_oracle_free_run():
     L.aaac_init_quantiles(W, g, n, tables)
     R, C = W.shape
     hist = []
-    for it in range(cfg.iters):
+    ws_a = L.workspace(L.workspace_bytes(L.OP_ASSIGN, R, C, g, S, n), DEV)
+    for it in range(cfg.iters + 1):
         T_in = _np(tables).astype(np.float64).reshape(2, n)
         codes, sel, err = _assign(W, I, tables, g, S, n)
+        # the error total, from the err-array variant and from the plain one
+        tot = torch.zeros(1, dtype=torch.float64, device=DEV)
+        tot2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+        c2 = torch.empty_like(codes)
+        s2 = torch.empty_like(sel)
+        L.aaac_assign(W, g, S, n, I, tables, c2, s2, err, tot, ws_a)
+        L.aaac_assign(W, g, S, n, I, tables, c2, s2, None, tot2, ws_a)
+        torch.cuda.synchronize()
+        assert torch.equal(c2, codes) and torch.equal(s2, sel)
         cq = par.unpack_gpu_codes(codes, R, C)
         sq = _np(sel).reshape(R, C // S)
         res = par.check_assign(W64, I64, T_in, g, S, cq, _np(sel), _np(err))
         a = res["oracle"]
-        hist.append(float(np.sum(np.where(sq == 1, a["E1"], a["E0"]))))
+        e_sel = float(np.sum(np.where(sq == 1, a["E1"], a["E0"])))
+        e_true = ref.total_error(W64, I64, cq, sq, T_in[0], T_in[1], g, S)
+        for got in (float(tot.item()), float(tot2.item())):
+            assert abs(got - e_true) <= 1e-6 * e_true, (it, got, e_true)
+        hist.append(e_sel)
+        _say("iter", it, "E", e_sel, "gpu", float(tot2.item()), "sel T1 frac", float(sq.mean()))
+        if it == cfg.iters:
+            break                                   # the final assign, against bf16 tables
         flags = L.REFINE_ROUND_BF16 if it == cfg.iters - 1 else 0
-        L.aaac_refine(W, g, S, n, I, codes, sel, tables, tables, flags)
+        rerr = torch.zeros(1, dtype=torch.float64, device=DEV)
+        if it == 0:
+            w2 = torch.zeros(1, dtype=torch.float64, device=DEV)
+        L.aaac_refine(W, g, S, n, I, codes, sel, tables, tables,
+                      flags | (L.REFINE_W2_KNOWN if it else 0), err=rerr, w2=w2)
         torch.cuda.synchronize()
-        want, _, _ = par.oracle_refine(W64, I64, cq, sq, T_in, g, S)
+        # the refine reports the same error of the assignment it consumed, and sum I w^2 (summed
+        # by the first refine, read by the later ones)
+        e_r, w2_r = float(rerr.item()), float(w2.item())
+        w2_o = float(np.sum(I64[None, :] * W64 ** 2))
+        assert abs(w2_r - w2_o) <= 1e-12 * w2_o
+        assert abs(e_r - e_true) <= 1e-6 * e_true, (it, e_r, e_true)
+        want, _, _, bound = par.oracle_refine(W64, I64, cq, sq, T_in, g, S)
         got = _np(tables).astype(np.float64).reshape(2, n)
         if flags:
-            assert np.array_equal(ref.bf16_round(got), got)
+            par.check_tables_bf16(got, want, bound)
         else:
-            par.check_tables(got, want)
-        _say("iter", it, "E", hist[-1], "sel T1 frac", float(sq.mean()))
-    h = np.asarray(hist)
+            par.check_tables(got, want, bound)
+    h = np.asarray(hist[:-1])
     assert np.all(np.diff(h) <= 1e-6 * h[:-1]), h
 
 

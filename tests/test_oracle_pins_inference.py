@@ -116,3 +116,59 @@ def test_awq_prescaled_error_equals_original_space_error():
     # a slip (importance divided by a instead of a^2) breaks the identity
     wrong = ref.total_error(Ws, Is * a, fin["codes"], fin["sel"], Tt[0], Tt[1], g, S)
     assert wrong != pytest.approx(orig, rel=1e-6)
+
+
+def _bf16_of_fraction(x):
+    """bf16 value (as a float) of an exact rational, ties to even, by exact rational arithmetic:
+    the quantum of x's binade (8 significant bits; 2^-133 below 2^-126), the quotient rounded by
+    Fraction's round-half-even, overflow past the largest finite value to infinity."""
+    from fractions import Fraction
+    if x == 0:
+        return 0.0
+    ax = abs(x)
+    e = ax.numerator.bit_length() - ax.denominator.bit_length()
+    if Fraction(2) ** e > ax:
+        e -= 1                                     # now 2^e <= ax < 2^(e+1)
+    e = max(e, -126)
+    q = Fraction(2) ** (e - 7)
+    r = round(ax / q) * q
+    if r >= Fraction(2) ** 128:
+        return float("inf") if x > 0 else float("-inf")
+    return float(r) if x > 0 else -float(r)
+
+
+def test_awq_prescale_matches_exact_rationals_for_any_scale():
+    """Non-power-of-two scales (AAAC summary §4, reading R15): W_scaled is the bf16 rounding of the
+    exact product w * a, and I_scaled the fp32 rounding of the fp64 rounding of the exact quotient
+    I / a^2, both computed here with Python Fractions (float(Fraction) rounds correctly). Slips
+    such as squaring a in fp32, dividing in fp32 or rounding the product to fp32 first disagree
+    with this on some entries."""
+    from fractions import Fraction
+    rng = np.random.default_rng(48)
+    R, C = 8, 512
+    W = _bf16_matrix(rng, R, C)
+    a = np.exp(rng.uniform(-3, 3, size=C)).astype(np.float32)
+    I = (np.exp(rng.uniform(-8, 8, size=C))).astype(np.float32)
+    Ws, Is = ref.awq_prescale(W, a, I)
+    fa = [Fraction(float(v)) for v in a]
+    want_W = np.array([[_bf16_of_fraction(Fraction(float(W[r, c])) * fa[c]) for c in range(C)]
+                       for r in range(R)])
+    assert np.array_equal(Ws, want_W)
+    want_I = np.array([np.float32(float(Fraction(float(I[c])) / (fa[c] * fa[c])))
+                       for c in range(C)], dtype=np.float32)
+    assert np.array_equal(Is, want_I)
+    # the pin has teeth: plausible slips each disagree somewhere
+    a2_fp32 = (a * a).astype(np.float64)                      # a^2 rounded to fp32 first
+    assert not np.array_equal((I.astype(np.float64) / a2_fp32).astype(np.float32), want_I)
+    assert not np.array_equal(I / (a * a), want_I)            # all in fp32
+    # products whose rounding to fp32 first would land on a bf16 rounding midpoint: the oracle
+    # must round the exact product once (found by search, then checked against the rationals)
+    w = ref.bf16_round(rng.standard_normal(1 << 20))
+    av = np.exp(rng.uniform(-3, 3, size=1 << 20)).astype(np.float32)
+    p64 = w * av.astype(np.float64)
+    twice = ref.bf16_round(p64.astype(np.float32).astype(np.float64)) != ref.bf16_round(p64)
+    idx = np.flatnonzero(twice)[:32]
+    assert idx.size > 0
+    Wd, _ = ref.awq_prescale(w[idx][None, :], av[idx])
+    want_d = [_bf16_of_fraction(Fraction(float(w[i])) * Fraction(float(av[i]))) for i in idx]
+    assert np.array_equal(Wd[0], np.array(want_d))
