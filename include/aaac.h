@@ -278,6 +278,26 @@ aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t
                               size_t ws_bytes, void* stream);
 
 /*
+ * aaac_refine_batch without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation). The
+ * counters and per-workgroup partials live in a fixed array in the library's device memory: each
+ * GPU the library runs on holds one copy, of 256 + 8 * 66 * 1024 * 8 bytes (about 4.3 MB), until
+ * the process ends; its address on a device is looked up once, on the first call there. Every
+ * other argument, and every result, is as for aaac_refine_batch (bit for bit the same). The call
+ * allocates nothing and launches a small kernel that clears the counters before the refine.
+ * All calls on one GPU share that array, so calls that overlap on one GPU (on different streams,
+ * or from different threads) race and must not be issued; calls on one stream are ordered.
+ * Errors: as aaac_refine_batch; AAAC_ERR_WORKSPACE_TOO_SMALL if a batch needed more scratch than
+ * the array holds (not possible within AAAC_MAX_BATCH matrices); AAAC_ERR_HIP if the array's
+ * address cannot be obtained.
+ */
+aaac_status aaac_refine_batch_noalloc(int count, const uint16_t* const* W, const int64_t* R,
+                                      const int64_t* C, int g, int S, int n,
+                                      const float* const* I, const uint8_t* const* codes,
+                                      const uint8_t* const* sel, float* const* tables, int flags,
+                                      double* err, double* w2, void* stream);
+
+/*
  * One iteration of the alternation (AAAC summary §2 mechanism 4) in one launch: the batched assign
  * against tables[i], writing codes[i] and sel[i], then the batched refine from those codes,
  * updating tables[i] in place (flags as for aaac_refine_batch). Codes, selectors and tables are

@@ -33,7 +33,7 @@ EXPORTED = (
     "aaac_init_quantiles", "aaac_assign", "aaac_refine", "aaac_pack", "aaac_dequant",
     "aaac_batch_workspace_bytes", "aaac_assign_batch", "aaac_refine_batch", "aaac_awq_prescale",
     "aaac_gemv", "aaac_gemv_batch", "aaac_assign_refine_batch", "aaac_init_quantiles_batch",
-    "aaac_pack_batch", "aaac_dequant_batch",
+    "aaac_pack_batch", "aaac_dequant_batch", "aaac_refine_batch_noalloc",
 )
 
 
@@ -92,6 +92,9 @@ def load(path: str = LIB_PATH):
                                       P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int, c_vp, c_vp,
                                       c_vp, c_size, c_vp]),
         "aaac_awq_prescale": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp]),
+        "aaac_refine_batch_noalloc": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
+                                              c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int,
+                                              c_vp, c_vp, c_vp]),
         "aaac_assign_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
                                              c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int,
                                              c_vp, c_size, c_vp]),
@@ -500,3 +503,32 @@ def aaac_gemv_batch(codes: Sequence[torch.Tensor], scales: Sequence[torch.Tensor
         _arr(c_i64, list(Cs)), g, S, n, _arr(c_vp, [t.data_ptr() for t in xs]), B,
         _arr(c_vp, [t.data_ptr() for t in ys]), _stream(stream))
     _check(st, "aaac_gemv_batch")
+
+
+def aaac_refine_batch_noalloc(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
+                              Is: Sequence[torch.Tensor], codes: Sequence[torch.Tensor],
+                              sels: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
+                              flags: int = 0, err: Optional[torch.Tensor] = None,
+                              w2: Optional[torch.Tensor] = None, stream=None):
+    """aaac_refine_batch with the library's fixed device scratch instead of a workspace (see
+    aaac.h): the call itself allocates nothing."""
+    lib = load()
+    k = len(Ws)
+    Rs = [W.shape[0] for W in Ws]
+    Cs = [W.shape[1] for W in Ws]
+    for i in range(k):
+        _need(Ws[i], "W[%d]" % i, torch.bfloat16)
+        _need(Is[i], "I[%d]" % i, torch.float32, Cs[i])
+        _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
+        _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
+        _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
+    if err is not None:
+        _need(err, "err", torch.float64, k)
+    if w2 is not None:
+        _need(w2, "w2", torch.float64, k)
+    st = lib.aaac_refine_batch_noalloc(
+        k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
+        _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in codes]),
+        _arr(c_vp, [t.data_ptr() for t in sels]), _arr(c_vp, [t.data_ptr() for t in tables]),
+        flags, _ptr(err), _ptr(w2), _stream(stream))
+    _check(st, "aaac_refine_batch_noalloc")

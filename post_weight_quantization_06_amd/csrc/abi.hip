@@ -185,11 +185,55 @@ aaac_status check_refine_ws(int count, void* ws, size_t ws_bytes, const char* wh
   return AAAC_OK;
 }
 
-aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
-                      int g, int S, int n, const float* const* I, const uint8_t* const* codes,
-                      const uint8_t* const* sel, const float* const* tin, float* const* tout,
-                      int flags, double* err, double* w2, void* ws, size_t ws_bytes, void* stream,
-                      const char* who) {
+// ------------------------------------------------------------------------------------------------
+// Fixed device scratch for aaac_refine_batch_noalloc: the refine workspace of a full batch (job
+// counters, then per-workgroup partials), one copy per GPU, alive until the process ends. Host
+// code reaches it only through the address hipGetSymbolAddress returns for the current device,
+// taken once per device on the first call there.
+// ------------------------------------------------------------------------------------------------
+constexpr size_t kScratchBytes = 256 + (size_t)kMaxJobs * kPartVals * kMaxRefineBlocks * sizeof(double);
+
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the current device, or nullptr (and a message) on failure.
+void* scratch_on_current_device(const char* who, aaac_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = fail(AAAC_ERR_HIP, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = fail(AAAC_ERR_INVALID_ARG, "%s: device %d beyond the %d this library serves", who, dev,
+               kMaxDevices);
+    return nullptr;
+  }
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    *st = fail(AAAC_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    return nullptr;
+  }
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
+// Clears n 32-bit words (a kernel rather than a memset, so that the call can be captured in a
+// graph).
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// Every argument of a refine call except the workspace.
+aaac_status check_refine_args(int count, const uint16_t* const* W, const int64_t* R,
+                              const int64_t* C, int g, int S, int n, const float* const* I,
+                              const uint8_t* const* codes, const uint8_t* const* sel,
+                              const float* const* tin, float* const* tout, int flags,
+                              const double* err, const double* w2, const char* who) {
   aaac_status st = check_batch(count, W, R, C, g, S, n, who);
   if (st != AAAC_OK) return st;
   if (flags & ~(AAAC_REFINE_ROUND_BF16 | AAAC_REFINE_W2_KNOWN))
@@ -200,12 +244,31 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
         !tout[i] || !aligned(tin[i], 4) || !aligned(tout[i], 4))
       return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: null or misaligned pointer", who, i);
   }
-  st = check_refine_ws(count, ws, ws_bytes, who);
-  if (st != AAAC_OK) return st;
   if (err && (!aligned(err, 8) || !w2 || !aligned(w2, 8)))
     return fail(AAAC_ERR_INVALID_ARG, "%s: err and w2 must be given together, 8-byte aligned", who);
   if (!err && (flags & AAAC_REFINE_W2_KNOWN))
     return fail(AAAC_ERR_INVALID_ARG, "%s: AAAC_REFINE_W2_KNOWN without err and w2", who);
+  return AAAC_OK;
+}
+
+aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                      int g, int S, int n, const float* const* I, const uint8_t* const* codes,
+                      const uint8_t* const* sel, const float* const* tin, float* const* tout,
+                      int flags, double* err, double* w2, void* ws, size_t ws_bytes, void* stream,
+                      const char* who, bool clear_counters = false) {
+  aaac_status st = check_refine_args(count, W, R, C, g, S, n, I, codes, sel, tin, tout, flags, err,
+                                     w2, who);
+  if (st != AAAC_OK) return st;
+  st = check_refine_ws(count, ws, ws_bytes, who);
+  if (st != AAAC_OK) return st;
+  if (clear_counters) {
+    // every argument is valid: clear the job counters first (a call that did not complete may
+    // have left them set)
+    hipLaunchKernelGGL(clear_words_kernel, dim3(1), dim3(64), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint32_t*>(ws), 64);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, who);
+  }
   RefineBatch b{};
   build_refine_batch(b, count, W, R, C, g, S, n, I, flags, ws);
   b.errs = err ? 1 : 0;
@@ -463,6 +526,31 @@ aaac_status aaac_refine_batch(int count, const uint16_t* const* W, const int64_t
   for (int i = 0; i < m; ++i) tin[i] = tables[i];
   return do_refine(count, W, R, C, g, S, n, I, codes, sel, tin, tables, flags, err, w2, ws,
                    ws_bytes, stream, "aaac_refine_batch");
+}
+
+aaac_status aaac_refine_batch_noalloc(int count, const uint16_t* const* W, const int64_t* R,
+                                      const int64_t* C, int g, int S, int n,
+                                      const float* const* I, const uint8_t* const* codes,
+                                      const uint8_t* const* sel, float* const* tables, int flags,
+                                      double* err, double* w2, void* stream) {
+  const char* who = "aaac_refine_batch_noalloc";
+  if (!tables) return fail(AAAC_ERR_INVALID_ARG, "%s: null tables array", who);
+  if (count < 1 || count > AAAC_MAX_BATCH)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: count=%d (need 1..%d)", who, count, AAAC_MAX_BATCH);
+  const size_t need = refine_ws_bytes(count);
+  if (need > kScratchBytes)
+    return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: needs %zu bytes of scratch, the fixed maximum is "
+                "%zu", who, need, kScratchBytes);
+  const float* tin[AAAC_MAX_BATCH];
+  for (int i = 0; i < count; ++i) tin[i] = tables[i];
+  // every argument first, then the scratch address (the first call on a device looks it up)
+  aaac_status st = check_refine_args(count, W, R, C, g, S, n, I, codes, sel, tin, tables, flags,
+                                     err, w2, who);
+  if (st != AAAC_OK) return st;
+  void* ws = scratch_on_current_device(who, &st);
+  if (!ws) return st;
+  return do_refine(count, W, R, C, g, S, n, I, codes, sel, tin, tables, flags, err, w2, ws,
+                   kScratchBytes, stream, who, /*clear_counters=*/true);
 }
 
 aaac_status aaac_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,

@@ -245,3 +245,19 @@ def test_pack_and_dequant_batches_reject_bad_arguments(lib):
     assert dq(1, P, P, None, P, R1, C1, 128, 16, 16, P, None) == INVALID         # S < g, no bitmap
     assert dq(1, P, P, None, P, R1, C1, 128, 128, 16, bad, None) == INVALID      # misaligned out
     assert dq(1, P, P, None, P, R1, C1, 128, 128, 17, P, None) == SHAPE
+
+
+def test_refine_noalloc_rejects_bad_arguments_before_touching_the_device(lib):
+    """The allocation-free refine checks every argument on the host before it looks up its device
+    scratch or launches anything."""
+    P = (ctypes.c_void_p * 1)(FAKE)
+    R = (i64 * 1)(64)
+    C = (i64 * 1)(1024)
+    f = lib.aaac_refine_batch_noalloc
+    assert f(0, P, R, C, 128, 128, 16, P, P, P, P, 0, None, None, None) == INVALID   # count
+    assert f(9, P, R, C, 128, 128, 16, P, P, P, P, 0, None, None, None) == INVALID
+    assert f(1, P, R, C, 100, 100, 16, P, P, P, P, 0, None, None, None) == SHAPE     # g
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 8, None, None, None) == INVALID   # flags
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 2, None, None, None) == INVALID   # W2 known
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, None, 0, None, None, None) == INVALID
+    assert b"noalloc" in lib.aaac_last_error()

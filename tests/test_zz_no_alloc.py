@@ -1,0 +1,96 @@
+"""aaac_refine_batch_noalloc (the refine without a workspace argument, for callers that cannot
+allocate) against aaac_refine_batch with a workspace: the same tables and error reports bit for bit,
+on two calls in a row, the second on a smaller batch; the call allocates nothing."""
+
+import pytest
+import torch
+
+from synth import layers as syn
+
+pytestmark = pytest.mark.gpu
+
+P = pytest.importorskip("post_weight_quantization_06_amd")
+L = P._lib
+
+DEV = "cuda"
+
+
+def _say(*a):
+    print("[case]", *a, flush=True)
+
+
+def _setup(shapes, g, S, n, seed):
+    Ws = [syn.make_weight(R, C, seed + 10 * i, DEV) for i, (R, C) in enumerate(shapes)]
+    Is = []
+    for i, (_, C) in enumerate(shapes):
+        X = syn.make_activations(64, C, seed + 10 * i + 1, DEV)
+        acc = torch.zeros(C, dtype=torch.float64, device=DEV)
+        I = torch.empty(C, dtype=torch.float32, device=DEV)
+        L.aaac_importance(X, acc, I)
+        Is.append(I)
+    tabs = [torch.empty(2 * n, dtype=torch.float32, device=DEV) for _ in shapes]
+    L.aaac_init_quantiles_batch(Ws, g, n, tabs)
+    codes = [torch.empty(R * C // 2, dtype=torch.uint8, device=DEV) for R, C in shapes]
+    sels = [torch.empty(R * C // S, dtype=torch.uint8, device=DEV) for R, C in shapes]
+    L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels)
+    torch.cuda.synchronize()
+    return Ws, Is, tabs, codes, sels
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    L.load()
+    yield
+
+
+@pytest.mark.parametrize("g,S,n", [(128, 128, 16), (16, 16, 15), (128, 8, 16)])
+def test_refine_noalloc_equals_refine_with_workspace(g, S, n):
+    # call 1: three matrices (ragged rows and widths); call 2: one smaller matrix, bf16 rounding and
+    # the W2 of call 1's first matrix passed back in
+    calls = [([(300, 2048), (64, 1024), (1000, 512)], 0),
+             ([(96, 512)], L.REFINE_ROUND_BF16 | L.REFINE_W2_KNOWN)]
+    for k, (shapes, flags) in enumerate(calls):
+        _say("noalloc", g, S, n, "call", k, shapes)
+        Ws, Is, tabs, codes, sels = _setup(shapes, g, S, n, 900 + 100 * k)
+        t_ref = [t.clone() for t in tabs]
+        t_new = [t.clone() for t in tabs]
+        m = len(shapes)
+        e_ref = torch.zeros(m, dtype=torch.float64, device=DEV)
+        e_new = torch.full((m,), -1.0, dtype=torch.float64, device=DEV)
+        w_ref = torch.zeros(m, dtype=torch.float64, device=DEV)
+        w_new = torch.full((m,), -1.0, dtype=torch.float64, device=DEV)
+        if flags & L.REFINE_W2_KNOWN:
+            # the W2 these matrices have, from a first refine of each path
+            L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, [t.clone() for t in tabs], 0,
+                                None, torch.zeros(m, dtype=torch.float64, device=DEV), w_ref)
+            L.aaac_refine_batch_noalloc(Ws, g, S, n, Is, codes, sels, [t.clone() for t in tabs],
+                                        0, torch.zeros(m, dtype=torch.float64, device=DEV), w_new)
+            torch.cuda.synchronize()
+            assert torch.equal(w_ref, w_new)
+        ws = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, [R for R, _ in shapes],
+                                                 [C for _, C in shapes], g, S, n), DEV)
+        L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, t_ref, flags, ws, e_ref, w_ref)
+        torch.cuda.synchronize()
+        before = torch.cuda.memory_allocated()
+        L.aaac_refine_batch_noalloc(Ws, g, S, n, Is, codes, sels, t_new, flags, e_new, w_new)
+        torch.cuda.synchronize()
+        assert torch.cuda.memory_allocated() == before
+        for a, b in zip(t_ref, t_new):
+            assert torch.equal(a, b), (g, S, n, k, a, b)
+        assert torch.equal(e_ref, e_new) and torch.equal(w_ref, w_new)
+        assert bool((e_new > 0).all())
+
+
+def test_refine_noalloc_rejects_bad_arguments_before_launch():
+    W = syn.make_weight(64, 1024, 5, DEV)
+    I = torch.ones(1024, dtype=torch.float32, device=DEV)
+    codes = torch.zeros(64 * 512, dtype=torch.uint8, device=DEV)
+    sel = torch.zeros(64 * 8, dtype=torch.uint8, device=DEV)
+    tab = torch.zeros(32, dtype=torch.float32, device=DEV)
+    with pytest.raises(L.AAACError):
+        L.aaac_refine_batch_noalloc([W], 128, 128, 16, [I], [codes], [sel], [tab], 8)
+    with pytest.raises(L.AAACError):           # W2 known without an error output
+        L.aaac_refine_batch_noalloc([W], 128, 128, 16, [I], [codes], [sel], [tab],
+                                    L.REFINE_W2_KNOWN)
