@@ -23,14 +23,15 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
-# kernels whose traffic is summarised: name prefixes of the dispatches (after "void ")
+# kernels whose traffic is summarised: name prefixes of the dispatches (after "void "); assign is
+# the loop's instance without error output
 KERNELS = {
-    "assign": ("aaac::assign_wide_kernel<", "aaac::assign_kernel<"),
+    "assign": ("aaac::assign_wide_kernel<0,", "aaac::assign_kernel<0,"),
     "refine": ("aaac::refine_kernel<",),
 }
 KERNEL_SOURCES = {
     "assign": ["assign.hip", "lookup.h", "common.h"],
-    "refine": ["refine.hip", "common.h"],
+    "refine": ["refine.hip", "lookup.h", "common.h"],
 }
 
 

@@ -1,22 +1,25 @@
-"""Text summaries of rocprofv3 runs of bench.py on the 8B-shaped decoder layer.
+"""Text summaries of rocprofv3 runs of bench.py.
 
 Turns the raw rocprofv3 output of the runs below (one counter group per run, all writing under
-one folder RAW) into the short Markdown summaries kept beside the traffic JSON:
+one folder RAW) into the short Markdown summaries kept in PROFILES, for one workload TAG
+(`32b_model`: the 64-layer 32B-shaped model, bench.py --config 5; `llama8b_layer`: the 8B-shaped
+decoder layer, --config 2):
 
-    rocprofv3 --kernel-trace --stats --output-format csv -d RAW/prof_c2 -o run -- \\
-        python -u bench.py --steps 2 --warmup 1 --no-cpu --one-stream
-    rocprofv3 --pmc FETCH_SIZE ... -d RAW/pmc_fetch ...      (the same bench command, 1 step)
-    rocprofv3 --pmc WRITE_SIZE ... -d RAW/pmc_write ...
-    rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU ... -d RAW/pmc_sq ...
-    rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_LDS ... -d RAW/pmc_sq2 ...
+    rocprofv3 --kernel-trace --stats --output-format csv -d RAW/prof_TAG -o run -- \\
+        python -u bench.py --config N --steps 2 --warmup 1 --no-cpu --one-stream
+    rocprofv3 --pmc FETCH_SIZE ... -d RAW/pmc_fetch_TAG ...  (bench.py --steps 1 --warmup 1)
+    rocprofv3 --pmc WRITE_SIZE ... -d RAW/pmc_write_TAG ...
+    rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU ... -d RAW/pmc_sq_TAG ...
+    rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_LDS ... -d RAW/pmc_sq2_TAG ...
     python -m post_weight_quantization_06_amd.pmc_traffic FETCH.csv WRITE.csv TRAFFIC.json
 
 Usage (from the repository root):
 
-    python -m post_weight_quantization_06_amd.prof_summary RAW PROFILES
+    python -m post_weight_quantization_06_amd.prof_summary RAW PROFILES [TAG]
 
-PROFILES holds hbm_traffic_assign_refine_llama8b_layer.json and receives the three .md files,
-whose command lines name RAW and PROFILES as given.
+Writes kernel_stats_TAG.md, hbm_traffic_assign_refine_TAG.{json,md} (the JSON from the two
+counter runs) and sq_counters_assign_refine_TAG.md, whose command lines name RAW and PROFILES as
+given. Missing counter runs are skipped.
 """
 
 from __future__ import annotations
@@ -27,27 +30,48 @@ import json
 import os
 import sys
 
-# the 8B-shaped layer: [out, in] of q, k, v, o, gate, up, down
-MATS = [(4096, 4096), (1024, 4096), (1024, 4096), (4096, 4096), (14336, 4096), (14336, 4096),
-        (4096, 14336)]
-N = sum(r * c for r, c in MATS)                      # 218,103,808 weights
-ALG = N * 2 + N // 2 + N // 128                      # bytes per assign or refine launch
-X_BYTES = 4 * 262144 * (3 * 4096 + 14336)            # the four activation streams, fp32
 PEAK = 8e12
 
-TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d {raw}/prof_c2 -o run "
-             "-- python -u bench.py --steps 2 --warmup 1 --no-cpu --one-stream")
+# workload tag -> (bench config, name, number of (warmup + timed) steps of the trace command)
+WORKLOADS = {
+    "32b_model": (5, "the 32B-shaped model (64 decoder layers, g=128, S=128, n=16, 10 iterations)"),
+    "llama8b_layer": (2, "the 8B-shaped decoder layer (g=128, S=128, n=16, 10 iterations)"),
+}
+TRACE_STEPS = 3      # the trace command runs 1 warmup + 2 timed steps
+
 SQ1 = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVE_CYCLES SQ_BUSY_CYCLES "
        "SQ_WAIT_INST_ANY SQ_INSTS_VMEM_RD")
 SQ2 = ("SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
        "SQ_ACTIVE_INST_ANY")
 WRITTEN_BY = ("Summary written by `python -m post_weight_quantization_06_amd.prof_summary {raw} "
-              "{prof}` from the raw output of the commands below.\n")
+              "{prof} {tag}` from the raw output of the commands below.\n")
+
+# kernel families: (key, name fragment); the loop kernels of every template instance
+ASSIGN = "aaac::assign_wide_kernel<"
+REFINE = "aaac::refine_kernel<"
 
 
-def _pmc_cmd(counters, out, raw):
+def workload(tag):
+    """(config id, description, matrix shapes, layers, bytes of activations read per layer)."""
+    from synth import layers as syn
+
+    cfg_id, desc = WORKLOADS[tag]
+    cfg = syn.config(cfg_id)
+    shapes = [(m.rows, m.cols) for m in cfg.matrices]
+    x_bytes = 4 * cfg.tokens * sum(K for _, K in cfg.x_streams())
+    return cfg_id, desc, shapes, cfg.layers, x_bytes
+
+
+def trace_cmd(raw, tag, cfg_id):
+    return ("rocprofv3 --kernel-trace --stats --output-format csv -d %s/prof_%s -o run -- "
+            "python -u bench.py --config %d --steps 2 --warmup 1 --no-cpu --one-stream"
+            % (raw, tag, cfg_id))
+
+
+def pmc_cmd(counters, out, raw, cfg_id):
     return ("rocprofv3 --pmc %s --output-format csv -d %s/%s -o run -- python -u bench.py "
-            "--steps 1 --warmup 1 --no-cpu --one-stream" % (counters, raw, out))
+            "--config %d --steps 1 --warmup 1 --no-cpu --no-inference --one-stream"
+            % (counters, raw, out, cfg_id))
 
 
 def _rows(path):
@@ -55,61 +79,75 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def kernel_stats(raw, prof, out_md):
-    rows = _rows(os.path.join(raw, "prof_c2", "run_kernel_stats.csv"))
-    out = ["# Kernel durations: 8B-shaped decoder layer (218,103,808 weights, g=128, S=128, n=16, "
-           "10 iterations)\n",
-           WRITTEN_BY.format(raw=raw, prof=prof),
+def _short(name):
+    return (name.replace("void ", "").replace("aaac::", "")
+            .replace("(anonymous namespace)::", "").split("(")[0])
+
+
+def loop_kernel_average(rows, frag):
+    """Calls-weighted average duration (ns) over every instance of a kernel family."""
+    sel = [r for r in rows if frag in r["Name"]]
+    calls = sum(int(r["Calls"]) for r in sel)
+    total = sum(float(r["TotalDurationNs"]) for r in sel)
+    return (total / calls if calls else float("nan")), calls
+
+
+def kernel_stats(raw, prof, tag, out_md):
+    cfg_id, desc, shapes, nl, x_bytes = workload(tag)
+    N = sum(R * C for R, C in shapes)
+    alg = N * 2 + N // 2 + N // 128
+    rows = _rows(os.path.join(raw, "prof_%s" % tag, "run_kernel_stats.csv"))
+    per = TRACE_STEPS * nl               # traced layer passes
+    out = ["# Kernel durations: %s\n" % desc,
+           WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
            "Command (from the repository root, on one MI355X):\n",
-           "```\n%s\n```\n" % TRACE_CMD.format(raw=raw),
-           "Source: `run_kernel_stats.csv`. One bench step runs importance on the 4 activation "
-           "streams, a batched init of the 7 matrices, 10 x (batched assign, batched refine), a final batched "
-           "assign, then one batched pack and one batched dequant; 3 steps (1 warmup + 2 timed) are traced, then "
-           "the decode GEMV (9 launches) and the AWQ pre-scale (3 rounds of 7 launches) on the "
-           "packed layer. Only this library's kernels are listed (input generation and copies "
-           "omitted); \"per step\" is the total divided by 3.\n",
-           "| kernel | calls | average (us) | min (us) | max (us) | per step (us) |",
+           "```\n%s\n```\n" % trace_cmd(raw, tag, cfg_id),
+           "Source: `run_kernel_stats.csv`. Per layer a bench step runs importance on the %d "
+           "activation streams, a batched init of the %d matrices, 10 x (batched assign, batched "
+           "refine; the first refine also sums I w^2 for the error reports), the final batched "
+           "assign with its error totals, one batched pack and one batched dequant; %d steps "
+           "(1 warmup + 2 timed) of %d layer%s are traced, then the decode GEMV and the AWQ "
+           "pre-scale on one packed layer. Only this library's kernels are listed (input "
+           "generation and copies omitted); \"per layer\" is the total divided by the %d traced "
+           "layer passes.\n" % (4 if len(shapes) > 3 else 2, len(shapes), TRACE_STEPS, nl,
+                               "s" if nl > 1 else "", per),
+           "| kernel | calls | average (us) | min (us) | max (us) | per layer (us) |",
            "|---|---|---|---|---|---|"]
     for r in rows:
         n = r["Name"]
         if "aaac::" not in n:
             continue
-        short = (n.replace("void ", "").replace("aaac::", "")
-                 .replace("(anonymous namespace)::", "").split("(")[0])
         once = ("gemv" in n) or ("awq" in n)
-        per_step = "after the steps" if once else "%.0f" % (float(r["TotalDurationNs"]) / 1e3 / 3)
+        per_layer = "after the steps" if once else "%.0f" % (
+            float(r["TotalDurationNs"]) / 1e3 / per)
         out.append("| `%s` | %s | %.1f | %.1f | %.1f | %s |" % (
-            short, r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
-            float(r["MaxNs"]) / 1e3, per_step))
+            _short(n), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, per_layer))
     out.append("")
-    out.append("Per-launch algorithmic bytes of assign and of refine: 218,103,808 x (2 + 0.5 + "
-               "1/128) B = %s B." % format(ALG, ","))
-    for key, frag in (("assign", "assign_wide_kernel"), ("refine", "refine_kernel<")):
-        r = [x for x in rows if frag in x["Name"]][0]
-        t = float(r["AverageNs"]) * 1e-9
-        out.append("- %s: %.1f us average -> %.0f GB/s = %.1f %% of 8 TB/s." % (
-            key, t * 1e6, ALG / t / 1e9, ALG / t / PEAK * 100))
-    imp = [x for x in rows if "importance_partial" in x["Name"]][0]
-    t_imp = float(imp["TotalDurationNs"]) / 3 * 1e-9
-    out.append("- importance: %.2f ms per step for %.1f GB of activations -> %.2f TB/s." % (
-        t_imp * 1e3, X_BYTES / 1e9, X_BYTES / t_imp / 1e12))
+    out.append("Per-launch algorithmic bytes of assign and of refine (one layer, %s weights): "
+               "N x (2 + 0.5 + 1/128) B = %s B." % (format(N, ","), format(alg, ",")))
+    for key, frag in (("assign", ASSIGN + "0,"), ("refine", REFINE)):
+        t_ns, calls = loop_kernel_average(rows, frag)
+        t = t_ns * 1e-9
+        out.append("- %s (%d launches, every instance): %.1f us average -> %.0f GB/s = %.1f %% "
+                   "of 8 TB/s." % (key, calls, t * 1e6, alg / t / 1e9, alg / t / PEAK * 100))
+    imp = [x for x in rows if "importance_partial" in x["Name"]]
+    if imp:
+        t_imp = sum(float(x["TotalDurationNs"]) for x in imp) / per * 1e-9
+        out.append("- importance: %.2f ms per layer for %.1f GB of activations -> %.2f TB/s." % (
+            t_imp * 1e3, x_bytes / 1e9, x_bytes / t_imp / 1e12))
     gm = [x for x in rows if "gemv_kernel" in x["Name"]]
     if gm:
-        gb = sum(R * C // 2 + 2 * (R * C // 128) + 2 * C + 4 * R for R, C in MATS)
+        gb = sum(R * C // 2 + 2 * (R * C // 128) + 2 * C + 4 * R for R, C in shapes)
         t = float(gm[0]["AverageNs"]) * 1e-9
-        fetch = [float(x["Counter_Value"])
-                 for x in _rows(os.path.join(raw, "pmc_fetch", "run_counter_collection.csv"))
-                 if "gemv_kernel" in x["Kernel_Name"]]
-        fb = sum(fetch) / len(fetch) * 1024 * 2 if fetch else float("nan")
-        out.append("- decode GEMV (after the steps; batch 1, all 7 packed matrices in one launch, "
-                   "512 MB read before each launch so the %.1f MB of codes, scales, x and y come "
-                   "from HBM): %.1f us -> %.0f GB/s = %.1f %% of 8 TB/s; FETCH_SIZE x 2 = %.1f MB "
-                   "per launch (no re-reads)." % (gb / 1e6, t * 1e6, gb / t / 1e9,
-                                                 gb / t / PEAK * 100, fb / 1e6))
+        out.append("- decode GEMV (after the steps; batch 1, the %d packed matrices of one layer "
+                   "in one launch, 512 MB read before each launch so the %.1f MB of codes, "
+                   "scales, x and y come from HBM): %.1f us -> %.0f GB/s = %.1f %% of 8 TB/s."
+                   % (len(shapes), gb / 1e6, t * 1e6, gb / t / 1e9, gb / t / PEAK * 100))
     aw = [x for x in rows if "awq_prescale" in x["Name"]]
     if aw:
-        ab = sum(4 * R * C + 12 * C for R, C in MATS)
-        tot = float(aw[0]["TotalDurationNs"]) * 1e-9 / (int(aw[0]["Calls"]) / 7)
+        ab = sum(4 * R * C + 12 * C for R, C in shapes)
+        tot = float(aw[0]["TotalDurationNs"]) * 1e-9 / (int(aw[0]["Calls"]) / len(shapes))
         out.append("- AWQ pre-scale (after the steps; one launch per matrix, read W and write "
                    "W diag(a): %.1f MB per layer): %.1f us per layer -> %.0f GB/s = %.1f %% of "
                    "8 TB/s." % (ab / 1e6, tot * 1e6, ab / tot / 1e9, ab / tot / PEAK * 100))
@@ -117,20 +155,24 @@ def kernel_stats(raw, prof, out_md):
         f.write("\n".join(out) + "\n")
 
 
-def traffic(raw, prof, traffic_json, out_md):
+def traffic(raw, prof, tag, traffic_json, out_md):
+    cfg_id, desc, shapes, _, _ = workload(tag)
+    N = sum(R * C for R, C in shapes)
+    alg = N * 2 + N // 2 + N // 128
     with open(traffic_json) as f:
         d = json.load(f)
-    out = ["# HBM traffic per launch: assign and refine on the 8B-shaped decoder layer\n",
-           WRITTEN_BY.format(raw=raw, prof=prof),
+    out = ["# HBM traffic per launch: assign and refine on %s\n" % desc,
+           WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
            "Two counter passes over the same command, one counter each (from the repository root, "
            "on one MI355X):\n",
-           "```", _pmc_cmd("FETCH_SIZE", "pmc_fetch", raw), _pmc_cmd("WRITE_SIZE", "pmc_write", raw),
+           "```", pmc_cmd("FETCH_SIZE", "pmc_fetch_" + tag, raw, cfg_id),
+           pmc_cmd("WRITE_SIZE", "pmc_write_" + tag, raw, cfg_id),
            "python -m post_weight_quantization_06_amd.pmc_traffic "
-           "%s/pmc_fetch/run_counter_collection.csv %s/pmc_write/run_counter_collection.csv "
-           "%s/hbm_traffic_assign_refine_llama8b_layer.json" % (raw, raw, prof), "```\n",
+           "%s/pmc_fetch_%s/run_counter_collection.csv %s/pmc_write_%s/run_counter_collection.csv "
+           "%s/hbm_traffic_assign_refine_%s.json" % (raw, tag, raw, tag, prof, tag), "```\n",
            "Calibration: bench.py copies 2^30 bytes device-to-device once before its warmup step "
            "(`__amd_rocclr_copyBuffer`, the largest copy dispatch). For that copy FETCH_SIZE reads "
-           "%.1f KiB (half of the 1,048,576 KiB actually read) and WRITE_SIZE %.1f KiB, so the read "
+           "%.1f KiB (of the 1,048,576 KiB actually read) and WRITE_SIZE %.1f KiB, so the read "
            "counter is scaled by %.4f and the write counter by %.4f.\n" % (
                d["fetch_kib_copy"], d["write_kib_copy"], d["fetch_scale"], d["write_scale"]),
            "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | read (scaled) | "
@@ -139,24 +181,12 @@ def traffic(raw, prof, traffic_json, out_md):
     for k, v in d["kernels"].items():
         out.append("| %s | %d | %.0f | %.0f | %.1f MB | %.1f MB | %.1f MB | %.1f MB | %.3f |" % (
             k, v["dispatches"], v["fetch_kib"], v["write_kib"], v["read_bytes"] / 1e6,
-            v["write_bytes"] / 1e6, v["bytes"] / 1e6, ALG / 1e6, v["bytes"] / ALG))
-    a = d["kernels"]["assign"]
-    r = d["kernels"]["refine"]
-    w_bytes = 2 * N
-    cs_bytes = N // 2 + N // 128
+            v["write_bytes"] / 1e6, v["bytes"] / 1e6, alg / 1e6, v["bytes"] / alg))
     out += ["",
-            "Algorithmic bytes per launch (218,103,808 weights): assign reads W (%.1f MB) and "
-            "writes codes (%.1f MB) and selectors (%.1f MB); refine reads the same three. The "
-            "importance vectors and tables (under 0.2 MB) are not counted." % (
-                w_bytes / 1e6, N / 2 / 1e6, N / 128 / 1e6),
-            "",
-            "- assign reads %.3fx the bf16 weights and writes %.3fx its codes + selectors. The "
-            "selector bytes (one per 128 weights) are written as single bytes from different "
-            "waves; partially written lines are the likely source of the extra write traffic." % (
-                a["read_bytes"] / w_bytes, a["write_bytes"] / cs_bytes),
-            "- refine reads %.3fx W + codes + selectors." % (r["read_bytes"] / ALG),
-            "- Neither kernel re-reads its inputs: both are limited by instruction issue, not by "
-            "HBM bytes.",
+            "Algorithmic bytes per launch (%s weights): assign reads W (%.1f MB) and writes codes "
+            "(%.1f MB) and selectors (%.1f MB); refine reads the same three. The importance "
+            "vectors and tables are not counted." % (format(N, ","), 2 * N / 1e6, N / 2 / 1e6,
+                                                    N / 128 / 1e6),
             "",
             "The JSON beside this file holds the same figures with a hash of each kernel's "
             "sources; bench.py reports `roofline.traffic` only while the hash still matches."]
@@ -164,24 +194,30 @@ def traffic(raw, prof, traffic_json, out_md):
         f.write("\n".join(out) + "\n")
 
 
-def sq_counters(raw, prof, out_md):
+def sq_counters(raw, prof, tag, out_md):
+    cfg_id, desc, shapes, _, _ = workload(tag)
+    N = sum(R * C for R, C in shapes)
+
     def agg(path):
         acc = collections.defaultdict(lambda: collections.defaultdict(list))
         for r in _rows(path):
-            for key, frag in (("assign", "assign_wide_kernel"), ("refine", "aaac::refine_kernel<")):
+            for key, frag in (("assign", ASSIGN + "0,"), ("refine", REFINE)):
                 if frag in r["Kernel_Name"]:
                     acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
         return acc
 
-    a1 = agg(os.path.join(raw, "pmc_sq", "run_counter_collection.csv"))
-    a2 = agg(os.path.join(raw, "pmc_sq2", "run_counter_collection.csv"))
-    out = ["# Instruction counters: assign and refine on the 8B-shaped decoder layer\n",
-           WRITTEN_BY.format(raw=raw, prof=prof),
+    a1 = agg(os.path.join(raw, "pmc_sq_" + tag, "run_counter_collection.csv"))
+    a2 = agg(os.path.join(raw, "pmc_sq2_" + tag, "run_counter_collection.csv"))
+    out = ["# Instruction counters: assign and refine on %s\n" % desc,
+           WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
            "Commands (from the repository root, on one MI355X; one counter group per run):\n",
-           "```", _pmc_cmd(SQ1, "pmc_sq", raw), _pmc_cmd(SQ2, "pmc_sq2", raw), "```\n",
-           "Averages per dispatch (one batched launch over all 7 matrices, 218,103,808 weights). "
-           "SQ_INSTS_* count wave-level instructions (64 lanes), so per-weight figures are count x "
-           "64 / weights. Cycle counters are in units of 4 clocks, summed over waves.\n",
+           "```", pmc_cmd(SQ1, "pmc_sq_" + tag, raw, cfg_id),
+           pmc_cmd(SQ2, "pmc_sq2_" + tag, raw, cfg_id), "```\n",
+           "Averages per dispatch (one batched launch over the %d matrices of a layer, %s "
+           "weights; assign: the loop's instance without error output). SQ_INSTS_* count "
+           "wave-level instructions (64 lanes), so per-weight figures are count x 64 / weights. "
+           "Cycle counters are in units of 4 clocks, summed over waves.\n" % (
+               len(shapes), format(N, ",")),
            "| kernel | counter | per dispatch | per weight (x64 / N) |", "|---|---|---|---|"]
     for key in ("assign", "refine"):
         for src in (a1, a2):
@@ -191,27 +227,27 @@ def sq_counters(raw, prof, out_md):
                 out.append("| %s | %s | %.4g | %s |" % (key, c, mean, pw))
 
     def per_weight(src, key, c):
-        v = src[key][c]
-        return sum(v) / len(v) * 64 / N
+        v = src[key].get(c)
+        return sum(v) / len(v) * 64 / N if v else float("nan")
 
     def share(src, key, c):
         # fraction of wave cycles: both counters are summed over waves in the same units
-        v = src[key][c]
-        w = a1[key]["SQ_WAVE_CYCLES"]
+        v = src[key].get(c)
+        w = a1[key].get("SQ_WAVE_CYCLES")
+        if not v or not w:
+            return float("nan")
         return 100.0 * (sum(v) / len(v)) / (sum(w) / len(w))
 
     valu = per_weight(a1, "assign", "SQ_INSTS_VALU")
     out += ["", "Reading (VALU issue is 64 lane-instructions per clock per CU; 256 CUs at "
                 "2.4 GHz):", "",
             "- assign: %.1f VALU and %.1f LDS instructions per weight. VALU alone needs %.0f us "
-            "at full issue; SQ_WAIT_INST_LDS (waiting to issue LDS instructions, bank conflicts of "
-            "the random record reads) takes %.0f %% of wave time." % (
+            "at full issue; SQ_WAIT_INST_LDS takes %.0f %% of wave time." % (
                 valu, per_weight(a1, "assign", "SQ_INSTS_LDS"), N * valu / 64 / 256 / 2.4e9 * 1e6,
                 share(a2, "assign", "SQ_WAIT_INST_LDS")),
             "- refine: %.1f VALU and %.2f LDS instructions (the two fp64 adds) per weight, one "
             "workgroup of four waves per CU (128 KB of bins). Per wave: VALU busy %.0f %%, LDS "
-            "issue %.0f %%, waiting %.0f %% of its cycles; one wave per SIMD cannot overlap "
-            "them." % (
+            "issue %.0f %%, waiting %.0f %% of its cycles." % (
                 per_weight(a1, "refine", "SQ_INSTS_VALU"), per_weight(a1, "refine", "SQ_INSTS_LDS"),
                 share(a2, "refine", "SQ_ACTIVE_INST_VALU"), share(a2, "refine", "SQ_ACTIVE_INST_LDS"),
                 share(a2, "refine", "SQ_WAIT_ANY"))]
@@ -220,14 +256,17 @@ def sq_counters(raw, prof, out_md):
 
 
 def main(argv):
-    if len(argv) != 3:
+    if len(argv) not in (3, 4):
         print(__doc__)
         return 2
     raw, prof = argv[1].rstrip("/"), argv[2].rstrip("/")
-    kernel_stats(raw, prof, os.path.join(prof, "kernel_stats_llama8b_layer.md"))
-    traffic(raw, prof, os.path.join(prof, "hbm_traffic_assign_refine_llama8b_layer.json"),
-            os.path.join(prof, "hbm_traffic_assign_refine_llama8b_layer.md"))
-    sq_counters(raw, prof, os.path.join(prof, "sq_counters_assign_refine_llama8b_layer.md"))
+    tag = argv[3] if len(argv) == 4 else "32b_model"
+    kernel_stats(raw, prof, tag, os.path.join(prof, "kernel_stats_%s.md" % tag))
+    tj = os.path.join(prof, "hbm_traffic_assign_refine_%s.json" % tag)
+    if os.path.exists(tj):
+        traffic(raw, prof, tag, tj, os.path.join(prof, "hbm_traffic_assign_refine_%s.md" % tag))
+    if os.path.exists(os.path.join(raw, "pmc_sq_" + tag, "run_counter_collection.csv")):
+        sq_counters(raw, prof, tag, os.path.join(prof, "sq_counters_assign_refine_%s.md" % tag))
     return 0
 
 
