@@ -42,10 +42,13 @@ struct LutScratch {
   uint32_t wsum[16];        // per-wave totals of the record scan
 };
 
-// The lookup structure in LDS: per record one word, (i0 | i1 << 4) | off0 << 8 | off1 << 16 (the
-// code base and the byte offsets of the two candidate pairs), and per table the pair arrays.
+// The lookup structure in LDS: per record one word, (i0 | i1 << 4) | off << 8: the code base and
+// the byte offset of the record's candidates in `combo`, whose entry (p0, p1) holds pair p0 of
+// table 0 and pair p1 of table 1, {T0[p0], T0[p0 + 1], T1[p1], T1[p1 + 1]} (one 16-byte read per
+// weight gives all four candidates). The per-table pair arrays are kept for building it.
 struct Lut {
   uint32_t rec[kLutRecs];
+  float4 combo[kPairs * kPairs];
   float2 pairs[2][kPairs];
   float tab[2][16];         // the raw tables, for the exact scan
 };
@@ -90,6 +93,11 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
                                              : make_float2(qnan, qnan);
   }
   __syncthreads();
+  // every combination of a table-0 pair and a table-1 pair
+  for (int e = tid; e < kPairs * kPairs; e += NT) {
+    const float2 a = lut.pairs[0][e / kPairs], b = lut.pairs[1][e % kPairs];
+    lut.combo[e] = make_float4(a.x, a.y, b.x, b.y);
+  }
   if (tid < 32) {
     const int c = tid >> 4, j = tid & 15;
     const float x = ls.raw[c][j];
@@ -151,7 +159,7 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
 #pragma unroll
   for (int k = 0; k < kPer; ++k) {
     P += lut.rec[r0 + k];
-    uint32_t off[2];
+    uint32_t pi[2];
     uint32_t code = 0;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -166,10 +174,10 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
       const bool single = m > 0 && inside == 0;
       const bool pair = m > 0 && inside == 1 && ls.six[c][j1] == ls.six[c][j0] + 1;
       const int i0 = ls.six[c][j0];
-      off[c] = (uint32_t)((single || pair) ? i0 : kNaNPair) * 8u;
+      pi[c] = (uint32_t)((single || pair) ? i0 : kNaNPair);
       code |= (single || pair) ? ((uint32_t)i0 << (4 * c)) : 0u;
     }
-    lut.rec[r0 + k] = code | (off[0] << 8) | (off[1] << 16);
+    lut.rec[r0 + k] = code | (((pi[0] * kPairs + pi[1]) * (uint32_t)sizeof(float4)) << 8);
   }
   __syncthreads();
 }
@@ -188,14 +196,12 @@ __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, c
   const uint32_t ra = __float_as_uint(t) << 2;
   const uint32_t rec = *reinterpret_cast<const uint32_t*>(
       reinterpret_cast<const uint8_t*>(lut.rec) + ra);
-  const float2 p0 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[0]) + ((rec >> 8) & 0xFFu));
-  const float2 p1 = *reinterpret_cast<const float2*>(
-      reinterpret_cast<const uint8_t*>(lut.pairs[1]) + (rec >> 16));
-  const float r0a = __builtin_fmaf(nse, p0.x, w);
-  const float r0b = __builtin_fmaf(nse, p0.y, w);
-  const float r1a = __builtin_fmaf(nse, p1.x, w);
-  const float r1b = __builtin_fmaf(nse, p1.y, w);
+  const float4 p = *reinterpret_cast<const float4*>(
+      reinterpret_cast<const uint8_t*>(lut.combo) + (rec >> 8));
+  const float r0a = __builtin_fmaf(nse, p.x, w);
+  const float r0b = __builtin_fmaf(nse, p.y, w);
+  const float r1a = __builtin_fmaf(nse, p.z, w);
+  const float r1b = __builtin_fmaf(nse, p.w, w);
   const bool d0 = fabsf(r0b) < fabsf(r0a);
   const bool d1 = fabsf(r1b) < fabsf(r1a);
   const float m0 = fminf(fabsf(r0a), fabsf(r0b));
@@ -274,13 +280,6 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
                                            const uint16_t* wsafe, const float* isafe,
                                            const uint4& va, const uint4& vb,
                                            const float (&Ik)[16], Row16& o) {
-  const uint32_t amax = block_max_u32_t<G16>(lane_absmax16_bits(va, vb), g16);
-  const float s = __uint_as_float(amax << 16);
-  const bool zero = (s == 0.0f);
-  const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
-  const float se = zero ? 1.0f : s;
-  const float Y = lut_y(se);
-  const float nse = -se;
   float w[16];
   {
     float wa[8], wb[8];
@@ -292,6 +291,15 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
       w[8 + k] = wb[k];
     }
   }
+  // the group scale: the largest |w| as an fp32 bit pattern (a bf16 value: low 16 bits zero)
+  const uint32_t sbits = block_max_u32_t<G16>(absmax16_f32_bits(w), g16);
+  const uint32_t amax = sbits >> 16;
+  const float s = __uint_as_float(sbits);
+  const bool zero = (s == 0.0f);
+  const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
+  const float se = zero ? 1.0f : s;
+  const float Y = lut_y(se);
+  const float nse = -se;
 
   uint32_t c[16];
   double accd = 0.0, e0d = 0.0, e1d = 0.0;

@@ -229,22 +229,17 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
                         t.I[1].z, t.I[1].w, t.I[2].x, t.I[2].y, t.I[2].z, t.I[2].w,
                         t.I[3].x, t.I[3].y, t.I[3].z, t.I[3].w};
   char* const lds = reinterpret_cast<char*>(&sh.bins[0][0][0]) + tid * sizeof(double);
-  // a lane past the last column gets scale 0, so its terms are zero (see accumulate_task)
-  float s[kWideRowsPerWave];
-#pragma unroll
-  for (int i = 0; i < kWideRowsPerWave; ++i) {
-    const float si = __uint_as_float(
-        block_max_u32_t<G16>(lane_absmax16_bits(t.va[i], t.vb[i]), g16) << 16);
-    s[i] = t.active ? si : 0.0f;
-  }
 #pragma unroll
   for (int i = 0; i < kWideRowsPerWave; ++i) {
     if (t.r0 + (int64_t)kWavesPerBlock * i >= t.R) break;
-    const double sd = (double)s[i];               // fp64 terms: exact for every bf16 scale
-    const double s2 = sd * sd;
     float w[16];
     unpack8(t.va[i], *reinterpret_cast<float(*)[8]>(&w[0]));
     unpack8(t.vb[i], *reinterpret_cast<float(*)[8]>(&w[8]));
+    // the group scale; a lane past the last column gets scale 0, so its terms are zero (see
+    // accumulate_task)
+    const float si = __uint_as_float(block_max_u32_t<G16>(absmax16_f32_bits(w), g16));
+    const double sd = t.active ? (double)si : 0.0;   // fp64 terms: exact for every bf16 scale
+    const double s2 = sd * sd;
     char* const row = lds + (t.sb[i] ? 16 * sizeof(sh.bins[0]) : 0);
     // every term of the row first, then every add: with one wave per SIMD, an add issued right
     // after the multiply that feeds it would wait for that result
