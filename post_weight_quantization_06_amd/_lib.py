@@ -97,7 +97,7 @@ def load(path: str = LIB_PATH):
                                               c_vp, c_vp, c_vp]),
         "aaac_assign_refine_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
                                              c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), c_int,
-                                             c_vp, c_size, c_vp]),
+                                             c_vp, c_vp, c_vp, c_size, c_vp]),
         "aaac_gemv": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
                               c_int, c_vp, c_vp]),
         "aaac_gemv_batch": (c_int, [c_int, P(c_vp), P(c_vp), P(c_vp), P(c_vp), P(c_i64),
@@ -422,8 +422,11 @@ def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
 def aaac_assign_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
                              Is: Sequence[torch.Tensor], tables: Sequence[torch.Tensor],
                              codes: Sequence[torch.Tensor], sels: Sequence[torch.Tensor],
-                             flags: int = 0, ws: Optional[torch.Tensor] = None, stream=None):
-    """One assign + refine iteration in one launch (tables updated in place)."""
+                             flags: int = 0, ws: Optional[torch.Tensor] = None,
+                             err: Optional[torch.Tensor] = None, w2: Optional[torch.Tensor] = None,
+                             stream=None):
+    """One assign + refine iteration in one launch (tables updated in place); flags, err and w2 as
+    for aaac_refine_batch."""
     lib = load()
     k = len(Ws)
     Rs = [W.shape[0] for W in Ws]
@@ -434,13 +437,17 @@ def aaac_assign_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _need(tables[i], "tables[%d]" % i, torch.float32, 2 * n)
         _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
         _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
+    if err is not None:
+        _need(err, "err", torch.float64, k)
+    if w2 is not None:
+        _need(w2, "w2", torch.float64, k)
     if ws is None:
         ws = workspace(batch_workspace_bytes(OP_REFINE, Rs, Cs, g, S, n), Ws[0].device)
     st = lib.aaac_assign_refine_batch(
         k, _arr(c_vp, [t.data_ptr() for t in Ws]), _arr(c_i64, Rs), _arr(c_i64, Cs), g, S, n,
         _arr(c_vp, [t.data_ptr() for t in Is]), _arr(c_vp, [t.data_ptr() for t in tables]),
         _arr(c_vp, [t.data_ptr() for t in codes]), _arr(c_vp, [t.data_ptr() for t in sels]),
-        flags, _ptr(ws), ws.numel(), _stream(stream))
+        flags, _ptr(err), _ptr(w2), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "aaac_assign_refine_batch")
 
 

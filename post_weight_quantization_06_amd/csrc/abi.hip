@@ -30,8 +30,6 @@ namespace {
 
 using namespace aaac;
 
-constexpr int64_t kMaxRefineBlocks = 1024;
-
 thread_local char g_err[512];
 
 aaac_status fail(aaac_status st, const char* fmt, ...) {
@@ -97,10 +95,10 @@ size_t assign_ws_bytes(int count) {
   return 256 + (size_t)count * kMaxAssignBlocks * sizeof(double);
 }
 
-aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
-                      int g, int S, int n, const float* const* I, const float* const* tables,
-                      uint8_t* const* codes, uint8_t* const* sel, double* err, double* err_total,
-                      void* ws, size_t ws_bytes, void* stream, const char* who) {
+aaac_status check_assign_args(int count, const uint16_t* const* W, const int64_t* R,
+                              const int64_t* C, int g, int S, int n, const float* const* I,
+                              const float* const* tables, uint8_t* const* codes,
+                              uint8_t* const* sel, const char* who) {
   aaac_status st = check_batch(count, W, R, C, g, S, n, who);
   if (st != AAAC_OK) return st;
   if (!I || !tables || !codes || !sel) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
@@ -111,18 +109,13 @@ aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, con
                   "%s: matrix %d: I, tables, codes or sel null or misaligned (I and codes need 16 "
                   "bytes)", who, i);
   }
-  if (err && !aligned(err, 8)) return fail(AAAC_ERR_INVALID_ARG, "%s: err misaligned", who);
-  if (err_total) {
-    if (!aligned(err_total, 8))
-      return fail(AAAC_ERR_INVALID_ARG, "%s: err_total misaligned", who);
-    if (!ws || !aligned(ws, 256))
-      return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned (needed with err_total)",
-                  who);
-    if (ws_bytes < assign_ws_bytes(count))
-      return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes,
-                  assign_ws_bytes(count));
-  }
-  AssignBatch b{};
+  return AAAC_OK;
+}
+
+// An assign batch in the 8-weight task numbering (the launcher renumbers for the wide mapping).
+void build_assign_batch(AssignBatch& b, int count, const uint16_t* const* W, const int64_t* R,
+                        const int64_t* C, int g, int S, int n, const float* const* I,
+                        const float* const* tables, uint8_t* const* codes, uint8_t* const* sel) {
   b.njobs = count;
   b.g = g;
   b.S = S;
@@ -137,10 +130,33 @@ aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, con
     j.tables = tables[i];
     j.codes = reinterpret_cast<uint32_t*>(codes[i]);
     j.sel = sel[i];
-    j.err = err;
-    j.err_total = err_total ? err_total + i : nullptr;
   }
   b.total_tasks = tb;
+}
+
+aaac_status do_assign(int count, const uint16_t* const* W, const int64_t* R, const int64_t* C,
+                      int g, int S, int n, const float* const* I, const float* const* tables,
+                      uint8_t* const* codes, uint8_t* const* sel, double* err, double* err_total,
+                      void* ws, size_t ws_bytes, void* stream, const char* who) {
+  aaac_status st = check_assign_args(count, W, R, C, g, S, n, I, tables, codes, sel, who);
+  if (st != AAAC_OK) return st;
+  if (err && !aligned(err, 8)) return fail(AAAC_ERR_INVALID_ARG, "%s: err misaligned", who);
+  if (err_total) {
+    if (!aligned(err_total, 8))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: err_total misaligned", who);
+    if (!ws || !aligned(ws, 256))
+      return fail(AAAC_ERR_INVALID_ARG, "%s: ws null or not 256-byte aligned (needed with err_total)",
+                  who);
+    if (ws_bytes < assign_ws_bytes(count))
+      return fail(AAAC_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %zu < %zu bytes", who, ws_bytes,
+                  assign_ws_bytes(count));
+  }
+  AssignBatch b{};
+  build_assign_batch(b, count, W, R, C, g, S, n, I, tables, codes, sel);
+  for (int i = 0; i < count; ++i) {
+    b.job[i].err = err;
+    b.job[i].err_total = err_total ? err_total + i : nullptr;
+  }
   if (err_total) {
     b.totals = 1;
     b.counters = static_cast<uint32_t*>(ws);
@@ -590,38 +606,36 @@ aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const 
                                      const int64_t* C, int g, int S, int n,
                                      const float* const* I, float* const* tables,
                                      uint8_t* const* codes, uint8_t* const* sel, int flags,
-                                     void* ws, size_t ws_bytes, void* stream) {
+                                     double* err, double* w2, void* ws, size_t ws_bytes,
+                                     void* stream) {
   const char* who = "aaac_assign_refine_batch";
-  aaac_status st = check_batch(count, W, R, C, g, S, n, who);
-  if (st != AAAC_OK) return st;
-  if (flags & ~AAAC_REFINE_ROUND_BF16)
-    return fail(AAAC_ERR_INVALID_ARG, "%s: unknown flags %d", who, flags);
-  if (!I || !tables || !codes || !sel) return fail(AAAC_ERR_INVALID_ARG, "%s: null array", who);
+  if (count < 1 || count > AAAC_MAX_BATCH || !tables || !codes || !sel)
+    return fail(AAAC_ERR_INVALID_ARG, "%s: count=%d (need 1..%d) and non-null arrays", who, count,
+                AAAC_MAX_BATCH);
+  const float* tin[AAAC_MAX_BATCH];
+  const uint8_t* cc[AAAC_MAX_BATCH];
+  const uint8_t* sc[AAAC_MAX_BATCH];
   for (int i = 0; i < count; ++i) {
-    if (!I[i] || !aligned(I[i], 16) || !tables[i] || !aligned(tables[i], 4) || !codes[i] ||
-        !aligned(codes[i], 16) || !sel[i])
-      return fail(AAAC_ERR_INVALID_ARG, "%s: matrix %d: null or misaligned pointer", who, i);
+    tin[i] = tables[i];
+    cc[i] = codes[i];
+    sc[i] = sel[i];
   }
+  aaac_status st = check_refine_args(count, W, R, C, g, S, n, I, cc, sc, tin, tables, flags, err,
+                                     w2, who);
+  if (st != AAAC_OK) return st;
   st = check_refine_ws(count, ws, ws_bytes, who);
   if (st != AAAC_OK) return st;
   if (S < kWideLane) {
     // 8-weight selection groups: the two launches
-    const float* tin[AAAC_MAX_BATCH];
-    for (int i = 0; i < count; ++i) tin[i] = tables[i];
     st = do_assign(count, W, R, C, g, S, n, I, tin, codes, sel, nullptr, nullptr, nullptr, 0,
                    stream, who);
     if (st != AAAC_OK) return st;
-    const uint8_t* cc[AAAC_MAX_BATCH];
-    const uint8_t* sc[AAAC_MAX_BATCH];
-    for (int i = 0; i < count; ++i) {
-      cc[i] = codes[i];
-      sc[i] = sel[i];
-    }
-    return do_refine(count, W, R, C, g, S, n, I, cc, sc, tin, tables, flags, nullptr, nullptr, ws,
+    return do_refine(count, W, R, C, g, S, n, I, cc, sc, tin, tables, flags, err, w2, ws,
                      ws_bytes, stream, who);
   }
   RefineBatch b{};
   build_refine_batch(b, count, W, R, C, g, S, n, I, flags, ws);
+  b.errs = err ? 1 : 0;
   for (int i = 0; i < count; ++i) {
     RefineJob& j = b.job[i];
     j.codes = reinterpret_cast<const uint32_t*>(codes[i]);
@@ -630,6 +644,8 @@ aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const 
     j.sel_out = sel[i];
     j.tables_in = tables[i];
     j.tables_out = tables[i];
+    j.err_out = err ? err + i : nullptr;
+    j.w2 = err ? w2 + i : nullptr;
   }
   return hip_status(launch_assign_refine(b, static_cast<hipStream_t>(stream)), who);
 }

@@ -1,12 +1,13 @@
 // Assign step (AAAC summary §2 mechanisms 2 and 4): nearest entries in both tables, selection of
 // the table with the lower activation-weighted error, selected codes and selectors written out.
-// The lookup structure, the per-weight search and the selection are in lookup.h.
+// The lookup structure, the per-weight search and the selection are in lookup.h; the wide
+// mapping's row and task walk in assign_body.h.
 //
 // Work split: workgroup b owns a contiguous range of tasks (rows x one column slab of one matrix);
 // each of its waves issues the loads of all its rows of a task before it processes the first one,
 // and the workgroup rebuilds the lookup structure in LDS whenever it moves to another matrix. Two
 // mappings: 16 weights per lane for selection groups of 16 or more, 8 weights per lane otherwise.
-#include "lookup.h"
+#include "assign_body.h"
 
 namespace aaac {
 
@@ -146,121 +147,13 @@ __device__ __forceinline__ double assign_row(const AssignJob& jb, const Lut& lut
   return sel ? L1 : L0;
 }
 
-// Sum of this workgroup's chosen errors over job j, then (last workgroup of the job, by an integer
-// ticket) the job's total: each lane's running sum in row order, the lanes of a wave by butterfly,
-// the waves in order, the workgroups' partials in workgroup order. Every order is fixed, so the
-// total is reproducible for a given call. Called by every thread of the workgroup (barriers).
-__device__ void finish_err_total(const AssignBatch& b, int j, double lane_sum) {
-  __shared__ double wsum[kWavesPerBlock];
-  __shared__ uint32_t ticket;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  const AssignJob& jb = b.job[j];
-  double* part = b.partials + (size_t)j * b.slots;
-  const double ws = block_sum_f64_t<kWave>(lane_sum, kWave);
-  __syncthreads();
-  if (lane == 0) wsum[wave] = ws;
-  __syncthreads();
-  if (tid == 0) {
-    part[(int)blockIdx.x - jb.wg_lo] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-    __threadfence();
-    ticket = atomicAdd(b.counters + j, 1u);
-  }
-  __syncthreads();
-  if (ticket != (uint32_t)(jb.wg_count - 1)) return;
-  // last workgroup of this job: every partial is visible after the fence
-  __threadfence();
-  const int cnt = jb.wg_count;
-  const int s0 = (tid * cnt) / kBlock, s1 = ((tid + 1) * cnt) / kBlock;
-  double acc = 0.0;
-  for (int i = s0; i < s1; ++i) acc += part[i];
-  const double t = block_sum_f64_t<kWave>(acc, kWave);
-  __syncthreads();
-  if (lane == 0) wsum[wave] = t;
-  __syncthreads();
-  if (tid == 0) {
-    *jb.err_total = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-    b.counters[j] = 0u;
-  }
-}
-
 }  // namespace
-
-template <int EM, int G16, int S16>
-__device__ __forceinline__ double assign_row16(const AssignJob& jb, const Lut& lut, int n,
-                                               int g16, int s16, int log2S, int64_t r, int c0,
-                                               bool active, const uint16_t* wsafe,
-                                               const float* isafe, const uint4& va,
-                                               const uint4& vb, const float (&Ik)[16]) {
-  Row16 o;
-  row16_core<EM, G16, S16>(lut, n, g16, s16, active, wsafe, isafe, va, vb, Ik, o);
-  const int64_t rc = r * jb.geom.C;          // wave-uniform; a multiple of S
-  if (active)
-    store_row16<EM>(o, jb.codes + (rc >> 3), jb.sel + (rc >> log2S),
-                    (EM == kErrFull && jb.err) ? jb.err + 2 * (rc >> log2S) : nullptr, s16, log2S,
-                    c0);
-  return (EM != kErrNone && active) ? o.Esel : 0.0;
-}
 
 template <int EM, int G16, int S16>
 __global__ __launch_bounds__(kBlock, 3) void assign_wide_kernel(AssignBatch b) {
   __shared__ Lut lut;
   __shared__ LutScratch ls;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = wave_index();
-  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane, n = b.n;
-  const int log2S = 31 - __builtin_clz((unsigned)b.S);
-  const bool totals = EM == kErrTotal || (EM == kErrFull && b.totals);
-  const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
-  int cur = -1;
-  double etot = 0.0;
-  for (int64_t task = task_lo(blockIdx.x, b.total_tasks, gridDim.x); task < t_end; ++task) {
-    int j = 0;
-    while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
-    const AssignJob& jb = b.job[j];
-    if (j != cur) {
-      if (EM != kErrNone && totals && cur >= 0) {
-        finish_err_total(b, cur, etot);
-        etot = 0.0;
-      }
-      __syncthreads();
-      build_lut<kBlock>(jb.tables, n, lut, ls);
-      cur = j;
-    }
-    const int64_t local = task - jb.geom.task_begin;
-    const int64_t rb = local / jb.geom.nslab;
-    const int slab = (int)(local - rb * jb.geom.nslab);
-    const int c0 = slab * kWideSlab + lane * kWideLane;
-    const bool active = c0 < jb.geom.C;
-    const int cl = active ? c0 : 0;           // inactive lanes read an element of their own matrix
-    const int64_t R = jb.geom.R, C = jb.geom.C;
-    const int64_t r0 = rb * kWideRowsPerTask + wave;
-    // every load of the task first, unconditional (rows past the end read the last row and are
-    // skipped below; that test is the same for the whole wave)
-    uint4 va[kWideRowsPerWave], vb[kWideRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kWideRowsPerWave; ++i) {
-      int64_t r = r0 + (int64_t)kWavesPerBlock * i;
-      r = r < R ? r : R - 1;
-      const uint16_t* p = jb.W + r * C;         // wave-uniform row base
-      va[i] = *reinterpret_cast<const uint4*>(p + cl);
-      vb[i] = *reinterpret_cast<const uint4*>(p + cl + 8);
-    }
-    float Ik[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 x = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
-      Ik[4 * q] = x.x; Ik[4 * q + 1] = x.y; Ik[4 * q + 2] = x.z; Ik[4 * q + 3] = x.w;
-    }
-#pragma unroll
-    for (int i = 0; i < kWideRowsPerWave; ++i) {
-      const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
-      if (r >= R) break;
-      const double e = assign_row16<EM, G16, S16>(jb, lut, n, g16, s16, log2S, r, c0, active,
-                                                  jb.W + r * C + cl, jb.I + cl, va[i], vb[i], Ik);
-      if (EM != kErrNone) etot += e;
-    }
-  }
-  if (EM != kErrNone && totals && cur >= 0) finish_err_total(b, cur, etot);
+  assign_wide_body<EM, G16, S16>(b, lut, ls, WholeBlock());
 }
 
 template <int EM, int G8, int S8>
@@ -282,7 +175,7 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
     const AssignJob& jb = b.job[j];
     if (j != cur) {
       if (EM != kErrNone && totals && cur >= 0) {
-        finish_err_total(b, cur, etot);
+        finish_err_total(b, cur, etot, WholeBlock());
         etot = 0.0;
       }
       __syncthreads();
@@ -324,7 +217,7 @@ __global__ __launch_bounds__(kBlock) void assign_kernel(AssignBatch b) {
       }
     }
   }
-  if (EM != kErrNone && totals && cur >= 0) finish_err_total(b, cur, etot);
+  if (EM != kErrNone && totals && cur >= 0) finish_err_total(b, cur, etot, WholeBlock());
 }
 
 // Grid of a launch: enough workgroups to fill every CU at the kernel's occupancy, at most one per

@@ -66,6 +66,17 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
 }
 
+// The threads that run one kernel body together, here the whole workgroup: tid() is the thread's
+// index in the group, wave() the wave's (wave-uniform), sync() the group's barrier. The bodies take
+// it as a parameter rather than reading threadIdx and calling __syncthreads themselves.
+struct WholeBlock {
+  __device__ __forceinline__ int tid() const { return (int)threadIdx.x; }
+  __device__ __forceinline__ int wave() const {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+  }
+  __device__ __forceinline__ void sync() const { __syncthreads(); }
+};
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 
@@ -277,6 +288,8 @@ struct RefineJob {
 
 // Per-workgroup partial values of a refine: 64 cell sums (num, den of 32 cells), sum I w^2, pad.
 constexpr int kPartVals = 66;
+// Largest refine grid; the workspace holds this many partials per matrix.
+constexpr int64_t kMaxRefineBlocks = 1024;
 
 struct RefineBatch {
   RefineJob job[kMaxJobs];

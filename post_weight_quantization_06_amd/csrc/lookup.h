@@ -53,9 +53,9 @@ struct Lut {
   float tab[2][16];         // the raw tables, for the exact scan
 };
 
-// Build the lookup structure for tables T (fp32 [2][n], global) with all NT threads of the block
-// (NT = blockDim.x, a power of two from 64 to 1024). Must be called by every thread; ends with a
-// barrier.
+// Build the lookup structure for tables T (fp32 [2][n], global) with the NT threads of the group pt
+// (a power of two from 64 to 1024). Must be called by every thread of the group; ends with the
+// group's barrier.
 //
 // Midpoint i of a table (between its distinct values i and i + 1) lies in the records
 // [mlo_i, mhi_i] and below every record past mhi_i. Per record, "below" (midpoints below it) and
@@ -65,10 +65,11 @@ struct Lut {
 // packed prefix sums are exact). The array lives in the record words themselves, and one prefix
 // scan over the 1024 records turns it into the counts, which each thread then replaces by its
 // records' final words.
-template <int NT>
-__device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScratch& ls) {
+template <int NT, class Part = WholeBlock>
+__device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& lut, LutScratch& ls,
+                                       Part pt = Part()) {
   static_assert(NT >= kWave && NT <= kLutRecs && (NT & (NT - 1)) == 0, "block size");
-  const int tid = threadIdx.x;
+  const int tid = pt.tid();
   const float qnan = __uint_as_float(0x7fc00000u);
   if (tid < 32) {
     const int c = tid >> 4, j = tid & 15;
@@ -79,7 +80,7 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
   constexpr int kPer = kLutRecs / NT;       // records per thread
 #pragma unroll
   for (int k = 0; k < kPer; ++k) lut.rec[tid + NT * k] = 0u;
-  __syncthreads();
+  pt.sync();
   if (tid < 32) {
     const int c = tid >> 4, j = tid & 15;
     const float x = ls.raw[c][j];
@@ -92,7 +93,7 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
     if (j < 2) lut.pairs[c][16 + j] = j == 0 ? make_float2(__builtin_inff(), __builtin_inff())
                                              : make_float2(qnan, qnan);
   }
-  __syncthreads();
+  pt.sync();
   // every combination of a table-0 pair and a table-1 pair
   for (int e = tid; e < kPairs * kPairs; e += NT) {
     const float2 a = lut.pairs[0][e / kPairs], b = lut.pairs[1][e % kPairs];
@@ -117,7 +118,7 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
     }
     if (j == 0) ls.m[c] = finite ? m : 0;
   }
-  __syncthreads();
+  pt.sync();
   if (tid < 32) {
     const int c = tid >> 4, i = tid & 15;
     if (i + 1 < ls.m[c]) {
@@ -135,7 +136,7 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
       if (in_range) atomicAdd(&lut.rec[mlo > 0 ? mlo : 0], in1);
     }
   }
-  __syncthreads();
+  pt.sync();
   // prefix sums: thread t owns the run of kPer consecutive records starting at t * kPer
   const int r0 = tid * kPer;
   uint32_t tot = 0;
@@ -150,7 +151,7 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
     if (lane >= d) incl += o;
   }
   if (lane == kWave - 1) ls.wsum[tid / kWave] = incl;
-  __syncthreads();
+  pt.sync();
   uint32_t P = incl - tot;
   const int wv = tid / kWave;
 #pragma unroll
@@ -179,25 +180,32 @@ __device__ __noinline__ void build_lut(const float* __restrict__ T, int n, Lut& 
     }
     lut.rec[r0 + k] = code | (((pi[0] * kPairs + pi[1]) * (uint32_t)sizeof(float4)) << 8);
   }
-  __syncthreads();
+  pt.sync();
 }
 
 // Y for a group scale se > 0 (the lookup's u = w / se, scaled into the record index).
 __device__ __forceinline__ float lut_y(float se) { return kLutY * __builtin_amdgcn_rcpf(se); }
 
-// Nearest entries of one weight in both tables from the lookup structure (see the layout above):
-// returns the record word with the code byte q0 | q1 << 4 in byte 0 (the increments never carry out
-// of a nibble: a pair whose second entry is past the table or NaN is never taken), and accumulates
-// I (m1^2 - m0^2) (and I m0^2, I m1^2 as EM asks).
-template <int EM>
-__device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, const Lut& lut,
-                                                  float Ik, float& acc, float& a0, float& a1) {
+// The lookup of one weight in two steps, so that callers can issue every record read of a row
+// before the candidate reads: the record word of w, then (from that word) the four candidates.
+__device__ __forceinline__ uint32_t lut_record(float w, float Y, const Lut& lut) {
   const float t = __builtin_fmaf(w, Y, kLutMagic);
   const uint32_t ra = __float_as_uint(t) << 2;
-  const uint32_t rec = *reinterpret_cast<const uint32_t*>(
-      reinterpret_cast<const uint8_t*>(lut.rec) + ra);
-  const float4 p = *reinterpret_cast<const float4*>(
-      reinterpret_cast<const uint8_t*>(lut.combo) + (rec >> 8));
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lut.rec) + ra);
+}
+
+__device__ __forceinline__ float4 lut_candidates(uint32_t rec, const Lut& lut) {
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(lut.combo) +
+                                          (rec >> 8));
+}
+
+// Nearest entries of one weight in both tables from its record word and candidates: returns the
+// record word with the code byte q0 | q1 << 4 in byte 0 (the increments never carry out of a
+// nibble: a pair whose second entry is past the table or NaN is never taken), and accumulates
+// I (m1^2 - m0^2) (and I m0^2, I m1^2 as EM asks).
+template <int EM>
+__device__ __forceinline__ uint32_t lut_decide(float w, float nse, uint32_t rec, const float4& p,
+                                               float Ik, float& acc, float& a0, float& a1) {
   const float r0a = __builtin_fmaf(nse, p.x, w);
   const float r0b = __builtin_fmaf(nse, p.y, w);
   const float r1a = __builtin_fmaf(nse, p.z, w);
@@ -213,6 +221,14 @@ __device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, c
     a1 = __builtin_fmaf(Ik, m1 * m1, a1);
   }
   return rec + (d0 ? 1u : 0u) + (d1 ? 16u : 0u);   // byte 0: the code byte
+}
+
+// Both steps for one weight (see the layout above).
+template <int EM>
+__device__ __forceinline__ uint32_t lookup_weight(float w, float Y, float nse, const Lut& lut,
+                                                  float Ik, float& acc, float& a0, float& a1) {
+  const uint32_t rec = lut_record(w, Y, lut);
+  return lut_decide<EM>(w, nse, rec, lut_candidates(rec, lut), Ik, acc, a0, a1);
 }
 
 // Exact fallback for one lane of the wide mapping, reading its 16 weights and importances again
@@ -266,21 +282,23 @@ __device__ __noinline__ void slow_lane16(const uint16_t* __restrict__ wp,
 struct Row16 {
   uint32_t E[2], O[2];
   uint32_t sel;      // 1 = T1
+  float s;           // the group scale (0 for an all-zero group)
   double E0, E1;     // group errors (kErrFull)
   double Esel;       // this lane's share of the row's chosen error (kErrTotal, kErrFull)
 };
 
-// One row: group scale, nearest entries of all sixteen weights, and the selection of each group.
-// G16 / S16 are the lanes per scale / selection group (0: the runtime g16 / s16). wsafe / isafe
-// address the lane's 16 weights and importances in memory (in bounds also for inactive lanes) for
-// the exact fallback. The compiler may interleave all sixteen lookups (the exact scan is out of
-// line, so the row stays within the register budget of four waves per SIMD).
-template <int EM, int G16, int S16>
-__device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s16, bool active,
-                                           const uint16_t* wsafe, const float* isafe,
-                                           const uint4& va, const uint4& vb,
-                                           const float (&Ik)[16], Row16& o) {
-  float w[16];
+// The scale of one row of the wide mapping: the lane's 16 weights unpacked, the group's largest
+// |w| (as an fp32 bit pattern: a bf16 value, low 16 bits zero), and the lookup constants.
+struct Row16Scale {
+  float s, Y, nse;
+  uint32_t amax;       // s as bf16 bits
+  bool zero;           // all-zero group
+  bool fast_scale;     // s within the range where the lookup's residuals are exact
+};
+
+template <int G16>
+__device__ __forceinline__ void row16_scale(const uint4& va, const uint4& vb, int g16,
+                                            float (&w)[16], Row16Scale& sc) {
   {
     float wa[8], wb[8];
     unpack8(va, wa);
@@ -291,31 +309,25 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
       w[8 + k] = wb[k];
     }
   }
-  // the group scale: the largest |w| as an fp32 bit pattern (a bf16 value: low 16 bits zero)
   const uint32_t sbits = block_max_u32_t<G16>(absmax16_f32_bits(w), g16);
-  const uint32_t amax = sbits >> 16;
-  const float s = __uint_as_float(sbits);
-  const bool zero = (s == 0.0f);
-  const bool fast_scale = zero || (s >= kFastScaleMin && s <= kFastScaleMax);
-  const float se = zero ? 1.0f : s;
-  const float Y = lut_y(se);
-  const float nse = -se;
+  sc.amax = sbits >> 16;
+  sc.s = __uint_as_float(sbits);
+  sc.zero = (sc.s == 0.0f);
+  sc.fast_scale = sc.zero || (sc.s >= kFastScaleMin && sc.s <= kFastScaleMax);
+  const float se = sc.zero ? 1.0f : sc.s;
+  sc.Y = lut_y(se);
+  sc.nse = -se;
+}
 
-  uint32_t c[16];
-  double accd = 0.0, e0d = 0.0, e1d = 0.0;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    // four weights per fp32 partial, then fp64
-    float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      c[4 * q + k] = lookup_weight<EM>(w[4 * q + k], Y, nse, lut, Ik[4 * q + k], acc, a0, a1);
-    accd = (q == 0) ? (double)acc : accd + (double)acc;
-    if (EM >= kErrTotal) {
-      e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
-      e1d = (q == 0) ? (double)a1 : e1d + (double)a1;
-    }
-  }
+// The rest of a row once every weight's code word c[k] (code byte in byte 0) and the lane's
+// partial sums are known: gather the codes, reduce D over the selection group, take the exact
+// scan where needed, select. wsafe / isafe address the lane's 16 weights and importances in memory
+// (in bounds also for inactive lanes) for the exact fallback.
+template <int EM, int S16>
+__device__ __forceinline__ void row16_finish(const Lut& lut, int n, int s16, bool active,
+                                             const uint16_t* wsafe, const float* isafe,
+                                             const uint32_t (&c)[16], double accd, double e0d,
+                                             double e1d, const Row16Scale& sc, Row16& o) {
   // byte 0 of c[k] is weight k's code byte; gather them by column parity
   uint32_t Ew[2], Ow[2];
 #pragma unroll
@@ -333,18 +345,18 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
   double L0 = e0d, L1 = e1d;
   double E0 = EM == kErrFull ? block_sum_f64_t<S16>(e0d, s16) : 0.0;
   double E1 = EM == kErrFull ? block_sum_f64_t<S16>(e1d, s16) : 0.0;
-  if (zero) {
+  if (sc.zero) {
     D = 0.0;
     E0 = 0.0;
     E1 = 0.0;
     L0 = 0.0;
     L1 = 0.0;
   }
-  const bool bad = active && (!fast_scale || !(fabs(D) < __builtin_inf()));
+  const bool bad = active && (!sc.fast_scale || !(fabs(D) < __builtin_inf()));
   if (__any(bad)) {
     double lD, lE0, lE1;
     uint64_t clo, chi;
-    slow_lane16<(EM >= kErrTotal)>(wsafe, isafe, amax, lut.tab, n, lD, lE0, lE1, clo, chi);
+    slow_lane16<(EM >= kErrTotal)>(wsafe, isafe, sc.amax, lut.tab, n, lD, lE0, lE1, clo, chi);
     const double sD = block_sum_f64_t<S16>(lD, s16);
     double sE0 = 0.0, sE1 = 0.0;
     if (EM == kErrFull) {
@@ -369,18 +381,45 @@ __device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s
   o.E[0] = Ew[0]; o.E[1] = Ew[1];
   o.O[0] = Ow[0]; o.O[1] = Ow[1];
   o.sel = (D < 0.0) ? 1u : 0u;
+  o.s = sc.s;
   o.E0 = E0;
   o.E1 = E1;
   o.Esel = o.sel ? L1 : L0;
 }
 
-// Store the selected codes (8 bytes), and once per selection group the selector (and errors).
-// codes_row, sel_row and err_row point at the row's first code word, selector and error pair
-// (wave-uniform); c0 is the lane's first column. Rows start on a selection-group boundary, so the
-// lane's offsets within the row follow from c0 alone.
-template <int EM>
-__device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes_row, uint8_t* sel_row,
-                                            double* err_row, int s16, int log2S, int c0) {
+// One row: group scale, nearest entries of all sixteen weights, and the selection of each group.
+// G16 / S16 are the lanes per scale / selection group (0: the runtime g16 / s16). The compiler
+// may interleave all sixteen lookups (the exact scan is out of line, so the row stays within the
+// register budget of four waves per SIMD).
+template <int EM, int G16, int S16>
+__device__ __forceinline__ void row16_core(const Lut& lut, int n, int g16, int s16, bool active,
+                                           const uint16_t* wsafe, const float* isafe,
+                                           const uint4& va, const uint4& vb,
+                                           const float (&Ik)[16], Row16& o) {
+  float w[16];
+  Row16Scale sc;
+  row16_scale<G16>(va, vb, g16, w, sc);
+  uint32_t c[16];
+  double accd = 0.0, e0d = 0.0, e1d = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // four weights per fp32 partial, then fp64
+    float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      c[4 * q + k] =
+          lookup_weight<EM>(w[4 * q + k], sc.Y, sc.nse, lut, Ik[4 * q + k], acc, a0, a1);
+    accd = (q == 0) ? (double)acc : accd + (double)acc;
+    if (EM >= kErrTotal) {
+      e0d = (q == 0) ? (double)a0 : e0d + (double)a0;
+      e1d = (q == 0) ? (double)a1 : e1d + (double)a1;
+    }
+  }
+  row16_finish<EM, S16>(lut, n, s16, active, wsafe, isafe, c, accd, e0d, e1d, sc, o);
+}
+
+// The selected codes of a row as two code words: nibble m of word h is weight 8h + m.
+__device__ __forceinline__ uint2 chosen_codes16(const Row16& o) {
   const uint32_t sh = o.sel ? 4u : 0u;
   uint32_t out[2];
 #pragma unroll
@@ -390,7 +429,17 @@ __device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes_row,
     const uint32_t hi = o.O[k] << (4u - sh);
     out[k] = (lo & 0x0F0F0F0Fu) | (hi & 0xF0F0F0F0u);
   }
-  *reinterpret_cast<uint2*>(codes_row + (c0 >> 3)) = make_uint2(out[0], out[1]);
+  return make_uint2(out[0], out[1]);
+}
+
+// Store the selected codes (8 bytes), and once per selection group the selector (and errors).
+// codes_row, sel_row and err_row point at the row's first code word, selector and error pair
+// (wave-uniform); c0 is the lane's first column. Rows start on a selection-group boundary, so the
+// lane's offsets within the row follow from c0 alone.
+template <int EM>
+__device__ __forceinline__ void store_row16(const Row16& o, uint32_t* codes_row, uint8_t* sel_row,
+                                            double* err_row, int s16, int log2S, int c0) {
+  *reinterpret_cast<uint2*>(codes_row + (c0 >> 3)) = chosen_codes16(o);
   if (((c0 >> 4) & (s16 - 1)) == 0) {
     const int h = c0 >> log2S;
     sel_row[h] = (uint8_t)o.sel;

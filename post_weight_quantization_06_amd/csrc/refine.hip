@@ -112,9 +112,9 @@ struct TaskRows {
 // where it is used (zero importance for the lane; rows past the end are skipped). Loads that are
 // never conditional let the compiler wait for exactly the task being used while later tasks' loads
 // stay in flight.
-__device__ __forceinline__ void load_task(const TaskCursor& c, int log2S, TaskRows& t) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+__device__ __forceinline__ void load_task(const TaskCursor& c, int log2S, int tid, TaskRows& t) {
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int c0 = c.slab * kSlab + lane * kPerLane;
   const int64_t R = c.R, C = c.C;
   const int64_t rb = c.rb;
@@ -139,8 +139,7 @@ __device__ __forceinline__ void load_task(const TaskCursor& c, int log2S, TaskRo
 
 template <int G8, bool ERRS>
 __device__ __forceinline__ void accumulate_task(const TaskRows& t, int g8, RefineShared& sh,
-                                                double& w2) {
-  const int tid = threadIdx.x;
+                                                int tid, double& w2) {
   const float If[8] = {t.I0.x, t.I0.y, t.I0.z, t.I0.w, t.I1.x, t.I1.y, t.I1.z, t.I1.w};
   double Id[8];
 #pragma unroll
@@ -192,9 +191,10 @@ struct TaskRows16 {
   bool active;
 };
 
-__device__ __forceinline__ void load_task16(const TaskCursor& c, int log2S, TaskRows16& t) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+__device__ __forceinline__ void load_task16(const TaskCursor& c, int log2S, int tid,
+                                            TaskRows16& t) {
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
   const int c0 = c.slab * kWideSlab + lane * kWideLane;
   const int64_t R = c.R, C = c.C;
   const int64_t rb = c.rb;
@@ -272,21 +272,21 @@ __device__ __forceinline__ void accumulate_task16(const TaskRows16& t, int g16, 
 }
 
 // The two task layouts behind one name each, chosen by the buffer type.
-__device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, TaskRows& t) {
-  load_task(c, log2S, t);
+__device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, int tid, TaskRows& t) {
+  load_task(c, log2S, tid, t);
 }
-__device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, TaskRows16& t) {
-  load_task16(c, log2S, t);
+__device__ __forceinline__ void load_rows(const TaskCursor& c, int log2S, int tid, TaskRows16& t) {
+  load_task16(c, log2S, tid, t);
 }
-template <int GL, bool ERRS>
+template <int GL, bool ERRS, int PART>
 __device__ __forceinline__ void accumulate_rows(const TaskRows& t, int gl, RefineShared& sh,
-                                                double& w2) {
-  accumulate_task<GL, ERRS>(t, gl, sh, w2);
+                                                int tid, double& w2) {
+  accumulate_task<GL, ERRS>(t, gl, sh, tid, w2);
 }
-template <int GL, bool ERRS>
+template <int GL, bool ERRS, int PART>
 __device__ __forceinline__ void accumulate_rows(const TaskRows16& t, int gl, RefineShared& sh,
-                                                double& w2) {
-  accumulate_task16<GL, 16, ERRS>(t, gl, sh, threadIdx.x, w2);
+                                                int tid, double& w2) {
+  accumulate_task16<GL, PART, ERRS>(t, gl, sh, tid, w2);
 }
 
 // Round a finite fp64 value to bf16 (ties to even) directly, without an intermediate fp32
@@ -304,25 +304,24 @@ __device__ __forceinline__ float f64_to_bf16_value(double x) {
 
 // Publish this workgroup's partial of job j (and zero the bins); the last workgroup of the job adds
 // all partials and writes the tables (and with ERRS the error of the incoming assignment; w2 is the
-// caller's running sum of I w^2, reset here). Every thread of the workgroup calls it (it holds
-// barriers); tid is the caller's index among the kBlock accumulating threads, and threads outside
-// [0, kBlock) only take part in the barriers.
-template <bool ERRS>
-__device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int tid, double& w2) {
+// caller's running sum of I w^2, reset here). pt is the group of kBlock threads that accumulates;
+// every thread of it calls this (it holds the group's barriers).
+template <bool ERRS, class Part>
+__device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, Part pt, double& w2) {
   // ERRS: this call summed I w^2 (w2); b.errs alone: W2 comes from the caller
-  const bool act = tid >= 0 && tid < kBlock;
+  const int tid = pt.tid();
   const RefineJob& jb = b.job[j];
   __shared__ double part4[4][kVals];
   __shared__ double w2s[kWavesPerBlock + 1];
   __shared__ uint32_t ticket;
   if (ERRS) {
     // this workgroup's sum of I w^2: lanes by butterfly, waves in order
-    const double ws = block_sum_f64_t<kWave>(act ? w2 : 0.0, kWave);
+    const double ws = block_sum_f64_t<kWave>(w2, kWave);
     w2 = 0.0;
-    if (act && (tid & (kWave - 1)) == 0) w2s[tid / kWave] = ws;
+    if ((tid & (kWave - 1)) == 0) w2s[tid / kWave] = ws;
   }
-  __syncthreads();
-  if (act) {
+  pt.sync();
+  {
     // value v = tid & 63 over the 64 columns of quarter q = tid >> 6: four interleaved sums over a
     // rotated column order (no bank conflicts), all reads issued before the adds, combined in a
     // fixed order
@@ -333,29 +332,27 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
     for (int i = 0; i < 64; ++i) a[i & 3] += col[(i + v) & 63];
     part4[q][v] = (a[0] + a[1]) + (a[2] + a[3]);
   }
-  __syncthreads();
-  if (act) {
+  pt.sync();
 #pragma unroll
-    for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
-  }
+  for (int k = 0; k < kVals; ++k) sh.bins[k >> 1][k & 1][tid] = 0.0;
   double* part = b.partials + (size_t)j * kPartVals * b.slots;
   const int slot = (int)blockIdx.x - jb.wg_lo;
-  if (act && tid < kVals) {
+  if (tid < kVals) {
     const double tot = ((part4[0][tid] + part4[1][tid]) + part4[2][tid]) + part4[3][tid];
     part[(size_t)tid * b.slots + slot] = tot;
     __threadfence();
   }
-  if (ERRS && act && tid == kVals) {
+  if (ERRS && tid == kVals) {
     part[(size_t)kW2 * b.slots + slot] = ((w2s[0] + w2s[1]) + w2s[2]) + w2s[3];
     __threadfence();
   }
-  __syncthreads();
+  pt.sync();
   if (tid == 0) ticket = atomicAdd(b.counters + j, 1u);
-  __syncthreads();
+  pt.sync();
   if (ticket != (uint32_t)(jb.wg_count - 1)) return;
   // last workgroup of this job: every partial is visible after the fence
   __threadfence();
-  if (act) {
+  {
     // the partials of value v, quarter q of the workgroups: eight loads in flight per step, added
     // in workgroup order
     const int v = tid & 63, q = tid >> 6;
@@ -374,7 +371,7 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
     for (; i < s1; ++i) s += pv[i];
     part4[q][v] = s;
   }
-  if (ERRS && act && (tid & 63) == 0) {
+  if (ERRS && (tid & 63) == 0) {
     // the I w^2 partials, quarter q of the workgroups per thread, in workgroup order
     const int q = tid >> 6;
     const int cnt = jb.wg_count;
@@ -383,9 +380,9 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
     for (int i = (q * cnt) / 4; i < ((q + 1) * cnt) / 4; ++i) s += pv[i];
     w2s[q] = s;
   }
-  __syncthreads();
+  pt.sync();
   __shared__ double eterm[kCells];
-  if (act && tid < kCells) {
+  if (tid < kCells) {
     const int c = tid >> 4, idx = tid & 15;
     const int vn = 2 * tid, vd = 2 * tid + 1;
     const double nsum = ((part4[0][vn] + part4[1][vn]) + part4[2][vn]) + part4[3][vn];
@@ -402,7 +399,7 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
     if (b.errs) eterm[tid] = et;
   }
   if (b.errs) {
-    __syncthreads();
+    pt.sync();
     if (tid == 0 && jb.err_out) {
       const double W2 = ERRS ? ((w2s[0] + w2s[1]) + w2s[2]) + w2s[3] : *jb.w2;
       double x = 0.0;
@@ -412,15 +409,18 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, int ti
     }
   }
   if (tid == 0) b.counters[j] = 0u;
-  __syncthreads();
+  pt.sync();
 }
 
 }  // namespace
 
-template <bool WIDE, int GL, bool ERRS>
-__global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
-  __shared__ RefineShared sh;
-  const int tid = threadIdx.x;
+namespace {
+
+// The refine kernel's work for one workgroup, with the bins in sh; pt names the kBlock threads
+// that run it. PART: weights of a row whose terms are formed before their adds (accumulate_task16).
+template <bool WIDE, int GL, bool ERRS, int PART = 16, class Part = WholeBlock>
+__device__ __forceinline__ void refine_body(const RefineBatch& b, RefineShared& sh, Part pt) {
+  const int tid = pt.tid();
   const int gl = b.g / (WIDE ? kWideLane : kPerLane);   // lanes per scale group
   const int log2S = 31 - __builtin_clz((unsigned)b.S);
 #pragma unroll
@@ -436,220 +436,296 @@ __global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
   // the cursor stops at the last task: past the end a buffer reloads that task and is never used
   TaskCursor c;
   cursor_init(b, t_begin, t_end - 1, c);
-  load_rows(c, log2S, A);
+  load_rows(c, log2S, tid, A);
   cursor_next(b, c);
   for (int64_t task = t_begin; task < t_end; task += 2) {
-    load_rows(c, log2S, B);
+    load_rows(c, log2S, tid, B);
     cursor_next(b, c);
     if (A.job != cur) {
-      if (cur >= 0) finish_job<ERRS>(b, cur, sh, threadIdx.x, w2);
+      if (cur >= 0) finish_job<ERRS>(b, cur, sh, pt, w2);
       cur = A.job;
     }
-    accumulate_rows<GL, ERRS>(A, gl, sh, w2);
+    accumulate_rows<GL, ERRS, PART>(A, gl, sh, tid, w2);
     if (task + 1 >= t_end) break;
-    load_rows(c, log2S, A);
+    load_rows(c, log2S, tid, A);
     cursor_next(b, c);
     if (B.job != cur) {
-      finish_job<ERRS>(b, cur, sh, threadIdx.x, w2);
+      finish_job<ERRS>(b, cur, sh, pt, w2);
       cur = B.job;
     }
-    accumulate_rows<GL, ERRS>(B, gl, sh, w2);
+    accumulate_rows<GL, ERRS, PART>(B, gl, sh, tid, w2);
   }
-  if (cur >= 0) finish_job<ERRS>(b, cur, sh, threadIdx.x, w2);
+  if (cur >= 0) finish_job<ERRS>(b, cur, sh, pt, w2);
+}
+
+}  // namespace
+
+template <bool WIDE, int GL, bool ERRS>
+__global__ __launch_bounds__(kBlock, 1) void refine_kernel(RefineBatch b) {
+  __shared__ RefineShared sh;
+  refine_body<WIDE, GL, ERRS>(b, sh, WholeBlock());
 }
 
 // ------------------------------------------------------------------------------------------------
 // Fused assign + accumulate: one launch per iteration of the loop (AAAC summary §2 mechanism 4,
 // the alternation of assignment and refinement).
 //
-// A workgroup of 16 waves: 12 assign waves and 4 accumulate waves, one workgroup per CU (the
-// accumulate waves hold the 128 KB of bins). The workgroup walks the same task range as a refine
-// workgroup, in steps of up to three tasks of one matrix. In step s the assign waves run the assign
-// of step s's tasks (four waves per task, the thread mapping of the assign kernel) and write codes
-// and selectors; the accumulate waves add up step s - 1 exactly as the refine kernel does (same
-// thread per column, same task and row order, same finish), reading the codes just written from
-// L2 and the selectors from LDS. Assign and accumulate waves share each SIMD, so one's VALU work
-// overlaps the other's LDS adds. Results are bitwise those of the assign launch followed by the
-// refine launch.
+// The refine kernel's grid, task ranges and thread mapping, with the assign step done in place:
+// a wave computes the codes and selections of a row from the lookup structure (lookup.h), writes
+// them, and adds the row's terms into its bins from the weights it already holds. W is read once
+// per iteration instead of twice and the codes are never read back. The bins keep the kernel at
+// one workgroup of four waves per CU, so each wave overlaps its own work: the weights of its next
+// task load while it runs the current one. Results are bitwise those of the assign launch
+// followed by the refine launch: the codes and selections come from the same per-row search, and
+// the same threads add the same terms in the same order.
 // ------------------------------------------------------------------------------------------------
-constexpr int kFusedAssignWaves = 12;
-constexpr int kFusedGroups = kFusedAssignWaves / kWavesPerBlock;          // tasks per step
-constexpr int kFusedThreads = (kFusedAssignWaves + kWavesPerBlock) * kWave;
-constexpr int kFusedAcc0 = kFusedAssignWaves * kWave;                    // first accumulate thread
-
 namespace {
 
 struct FusedShared {
   RefineShared rs;
   Lut lut;
   LutScratch ls;
-  // selector of each (task of the step, row of the task, lane) as written by the assign waves;
-  // two copies, for the step being assigned and the step being accumulated
-  uint8_t sig[2][kFusedGroups][kWideRowsPerTask][kWave];
 };
 
-// Tasks [lo, hi) of the step starting at `task`: up to kFusedGroups tasks, all of one matrix.
-__device__ __forceinline__ void fused_step(const RefineBatch& b, int64_t task, int64_t t_end,
-                                           int& job, int64_t& hi) {
-  int j = 0;
-  while (j + 1 < b.njobs && task >= b.job[j + 1].geom.task_begin) ++j;
-  const int64_t job_end = b.job[j].geom.task_begin + b.job[j].geom.ntasks;
-  hi = task + kFusedGroups;
-  hi = hi < job_end ? hi : job_end;
-  hi = hi < t_end ? hi : t_end;
-  job = j;
-}
-
-template <int G16, int S16>
-__device__ __forceinline__ void fused_assign_task(const RefineBatch& b, const RefineJob& jb,
-                                                  int64_t task, int w, int buf, int grp,
-                                                  const Lut& lut, FusedShared& sh) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane, n = b.n;
-  const int log2S = 31 - __builtin_clz((unsigned)b.S);
-  const int64_t local = task - jb.geom.task_begin;
-  const int64_t rb = local / jb.geom.nslab;
-  const int slab = (int)(local - rb * jb.geom.nslab);
-  const int c0 = slab * kWideSlab + lane * kWideLane;
-  const bool active = c0 < jb.geom.C;
-  const int cl = active ? c0 : 0;
-  const int64_t R = jb.geom.R, C = jb.geom.C;
-  const int64_t r0 = rb * kWideRowsPerTask + w;
+// One task's weights and importances in registers (loads as in load_task16).
+struct FusedRows {
   uint4 va[kWideRowsPerWave], vb[kWideRowsPerWave];
-#pragma unroll
-  for (int i = 0; i < kWideRowsPerWave; ++i) {
-    int64_t r = r0 + (int64_t)kWavesPerBlock * i;
-    r = r < R ? r : R - 1;
-    const uint16_t* p = jb.W + r * C;
-    va[i] = *reinterpret_cast<const uint4*>(p + cl);
-    vb[i] = *reinterpret_cast<const uint4*>(p + cl + 8);
-  }
-  float Ik[16];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float4 x = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
-    Ik[4 * q] = x.x; Ik[4 * q + 1] = x.y; Ik[4 * q + 2] = x.z; Ik[4 * q + 3] = x.w;
-  }
-#pragma unroll
-  for (int i = 0; i < kWideRowsPerWave; ++i) {
-    const int64_t r = r0 + (int64_t)kWavesPerBlock * i;
-    if (r >= R) break;
-    Row16 o;
-    row16_core<kErrNone, G16, S16>(lut, n, g16, s16, active, jb.W + r * C + cl, jb.I + cl, va[i],
-                                vb[i], Ik, o);
-    const int64_t rc = r * C;
-    if (active)
-      store_row16<kErrNone>(o, jb.codes_out + (rc >> 3), jb.sel_out + (rc >> log2S), nullptr, s16,
-                         log2S, c0);
-    sh.sig[buf][grp][w + kWavesPerBlock * i][lane] = (uint8_t)o.sel;
-  }
-}
+  float4 I[4];
+  int64_t r0, R, C;
+  int c0;
+  int job;
+  bool active;
+};
 
-// The accumulate side of one task: wave w of the accumulate waves adds rows w, w + 4, ... exactly
-// as the refine kernel's wave w does, with the selectors from LDS.
-template <int G16>
-__device__ __forceinline__ void fused_accumulate_task(const RefineBatch& b, const RefineJob& jb,
-                                                      int j, int64_t task, int w, int buf,
-                                                      int grp, FusedShared& sh) {
+__device__ __forceinline__ void load_fused(const TaskCursor& c, FusedRows& t) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t local = task - jb.geom.task_begin;
-  const int64_t rb = local / jb.geom.nslab;
-  const int slab = (int)(local - rb * jb.geom.nslab);
-  TaskRows16 t;
-  const int c0 = slab * kWideSlab + lane * kWideLane;
-  const int64_t R = jb.geom.R, C = jb.geom.C;
+  const int wave = threadIdx.x / kWave;
+  const int c0 = c.slab * kWideSlab + lane * kWideLane;
+  const int64_t R = c.R, C = c.C;
   t.active = c0 < C;
-  const int cl = t.active ? c0 : 0;
-  t.job = j;
+  const int64_t cl = t.active ? c0 : 0;
+  t.c0 = c0;
+  t.job = c.job;
   t.R = R;
-  t.r0 = rb * kWideRowsPerTask + w;
+  t.C = C;
+  t.r0 = c.rb * kWideRowsPerTask + wave;
 #pragma unroll
   for (int i = 0; i < kWideRowsPerWave; ++i) {
     int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
     r = r < R ? r : R - 1;
     const int64_t base = r * C + cl;
-    t.va[i] = *reinterpret_cast<const uint4*>(jb.W + base);
-    t.vb[i] = *reinterpret_cast<const uint4*>(jb.W + base + 8);
-    t.cw[i] = *reinterpret_cast<const uint2*>(jb.codes_out + (base >> 3));
-    t.sb[i] = sh.sig[buf][grp][w + kWavesPerBlock * i][lane];
+    t.va[i] = *reinterpret_cast<const uint4*>(c.W + base);
+    t.vb[i] = *reinterpret_cast<const uint4*>(c.W + base + 8);
   }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(jb.I + cl + 4 * q);
-  double w2 = 0.0;
-  accumulate_task16<G16, 8>(t, b.g / kWideLane, sh.rs, (int)threadIdx.x - kFusedAcc0, w2);
+  for (int q = 0; q < 4; ++q) t.I[q] = *reinterpret_cast<const float4*>(c.I + cl + 4 * q);
+}
+
+// A row whose codes and selections are known and whose terms are not added yet: its adds are
+// issued during the next row's search, so that they never sit in the LDS queue in front of that
+// row's lookups. A pending row with zero scale and importance adds zeros (nothing changes).
+struct Pending {
+  float w[16];
+  float If[16];
+  uint2 cw;                  // chosen codes, nibble m of word h: weight 8h + m
+  double sd, s2;             // s and s^2 in fp64 (0 for an inactive lane)
+  uint32_t off;              // byte offset of the chosen table's bins
+  bool active;
+};
+
+constexpr uint32_t kBinRow = sizeof(double) * 2 * kBlock;   // one cell's {num, den} columns
+
+__device__ __forceinline__ void pending_clear(Pending& p) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    p.w[k] = 0.0f;
+    p.If[k] = 0.0f;
+  }
+  p.cw = make_uint2(0u, 0u);
+  p.sd = 0.0;
+  p.s2 = 0.0;
+  p.off = 0u;
+  p.active = false;
+}
+
+// Terms of weight k of the pending row and their adds (the refine kernel's terms and order:
+// num, then den, weights in column order).
+template <bool ERRS>
+__device__ __forceinline__ void pending_add(const Pending& p, int k, char* lds, double& w2) {
+  const uint32_t word = k < 8 ? p.cw.x : p.cw.y;
+  const uint32_t q = (word >> (4 * (k & 7))) & 15u;
+  double* const a = reinterpret_cast<double*>(lds + p.off + q * kBinRow);
+  const double Id = (double)p.If[k];
+  const double wd = (double)p.w[k];
+  atomicAdd(a, Id * (p.sd * wd));
+  atomicAdd(a + kBlock, Id * p.s2);
+  if (ERRS) w2 = __builtin_fma(p.active ? Id : 0.0, wd * wd, w2);
+}
+
+template <bool ERRS>
+__device__ __forceinline__ void pending_flush(const Pending& p, char* lds, double& w2) {
+#pragma unroll
+  for (int k = 0; k < 16; ++k) pending_add<ERRS>(p, k, lds, w2);
+}
+
+// One row: the search of row16_core (same arithmetic, so the same codes and selections) with the
+// pending row's adds placed between its LDS reads: every record read first, then four of the
+// pending adds while they are in flight, then every candidate read, then the decisions with the
+// other twelve adds among them. The row then becomes the pending row.
+template <int G16, int S16, bool ERRS>
+__device__ __forceinline__ void fused_row(const Lut& lut, int n, int g16, int s16, bool active,
+                                          const uint16_t* wsafe, const float* isafe,
+                                          const uint4& va, const uint4& vb,
+                                          const float (&If)[16], Pending& pend, char* lds,
+                                          double& w2, Row16& o) {
+  float w[16];
+  Row16Scale sc;
+  row16_scale<G16>(va, vb, g16, w, sc);
+  uint32_t rec[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) rec[k] = lut_record(w[k], sc.Y, lut);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pending_add<ERRS>(pend, k, lds, w2);
+  __builtin_amdgcn_sched_barrier(0);
+  float4 cand[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) cand[k] = lut_candidates(rec[k], lut);
+  __builtin_amdgcn_sched_barrier(0);
+  uint32_t c[16];
+  double accd = 0.0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float acc = 0.0f, a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int kk = 4 * q + k;
+      c[kk] = lut_decide<kErrNone>(w[kk], sc.nse, rec[kk], cand[kk], If[kk], acc, a0, a1);
+      if (kk < 12) pending_add<ERRS>(pend, kk + 4, lds, w2);
+      // keep the adds spread among the decisions
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    accd = (q == 0) ? (double)acc : accd + (double)acc;
+  }
+  row16_finish<kErrNone, S16>(lut, n, s16, active, wsafe, isafe, c, accd, 0.0, 0.0, sc, o);
+  // this row is the next pending row
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    pend.w[k] = w[k];
+    pend.If[k] = If[k];
+  }
+  pend.cw = chosen_codes16(o);
+  pend.sd = active ? (double)o.s : 0.0;   // fp64 terms: exact for every bf16 scale
+  pend.s2 = pend.sd * pend.sd;
+  pend.off = o.sel ? 16u * kBinRow : 0u;
+  pend.active = active;
+}
+
+// Every row of one task (rows past the end are the same for the whole wave and are skipped).
+template <int G16, int S16, bool ERRS>
+__device__ __forceinline__ void fused_task(const RefineBatch& b, const FusedRows& t,
+                                           FusedShared& sh, int g16, int s16, int log2S,
+                                           Pending& pend, double& w2) {
+  const RefineJob& jb = b.job[t.job];
+  const float If[16] = {t.I[0].x, t.I[0].y, t.I[0].z, t.I[0].w, t.I[1].x, t.I[1].y,
+                        t.I[1].z, t.I[1].w, t.I[2].x, t.I[2].y, t.I[2].z, t.I[2].w,
+                        t.I[3].x, t.I[3].y, t.I[3].z, t.I[3].w};
+  const int cl = t.active ? t.c0 : 0;
+  char* const lds = reinterpret_cast<char*>(&sh.rs.bins[0][0][0]) + threadIdx.x * sizeof(double);
+#pragma unroll
+  for (int i = 0; i < kWideRowsPerWave; ++i) {
+    const int64_t r = t.r0 + (int64_t)kWavesPerBlock * i;
+    if (r >= t.R) break;
+    const int64_t rc = r * t.C;               // wave-uniform; a multiple of S
+    Row16 o;
+    fused_row<G16, S16, ERRS>(sh.lut, b.n, g16, s16, t.active, jb.W + rc + cl, jb.I + cl,
+                              t.va[i], t.vb[i], If, pend, lds, w2, o);
+    if (t.active) {
+      *reinterpret_cast<uint2*>(jb.codes_out + (rc >> 3) + (t.c0 >> 3)) = pend.cw;
+      if (((t.c0 >> 4) & (s16 - 1)) == 0) jb.sel_out[(rc >> log2S) + (t.c0 >> log2S)] = (uint8_t)o.sel;
+    }
+  }
 }
 
 }  // namespace
 
-template <int G16, int S16>
-__global__ __launch_bounds__(kFusedThreads, 1) void assign_refine_kernel(RefineBatch b) {
+template <int G16, int S16, bool ERRS>
+__global__ __launch_bounds__(kBlock, 1) void assign_refine_kernel(RefineBatch b) {
   __shared__ FusedShared sh;
   const int tid = threadIdx.x;
-  const int wave = wave_index();
-  const bool acc_wave = wave >= kFusedAssignWaves;
-  const int atid = tid - kFusedAcc0;                   // index among the accumulating threads
-  if (acc_wave) {
+  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane;
+  const int log2S = 31 - __builtin_clz((unsigned)b.S);
 #pragma unroll
-    for (int k = 0; k < kVals; ++k) sh.rs.bins[k >> 1][k & 1][atid] = 0.0;
-  }
+  for (int k = 0; k < kVals; ++k) sh.rs.bins[k >> 1][k & 1][tid] = 0.0;
   const int64_t t_begin = task_lo(blockIdx.x, b.total_tasks, gridDim.x);
   const int64_t t_end = task_lo(blockIdx.x + 1, b.total_tasks, gridDim.x);
-  int lut_job = -1, acc_job = -1;
-  double w2_unused = 0.0;
-  int prev_job = -1;
-  int64_t prev_lo = 0, prev_hi = 0;                    // the step the accumulate waves take next
-  int buf = 0;
-  for (int64_t lo = t_begin;; buf ^= 1) {
-    int job = -1;
-    int64_t hi = lo;
-    if (lo < t_end) fused_step(b, lo, t_end, job, hi);
-    if (job < 0 && prev_job < 0) break;
-    // matrix changes, with every thread: the accumulate side finishes its matrix before it starts
-    // the next one; the assign side builds the lookup structure of its new matrix
-    if (prev_job >= 0 && prev_job != acc_job) {
-      if (acc_job >= 0) finish_job<false>(b, acc_job, sh.rs, atid, w2_unused);
-      acc_job = prev_job;
+  if (t_begin >= t_end) return;
+  // two statically named buffers, as in the refine kernel: task t + 1 loads while t runs
+  FusedRows A, B;
+  int cur = -1;
+  double w2 = 0.0;
+  char* const lds = reinterpret_cast<char*>(&sh.rs.bins[0][0][0]) + tid * sizeof(double);
+  Pending pend;
+  pending_clear(pend);
+  TaskCursor c;
+  cursor_init(b, t_begin, t_end - 1, c);
+  load_fused(c, A);
+  cursor_next(b, c);
+  for (int64_t task = t_begin; task < t_end; task += 2) {
+    load_fused(c, B);
+    cursor_next(b, c);
+    if (A.job != cur) {
+      // the pending row belongs to the matrix being left. The last barrier of finish_job (or the
+      // kernel's start) orders the rebuild after every wave's last use of the previous lookup
+      // structure.
+      if (cur >= 0) {
+        pending_flush<ERRS>(pend, lds, w2);
+        pending_clear(pend);
+        finish_job<ERRS>(b, cur, sh.rs, WholeBlock(), w2);
+      }
+      build_lut<kBlock>(b.job[A.job].tables_in, b.n, sh.lut, sh.ls);
+      cur = A.job;
     }
-    if (job >= 0 && job != lut_job) {
-      __syncthreads();
-      build_lut<kFusedThreads>(b.job[job].tables_in, b.n, sh.lut, sh.ls);
-      lut_job = job;
+    fused_task<G16, S16, ERRS>(b, A, sh, g16, s16, log2S, pend, w2);
+    if (task + 1 >= t_end) break;
+    load_fused(c, A);
+    cursor_next(b, c);
+    if (B.job != cur) {
+      pending_flush<ERRS>(pend, lds, w2);
+      pending_clear(pend);
+      finish_job<ERRS>(b, cur, sh.rs, WholeBlock(), w2);
+      build_lut<kBlock>(b.job[B.job].tables_in, b.n, sh.lut, sh.ls);
+      cur = B.job;
     }
-    if (!acc_wave) {
-      const int grp = wave / kWavesPerBlock;
-      if (job >= 0 && lo + grp < hi)
-        fused_assign_task<G16, S16>(b, b.job[job], lo + grp, wave % kWavesPerBlock, buf, grp,
-                                    sh.lut, sh);
-    } else if (prev_job >= 0) {
-      // the codes of step s - 1 were written by this workgroup's assign waves before the last
-      // barrier (a workgroup-scope release and acquire: all waves share this CU's write-through
-      // cache, so a line cached earlier cannot hide them)
-      for (int64_t t = prev_lo; t < prev_hi; ++t)
-        fused_accumulate_task<G16>(b, b.job[prev_job], prev_job, t, wave - kFusedAssignWaves,
-                                   buf ^ 1, (int)(t - prev_lo), sh);
-    }
-    __syncthreads();
-    prev_job = job;
-    prev_lo = lo;
-    prev_hi = hi;
-    lo = hi;
+    fused_task<G16, S16, ERRS>(b, B, sh, g16, s16, log2S, pend, w2);
   }
-  if (acc_job >= 0) finish_job<false>(b, acc_job, sh.rs, atid, w2_unused);
+  pending_flush<ERRS>(pend, lds, w2);
+  finish_job<ERRS>(b, cur, sh.rs, WholeBlock(), w2);
 }
+
+namespace {
+
+template <bool ERRS>
+hipError_t launch_assign_refine_t(RefineBatch& b, hipStream_t stream) {
+  const dim3 grid(b.nblocks), block(kBlock);
+  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane;
+  if (g16 == 8 && s16 == 8)
+    hipLaunchKernelGGL((assign_refine_kernel<8, 8, ERRS>), grid, block, 0, stream, b);
+  else if (g16 == 8 && s16 == 1)
+    hipLaunchKernelGGL((assign_refine_kernel<8, 1, ERRS>), grid, block, 0, stream, b);
+  else if (g16 == 1 && s16 == 1)
+    hipLaunchKernelGGL((assign_refine_kernel<1, 1, ERRS>), grid, block, 0, stream, b);
+  else
+    hipLaunchKernelGGL((assign_refine_kernel<0, 0, ERRS>), grid, block, 0, stream, b);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 hipError_t launch_assign_refine(RefineBatch& b, hipStream_t stream) {
   if (b.nblocks <= 0) return hipSuccess;
-  const dim3 grid(b.nblocks), block(kFusedThreads);
-  const int g16 = b.g / kWideLane, s16 = b.S / kWideLane;
-  if (g16 == 8 && s16 == 8)
-    hipLaunchKernelGGL((assign_refine_kernel<8, 8>), grid, block, 0, stream, b);
-  else if (g16 == 8 && s16 == 1)
-    hipLaunchKernelGGL((assign_refine_kernel<8, 1>), grid, block, 0, stream, b);
-  else if (g16 == 1 && s16 == 1)
-    hipLaunchKernelGGL((assign_refine_kernel<1, 1>), grid, block, 0, stream, b);
-  else
-    hipLaunchKernelGGL((assign_refine_kernel<0, 0>), grid, block, 0, stream, b);
-  return hipGetLastError();
+  // the I w^2 sum only when the caller does not have it
+  if (b.errs && !(b.flags & 2)) return launch_assign_refine_t<true>(b, stream);
+  return launch_assign_refine_t<false>(b, stream);
 }
 
 MatrixGeom refine_geom(int64_t R, int64_t C, int64_t task_begin, int S) {

@@ -196,10 +196,18 @@ def test_assign_refine_batch_rejects_bad_arguments(lib):
     C = (i64 * 1)(1024)
     f = lib.aaac_assign_refine_batch
     need = lib.aaac_batch_workspace_bytes(OP_REFINE, 1, R, C, 128, 128, 16)
-    assert f(0, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(need), None) == INVALID
-    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 4, FAKE, ctypes.c_size_t(need), None) == INVALID
-    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(16), None) == WS_SMALL
-    assert f(1, P, R, C, 100, 100, 16, P, P, P, P, 0, FAKE, ctypes.c_size_t(need), None) == SHAPE
+    N = ctypes.c_size_t(need)
+    assert f(0, P, R, C, 128, 128, 16, P, P, P, P, 0, None, None, FAKE, N, None) == INVALID
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 4, None, None, FAKE, N, None) == INVALID
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 0, None, None, FAKE, ctypes.c_size_t(16),
+             None) == WS_SMALL
+    assert f(1, P, R, C, 100, 100, 16, P, P, P, P, 0, None, None, FAKE, N, None) == SHAPE
+    # error outputs: err and w2 together, 8-byte aligned; the W2-known flag needs them
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 0, FAKE, None, FAKE, N, None) == INVALID
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 0, ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE,
+             N, None) == INVALID
+    assert f(1, P, R, C, 128, 128, 16, P, P, P, P, 2, None, None, FAKE, N, None) == INVALID
+    assert b"W2_KNOWN" in lib.aaac_last_error()
 
 
 def test_init_batch_workspace_and_arguments(lib):

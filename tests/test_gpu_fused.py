@@ -62,16 +62,30 @@ def _run_both(shapes, g, S, n, iters, seed):
     Cs = [C for _, C in shapes]
     wsf = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), DEV)
     ws2 = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), DEV)
+    k = len(shapes)
+    ef, wf = (torch.zeros(k, dtype=torch.float64, device=DEV) for _ in range(2))
+    e2, w2 = (torch.zeros(k, dtype=torch.float64, device=DEV) for _ in range(2))
     for it in range(iters):
-        flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
-        L.aaac_assign_refine_batch(Ws, g, S, n, Is, tf, cf, sf, flags, wsf)
+        # the error outputs every iteration: I w^2 summed on the first, read back after that
+        flags = (L.REFINE_ROUND_BF16 if it == iters - 1 else 0) | (L.REFINE_W2_KNOWN if it else 0)
+        L.aaac_assign_refine_batch(Ws, g, S, n, Is, tf, cf, sf, flags, wsf, err=ef, w2=wf)
         L.aaac_assign_batch(Ws, g, S, n, Is, t2, c2, s2)
-        L.aaac_refine_batch(Ws, g, S, n, Is, c2, s2, t2, flags, ws2)
+        L.aaac_refine_batch(Ws, g, S, n, Is, c2, s2, t2, flags, ws2, err=e2, w2=w2)
         torch.cuda.synchronize()
-        for i in range(len(shapes)):
+        for i in range(k):
             assert torch.equal(cf[i], c2[i]), ("codes", it, shapes[i])
             assert torch.equal(sf[i], s2[i]), ("sel", it, shapes[i])
             assert torch.equal(tf[i], t2[i]), ("tables", it, shapes[i], _np(tf[i]), _np(t2[i]))
+        assert torch.equal(ef, e2), ("err", it, _np(ef), _np(e2))
+        assert torch.equal(wf, w2), ("w2", it, _np(wf), _np(w2))
+    # and without error outputs
+    L.aaac_assign_refine_batch(Ws, g, S, n, Is, tf, cf, sf, 0, wsf)
+    L.aaac_assign_batch(Ws, g, S, n, Is, t2, c2, s2)
+    L.aaac_refine_batch(Ws, g, S, n, Is, c2, s2, t2, 0, ws2)
+    torch.cuda.synchronize()
+    for i in range(k):
+        assert torch.equal(cf[i], c2[i]) and torch.equal(sf[i], s2[i])
+        assert torch.equal(tf[i], t2[i])
     # the workspaces are left zeroed for the next call
     assert int(wsf[:256].count_nonzero()) == 0
     return Ws, Is, tf, cf, sf
@@ -117,3 +131,4 @@ def test_fused_full_size_llama8b_layer():
     shapes = [(m.rows, m.cols) for m in cfg.matrices]
     _say("fused full size", cfg.name)
     _run_both(shapes, cfg.g, cfg.S, cfg.n, iters=cfg.iters, seed=2)
+
