@@ -30,7 +30,7 @@ KERNELS = {
     "refine": ("aaac::refine_kernel<",),
 }
 KERNEL_SOURCES = {
-    "assign": ["assign.hip", "lookup.h", "common.h"],
+    "assign": ["assign.hip", "assign_body.h", "lookup.h", "common.h"],
     "refine": ["refine.hip", "lookup.h", "common.h"],
 }
 
