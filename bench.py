@@ -218,6 +218,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cpu-workers", type=int, default=16,
                     help="oracle worker processes (capped by the host's CPU count)")
+    ap.add_argument("--fused", action="store_true",
+                    help="run each iteration as one aaac_assign_refine_batch launch (bitwise the "
+                         "same results) instead of the assign and refine launches")
     ap.add_argument("--one-stream", action="store_true",
                     help="run init after importance on one stream (for per-kernel profiles)")
     args = ap.parse_args()
@@ -328,7 +331,7 @@ def main():
                                   wsp.get(("importance", xid), L.workspace_bytes(
                                       L.OP_IMPORTANCE, Xs[xid].shape[0], K)))
             stream.wait_stream(side)
-            pkg.run_loop(Ws[l], Is, buf, wsp, init=False, probe=t)
+            pkg.run_loop(Ws[l], Is, buf, wsp, init=False, probe=t, fused=args.fused)
             L.aaac_dequant_batch(buf.codes, buf.scales, buf.bitmaps, buf.tables_bf16, Rs, Cs,
                                  g, S, n, W_hat)
             if timing is None:
@@ -366,15 +369,24 @@ def main():
     r_ms = [x.elapsed_time(y) for t in recs for x, y in t.r]
     a_avg = sum(a_ms) / len(a_ms)
     r_avg = sum(r_ms) / len(r_ms)
+    # one launch reads W and writes the codes and selectors (the fused launch does no more)
     bytes_launch = algorithmic_bytes(numel_layer, S)
-    dom, dom_ms = ("assign", a_avg) if a_avg >= r_avg else ("refine", r_avg)
+    if args.fused:
+        dom, dom_ms = "fused", a_avg
+    else:
+        dom, dom_ms = ("assign", a_avg) if a_avg >= r_avg else ("refine", r_avg)
     achieved = bytes_launch / (dom_ms * 1e-3) / 1e9
     value = 2.0 * numel * iters / (loop_ms * 1e-3) / 1e9
-    print("[bench] step %.3f ms, loop %.3f ms, assign %.1f us (%.0f GB/s), refine %.1f us "
-          "(%.0f GB/s), wall %.2f s" % (step_ms, loop_ms, a_avg * 1e3,
-                                        bytes_launch / a_avg / 1e6, r_avg * 1e3,
-                                        bytes_launch / r_avg / 1e6, wall),
-          file=sys.stderr, flush=True)
+    if args.fused:
+        print("[bench] step %.3f ms, loop %.3f ms, fused %.1f us (%.0f GB/s), wall %.2f s" % (
+            step_ms, loop_ms, a_avg * 1e3, bytes_launch / a_avg / 1e6, wall),
+            file=sys.stderr, flush=True)
+    else:
+        print("[bench] step %.3f ms, loop %.3f ms, assign %.1f us (%.0f GB/s), refine %.1f us "
+              "(%.0f GB/s), wall %.2f s" % (step_ms, loop_ms, a_avg * 1e3,
+                                            bytes_launch / a_avg / 1e6, r_avg * 1e3,
+                                            bytes_launch / r_avg / 1e6, wall),
+              file=sys.stderr, flush=True)
     # the error totals of the last step: non-increasing over the iterations of every matrix
     for l in range(nl):
         pkg.check_history(bufs[l].err, w2=bufs[l].w2)
@@ -382,7 +394,7 @@ def main():
     print("[bench] error history, last layer, first matrix: %s" % ", ".join(
         "%.6g" % x for x in last), file=sys.stderr, flush=True)
     traffic = None
-    if args.config in TRAFFIC_SUMMARY:
+    if args.config in TRAFFIC_SUMMARY and not args.fused:
         t = pmc_traffic.load_traffic(TRAFFIC_SUMMARY[args.config], dom)
         traffic = None if t is None else int(round(t))
     inference = None
@@ -421,19 +433,24 @@ def main():
                    "numel": numel, "g": g, "S": S, "n": n, "iters": iters,
                    "calib_tokens": cfg.tokens},
         "loop_ms_per_step": round(loop_ms, 4),
-        "assign_us": round(a_avg * 1e3, 2),
-        "refine_us": round(r_avg * 1e3, 2),
-        "hbm_frac_assign": round(bytes_launch / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "hbm_frac_refine": round(bytes_launch / (r_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "iteration": "one fused launch" if args.fused else "assign and refine launches",
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "bytes per launch",
                      "algorithmic_bytes": int(round(bytes_launch)),
-                     "launches_timed": len(a_ms) if dom == "assign" else len(r_ms)},
+                     "launches_timed": len(r_ms) if dom == "refine" else len(a_ms)},
         "cpu_baseline": cpu,
         "inference": inference,
     }
+    if args.fused:
+        out["fused_us"] = round(a_avg * 1e3, 2)
+        out["hbm_frac_fused"] = round(bytes_launch / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    else:
+        out["assign_us"] = round(a_avg * 1e3, 2)
+        out["refine_us"] = round(r_avg * 1e3, 2)
+        out["hbm_frac_assign"] = round(bytes_launch / (a_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        out["hbm_frac_refine"] = round(bytes_launch / (r_avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     print(json.dumps(out), flush=True)
 
 

@@ -3,10 +3,11 @@
 Turns the raw rocprofv3 output of the runs below (one counter group per run, all writing under
 one folder RAW) into the short Markdown summaries kept in PROFILES, for one workload TAG
 (`32b_model`: the 64-layer 32B-shaped model, bench.py --config 5; `llama8b_layer`: the 8B-shaped
-decoder layer, --config 2):
+decoder layer, --config 2; `32b_model_fused`: the 32B-shaped model with each iteration as one
+fused launch, --config 5 --fused):
 
     rocprofv3 --kernel-trace --stats --output-format csv -d RAW/prof_TAG -o run -- \\
-        python -u bench.py --config N --steps 2 --warmup 1 --no-cpu --one-stream
+        python -u bench.py --config N [--fused] --steps 2 --warmup 1 --no-cpu --one-stream
     rocprofv3 --pmc FETCH_SIZE ... -d RAW/pmc_fetch_TAG ...  (bench.py --steps 1 --warmup 1)
     rocprofv3 --pmc WRITE_SIZE ... -d RAW/pmc_write_TAG ...
     rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU ... -d RAW/pmc_sq_TAG ...
@@ -32,10 +33,14 @@ import sys
 
 PEAK = 8e12
 
-# workload tag -> (bench config, name, number of (warmup + timed) steps of the trace command)
+# workload tag -> (bench config, name, fused iterations)
 WORKLOADS = {
-    "32b_model": (5, "the 32B-shaped model (64 decoder layers, g=128, S=128, n=16, 10 iterations)"),
-    "llama8b_layer": (2, "the 8B-shaped decoder layer (g=128, S=128, n=16, 10 iterations)"),
+    "32b_model": (5, "the 32B-shaped model (64 decoder layers, g=128, S=128, n=16, 10 iterations)",
+                  False),
+    "llama8b_layer": (2, "the 8B-shaped decoder layer (g=128, S=128, n=16, 10 iterations)", False),
+    "32b_model_fused": (5, "the 32B-shaped model (64 decoder layers, g=128, S=128, n=16, 10 "
+                           "iterations), each iteration one fused assign + accumulate launch",
+                        True),
 }
 TRACE_STEPS = 3      # the trace command runs 1 warmup + 2 timed steps
 
@@ -49,13 +54,25 @@ WRITTEN_BY = ("Summary written by `python -m post_weight_quantization_06_amd.pro
 # kernel families: (key, name fragment); the loop kernels of every template instance
 ASSIGN = "aaac::assign_wide_kernel<"
 REFINE = "aaac::refine_kernel<"
+FUSED = "aaac::assign_refine_kernel<"
+
+
+def loop_families(tag):
+    """The loop kernels of a workload: (key, name fragment) for each family."""
+    if WORKLOADS[tag][2]:
+        return (("fused", FUSED),)
+    return (("assign", ASSIGN + "0,"), ("refine", REFINE))
+
+
+def _flags(tag):
+    return " --fused" if WORKLOADS[tag][2] else ""
 
 
 def workload(tag):
     """(config id, description, matrix shapes, layers, bytes of activations read per layer)."""
     from synth import layers as syn
 
-    cfg_id, desc = WORKLOADS[tag]
+    cfg_id, desc, _ = WORKLOADS[tag]
     cfg = syn.config(cfg_id)
     shapes = [(m.rows, m.cols) for m in cfg.matrices]
     x_bytes = 4 * cfg.tokens * sum(K for _, K in cfg.x_streams())
@@ -64,14 +81,14 @@ def workload(tag):
 
 def trace_cmd(raw, tag, cfg_id):
     return ("rocprofv3 --kernel-trace --stats --output-format csv -d %s/prof_%s -o run -- "
-            "python -u bench.py --config %d --steps 2 --warmup 1 --no-cpu --one-stream"
-            % (raw, tag, cfg_id))
+            "python -u bench.py --config %d%s --steps 2 --warmup 1 --no-cpu --one-stream"
+            % (raw, tag, cfg_id, _flags(tag)))
 
 
-def pmc_cmd(counters, out, raw, cfg_id):
+def pmc_cmd(counters, out, raw, cfg_id, tag):
     return ("rocprofv3 --pmc %s --output-format csv -d %s/%s -o run -- python -u bench.py "
-            "--config %d --steps 1 --warmup 1 --no-cpu --no-inference --one-stream"
-            % (counters, raw, out, cfg_id))
+            "--config %d%s --steps 1 --warmup 1 --no-cpu --no-inference --one-stream"
+            % (counters, raw, out, cfg_id, _flags(tag)))
 
 
 def _rows(path):
@@ -103,14 +120,16 @@ def kernel_stats(raw, prof, tag, out_md):
            "Command (from the repository root, on one MI355X):\n",
            "```\n%s\n```\n" % trace_cmd(raw, tag, cfg_id),
            "Source: `run_kernel_stats.csv`. Per layer a bench step runs importance on the %d "
-           "activation streams, a batched init of the %d matrices, 10 x (batched assign, batched "
-           "refine; the first refine also sums I w^2 for the error reports), the final batched "
+           "activation streams, a batched init of the %d matrices, 10 x (%s; the first also sums "
+           "I w^2 for the error reports), the final batched "
            "assign with its error totals, one batched pack and one batched dequant; %d steps "
            "(1 warmup + 2 timed) of %d layer%s are traced, then the decode GEMV and the AWQ "
            "pre-scale on one packed layer. Only this library's kernels are listed (input "
            "generation and copies omitted); \"per layer\" is the total divided by the %d traced "
-           "layer passes.\n" % (4 if len(shapes) > 3 else 2, len(shapes), TRACE_STEPS, nl,
-                               "s" if nl > 1 else "", per),
+           "layer passes.\n" % (4 if len(shapes) > 3 else 2, len(shapes),
+                               "one batched fused assign + accumulate launch"
+                               if WORKLOADS[tag][2] else "batched assign, batched refine",
+                               TRACE_STEPS, nl, "s" if nl > 1 else "", per),
            "| kernel | calls | average (us) | min (us) | max (us) | per layer (us) |",
            "|---|---|---|---|---|---|"]
     for r in rows:
@@ -124,9 +143,10 @@ def kernel_stats(raw, prof, tag, out_md):
             _short(n), r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, per_layer))
     out.append("")
-    out.append("Per-launch algorithmic bytes of assign and of refine (one layer, %s weights): "
+    out.append("Per-launch algorithmic bytes of each loop launch (one layer, %s weights; the "
+               "fused launch reads W and writes codes and selectors once): "
                "N x (2 + 0.5 + 1/128) B = %s B." % (format(N, ","), format(alg, ",")))
-    for key, frag in (("assign", ASSIGN + "0,"), ("refine", REFINE)):
+    for key, frag in loop_families(tag):
         t_ns, calls = loop_kernel_average(rows, frag)
         t = t_ns * 1e-9
         out.append("- %s (%d launches, every instance): %.1f us average -> %.0f GB/s = %.1f %% "
@@ -165,8 +185,8 @@ def traffic(raw, prof, tag, traffic_json, out_md):
            WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
            "Two counter passes over the same command, one counter each (from the repository root, "
            "on one MI355X):\n",
-           "```", pmc_cmd("FETCH_SIZE", "pmc_fetch_" + tag, raw, cfg_id),
-           pmc_cmd("WRITE_SIZE", "pmc_write_" + tag, raw, cfg_id),
+           "```", pmc_cmd("FETCH_SIZE", "pmc_fetch_" + tag, raw, cfg_id, tag),
+           pmc_cmd("WRITE_SIZE", "pmc_write_" + tag, raw, cfg_id, tag),
            "python -m post_weight_quantization_06_amd.pmc_traffic "
            "%s/pmc_fetch_%s/run_counter_collection.csv %s/pmc_write_%s/run_counter_collection.csv "
            "%s/hbm_traffic_assign_refine_%s.json" % (raw, tag, raw, tag, prof, tag), "```\n",
@@ -201,25 +221,26 @@ def sq_counters(raw, prof, tag, out_md):
     def agg(path):
         acc = collections.defaultdict(lambda: collections.defaultdict(list))
         for r in _rows(path):
-            for key, frag in (("assign", ASSIGN + "0,"), ("refine", REFINE)):
+            for key, frag in loop_families(tag):
                 if frag in r["Kernel_Name"]:
                     acc[key][r["Counter_Name"]].append(float(r["Counter_Value"]))
         return acc
 
     a1 = agg(os.path.join(raw, "pmc_sq_" + tag, "run_counter_collection.csv"))
     a2 = agg(os.path.join(raw, "pmc_sq2_" + tag, "run_counter_collection.csv"))
-    out = ["# Instruction counters: assign and refine on %s\n" % desc,
+    keys = [k for k, _ in loop_families(tag)]
+    out = ["# Instruction counters: %s on %s\n" % (" and ".join(keys), desc),
            WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
            "Commands (from the repository root, on one MI355X; one counter group per run):\n",
-           "```", pmc_cmd(SQ1, "pmc_sq_" + tag, raw, cfg_id),
-           pmc_cmd(SQ2, "pmc_sq2_" + tag, raw, cfg_id), "```\n",
+           "```", pmc_cmd(SQ1, "pmc_sq_" + tag, raw, cfg_id, tag),
+           pmc_cmd(SQ2, "pmc_sq2_" + tag, raw, cfg_id, tag), "```\n",
            "Averages per dispatch (one batched launch over the %d matrices of a layer, %s "
            "weights; assign: the loop's instance without error output). SQ_INSTS_* count "
            "wave-level instructions (64 lanes), so per-weight figures are count x 64 / weights. "
            "Cycle counters are in units of 4 clocks, summed over waves.\n" % (
                len(shapes), format(N, ",")),
            "| kernel | counter | per dispatch | per weight (x64 / N) |", "|---|---|---|---|"]
-    for key in ("assign", "refine"):
+    for key in keys:
         for src in (a1, a2):
             for c, v in src[key].items():
                 mean = sum(v) / len(v)
@@ -238,19 +259,32 @@ def sq_counters(raw, prof, tag, out_md):
             return float("nan")
         return 100.0 * (sum(v) / len(v)) / (sum(w) / len(w))
 
-    valu = per_weight(a1, "assign", "SQ_INSTS_VALU")
     out += ["", "Reading (VALU issue is 64 lane-instructions per clock per CU; 256 CUs at "
-                "2.4 GHz):", "",
-            "- assign: %.1f VALU and %.1f LDS instructions per weight. VALU alone needs %.0f us "
-            "at full issue; SQ_WAIT_INST_LDS takes %.0f %% of wave time." % (
-                valu, per_weight(a1, "assign", "SQ_INSTS_LDS"), N * valu / 64 / 256 / 2.4e9 * 1e6,
-                share(a2, "assign", "SQ_WAIT_INST_LDS")),
-            "- refine: %.1f VALU and %.2f LDS instructions (the two fp64 adds) per weight, one "
-            "workgroup of four waves per CU (128 KB of bins). Per wave: VALU busy %.0f %%, LDS "
-            "issue %.0f %%, waiting %.0f %% of its cycles." % (
-                per_weight(a1, "refine", "SQ_INSTS_VALU"), per_weight(a1, "refine", "SQ_INSTS_LDS"),
-                share(a2, "refine", "SQ_ACTIVE_INST_VALU"), share(a2, "refine", "SQ_ACTIVE_INST_LDS"),
-                share(a2, "refine", "SQ_WAIT_ANY"))]
+                "2.4 GHz):", ""]
+    if "assign" in keys:
+        valu = per_weight(a1, "assign", "SQ_INSTS_VALU")
+        out.append("- assign: %.1f VALU and %.1f LDS instructions per weight. VALU alone needs "
+                   "%.0f us at full issue; SQ_WAIT_INST_LDS takes %.0f %% of wave time." % (
+                       valu, per_weight(a1, "assign", "SQ_INSTS_LDS"),
+                       N * valu / 64 / 256 / 2.4e9 * 1e6, share(a2, "assign", "SQ_WAIT_INST_LDS")))
+    if "refine" in keys:
+        out.append("- refine: %.1f VALU and %.2f LDS instructions (the two fp64 adds) per weight, "
+                   "one workgroup of four waves per CU (128 KB of bins). Per wave: VALU busy "
+                   "%.0f %%, LDS issue %.0f %%, waiting %.0f %% of its cycles." % (
+                       per_weight(a1, "refine", "SQ_INSTS_VALU"),
+                       per_weight(a1, "refine", "SQ_INSTS_LDS"),
+                       share(a2, "refine", "SQ_ACTIVE_INST_VALU"),
+                       share(a2, "refine", "SQ_ACTIVE_INST_LDS"), share(a2, "refine", "SQ_WAIT_ANY")))
+    if "fused" in keys:
+        valu = per_weight(a1, "fused", "SQ_INSTS_VALU")
+        out.append("- fused: %.1f VALU and %.2f LDS instructions (two lookups and two fp64 adds) "
+                   "per weight, one workgroup of four waves per CU (the bins). VALU alone needs "
+                   "%.0f us at full issue. Per wave: VALU busy %.0f %%, LDS issue %.0f %%, "
+                   "waiting %.0f %% of its cycles." % (
+                       valu, per_weight(a1, "fused", "SQ_INSTS_LDS"),
+                       N * valu / 64 / 256 / 2.4e9 * 1e6,
+                       share(a2, "fused", "SQ_ACTIVE_INST_VALU"),
+                       share(a2, "fused", "SQ_ACTIVE_INST_LDS"), share(a2, "fused", "SQ_WAIT_ANY")))
     with open(out_md, "w") as f:
         f.write("\n".join(out) + "\n")
 

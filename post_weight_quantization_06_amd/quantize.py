@@ -156,12 +156,15 @@ class Probe:
 
 def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerBuffers,
              wsp: Workspaces, init: bool = True, pack: bool = True,
-             probe: Optional[Probe] = None, totals: bool = True) -> LayerBuffers:
+             probe: Optional[Probe] = None, totals: bool = True,
+             fused: bool = False) -> LayerBuffers:
     """Enqueue the quantization of matrices Ws (bf16 [R_i, C_i]) with importances Is (fp32 [C_i])
     into buf: batched init (unless init is False: then buf.tables hold the starting tables),
     buf.iters x (batched assign, batched refine; the last refine rounds the tables to bf16), the
     final assign, and pack. With totals, every refine reports the error of the assignment it
-    consumes and the final assign its own (buf.err), and the first refine sums buf.w2."""
+    consumes and the final assign its own (buf.err), and the first refine sums buf.w2. With fused,
+    each iteration is one aaac_assign_refine_batch call instead of the two (bitwise the same
+    results; the probe's assign interval then covers the whole call)."""
     g, S, n, iters = buf.g, buf.S, buf.n, buf.iters
     if iters < 1:
         raise ValueError("iters must be >= 1 (the last refine rounds the tables to bf16)")
@@ -180,18 +183,30 @@ def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerB
     pr.loop_begin()
     for it in range(iters):
         flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
+        if totals and it > 0:
+            flags |= L.REFINE_W2_KNOWN
         pr.before_assign(it)
-        for b in sl:
-            L.aaac_assign_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b], buf.sels[b])
-        pr.before_refine(it)
-        for b in sl:
-            ws_r = wsp.get(("refine", b.start), L.batch_workspace_bytes(
-                L.OP_REFINE, Rs[b], Cs[b], g, S, n))
-            if totals and it > 0:
-                flags |= L.REFINE_W2_KNOWN
-            L.aaac_refine_batch(Ws[b], g, S, n, Is[b], buf.codes[b], buf.sels[b], buf.tables[b],
-                                flags, ws_r, buf.err[it, b] if totals else None,
-                                buf.w2[b] if totals else None)
+        if fused:
+            for b in sl:
+                ws_r = wsp.get(("refine", b.start), L.batch_workspace_bytes(
+                    L.OP_REFINE, Rs[b], Cs[b], g, S, n))
+                L.aaac_assign_refine_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b],
+                                           buf.sels[b], flags, ws_r,
+                                           buf.err[it, b] if totals else None,
+                                           buf.w2[b] if totals else None)
+            pr.before_refine(it)
+        else:
+            for b in sl:
+                L.aaac_assign_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b],
+                                    buf.sels[b])
+            pr.before_refine(it)
+            for b in sl:
+                ws_r = wsp.get(("refine", b.start), L.batch_workspace_bytes(
+                    L.OP_REFINE, Rs[b], Cs[b], g, S, n))
+                L.aaac_refine_batch(Ws[b], g, S, n, Is[b], buf.codes[b], buf.sels[b],
+                                    buf.tables[b], flags, ws_r,
+                                    buf.err[it, b] if totals else None,
+                                    buf.w2[b] if totals else None)
         pr.after_refine(it)
     pr.loop_end()
     for b in sl:

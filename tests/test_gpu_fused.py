@@ -132,3 +132,26 @@ def test_fused_full_size_llama8b_layer():
     _say("fused full size", cfg.name)
     _run_both(shapes, cfg.g, cfg.S, cfg.n, iters=cfg.iters, seed=2)
 
+
+
+@pytest.mark.parametrize("g,S,n", [(128, 128, 16), (128, 16, 16)])
+def test_run_loop_fused_equals_two_launch_loop(g, S, n):
+    """quantize.run_loop with one fused launch per iteration: every output and the error history
+    bitwise those of the two-launch loop."""
+    shapes = [(37, 1152), (16, 4096), (300, 2048)]
+    shapes = [(R, C) for R, C in shapes if C % g == 0]
+    _say("run_loop fused", g, S, n, shapes)
+    Ws, Is, _ = _setup(shapes, g, S, n, 9)
+    out = []
+    for fused in (False, True):
+        buf = P.LayerBuffers(shapes, g, S, n, 6, DEV)
+        P.run_loop(Ws, Is, buf, P.Workspaces(DEV), fused=fused)
+        torch.cuda.synchronize()
+        out.append(buf)
+    a, b = out
+    for i in range(len(shapes)):
+        assert torch.equal(a.codes[i], b.codes[i]) and torch.equal(a.sels[i], b.sels[i])
+        assert torch.equal(a.tables[i], b.tables[i]) and torch.equal(a.scales[i], b.scales[i])
+        assert torch.equal(a.tables_bf16[i], b.tables_bf16[i])
+    assert torch.equal(a.err, b.err) and torch.equal(a.w2, b.w2)
+    P.check_history(b.err, w2=b.w2)

@@ -80,3 +80,41 @@ def test_workloads_match_the_registry():
     assert cfg_id == 5 and layers == 64 and len(shapes) == 7
     assert sum(R * C for R, C in shapes) == 487587840
     assert x_bytes == 4 * 524288 * (3 * 5120 + 27648)
+
+
+def test_fused_workload_summaries(tmp_path):
+    tag = "32b_model_fused"
+    n32 = 487587840
+    alg32 = n32 * 2 + n32 // 2 + n32 // 128
+    raw = tmp_path / "raw"
+    stats_hdr = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs",
+                 "StdDev"]
+    _write_csv(str(raw / ("prof_" + tag) / "run_kernel_stats.csv"), stats_hdr, [
+        ["void aaac::assign_refine_kernel<8, 8, false>(aaac::RefineBatch)", 1728, 1728 * 800000,
+         800000, 50, 790000, 810000, 1],
+        ["void aaac::assign_refine_kernel<8, 8, true>(aaac::RefineBatch)", 192, 192 * 800000,
+         800000, 5, 790000, 810000, 1],
+        ["void aaac::assign_wide_kernel<1, 8, 8>(aaac::AssignBatch)", 192, 192 * 400000,
+         400000, 5, 399000, 401000, 1],
+    ])
+    pmc_hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    name = "void aaac::assign_refine_kernel<8, 8, false>"
+    _write_csv(str(raw / ("pmc_sq_" + tag) / "run_counter_collection.csv"), pmc_hdr,
+               [[name, "SQ_INSTS_VALU", n32 // 64 * 34], [name, "SQ_INSTS_LDS", n32 // 64 * 4],
+                [name, "SQ_WAVE_CYCLES", 1000.0]])
+    _write_csv(str(raw / ("pmc_sq2_" + tag) / "run_counter_collection.csv"), pmc_hdr,
+               [[name, "SQ_ACTIVE_INST_VALU", 560.0], [name, "SQ_ACTIVE_INST_LDS", 130.0],
+                [name, "SQ_WAIT_ANY", 250.0]])
+    prof = tmp_path / "prof"
+    prof.mkdir()
+    assert ps.main(["prof_summary", str(raw), str(prof), tag]) == 0
+    stats = (prof / ("kernel_stats_%s.md" % tag)).read_text()
+    # every instance of the fused kernel, no assign or refine lines
+    assert "- fused (1920 launches, every instance): 800.0 us average -> %.0f GB/s" % (
+        alg32 / 800e-6 / 1e9) in stats
+    assert "- assign (" not in stats and "- refine (" not in stats
+    assert "--config 5 --fused --steps 2" in stats
+    sq = (prof / ("sq_counters_assign_refine_%s.md" % tag)).read_text()
+    assert "- fused: 34.0 VALU and 4.00 LDS" in sq
+    assert "VALU busy 56 %, LDS issue 13 %, waiting 25 %" in sq
+    assert not (prof / ("hbm_traffic_assign_refine_%s.md" % tag)).exists()
