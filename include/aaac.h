@@ -152,15 +152,22 @@ aaac_status aaac_refine(const uint16_t* W, int64_t R, int64_t C, int g, int S, i
 
 /*
  * Pack, AAAC summary §2 mechanism 3 and §4: the stored format.
- *   scales  [R * C / g] bf16 bit patterns of s = max |w| over each scale group; when S == g the
- *           sign bit holds the selector (1 = T1), when S < g it is 0.
- *   bitmap  S < g: [ceil(R * C / S / 8)] bytes, bit i (byte i >> 3, bit i & 7) = selector of the
- *           i-th selection group in row-major order (1 / S extra bits per weight). S == g: NULL.
+ *   codes_u8  NULL, or codes given one per byte: u8 [R * C], the code of (r, c) in the low nibble
+ *             of byte r * C + c (the high nibble is ignored). Then codes_out (u8 [R * C / 2], not
+ *             NULL, 4-byte aligned; codes_u8 8-byte aligned) receives them two per byte, the even
+ *             column in the low nibble: the layout aaac_assign writes and aaac_dequant reads. Codes
+ *             from aaac_assign are already in that layout and need neither (both NULL).
+ *   scales    [R * C / g] bf16 bit patterns of s = max |w| over each scale group; when S == g the
+ *             sign bit holds the selector (1 = T1), when S < g it is 0.
+ *   bitmap    S < g: [ceil(R * C / S / 8)] bytes, bit i (byte i >> 3, bit i & 7) = selector of the
+ *             i-th selection group in row-major order (1 / S extra bits per weight). S == g: NULL.
  *   tables_bf16 [2][n] bf16 bit patterns of the tables (ties to even).
- * codes are already packed by aaac_assign and are not touched.
+ * Errors: AAAC_ERR_INVALID_ARG for codes_u8 without codes_out (or the reverse) or a misaligned
+ * pointer; shape errors as for aaac_assign.
  */
 aaac_status aaac_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
-                      const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
+                      const uint8_t* sel, const float* tables, const uint8_t* codes_u8,
+                      uint8_t* codes_out, uint16_t* scales, uint8_t* bitmap,
                       uint16_t* tables_bf16, void* stream);
 
 /*

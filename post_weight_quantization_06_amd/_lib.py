@@ -76,7 +76,7 @@ def load(path: str = LIB_PATH):
         "aaac_refine": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
                                 c_vp, c_int, c_vp, c_vp, c_vp, c_size, c_vp]),
         "aaac_pack": (c_int, [c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp, c_vp, c_vp, c_vp,
-                              c_vp, c_vp]),
+                              c_vp, c_vp, c_vp, c_vp]),
         "aaac_dequant": (c_int, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_int, c_int, c_int, c_vp,
                                  c_vp]),
         "aaac_init_quantiles_batch": (c_int, [c_int, P(c_vp), P(c_i64), P(c_i64), c_int, c_int,
@@ -253,7 +253,10 @@ def aaac_refine(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, codes:
 
 def aaac_pack(W: torch.Tensor, g: int, S: int, n: int, sel: torch.Tensor, tables: torch.Tensor,
               scales: torch.Tensor, bitmap: Optional[torch.Tensor], tables_bf16: torch.Tensor,
+              codes_u8: Optional[torch.Tensor] = None, codes_out: Optional[torch.Tensor] = None,
               stream=None):
+    """codes_u8 (u8 [R*C], one code per byte) and codes_out (u8 [R*C/2]): pack codes given one per
+    byte into the two-per-byte layout, or both None."""
     lib = load()
     R, C = W.shape
     _need(W, "W", torch.bfloat16)
@@ -263,8 +266,13 @@ def aaac_pack(W: torch.Tensor, g: int, S: int, n: int, sel: torch.Tensor, tables
     _need(tables_bf16, "tables_bf16", torch.int16, 2 * n)
     if bitmap is not None:
         _need(bitmap, "bitmap", torch.uint8, (R * C // S + 7) // 8)
-    st = lib.aaac_pack(_ptr(W), R, C, g, S, n, _ptr(sel), _ptr(tables), _ptr(scales),
-                       _ptr(bitmap), _ptr(tables_bf16), _stream(stream))
+    if codes_u8 is not None:
+        _need(codes_u8, "codes_u8", torch.uint8, R * C)
+    if codes_out is not None:
+        _need(codes_out, "codes_out", torch.uint8, R * C // 2)
+    st = lib.aaac_pack(_ptr(W), R, C, g, S, n, _ptr(sel), _ptr(tables), _ptr(codes_u8),
+                       _ptr(codes_out), _ptr(scales), _ptr(bitmap), _ptr(tables_bf16),
+                       _stream(stream))
     _check(st, "aaac_pack")
 
 

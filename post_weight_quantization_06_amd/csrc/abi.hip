@@ -570,11 +570,21 @@ aaac_status aaac_refine_batch_noalloc(int count, const uint16_t* const* W, const
 }
 
 aaac_status aaac_pack(const uint16_t* W, int64_t R, int64_t C, int g, int S, int n,
-                      const uint8_t* sel, const float* tables, uint16_t* scales, uint8_t* bitmap,
+                      const uint8_t* sel, const float* tables, const uint8_t* codes_u8,
+                      uint8_t* codes_out, uint16_t* scales, uint8_t* bitmap,
                       uint16_t* tables_bf16, void* stream) {
+  const char* who = "aaac_pack";
+  if ((codes_u8 != nullptr) != (codes_out != nullptr))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: codes_u8 and codes_out must be given together", who);
+  if (codes_u8 && (!aligned(codes_u8, 8) || !aligned(codes_out, 4)))
+    return fail(AAAC_ERR_INVALID_ARG, "%s: codes_u8 needs 8-byte and codes_out 4-byte alignment",
+                who);
   uint8_t* const bm[1] = {bitmap};
-  return do_pack(1, &W, &R, &C, g, S, n, &sel, &tables, &scales, bm, &tables_bf16, stream,
-                 "aaac_pack");
+  aaac_status st = do_pack(1, &W, &R, &C, g, S, n, &sel, &tables, &scales, bm, &tables_bf16,
+                           stream, who);
+  if (st != AAAC_OK || !codes_u8) return st;
+  return hip_status(launch_pack_codes(codes_u8, codes_out, R, C, static_cast<hipStream_t>(stream)),
+                    who);
 }
 
 aaac_status aaac_pack_batch(int count, const uint16_t* const* W, const int64_t* R,

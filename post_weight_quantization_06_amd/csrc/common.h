@@ -331,6 +331,9 @@ hipError_t launch_pack(int count, const uint16_t* const* W, const int64_t* R, co
                        int g, int S, int n, const uint8_t* const* sel, const float* const* tables,
                        uint16_t* const* scales, uint8_t* const* bitmap,
                        uint16_t* const* tables_bf16, hipStream_t stream);
+// Codes one per byte ([R * C], low nibble) into two per byte ([R * C / 2]).
+hipError_t launch_pack_codes(const uint8_t* codes_u8, uint8_t* codes_out, int64_t R, int64_t C,
+                             hipStream_t stream);
 hipError_t launch_dequant(int count, const uint8_t* const* codes, const uint16_t* const* scales,
                           const uint8_t* const* bitmap, const uint16_t* const* tables_bf16,
                           const int64_t* R, const int64_t* C, int g, int S, int n,

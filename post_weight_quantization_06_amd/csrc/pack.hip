@@ -244,6 +244,35 @@ hipError_t launch_pack(int count, const uint16_t* const* W, const int64_t* R, co
   return hipGetLastError();
 }
 
+// Codes given one per byte (low nibble; the high nibble is ignored) packed two per byte, the even
+// column in the low nibble: 8 codes in, one 32-bit word out per thread.
+__global__ __launch_bounds__(kBlock) void pack_codes_kernel(const uint2* __restrict__ in,
+                                                            uint32_t* __restrict__ out,
+                                                            int64_t items) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items; i += stride) {
+    const uint2 v = in[i];
+    // bytes b0..b3 of v.x hold codes 0..3; keep each low nibble and pair them
+    const uint32_t x = v.x & 0x0F0F0F0Fu, y = v.y & 0x0F0F0F0Fu;
+    const uint32_t px = (x | (x >> 4)) & 0x00FF00FFu;    // bytes 0 and 2: codes 0|1, 2|3
+    const uint32_t py = (y | (y >> 4)) & 0x00FF00FFu;
+    out[i] = __builtin_amdgcn_perm(py, px, 0x06040200u);
+  }
+}
+
+hipError_t launch_pack_codes(const uint8_t* codes_u8, uint8_t* codes_out, int64_t R, int64_t C,
+                             hipStream_t stream) {
+  const int64_t items = R * C / 8;
+  if (items <= 0) return hipSuccess;
+  const int64_t cap = (int64_t)device_cu_count() * 8;
+  int64_t grid = (items + kBlock - 1) / kBlock;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)grid), dim3(kBlock), 0, stream,
+                     reinterpret_cast<const uint2*>(codes_u8),
+                     reinterpret_cast<uint32_t*>(codes_out), items);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(int count, const uint8_t* const* codes, const uint16_t* const* scales,
                           const uint8_t* const* bitmap, const uint16_t* const* tables_bf16,
                           const int64_t* R, const int64_t* C, int g, int S, int n,

@@ -144,10 +144,18 @@ def test_refine_rejects_small_workspace_and_unknown_flags(lib):
 
 def test_pack_and_dequant_bitmap_rule(lib):
     # S == g forbids a bitmap, S < g requires one
-    assert lib.aaac_pack(FAKE, i64(64), i64(1024), 128, 128, 16, FAKE, FAKE, FAKE, FAKE, FAKE,
-                         None) == INVALID
-    assert lib.aaac_pack(FAKE, i64(64), i64(1024), 128, 16, 16, FAKE, FAKE, FAKE, None, FAKE,
-                         None) == INVALID
+    assert lib.aaac_pack(FAKE, i64(64), i64(1024), 128, 128, 16, FAKE, FAKE, None, None, FAKE,
+                         FAKE, FAKE, None) == INVALID
+    assert lib.aaac_pack(FAKE, i64(64), i64(1024), 128, 16, 16, FAKE, FAKE, None, None, FAKE,
+                         None, FAKE, None) == INVALID
+    # codes one per byte: codes_u8 and codes_out together, aligned
+    assert lib.aaac_pack(FAKE, i64(64), i64(1024), 128, 128, 16, FAKE, FAKE, FAKE, None, FAKE,
+                         None, FAKE, None) == INVALID
+    assert lib.aaac_pack(FAKE, i64(64), i64(1024), 128, 128, 16, FAKE, FAKE, None, FAKE, FAKE,
+                         None, FAKE, None) == INVALID
+    assert lib.aaac_pack(FAKE, i64(64), i64(1024), 128, 128, 16, FAKE, FAKE,
+                         ctypes.c_void_p((1 << 20) + 4), FAKE, FAKE, None, FAKE, None) == INVALID
+    assert b"codes_u8" in lib.aaac_last_error()
     assert lib.aaac_dequant(FAKE, FAKE, FAKE, FAKE, i64(64), i64(1024), 128, 128, 16, FAKE,
                             None) == INVALID
     assert lib.aaac_dequant(FAKE, FAKE, None, FAKE, i64(64), i64(1024), 128, 16, 16, FAKE,

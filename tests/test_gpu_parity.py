@@ -562,6 +562,39 @@ def test_pack_and_dequant_bit_exact(R, C, g, S, n):
         assert np.all(np.abs(_np(y).astype(np.float64) - y_ref) <= bound)
 
 
+@pytest.mark.parametrize("R,C,g,S", [(1, 8, 8, 8), (3, 24, 8, 8), (37, 1152, 128, 128),
+                                     (64, 1024, 128, 16)])
+def test_pack_codes_given_one_per_byte(R, C, g, S):
+    """aaac_pack with codes one per byte: packed two per byte exactly as the oracle's pack (the high
+    nibble of each input byte ignored), and the scales, bitmap and tables as without them."""
+    _say("pack codes_u8", R, C, g, S)
+    n = 16
+    W = _weight(R, C, 4100 + C)
+    gen = torch.Generator(device=DEV).manual_seed(R * 7 + C)
+    q8 = torch.randint(0, 256, (R * C,), dtype=torch.uint8, device=DEV, generator=gen)
+    sel = torch.randint(0, 2, (R * C // S,), dtype=torch.uint8, device=DEV, generator=gen)
+    tabs = torch.linspace(-1.0, 1.0, 2 * n, device=DEV).to(torch.bfloat16).float()
+    out = [torch.full((R * C // 2,), 0xAB, dtype=torch.uint8, device=DEV)]
+    res = []
+    for codes_u8, codes_out in ((q8, out[0]), (None, None)):
+        scales = torch.empty(R * C // g, dtype=torch.int16, device=DEV)
+        bitmap = (torch.empty((R * C // S + 7) // 8, dtype=torch.uint8, device=DEV)
+                  if S < g else None)
+        tb = torch.empty(2 * n, dtype=torch.int16, device=DEV)
+        L.aaac_pack(W, g, S, n, sel, tabs, scales, bitmap, tb, codes_u8=codes_u8,
+                    codes_out=codes_out)
+        res.append((scales, bitmap, tb))
+    torch.cuda.synchronize()
+    codes = (_np(q8).astype(np.int64) & 15).reshape(R, C)
+    T = _np(tabs).astype(np.float64).reshape(2, n)
+    p = ref.pack(par.to_np64(W), codes, _np(sel).reshape(R, C // S), (T[0], T[1]), g, S)
+    assert np.array_equal(_np(out[0]).reshape(R, C // 2), p["codes"])
+    (s1, b1, t1), (s2, b2, t2) = res
+    assert torch.equal(s1, s2) and torch.equal(t1, t2)
+    assert (b1 is None and b2 is None) or torch.equal(b1, b2)
+    assert np.array_equal(_np(s1).view(np.uint16).reshape(p["scales"].shape), p["scales"])
+
+
 def test_pack_and_dequant_batches_equal_single_calls():
     """One batched pack and one batched dequant over matrices of several shapes give the single
     calls' outputs bit for bit: selector in the scale sign bit, separate bitmaps, NVFP4-style
