@@ -134,12 +134,14 @@ aaac_status aaac_assign(const uint16_t* W, int64_t R, int64_t C, int g, int S, i
  * flags        0, or AAAC_REFINE_ROUND_BF16 (round the new entries to bf16; used on the last
  *              iteration so that the final assign runs against the stored tables) and/or
  *              AAAC_REFINE_W2_KNOWN (see w2; needs err).
- * err          NULL, or one fp64 receiving the total weighted error of the incoming assignment
- *              (the codes and selectors under tables_in: the quantity aaac_assign's err_total
- *              reports), formed from the cell sums as E = W2 - 2 sum_cells T num +
- *              sum_cells T^2 den with W2 = sum I_k w_k^2 (sums of exact fp64 terms). Its absolute
- *              accuracy is about 1e-15 W2, far below E except for matrices quantized almost
- *              exactly (aaac_assign's err_total has no such limit).
+ * err          NULL, or two fp64: err[0] receives the total weighted error of the incoming
+ *              assignment under tables_in (the codes and selectors as the assign half-step left
+ *              them: the quantity aaac_assign's err_total reports), err[1] the same assignment's
+ *              error under the tables this call writes (after this half-step; after the bf16
+ *              rounding when that flag is set). Both are formed from the cell sums as
+ *              E = W2 - 2 sum_cells T num + sum_cells T^2 den with W2 = sum I_k w_k^2 (sums of
+ *              exact fp64 terms). Their absolute accuracy is about 1e-15 W2, far below E except
+ *              for matrices quantized almost exactly (aaac_assign's err_total has no such limit).
  * w2           with err: one fp64. Without AAAC_REFINE_W2_KNOWN the kernel sums W2 (one more fp64
  *              fma per weight) and writes it here; with the flag it reads W2 from here (the value
  *              an earlier call on the same W and I wrote), at no cost per weight. NULL without err.
@@ -254,7 +256,8 @@ aaac_status aaac_awq_prescale(const uint16_t* W, int64_t R, int64_t C, const flo
  * aaac_batch_workspace_bytes(AAAC_OP_REFINE, count, R, C, g, S, n) bytes, same zero-fill rule as
  * above. assign: err_total is NULL or fp64 [count] (the total of matrix i in err_total[i]), with
  * a workspace of aaac_batch_workspace_bytes(AAAC_OP_ASSIGN, count, R, C, g, S, n) bytes.
- * refine: err and w2 are NULL or fp64 [count] each (matrix i's at index i, as in aaac_refine).
+ * refine: err is NULL or fp64 [2][count] (matrix i's error before the update at err[i], after it
+ * at err[count + i]), w2 NULL or fp64 [count] (matrix i's at index i); as in aaac_refine.
  */
 #define AAAC_MAX_BATCH 8
 
@@ -308,7 +311,8 @@ aaac_status aaac_refine_batch_noalloc(int count, const uint16_t* const* W, const
  * One iteration of the alternation (AAAC summary §2 mechanism 4) in one launch: the batched assign
  * against tables[i], writing codes[i] and sel[i], then the batched refine from those codes,
  * updating tables[i] in place. flags, err and w2 are as for aaac_refine_batch: err[i] receives the
- * weighted error of the assignment this call makes, under the tables it was made with. Codes,
+ * weighted error of the assignment this call makes under the tables it was made with, and
+ * err[count + i] under the tables it writes. Codes,
  * selectors, tables and errors are bitwise those of aaac_assign_batch followed by
  * aaac_refine_batch with the same arguments. With S >= 16 one kernel does both: each wave assigns
  * a row and adds its terms into the refine bins at once, so W is read once. With S = 8 the call

@@ -229,8 +229,8 @@ def aaac_refine(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, codes:
                 sel: torch.Tensor, tables_in: torch.Tensor, tables_out: torch.Tensor,
                 flags: int = 0, ws: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
                 w2: Optional[torch.Tensor] = None, stream=None):
-    """err: fp64 [1] receiving the error of the incoming assignment, with w2 fp64 [1] (sum I w^2:
-    written, or read with REFINE_W2_KNOWN), or both None."""
+    """err: fp64 [2] receiving the assignment's error before and after the update, with w2 fp64
+    [1] (sum I w^2: written, or read with REFINE_W2_KNOWN), or both None."""
     lib = load()
     R, C = W.shape
     _need(W, "W", torch.bfloat16)
@@ -240,7 +240,7 @@ def aaac_refine(W: torch.Tensor, g: int, S: int, n: int, I: torch.Tensor, codes:
     _need(tables_in, "tables_in", torch.float32, 2 * n)
     _need(tables_out, "tables_out", torch.float32, 2 * n)
     if err is not None:
-        _need(err, "err", torch.float64, 1)
+        _need(err, "err", torch.float64, 2)
     if w2 is not None:
         _need(w2, "w2", torch.float64, 1)
     if ws is None:
@@ -401,8 +401,9 @@ def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
                       flags: int = 0, ws: Optional[torch.Tensor] = None,
                       err: Optional[torch.Tensor] = None, w2: Optional[torch.Tensor] = None,
                       stream=None):
-    """err, w2: fp64 [len(Ws)] each (the incoming assignment's error per matrix, and sum I w^2 per
-    matrix: written, or read with REFINE_W2_KNOWN), or both None."""
+    """err: fp64 [2, len(Ws)] (row 0: each matrix's assignment error before the update, row 1:
+    after it) and w2: fp64 [len(Ws)] (sum I w^2 per matrix: written, or read with
+    REFINE_W2_KNOWN), or both None."""
     lib = load()
     k = len(Ws)
     Rs = [W.shape[0] for W in Ws]
@@ -414,7 +415,7 @@ def aaac_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
         _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
     if err is not None:
-        _need(err, "err", torch.float64, k)
+        _need(err, "err", torch.float64, 2 * k)
     if w2 is not None:
         _need(w2, "w2", torch.float64, k)
     if ws is None:
@@ -433,8 +434,8 @@ def aaac_assign_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
                              flags: int = 0, ws: Optional[torch.Tensor] = None,
                              err: Optional[torch.Tensor] = None, w2: Optional[torch.Tensor] = None,
                              stream=None):
-    """One assign + refine iteration in one launch (tables updated in place); flags, err and w2 as
-    for aaac_refine_batch."""
+    """One assign + refine iteration in one launch (tables updated in place); flags, err (fp64
+    [2, len(Ws)]) and w2 as for aaac_refine_batch."""
     lib = load()
     k = len(Ws)
     Rs = [W.shape[0] for W in Ws]
@@ -446,7 +447,7 @@ def aaac_assign_refine_batch(Ws: Sequence[torch.Tensor], g: int, S: int, n: int,
         _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
         _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
     if err is not None:
-        _need(err, "err", torch.float64, k)
+        _need(err, "err", torch.float64, 2 * k)
     if w2 is not None:
         _need(w2, "w2", torch.float64, k)
     if ws is None:
@@ -538,7 +539,7 @@ def aaac_refine_batch_noalloc(Ws: Sequence[torch.Tensor], g: int, S: int, n: int
         _need(codes[i], "codes[%d]" % i, torch.uint8, Rs[i] * Cs[i] // 2)
         _need(sels[i], "sel[%d]" % i, torch.uint8, Rs[i] * Cs[i] // S)
     if err is not None:
-        _need(err, "err", torch.float64, k)
+        _need(err, "err", torch.float64, 2 * k)
     if w2 is not None:
         _need(w2, "w2", torch.float64, k)
     st = lib.aaac_refine_batch_noalloc(

@@ -295,6 +295,7 @@ aaac_status do_refine(int count, const uint16_t* const* W, const int64_t* R, con
     j.tables_in = tin[i];
     j.tables_out = tout[i];
     j.err_out = err ? err + i : nullptr;
+    j.err_after = err ? err + count + i : nullptr;
     j.w2 = err ? w2 + i : nullptr;
   }
   return hip_status(launch_refine(b, static_cast<hipStream_t>(stream)), who);
@@ -655,6 +656,7 @@ aaac_status aaac_assign_refine_batch(int count, const uint16_t* const* W, const 
     j.tables_in = tables[i];
     j.tables_out = tables[i];
     j.err_out = err ? err + i : nullptr;
+    j.err_after = err ? err + count + i : nullptr;
     j.w2 = err ? w2 + i : nullptr;
   }
   return hip_status(launch_assign_refine(b, static_cast<hipStream_t>(stream)), who);

@@ -280,7 +280,8 @@ struct RefineJob {
   float* tables_out;
   uint32_t* codes_out;      // fused assign + accumulate only: where the assign step writes
   uint8_t* sel_out;
-  double* err_out;          // nullable: error of the incoming assignment
+  double* err_out;          // nullable: error of the incoming assignment under tables_in
+  double* err_after;        // with err_out: the same assignment's error under tables_out
   double* w2;               // with err_out: sum I w^2 (output, or input with the W2-known flag)
   int32_t wg_lo;            // first workgroup whose task range meets this job
   int32_t wg_count;         // number of such workgroups

@@ -15,12 +15,14 @@
 // The bins take 128 KB, one workgroup per CU; to keep enough bytes in flight each wave loads the
 // rows of its next task before it accumulates the current one.
 //
-// Error of the incoming assignment (optional). With the cell sums, the total weighted error of the
-// codes and selectors under the tables they were chosen with is
+// Errors of the assignment (optional). With the cell sums, the total weighted error of the codes
+// and selectors under any tables T is
 //   E = sum I (w - s T_c[q])^2 = W2 - 2 sum_cells T num + sum_cells T^2 den,   W2 = sum I w^2,
-// formed by the last workgroup of the matrix before it writes the new tables. W2 depends only on
-// W and I: the caller either has it from an earlier call (then it costs nothing), or every thread
-// sums I w^2 over its weights in a register (exact fp64 terms), one more fp64 fma per weight.
+// formed by the last workgroup of the matrix twice: with the tables the codes were chosen with
+// (the error after the assign half-step) and with the tables it writes (after this half-step).
+// W2 depends only on W and I: the caller either has it from an earlier call (then it costs
+// nothing), or every thread sums I w^2 over its weights in a register (exact fp64 terms), one more
+// fp64 fma per weight.
 #include <type_traits>
 
 #include "common.h"
@@ -381,30 +383,40 @@ __device__ void finish_job(const RefineBatch& b, int j, RefineShared& sh, Part p
     w2s[q] = s;
   }
   pt.sync();
-  __shared__ double eterm[kCells];
+  __shared__ double eterm[2][kCells];
   if (tid < kCells) {
     const int c = tid >> 4, idx = tid & 15;
     const int vn = 2 * tid, vd = 2 * tid + 1;
     const double nsum = ((part4[0][vn] + part4[1][vn]) + part4[2][vn]) + part4[3][vn];
     const double dsum = ((part4[0][vd] + part4[1][vd]) + part4[2][vd]) + part4[3][vd];
-    double et = 0.0;
+    double et = 0.0, en = 0.0;
     if (idx < b.n) {
       const float old = jb.tables_in[c * b.n + idx];
       const double val = dsum > 0.0 ? nsum / dsum : (double)old;
-      // this cell's part of the incoming error: T^2 den - 2 T num with the old entry T
-      const double T = (double)old;
+      const float nv = (b.flags & 1) ? f64_to_bf16_value(val) : (float)val;
+      jb.tables_out[c * b.n + idx] = nv;
+      // this cell's part of the assignment's error, T^2 den - 2 T num, with the old entry and
+      // with the entry just written
+      const double T = (double)old, Tn = (double)nv;
       et = T * (T * dsum - 2.0 * nsum);
-      jb.tables_out[c * b.n + idx] = (b.flags & 1) ? f64_to_bf16_value(val) : (float)val;
+      en = Tn * (Tn * dsum - 2.0 * nsum);
     }
-    if (b.errs) eterm[tid] = et;
+    if (b.errs) {
+      eterm[0][tid] = et;
+      eterm[1][tid] = en;
+    }
   }
   if (b.errs) {
     pt.sync();
     if (tid == 0 && jb.err_out) {
       const double W2 = ERRS ? ((w2s[0] + w2s[1]) + w2s[2]) + w2s[3] : *jb.w2;
-      double x = 0.0;
-      for (int k = 0; k < kCells; ++k) x += eterm[k];
+      double x = 0.0, y = 0.0;
+      for (int k = 0; k < kCells; ++k) {
+        x += eterm[0][k];
+        y += eterm[1][k];
+      }
       jb.err_out[0] = W2 + x;
+      jb.err_after[0] = W2 + y;
       if (ERRS) *jb.w2 = W2;
     }
   }

@@ -6,11 +6,14 @@ activations).
 Control flow only: every step is one library call enqueued on the current stream; the host does not
 synchronize inside the loop. Device buffers come from torch.
 
-The total weighted error of every assignment is kept on the device in a history
-[iters + 1, matrices]: row t is the error of iteration t's assignment, reported by the refine that
-consumes it (from its cell sums, at the cost of one register sum per thread), and the last row is
-the final assign's own err_total against the bf16 tables. The alternation is a k-means descent, so
-rows 0 .. iters-1 never increase; `check_history` verifies that after the loop (one host read).
+The total weighted error after every half-step is kept on the device in a history
+[2 iters + 1, matrices]: rows 2t and 2t + 1 are the error of iteration t's assignment under the
+tables it was chosen with and under the tables refine t wrote, both reported by that refine from
+its cell sums (W2 = sum I w^2 is one register sum per thread on the first refine), and the last row
+is the final assign's own err_total against the bf16 tables. The alternation is a descent (each
+half-step minimizes the error over its own variables), so the history never increases except
+across the last refine, whose entries are rounded to bf16; `check_history` verifies that after the
+loop (one host read).
 """
 
 from __future__ import annotations
@@ -40,7 +43,9 @@ class QuantizedMatrix:
     scales: torch.Tensor         # int16 [R, C/g] bf16 bits, sign bit = selector when S == g
     bitmap: Optional[torch.Tensor]  # uint8 [ceil(R C / S / 8)] when S < g
     tables_bf16: torch.Tensor    # int16 [2, n] bf16 bits
-    err_history: Optional[torch.Tensor] = None   # fp64 [iters + 1] total error per assign
+    # fp64 [2 iters + 1]: the total error after every half-step (assign 0, refine 0, assign 1, ...,
+    # refine iters-1 on bf16 tables, the final assign)
+    err_history: Optional[torch.Tensor] = None
 
     def dequant(self, out: Optional[torch.Tensor] = None) -> torch.Tensor:
         if out is None:
@@ -116,21 +121,31 @@ class LayerBuffers:
         self.bitmaps = ([torch.empty((R * C // S + 7) // 8, dtype=torch.uint8, device=dev)
                          for R, C in shapes] if S < g else None)
         self.tables_bf16 = [torch.empty(2 * n, dtype=torch.int16, device=dev) for _ in shapes]
-        # error history: err[t, i] = total error of iteration t's assignment of matrix i (rows
-        # 0 .. iters-1 from the refine that consumes it, the last row from the final assign);
-        # w2[i] = sum I w^2 of matrix i (summed by the first refine, read by the others)
-        self.err = torch.zeros(iters + 1, len(shapes), dtype=torch.float64, device=dev)
+        # error history, one tensor per batch of matrices (the calls write a batch's rows whole):
+        # row 2t = total error of iteration t's assignment under the tables it was chosen with,
+        # row 2t + 1 = the same assignment under the tables refine t wrote (both from refine t),
+        # row 2 iters = the final assign's; w2[i] = sum I w^2 of matrix i (summed by the first
+        # refine, read by the others)
+        self.batches = list(_batches(len(shapes)))
+        self.err_b = [torch.zeros(2 * iters + 1, b.stop - b.start, dtype=torch.float64,
+                                  device=dev) for b in self.batches]
         self.w2 = torch.zeros(len(shapes), dtype=torch.float64, device=dev)
+
+    @property
+    def err(self) -> torch.Tensor:
+        """fp64 [2 iters + 1, matrices]: the half-step error history of every matrix."""
+        return self.err_b[0] if len(self.err_b) == 1 else torch.cat(self.err_b, dim=1)
 
     def results(self) -> List[QuantizedMatrix]:
         out = []
+        err = self.err
         for i, (R, C) in enumerate(self.shapes):
             out.append(QuantizedMatrix(
                 R, C, self.g, self.S, self.n, self.codes[i].view(R, C // 2),
                 self.sels[i].view(R, C // self.S), self.tables[i].view(2, self.n),
                 self.scales[i].view(R, C // self.g),
                 self.bitmaps[i] if self.bitmaps is not None else None,
-                self.tables_bf16[i].view(2, self.n), self.err[:, i]))
+                self.tables_bf16[i].view(2, self.n), err[:, i]))
         return out
 
 
@@ -162,7 +177,8 @@ def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerB
     into buf: batched init (unless init is False: then buf.tables hold the starting tables),
     buf.iters x (batched assign, batched refine; the last refine rounds the tables to bf16), the
     final assign, and pack. With totals, every refine reports the error of the assignment it
-    consumes and the final assign its own (buf.err), and the first refine sums buf.w2. With fused,
+    consumes before and after its update and the final assign its own (buf.err: every half-step),
+    and the first refine sums buf.w2. With fused,
     each iteration is one aaac_assign_refine_batch call instead of the two (bitwise the same
     results; the probe's assign interval then covers the whole call)."""
     g, S, n, iters = buf.g, buf.S, buf.n, buf.iters
@@ -174,7 +190,7 @@ def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerB
     if [tuple(W.shape) for W in Ws] != buf.shapes:
         raise ValueError("matrix shapes do not match the buffers")
     pr = probe or Probe()
-    sl = list(_batches(k))
+    sl = buf.batches
     if init:
         for b in sl:
             need = L.batch_workspace_bytes(L.OP_INIT, Rs[b], Cs[b], g, 8, n)
@@ -187,12 +203,12 @@ def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerB
             flags |= L.REFINE_W2_KNOWN
         pr.before_assign(it)
         if fused:
-            for b in sl:
+            for bi, b in enumerate(sl):
                 ws_r = wsp.get(("refine", b.start), L.batch_workspace_bytes(
                     L.OP_REFINE, Rs[b], Cs[b], g, S, n))
                 L.aaac_assign_refine_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b],
                                            buf.sels[b], flags, ws_r,
-                                           buf.err[it, b] if totals else None,
+                                           buf.err_b[bi][2 * it:2 * it + 2] if totals else None,
                                            buf.w2[b] if totals else None)
             pr.before_refine(it)
         else:
@@ -200,21 +216,21 @@ def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerB
                 L.aaac_assign_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b],
                                     buf.sels[b])
             pr.before_refine(it)
-            for b in sl:
+            for bi, b in enumerate(sl):
                 ws_r = wsp.get(("refine", b.start), L.batch_workspace_bytes(
                     L.OP_REFINE, Rs[b], Cs[b], g, S, n))
                 L.aaac_refine_batch(Ws[b], g, S, n, Is[b], buf.codes[b], buf.sels[b],
                                     buf.tables[b], flags, ws_r,
-                                    buf.err[it, b] if totals else None,
+                                    buf.err_b[bi][2 * it:2 * it + 2] if totals else None,
                                     buf.w2[b] if totals else None)
         pr.after_refine(it)
     pr.loop_end()
-    for b in sl:
+    for bi, b in enumerate(sl):
         ws_a = (wsp.get(("assign", b.start), L.batch_workspace_bytes(L.OP_ASSIGN, Rs[b], Cs[b],
                                                                         g, S, n))
                 if totals else None)
         L.aaac_assign_batch(Ws[b], g, S, n, Is[b], buf.tables[b], buf.codes[b], buf.sels[b],
-                            buf.err[iters, b] if totals else None, ws_a)
+                            buf.err_b[bi][2 * iters] if totals else None, ws_a)
     if pack:
         for b in sl:
             L.aaac_pack_batch(Ws[b], g, S, n, buf.sels[b], buf.tables[b], buf.scales[b],
@@ -224,25 +240,32 @@ def run_loop(Ws: Sequence[torch.Tensor], Is: Sequence[torch.Tensor], buf: LayerB
 
 
 def check_history(err: torch.Tensor, rtol: float = MONOTONE_RTOL,
-                  w2: Optional[torch.Tensor] = None):
-    """Raise if the total error of some matrix increased from one iteration's assignment to the
-    next (rows 0 .. iters-1 of the history; the last row, against the bf16-rounded tables, is not
-    comparable). w2 (sum I w^2 per matrix, or None) widens the slack by the 1e-15 W2 accuracy of
-    the errors refine reports. Reads the history from the device (synchronizes)."""
+                  w2: Optional[torch.Tensor] = None, half_steps: bool = True):
+    """Raise if the total error of some matrix increased along its history. With half_steps, err is
+    the [2 iters + 1, matrices] history of run_loop (after every assign and every refine): every
+    step may only lower the error, except the last refine, whose entries are rounded to bf16 (the
+    final assign against them may then only lower it again). Without, err holds one row per
+    iteration's assignment and a last row against the bf16 tables, which is not compared. The
+    slack is rtol of the earlier value (the tie band of the decisions) plus, with w2 (sum I w^2 per
+    matrix), the 1e-15 W2 accuracy of the errors refine reports. Reads the history from the device
+    (synchronizes)."""
     h = err.detach().double().cpu()
     if h.dim() == 1:
         h = h[:, None]
-    body = h[:-1]
-    if body.shape[0] >= 2:
-        slack = body[:-1] * rtol
-        if w2 is not None:
-            slack = slack + 1e-13 * w2.detach().double().cpu().reshape(1, -1)
-        bad = body[1:] > body[:-1] + slack
+    rows = h.shape[0]
+    if half_steps:
+        steps = [r for r in range(rows - 1) if r != rows - 3]
+    else:
+        steps = list(range(rows - 2))
+    extra = 0.0 if w2 is None else 1e-13 * w2.detach().double().cpu().reshape(1, -1)
+    for r in steps:
+        slack = h[r:r + 1] * rtol + extra
+        bad = h[r + 1:r + 2] > h[r:r + 1] + slack
         if bool(bad.any()):
-            t, m = [int(x) for x in bad.nonzero()[0]]
-            raise RuntimeError("total error increased for matrix %d from iteration %d to %d: "
-                               "%.17g -> %.17g" % (m, t, t + 1, float(body[t, m]),
-                                                   float(body[t + 1, m])))
+            m = int(bad.nonzero()[0][1])
+            raise RuntimeError("total error increased for matrix %d from history row %d to %d: "
+                               "%.17g -> %.17g" % (m, r, r + 1, float(h[r, m]),
+                                                   float(h[r + 1, m])))
     return h
 
 

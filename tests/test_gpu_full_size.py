@@ -141,7 +141,7 @@ def _run_layer(cfg_id, layer, init_check, refine_check):
                 assert abs(got - want) <= 1e-6 * want, (mats[i].name, it, got, want)
                 e_want[i] = want
         # as the loop driver runs it: the first refine sums I w^2, the later ones read it
-        rerr = torch.zeros(len(mats), dtype=torch.float64, device=DEV)
+        rerr = torch.zeros(2, len(mats), dtype=torch.float64, device=DEV)
         if it == 0:
             w2 = torch.zeros(len(mats), dtype=torch.float64, device=DEV)
         L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, tabs,
@@ -150,7 +150,7 @@ def _run_layer(cfg_id, layer, init_check, refine_check):
             torch.cuda.synchronize()
             for i in refine_check:
                 # the refine reports the error of the assignment it consumed, and sum I w^2
-                e_r, w2_r = float(rerr[i].item()), float(w2[i].item())
+                e_r, w2_r = float(rerr[0, i].item()), float(w2[i].item())
                 w2_o = float(np.sum(Is64[i][None, :] * W64s[i] ** 2))
                 assert abs(w2_r - w2_o) <= 1e-12 * w2_o, (mats[i].name, w2_r, w2_o)
                 assert abs(e_r - e_want[i]) <= 1e-6 * e_want[i] + 1e-13 * w2_o, (
@@ -165,13 +165,19 @@ def _run_layer(cfg_id, layer, init_check, refine_check):
                     par.check_tables_bf16(got, want, bound)
                 else:
                     par.check_tables(got, want, bound)
+                # the same assignment's error under the tables just written
+                w2_o = float(np.sum(Is64[i][None, :] * W64s[i] ** 2))
+                e_after = par.total_error_rows(W64s[i], Is64[i], q, s, got, g, S)
+                e_r1 = float(rerr[1, i].item())
+                assert abs(e_r1 - e_after) <= 1e-6 * e_after + 1e-13 * w2_o, (
+                    mats[i].name, it, e_r1, e_after)
             _say("iter", it, "checked")
 
     # final assign against the bf16 tables, then pack and dequant
     L.aaac_assign_batch(Ws, g, S, n, Is, tabs, codes, sels, hist[iters], ws_a)
     torch.cuda.synchronize()
     _check_assign_rows(W64s, Is64, tabs, g, S, codes, sels, rows)
-    h = P.check_history(hist, w2=w2)
+    h = P.check_history(hist, w2=w2, half_steps=False)
     _say("error history (first matrix)", h[:, 0].tolist())
     for i, W in enumerate(Ws):
         R, C = Rs[i], Cs[i]

@@ -63,8 +63,8 @@ def _run_both(shapes, g, S, n, iters, seed):
     wsf = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), DEV)
     ws2 = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, Rs, Cs, g, S, n), DEV)
     k = len(shapes)
-    ef, wf = (torch.zeros(k, dtype=torch.float64, device=DEV) for _ in range(2))
-    e2, w2 = (torch.zeros(k, dtype=torch.float64, device=DEV) for _ in range(2))
+    ef, e2 = (torch.zeros(2, k, dtype=torch.float64, device=DEV) for _ in range(2))
+    wf, w2 = (torch.zeros(k, dtype=torch.float64, device=DEV) for _ in range(2))
     for it in range(iters):
         # the error outputs every iteration: I w^2 summed on the first, read back after that
         flags = (L.REFINE_ROUND_BF16 if it == iters - 1 else 0) | (L.REFINE_W2_KNOWN if it else 0)

@@ -476,18 +476,21 @@ def test_refine_and_loop_extreme_group_scales(kind):
         par.check_assign(W64, I64, T_in, g, S, cq, _np(sel), _np(err))
         _check_err_total(W, I, tables, g, S, n, codes, sel)
         flags = L.REFINE_ROUND_BF16 if it == iters - 1 else 0
-        rerr = torch.zeros(1, dtype=torch.float64, device=DEV)
+        rerr = torch.zeros(2, dtype=torch.float64, device=DEV)
         w2 = torch.zeros(1, dtype=torch.float64, device=DEV)
         L.aaac_refine(W, g, S, n, I, codes, sel, tables, tables, flags, err=rerr, w2=w2)
         torch.cuda.synchronize()
         got = _np(tables).astype(np.float64).reshape(2, n)
         assert np.all(np.isfinite(got)), got
-        # the refine's error report: W2 exact to rounding, E within its stated 1e-15 W2 accuracy
-        e_r, w2_r = float(rerr.item()), float(w2.item())
+        # the refine's error reports (before and after its update): W2 exact to rounding, E within
+        # its stated 1e-15 W2 accuracy
+        e_r, e_after, w2_r = float(rerr[0].item()), float(rerr[1].item()), float(w2.item())
         w2_o = float(np.sum(I64[None, :] * W64 ** 2))
         e_o = ref.total_error(W64, I64, cq, sq, T_in[0], T_in[1], g, S)
+        e_o_after = ref.total_error(W64, I64, cq, sq, got[0], got[1], g, S)
         assert abs(w2_r - w2_o) <= 1e-12 * w2_o
         assert abs(e_r - e_o) <= 1e-6 * e_o + 1e-13 * w2_o, (e_r, e_o, w2_o)
+        assert abs(e_after - e_o_after) <= 1e-6 * e_o_after + 1e-13 * w2_o, (e_after, e_o_after)
         want, _, _, bound = par.oracle_refine(W64, I64, cq, sq, T_in, g, S)
         if flags:
             par.check_tables_bf16(got, want, bound)
@@ -786,26 +789,35 @@ def test_loop_single_layer_against_oracle_free_run():
         if it == cfg.iters:
             break                                   # the final assign, against bf16 tables
         flags = L.REFINE_ROUND_BF16 if it == cfg.iters - 1 else 0
-        rerr = torch.zeros(1, dtype=torch.float64, device=DEV)
+        rerr = torch.zeros(2, dtype=torch.float64, device=DEV)
         if it == 0:
             w2 = torch.zeros(1, dtype=torch.float64, device=DEV)
         L.aaac_refine(W, g, S, n, I, codes, sel, tables, tables,
                       flags | (L.REFINE_W2_KNOWN if it else 0), err=rerr, w2=w2)
         torch.cuda.synchronize()
-        # the refine reports the same error of the assignment it consumed, and sum I w^2 (summed
-        # by the first refine, read by the later ones)
-        e_r, w2_r = float(rerr.item()), float(w2.item())
+        # the refine reports the same error of the assignment it consumed, the error of that
+        # assignment under the tables it wrote, and sum I w^2 (summed by the first refine, read by
+        # the later ones)
+        e_r, e_after, w2_r = float(rerr[0].item()), float(rerr[1].item()), float(w2.item())
         w2_o = float(np.sum(I64[None, :] * W64 ** 2))
         assert abs(w2_r - w2_o) <= 1e-12 * w2_o
         assert abs(e_r - e_true) <= 1e-6 * e_true, (it, e_r, e_true)
         want, _, _, bound = par.oracle_refine(W64, I64, cq, sq, T_in, g, S)
         got = _np(tables).astype(np.float64).reshape(2, n)
+        e_true_after = ref.total_error(W64, I64, cq, sq, got[0], got[1], g, S)
+        assert abs(e_after - e_true_after) <= 1e-6 * e_true_after, (it, e_after, e_true_after)
+        # the refine half-step never raises the error (before the bf16 rounding of the last one)
+        if not flags:
+            assert e_true_after <= e_true * (1 + 1e-12), (it, e_true_after, e_true)
+        hist.append(e_true_after)
         if flags:
             par.check_tables_bf16(got, want, bound)
         else:
             par.check_tables(got, want, bound)
-    h = np.asarray(hist[:-1])
-    assert np.all(np.diff(h) <= 1e-6 * h[:-1]), h
+    # every half-step, except across the last refine (bf16 entries), keeps the error from rising
+    h = np.asarray(hist)
+    steps = [r for r in range(len(h) - 1) if r != len(h) - 3]
+    assert all(h[r + 1] <= h[r] * (1 + 1e-6) for r in steps), h
 
 
 def test_assign_single_table_round_to_nearest():

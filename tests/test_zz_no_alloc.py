@@ -57,16 +57,17 @@ def test_refine_noalloc_equals_refine_with_workspace(g, S, n):
         t_ref = [t.clone() for t in tabs]
         t_new = [t.clone() for t in tabs]
         m = len(shapes)
-        e_ref = torch.zeros(m, dtype=torch.float64, device=DEV)
-        e_new = torch.full((m,), -1.0, dtype=torch.float64, device=DEV)
+        e_ref = torch.zeros(2, m, dtype=torch.float64, device=DEV)
+        e_new = torch.full((2, m), -1.0, dtype=torch.float64, device=DEV)
         w_ref = torch.zeros(m, dtype=torch.float64, device=DEV)
         w_new = torch.full((m,), -1.0, dtype=torch.float64, device=DEV)
         if flags & L.REFINE_W2_KNOWN:
             # the W2 these matrices have, from a first refine of each path
             L.aaac_refine_batch(Ws, g, S, n, Is, codes, sels, [t.clone() for t in tabs], 0,
-                                None, torch.zeros(m, dtype=torch.float64, device=DEV), w_ref)
+                                None, torch.zeros(2, m, dtype=torch.float64, device=DEV), w_ref)
             L.aaac_refine_batch_noalloc(Ws, g, S, n, Is, codes, sels, [t.clone() for t in tabs],
-                                        0, torch.zeros(m, dtype=torch.float64, device=DEV), w_new)
+                                        0, torch.zeros(2, m, dtype=torch.float64, device=DEV),
+                                        w_new)
             torch.cuda.synchronize()
             assert torch.equal(w_ref, w_new)
         ws = L.workspace(L.batch_workspace_bytes(L.OP_REFINE, [R for R, _ in shapes],
