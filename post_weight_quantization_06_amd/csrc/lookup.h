@@ -313,7 +313,8 @@ __device__ __forceinline__ void row16_scale(const uint4& va, const uint4& vb, in
   sc.amax = sbits >> 16;
   sc.s = __uint_as_float(sbits);
   sc.zero = (sc.s == 0.0f);
-  sc.fast_scale = sc.zero || (sc.s >= kFastScaleMin && sc.s <= kFastScaleMax);
+  // bitwise, not short-circuit: a branch here would split the row's schedule in two
+  sc.fast_scale = sc.zero | ((sc.s >= kFastScaleMin) & (sc.s <= kFastScaleMax));
   const float se = sc.zero ? 1.0f : sc.s;
   sc.Y = lut_y(se);
   sc.nse = -se;
