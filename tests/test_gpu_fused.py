@@ -126,11 +126,50 @@ def test_fused_step_parity_with_oracle():
 
 
 @pytest.mark.timeout(300)
-def test_fused_full_size_llama8b_layer():
-    cfg = syn.config(2)
+@pytest.mark.parametrize("cfg_id", [2, 3, 4, 5])
+def test_fused_full_size_layers(cfg_id):
+    """Whole layers of the 8B-shaped (INT4 and NVFP4-style), 13B-shaped (S = 16 bitmap) and
+    32B-shaped workloads over all their iterations, bitwise against the two launches."""
+    cfg = syn.config(cfg_id)
     shapes = [(m.rows, m.cols) for m in cfg.matrices]
     _say("fused full size", cfg.name)
-    _run_both(shapes, cfg.g, cfg.S, cfg.n, iters=cfg.iters, seed=2)
+    _run_both(shapes, cfg.g, cfg.S, cfg.n, iters=cfg.iters, seed=cfg_id)
+
+
+@pytest.mark.parametrize("kind", ["edge", "up", "down"])
+def test_fused_extreme_group_scales(kind):
+    """Groups whose scales leave the fast range (zero, subnormal, 3e30 and 2^+-100 scales: the
+    exact scan) through the fused iteration, bitwise against the two launches."""
+    from tests import test_gpu_parity as gp
+
+    g, S, n = 128, 128, 16
+    W = gp._edge_matrix(kind, 64, 512)
+    _say("fused extreme scales", kind)
+    gen = torch.Generator(device=DEV).manual_seed(73)
+    I = torch.rand(512, device=DEV, generator=gen) * 4.0 + 0.05
+    if kind == "edge":
+        I[:32] = 0
+        I[100:104] = 1e20
+    tabs = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(W, g, n, tabs)
+    Ws, Is = [W], [I]
+    tf, t2 = [tabs.clone()], [tabs.clone()]
+    cf, sf = _buffers([(64, 512)], S)
+    c2, s2 = _buffers([(64, 512)], S)
+    wsb = L.batch_workspace_bytes(L.OP_REFINE, [64], [512], g, S, n)
+    wsf, ws2 = L.workspace(wsb, DEV), L.workspace(wsb, DEV)
+    ef, e2 = (torch.zeros(2, 1, dtype=torch.float64, device=DEV) for _ in range(2))
+    wf, w2 = (torch.zeros(1, dtype=torch.float64, device=DEV) for _ in range(2))
+    for it in range(3):
+        flags = (L.REFINE_ROUND_BF16 if it == 2 else 0) | (L.REFINE_W2_KNOWN if it else 0)
+        L.aaac_assign_refine_batch(Ws, g, S, n, Is, tf, cf, sf, flags, wsf, err=ef, w2=wf)
+        L.aaac_assign_batch(Ws, g, S, n, Is, t2, c2, s2)
+        L.aaac_refine_batch(Ws, g, S, n, Is, c2, s2, t2, flags, ws2, err=e2, w2=w2)
+        torch.cuda.synchronize()
+        assert torch.equal(cf[0], c2[0]) and torch.equal(sf[0], s2[0]), (kind, it)
+        assert torch.equal(tf[0], t2[0]), (kind, it, _np(tf[0]), _np(t2[0]))
+        assert bool(torch.isfinite(tf[0]).all())
+        assert torch.equal(ef, e2) and torch.equal(wf, w2)
 
 
 
