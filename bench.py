@@ -37,6 +37,9 @@ TRAFFIC_SUMMARY = {
     2: os.path.join(ROOT, "profiles", "hbm_traffic_assign_refine_llama8b_layer.json"),
     5: os.path.join(ROOT, "profiles", "hbm_traffic_assign_refine_32b_model.json"),
 }
+TRAFFIC_SUMMARY_FUSED = {
+    5: os.path.join(ROOT, "profiles", "hbm_traffic_assign_refine_32b_model_fused.json"),
+}
 
 
 def algorithmic_bytes(numel, S):
@@ -394,8 +397,9 @@ def main():
     print("[bench] error history, last layer, first matrix: %s" % ", ".join(
         "%.6g" % x for x in last), file=sys.stderr, flush=True)
     traffic = None
-    if args.config in TRAFFIC_SUMMARY and not args.fused:
-        t = pmc_traffic.load_traffic(TRAFFIC_SUMMARY[args.config], dom)
+    summaries = TRAFFIC_SUMMARY_FUSED if args.fused else TRAFFIC_SUMMARY
+    if args.config in summaries:
+        t = pmc_traffic.load_traffic(summaries[args.config], dom)
         traffic = None if t is None else int(round(t))
     inference = None
     if not args.no_inference:

@@ -24,14 +24,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 
 # kernels whose traffic is summarised: name prefixes of the dispatches (after "void "); assign is
-# the loop's instance without error output
+# the loop's instance without error output, fused the one-launch iteration
 KERNELS = {
     "assign": ("aaac::assign_wide_kernel<0,", "aaac::assign_kernel<0,"),
     "refine": ("aaac::refine_kernel<",),
+    "fused": ("aaac::assign_refine_kernel<",),
 }
 KERNEL_SOURCES = {
     "assign": ["assign.hip", "assign_body.h", "lookup.h", "common.h"],
     "refine": ["refine.hip", "lookup.h", "common.h"],
+    "fused": ["refine.hip", "lookup.h", "common.h"],
 }
 
 

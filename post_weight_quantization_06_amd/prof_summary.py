@@ -181,7 +181,8 @@ def traffic(raw, prof, tag, traffic_json, out_md):
     alg = N * 2 + N // 2 + N // 128
     with open(traffic_json) as f:
         d = json.load(f)
-    out = ["# HBM traffic per launch: assign and refine on %s\n" % desc,
+    out = ["# HBM traffic per launch: %s on %s\n" % (
+               " and ".join(k for k, _ in loop_families(tag)), desc),
            WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
            "Two counter passes over the same command, one counter each (from the repository root, "
            "on one MI355X):\n",
@@ -202,11 +203,13 @@ def traffic(raw, prof, tag, traffic_json, out_md):
         out.append("| %s | %d | %.0f | %.0f | %.1f MB | %.1f MB | %.1f MB | %.1f MB | %.3f |" % (
             k, v["dispatches"], v["fetch_kib"], v["write_kib"], v["read_bytes"] / 1e6,
             v["write_bytes"] / 1e6, v["bytes"] / 1e6, alg / 1e6, v["bytes"] / alg))
+    who = ("the fused launch reads W (%.1f MB) and writes codes (%.1f MB) and selectors "
+           "(%.1f MB), once per iteration" if WORKLOADS[tag][2] else
+           "assign reads W (%.1f MB) and writes codes (%.1f MB) and selectors (%.1f MB); refine "
+           "reads the same three") % (2 * N / 1e6, N / 2 / 1e6, N / 128 / 1e6)
     out += ["",
-            "Algorithmic bytes per launch (%s weights): assign reads W (%.1f MB) and writes codes "
-            "(%.1f MB) and selectors (%.1f MB); refine reads the same three. The importance "
-            "vectors and tables are not counted." % (format(N, ","), 2 * N / 1e6, N / 2 / 1e6,
-                                                    N / 128 / 1e6),
+            "Algorithmic bytes per launch (%s weights): %s. The importance vectors and tables are "
+            "not counted." % (format(N, ","), who),
             "",
             "The JSON beside this file holds the same figures with a hash of each kernel's "
             "sources; bench.py reports `roofline.traffic` only while the hash still matches."]
