@@ -94,6 +94,14 @@ def test_assign_rejects_bad_shapes_and_pointers_before_launch(lib):
     assert _assign(lib, 64, 1024, 128, 256, 16) == SHAPE
     assert _assign(lib, 64, 1000, 128, 128, 16) == SHAPE
     assert _assign(lib, 0, 1024, 128, 128, 16) == SHAPE
+    assert _assign(lib, -1, 1024, 128, 128, 16) == SHAPE               # negative R
+    assert _assign(lib, 64, 0, 8, 8, 16) == SHAPE                      # empty rows
+    assert _assign(lib, 64, 4, 8, 8, 16) == SHAPE                      # C < 8
+    assert _assign(lib, 64, 1 << 31, 128, 128, 16) == SHAPE            # C >= 2^31
+    assert _assign(lib, 64, 1024, 4, 4, 16) == SHAPE                   # g < 8
+    assert _assign(lib, 64, 2048, 1024, 128, 16) == SHAPE              # g > 512
+    assert _assign(lib, 64, 1024, 128, 4, 16) == SHAPE                 # S < 8
+    assert _assign(lib, 64, 1024, 128, 128, 1) == SHAPE                # n < 2
     assert _assign(lib, 64, 1024, 128, 128, 17) == SHAPE
     assert _assign(lib, 1 << 21, 1 << 19, 128, 128, 16) == SHAPE   # R*C >= 2^40
     assert b"n=17" in lib.aaac_last_error() or b"2^40" in lib.aaac_last_error()
