@@ -145,6 +145,22 @@ def cpu_baseline(pool, jobs, g, S, n, budget_s, workers):
                      "workers": workers}}
 
 
+def _env_info(torch, dev):
+    """The GPU, its architecture and the software versions the numbers were taken with."""
+    rocm = None
+    for path in ("/opt/rocm/.info/version", "/opt/rocm/.info/version-dev"):
+        try:
+            with open(path) as f:
+                rocm = f.read().strip()
+            break
+        except OSError:
+            pass
+    props = torch.cuda.get_device_properties(dev)
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "cus": props.multi_processor_count, "rocm": rocm, "hip": torch.version.hip,
+            "torch": torch.__version__}
+
+
 # ------------------------------------------------------------------------------------------------
 # Inference side (outside the metric)
 # ------------------------------------------------------------------------------------------------
@@ -446,6 +462,7 @@ def main():
                      "launches_timed": len(r_ms) if dom == "refine" else len(a_ms)},
         "cpu_baseline": cpu,
         "inference": inference,
+        "env": _env_info(torch, dev),
     }
     if args.fused:
         out["fused_us"] = round(a_avg * 1e3, 2)
