@@ -820,6 +820,80 @@ def test_loop_single_layer_against_oracle_free_run():
     assert all(h[r + 1] <= h[r] * (1 + 1e-6) for r in steps), h
 
 
+FREE_RUN = [  # (rows, g, S, n) on the 2048-column layer, 8 iterations
+    (2048, 128, 128, 16),   # the 2048x2048 layer as configured
+    (1024, 16, 16, 15),     # NVFP4-style groups, 15-entry tables
+    (1024, 128, 16, 16),    # selection groups of 16 under a scale group of 128
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rows,g,S,n", FREE_RUN)
+def test_free_run_against_the_oracle_loop(rows, g, S, n):
+    """The GPU loop and the oracle's own loop side by side, each from its own init: at every
+    half-step the two runs' tables, codes, selectors and total errors are compared and reported.
+    A table entry that parts from the oracle's by more than the table tolerance (a near-tie
+    selector flip moves a whole group) is reported as a divergence, and the oracle then goes on
+    from the GPU's tables."""
+    cfg = syn.config(1)
+    m = cfg.matrices[0]
+    W = syn.make_weight(m.rows, m.cols, syn.seed_for(1, 0, m.tensor_id), DEV)[:rows].contiguous()
+    _, _, I = _importance(m.cols, cfg.tokens, syn.seed_for(1, 0, m.x_id))
+    iters = cfg.iters
+    R, C = W.shape
+    _say("free run", R, C, g, S, n, iters)
+    W64, I64 = par.to_np64(W), par.to_np64(I)
+    tables = torch.empty(2 * n, dtype=torch.float32, device=DEV)
+    L.aaac_init_quantiles(W, g, n, tables)
+    To = np.stack(ref.init_tables(W64, g, n))
+    Tg = _np(tables).astype(np.float64).reshape(2, n)
+    # the two inits agree bit for bit (the GPU's tables are the fp32 values of the oracle's)
+    assert np.array_equal(Tg, To.astype(np.float32).astype(np.float64))
+    divergences = []
+    for it in range(iters + 1):
+        codes, sel, _ = _assign(W, I, tables, g, S, n, err=False)
+        cq = par.unpack_gpu_codes(codes, R, C)
+        sq = _np(sel).reshape(R, C // S)
+        a = par.oracle_assign_rows(W64, I64, To[0], To[1], g, S)
+        Tg = _np(tables).astype(np.float64).reshape(2, n)
+        Eg = ref.total_error(W64, I64, cq, sq, Tg[0], Tg[1], g, S)
+        Eo = ref.total_error(W64, I64, a["codes"], a["sel"], To[0], To[1], g, S)
+        code_mis = float(np.mean(cq != a["codes"]))
+        sel_mis = float(np.mean(sq != a["sel"]))
+        _say("iter %d assign: E gpu %.12g oracle %.12g (rel %.2e), codes differ %.2e, "
+             "selectors differ %.2e" % (it, Eg, Eo, abs(Eg - Eo) / Eo, code_mis, sel_mis))
+        # same tables up to the tolerance: the assignments agree but for near ties
+        assert code_mis <= 1e-4 and sel_mis <= 1e-3, (it, code_mis, sel_mis)
+        assert abs(Eg - Eo) <= 1e-5 * Eo, (it, Eg, Eo)
+        if it == iters:
+            break
+        last = it == iters - 1
+        L.aaac_refine(W, g, S, n, I, codes, sel, tables, tables,
+                      L.REFINE_ROUND_BF16 if last else 0)
+        torch.cuda.synchronize()
+        Tg = _np(tables).astype(np.float64).reshape(2, n)
+        To = np.stack(ref.refine(W64, I64, a["codes"], a["sel"], To[0], To[1], g, S))
+        floor = 1e-2 * np.max(np.abs(To), axis=1, keepdims=True)
+        rel = float(np.max(np.abs(Tg - To) / np.maximum(np.abs(To), floor)))
+        if last:
+            try:
+                par.check_tables_bf16(Tg, To)
+                parted = False
+            except AssertionError:
+                parted = True
+            To = ref.bf16_round(To)
+        else:
+            parted = rel > par.TABLE_RTOL
+        _say("iter %d refine: largest table difference %.2e%s"
+             % (it, rel, " (diverged: the oracle continues from the GPU's tables)" if parted
+                else ""))
+        if parted:
+            divergences.append((it, rel))
+        if parted or last:
+            To = Tg.copy()
+    _say("free run", R, C, g, S, n, "divergences:", divergences if divergences else "none")
+
+
 def test_assign_single_table_round_to_nearest():
     """T0 = T1 = {j/8}: codes = clamp(ceil(8u - 1/2), -8, 7) + 8 exactly (half-way points take
     the lower entry) and every group keeps T0."""
