@@ -12,6 +12,7 @@ fused launch, --config 5 --fused):
     rocprofv3 --pmc WRITE_SIZE ... -d RAW/pmc_write_TAG ...
     rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU ... -d RAW/pmc_sq_TAG ...
     rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_LDS ... -d RAW/pmc_sq2_TAG ...
+    rocprofv3 --pmc SQ_LDS_IDX_ACTIVE ... GRBM_GUI_ACTIVE -d RAW/pmc_lds_TAG ...
     python -m post_weight_quantization_06_amd.pmc_traffic FETCH.csv WRITE.csv TRAFFIC.json
 
 Usage (from the repository root):
@@ -48,6 +49,11 @@ SQ1 = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_LDS SQ_INSTS_SALU SQ_WAVE_CYCLES SQ_BUSY
        "SQ_WAIT_INST_ANY SQ_INSTS_VMEM_RD")
 SQ2 = ("SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT "
        "SQ_ACTIVE_INST_ANY")
+# how busy the CU's units are: the LDS (cycles it works on indexed operations, and cycles it stalls
+# on bank or address conflicts) and the VALU, against the dispatch's active GPU cycles
+SQ3 = ("SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_DATA_FIFO_FULL "
+       "SQ_ACTIVE_INST_VALU SQ_INSTS_LDS_ATOMIC GRBM_GUI_ACTIVE")
+CUS = 256
 WRITTEN_BY = ("Summary written by `python -m post_weight_quantization_06_amd.prof_summary {raw} "
               "{prof} {tag}` from the raw output of the commands below.\n")
 
@@ -231,12 +237,17 @@ def sq_counters(raw, prof, tag, out_md):
 
     a1 = agg(os.path.join(raw, "pmc_sq_" + tag, "run_counter_collection.csv"))
     a2 = agg(os.path.join(raw, "pmc_sq2_" + tag, "run_counter_collection.csv"))
+    p3 = os.path.join(raw, "pmc_lds_" + tag, "run_counter_collection.csv")
+    a3 = agg(p3) if os.path.exists(p3) else None
     keys = [k for k, _ in loop_families(tag)]
     out = ["# Instruction counters: %s on %s\n" % (" and ".join(keys), desc),
            WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
            "Commands (from the repository root, on one MI355X; one counter group per run):\n",
            "```", pmc_cmd(SQ1, "pmc_sq_" + tag, raw, cfg_id, tag),
-           pmc_cmd(SQ2, "pmc_sq2_" + tag, raw, cfg_id, tag), "```\n",
+           pmc_cmd(SQ2, "pmc_sq2_" + tag, raw, cfg_id, tag)]
+    if a3 is not None:
+        out.append(pmc_cmd(SQ3, "pmc_lds_" + tag, raw, cfg_id, tag))
+    out += ["```\n",
            "Averages per dispatch (one batched launch over the %d matrices of a layer, %s "
            "weights; assign: the loop's instance without error output). SQ_INSTS_* count "
            "wave-level instructions (64 lanes), so per-weight figures are count x 64 / weights. "
@@ -244,7 +255,7 @@ def sq_counters(raw, prof, tag, out_md):
                len(shapes), format(N, ",")),
            "| kernel | counter | per dispatch | per weight (x64 / N) |", "|---|---|---|---|"]
     for key in keys:
-        for src in (a1, a2):
+        for src in (a1, a2) + ((a3,) if a3 is not None else ()):
             for c, v in src[key].items():
                 mean = sum(v) / len(v)
                 pw = "%.2f" % (mean * 64 / N) if c.startswith("SQ_INSTS") else ""
@@ -262,6 +273,14 @@ def sq_counters(raw, prof, tag, out_md):
             return float("nan")
         return 100.0 * (sum(v) / len(v)) / (sum(w) / len(w))
 
+    def busy(key, c):
+        # percent of the dispatch's active cycles, per CU (the profiler's LdsUtil, VALUBusy and
+        # LDSBankConflict: counter / (GRBM_GUI_ACTIVE x CUs))
+        v, g = a3[key].get(c), a3[key].get("GRBM_GUI_ACTIVE")
+        if not v or not g:
+            return float("nan")
+        return 100.0 * (sum(v) / len(v)) / ((sum(g) / len(g)) * CUS)
+
     out += ["", "Reading (VALU issue is 64 lane-instructions per clock per CU; 256 CUs at "
                 "2.4 GHz):", ""]
     if "assign" in keys:
@@ -278,6 +297,13 @@ def sq_counters(raw, prof, tag, out_md):
                        per_weight(a1, "refine", "SQ_INSTS_LDS"),
                        share(a2, "refine", "SQ_ACTIVE_INST_VALU"),
                        share(a2, "refine", "SQ_ACTIVE_INST_LDS"), share(a2, "refine", "SQ_WAIT_ANY")))
+    if a3 is not None:
+        for key in keys:
+            out.append("- %s, per CU over the dispatch's active cycles: LDS busy with indexed "
+                       "operations %.0f %% (of which stalled on bank conflicts %.0f %%, on address "
+                       "conflicts %.0f %%), VALU issuing %.0f %%." % (
+                           key, busy(key, "SQ_LDS_IDX_ACTIVE"), busy(key, "SQ_LDS_BANK_CONFLICT"),
+                           busy(key, "SQ_LDS_ADDR_CONFLICT"), busy(key, "SQ_ACTIVE_INST_VALU")))
     if "fused" in keys:
         valu = per_weight(a1, "fused", "SQ_INSTS_VALU")
         out.append("- fused: %.1f VALU and %.2f LDS instructions (two lookups and two fp64 adds) "

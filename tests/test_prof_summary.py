@@ -75,6 +75,29 @@ def test_summaries_from_fake_runs(tmp_path):
     assert "VALU busy 44 %, LDS issue 30 %, waiting 14 %" in sq
 
 
+def test_unit_busy_lines_from_the_lds_pass(tmp_path):
+    raw, prof = _fake_raw(tmp_path)
+    pmc_hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    cycles = 700000.0                    # the dispatch's active GPU cycles
+    lds = []
+    for name, idx, valu in (("aaac::assign_wide_kernel<0, 8, 8>", 0.25, 0.86),
+                            ("void aaac::refine_kernel<true, 8, false>", 0.93, 0.40)):
+        lds += [[name, "SQ_LDS_IDX_ACTIVE", idx * cycles * 256],
+                [name, "SQ_LDS_BANK_CONFLICT", 0.10 * cycles * 256],
+                [name, "SQ_LDS_ADDR_CONFLICT", 0.0],
+                [name, "SQ_ACTIVE_INST_VALU", valu * cycles * 256],
+                [name, "GRBM_GUI_ACTIVE", cycles]]
+    _write_csv(str(raw / ("pmc_lds_" + TAG) / "run_counter_collection.csv"), pmc_hdr, lds)
+    assert ps.main(["prof_summary", str(raw), str(prof), TAG]) == 0
+    sq = (prof / ("sq_counters_assign_refine_%s.md" % TAG)).read_text()
+    assert "GRBM_GUI_ACTIVE -d %s/pmc_lds_%s" % (raw, TAG) in sq.replace("--output-format csv ", "")
+    assert ("- assign, per CU over the dispatch's active cycles: LDS busy with indexed operations "
+            "25 % (of which stalled on bank conflicts 10 %, on address conflicts 0 %), VALU "
+            "issuing 86 %.") in sq
+    assert "- refine, per CU over the dispatch's active cycles: LDS busy with indexed " \
+           "operations 93 %" in sq
+
+
 def test_workloads_match_the_registry():
     cfg_id, _, shapes, layers, x_bytes = ps.workload("32b_model")
     assert cfg_id == 5 and layers == 64 and len(shapes) == 7
