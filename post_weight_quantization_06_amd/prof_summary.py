@@ -54,6 +54,7 @@ SQ2 = ("SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_L
 SQ3 = ("SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_DATA_FIFO_FULL "
        "SQ_ACTIVE_INST_VALU SQ_INSTS_LDS_ATOMIC GRBM_GUI_ACTIVE")
 CUS = 256
+XCDS = 8      # GRBM_GUI_ACTIVE comes back summed over the 8 XCDs, each counting the dispatch's cycles
 WRITTEN_BY = ("Summary written by `python -m post_weight_quantization_06_amd.prof_summary {raw} "
               "{prof} {tag}` from the raw output of the commands below.\n")
 
@@ -273,13 +274,28 @@ def sq_counters(raw, prof, tag, out_md):
             return float("nan")
         return 100.0 * (sum(v) / len(v)) / (sum(w) / len(w))
 
+    def cycles(key):
+        # the dispatch's active cycles (one XCD's GRBM_GUI_ACTIVE)
+        g = a3[key].get("GRBM_GUI_ACTIVE")
+        return (sum(g) / len(g)) / XCDS if g else float("nan")
+
     def busy(key, c):
         # percent of the dispatch's active cycles, per CU (the profiler's LdsUtil, VALUBusy and
-        # LDSBankConflict: counter / (GRBM_GUI_ACTIVE x CUs))
-        v, g = a3[key].get(c), a3[key].get("GRBM_GUI_ACTIVE")
-        if not v or not g:
+        # LDSBankConflict: counter / (active cycles x CUs))
+        v = a3[key].get(c)
+        if not v:
             return float("nan")
-        return 100.0 * (sum(v) / len(v)) / ((sum(g) / len(g)) * CUS)
+        return 100.0 * (sum(v) / len(v)) / (cycles(key) * CUS)
+
+    # the clock the kernels ran at: active cycles over the kernel trace's average duration
+    trace = os.path.join(raw, "prof_%s" % tag, "run_kernel_stats.csv")
+    clock = {}
+    if a3 is not None and os.path.exists(trace):
+        rows = _rows(trace)
+        for key, frag in loop_families(tag):
+            ns, calls = loop_kernel_average(rows, frag)
+            if calls:
+                clock[key] = cycles(key) / (ns * 1e-9)
 
     out += ["", "Reading (VALU issue is 64 lane-instructions per clock per CU; 256 CUs at "
                 "2.4 GHz):", ""]
@@ -299,11 +315,18 @@ def sq_counters(raw, prof, tag, out_md):
                        share(a2, "refine", "SQ_ACTIVE_INST_LDS"), share(a2, "refine", "SQ_WAIT_ANY")))
     if a3 is not None:
         for key in keys:
-            out.append("- %s, per CU over the dispatch's active cycles: LDS busy with indexed "
-                       "operations %.0f %% (of which stalled on bank conflicts %.0f %%, on address "
-                       "conflicts %.0f %%), VALU issuing %.0f %%." % (
-                           key, busy(key, "SQ_LDS_IDX_ACTIVE"), busy(key, "SQ_LDS_BANK_CONFLICT"),
+            ghz = clock.get(key)
+            out.append("- %s, per CU over the dispatch's active cycles (GRBM_GUI_ACTIVE / %d XCDs"
+                       "%s): LDS busy with indexed operations %.0f %% (of which stalled on bank "
+                       "conflicts %.0f %%, on address conflicts %.0f %%), VALU issuing %.0f %%." % (
+                           key, XCDS,
+                           "; %.2f GHz over the trace's average duration" % (ghz / 1e9)
+                           if ghz else "",
+                           busy(key, "SQ_LDS_IDX_ACTIVE"), busy(key, "SQ_LDS_BANK_CONFLICT"),
                            busy(key, "SQ_LDS_ADDR_CONFLICT"), busy(key, "SQ_ACTIVE_INST_VALU")))
+            if ghz:
+                out[-1] += (" At that clock the VALU instructions alone need %.0f us at full issue."
+                            % (N * per_weight(a1, key, "SQ_INSTS_VALU") / 64 / CUS / ghz * 1e6))
     if "fused" in keys:
         valu = per_weight(a1, "fused", "SQ_INSTS_VALU")
         out.append("- fused: %.1f VALU and %.2f LDS instructions (two lookups and two fp64 adds) "

@@ -86,16 +86,17 @@ def test_unit_busy_lines_from_the_lds_pass(tmp_path):
                 [name, "SQ_LDS_BANK_CONFLICT", 0.10 * cycles * 256],
                 [name, "SQ_LDS_ADDR_CONFLICT", 0.0],
                 [name, "SQ_ACTIVE_INST_VALU", valu * cycles * 256],
-                [name, "GRBM_GUI_ACTIVE", cycles]]
+                [name, "GRBM_GUI_ACTIVE", cycles * ps.XCDS]]
     _write_csv(str(raw / ("pmc_lds_" + TAG) / "run_counter_collection.csv"), pmc_hdr, lds)
     assert ps.main(["prof_summary", str(raw), str(prof), TAG]) == 0
     sq = (prof / ("sq_counters_assign_refine_%s.md" % TAG)).read_text()
     assert "GRBM_GUI_ACTIVE -d %s/pmc_lds_%s" % (raw, TAG) in sq.replace("--output-format csv ", "")
-    assert ("- assign, per CU over the dispatch's active cycles: LDS busy with indexed operations "
-            "25 % (of which stalled on bank conflicts 10 %, on address conflicts 0 %), VALU "
-            "issuing 86 %.") in sq
-    assert "- refine, per CU over the dispatch's active cycles: LDS busy with indexed " \
-           "operations 93 %" in sq
+    # 700,000 cycles in the 150 us average of the fake trace: 4.67 GHz
+    assert ("- assign, per CU over the dispatch's active cycles (GRBM_GUI_ACTIVE / 8 XCDs; 4.67 "
+            "GHz over the trace's average duration): LDS busy with indexed operations 25 % (of "
+            "which stalled on bank conflicts 10 %, on address conflicts 0 %), VALU issuing "
+            "86 %.") in sq
+    assert "LDS busy with indexed operations 93 %" in sq
 
 
 def test_workloads_match_the_registry():
