@@ -13,6 +13,7 @@ fused launch, --config 5 --fused):
     rocprofv3 --pmc SQ_WAVES SQ_INSTS_VALU ... -d RAW/pmc_sq_TAG ...
     rocprofv3 --pmc SQ_WAIT_ANY SQ_WAIT_INST_LDS ... -d RAW/pmc_sq2_TAG ...
     rocprofv3 --pmc SQ_LDS_IDX_ACTIVE ... GRBM_GUI_ACTIVE -d RAW/pmc_lds_TAG ...
+    rocprofv3 --pmc SQ_WAVE_CYCLES ... GRBM_GUI_ACTIVE -d RAW/pmc_gemv_TAG ...  (with the GEMV)
     python -m post_weight_quantization_06_amd.pmc_traffic FETCH.csv WRITE.csv TRAFFIC.json
 
 Usage (from the repository root):
@@ -53,6 +54,10 @@ SQ2 = ("SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_L
 # on bank or address conflicts) and the VALU, against the dispatch's active GPU cycles
 SQ3 = ("SQ_LDS_IDX_ACTIVE SQ_LDS_BANK_CONFLICT SQ_LDS_ADDR_CONFLICT SQ_LDS_DATA_FIFO_FULL "
        "SQ_ACTIVE_INST_VALU SQ_INSTS_LDS_ATOMIC GRBM_GUI_ACTIVE")
+# the decode GEMV that bench.py runs after its steps: instruction counts and unit business
+SQG = ("SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_INSTS_LDS SQ_WAIT_INST_LDS SQ_LDS_IDX_ACTIVE "
+       "SQ_LDS_BANK_CONFLICT SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE")
+GEMV = "gemv_kernel<"
 CUS = 256
 XCDS = 8      # GRBM_GUI_ACTIVE comes back summed over the 8 XCDs, each counting the dispatch's cycles
 WRITTEN_BY = ("Summary written by `python -m post_weight_quantization_06_amd.prof_summary {raw} "
@@ -341,6 +346,44 @@ def sq_counters(raw, prof, tag, out_md):
         f.write("\n".join(out) + "\n")
 
 
+def gemv_counters(raw, prof, tag, out_md):
+    """Counters of the decode GEMV launches (one batched launch over the matrices of a layer)."""
+    cfg_id, desc, shapes, _, _ = workload(tag)
+    N = sum(R * C for R, C in shapes)
+    acc = collections.defaultdict(list)
+    for r in _rows(os.path.join(raw, "pmc_gemv_" + tag, "run_counter_collection.csv")):
+        if GEMV in r["Kernel_Name"]:
+            acc[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    mean = {c: sum(v) / len(v) for c, v in acc.items()}
+    cmd = ("rocprofv3 --pmc %s --output-format csv -d %s/pmc_gemv_%s -o run -- python -u bench.py "
+           "--config %d --steps 1 --warmup 1 --no-cpu --one-stream" % (SQG, raw, tag, cfg_id))
+    out = ["# Decode GEMV counters: %s\n" % desc,
+           WRITTEN_BY.format(raw=raw, prof=prof, tag=tag),
+           "Command (from the repository root, on one MI355X):\n", "```", cmd, "```\n",
+           "Averages over the %d GEMV launches that bench.py times after its steps (batch 1, the %d "
+           "packed matrices of one layer in one launch, %s weights). SQ_INSTS_* count wave-level "
+           "instructions, so per-code-byte figures are count x 64 / (weights / 2).\n"
+           % (len(acc.get("SQ_INSTS_VALU", [])), len(shapes), format(N, ",")),
+           "| counter | per launch | per code byte |", "|---|---|---|"]
+    for c, v in mean.items():
+        pb = "%.2f" % (v * 64 / (N / 2)) if c.startswith("SQ_INSTS") else ""
+        out.append("| %s | %.4g | %s |" % (c, v, pb))
+    cyc = mean.get("GRBM_GUI_ACTIVE", float("nan")) / XCDS
+
+    def pct(c):
+        return 100.0 * mean.get(c, float("nan")) / (cyc * CUS)
+
+    out += ["", "Reading: per CU over the launch's active cycles (GRBM_GUI_ACTIVE / %d XCDs), the "
+                "LDS is busy with indexed operations %.0f %% (stalled on bank conflicts %.0f %%) "
+                "and the VALU issues %.0f %%; waves wait on LDS results %.0f %% of their cycles."
+                % (XCDS, pct("SQ_LDS_IDX_ACTIVE"), pct("SQ_LDS_BANK_CONFLICT"),
+                   pct("SQ_ACTIVE_INST_VALU"),
+                   100.0 * mean.get("SQ_WAIT_INST_LDS", float("nan"))
+                   / mean.get("SQ_WAVE_CYCLES", float("nan")))]
+    with open(out_md, "w") as f:
+        f.write("\n".join(out) + "\n")
+
+
 def main(argv):
     if len(argv) not in (3, 4):
         print(__doc__)
@@ -353,6 +396,8 @@ def main(argv):
         traffic(raw, prof, tag, tj, os.path.join(prof, "hbm_traffic_assign_refine_%s.md" % tag))
     if os.path.exists(os.path.join(raw, "pmc_sq_" + tag, "run_counter_collection.csv")):
         sq_counters(raw, prof, tag, os.path.join(prof, "sq_counters_assign_refine_%s.md" % tag))
+    if os.path.exists(os.path.join(raw, "pmc_gemv_" + tag, "run_counter_collection.csv")):
+        gemv_counters(raw, prof, tag, os.path.join(prof, "sq_counters_gemv_%s.md" % tag))
     return 0
 
 

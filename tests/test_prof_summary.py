@@ -99,6 +99,26 @@ def test_unit_busy_lines_from_the_lds_pass(tmp_path):
     assert "LDS busy with indexed operations 93 %" in sq
 
 
+def test_gemv_counter_summary(tmp_path):
+    raw, prof = _fake_raw(tmp_path)
+    pmc_hdr = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    cycles = 180000.0
+    name = "void aaac::(anonymous namespace)::gemv_kernel<1, 1, 1, true>(aaac::GemvBatch)"
+    rows = [[name, "SQ_INSTS_VALU", N // 2 // 64 * 3.0], [name, "SQ_INSTS_LDS", N // 2 // 64],
+            [name, "SQ_LDS_IDX_ACTIVE", 0.66 * cycles * 256],
+            [name, "SQ_LDS_BANK_CONFLICT", 0.38 * cycles * 256],
+            [name, "SQ_ACTIVE_INST_VALU", 0.44 * cycles * 256],
+            [name, "SQ_WAIT_INST_LDS", 17.0], [name, "SQ_WAVE_CYCLES", 100.0],
+            [name, "GRBM_GUI_ACTIVE", cycles * ps.XCDS],
+            ["void aaac::refine_kernel<true, 8, false>(aaac::RefineBatch)", "SQ_INSTS_VALU", 1.0]]
+    _write_csv(str(raw / ("pmc_gemv_" + TAG) / "run_counter_collection.csv"), pmc_hdr, rows)
+    assert ps.main(["prof_summary", str(raw), str(prof), TAG]) == 0
+    g = (prof / ("sq_counters_gemv_%s.md" % TAG)).read_text()
+    assert "| SQ_INSTS_VALU | " in g and "| 3.00 |" in g and "| 1.00 |" in g
+    assert ("the LDS is busy with indexed operations 66 % (stalled on bank conflicts 38 %) and the "
+            "VALU issues 44 %; waves wait on LDS results 17 % of their cycles.") in g
+
+
 def test_workloads_match_the_registry():
     cfg_id, _, shapes, layers, x_bytes = ps.workload("32b_model")
     assert cfg_id == 5 and layers == 64 and len(shapes) == 7
