@@ -312,9 +312,8 @@ aaac_status aaac_refine_batch_noalloc(int count, const uint16_t* const* W, const
  * against tables[i], writing codes[i] and sel[i], then the batched refine from those codes,
  * updating tables[i] in place. flags, err and w2 are as for aaac_refine_batch: err[i] receives the
  * weighted error of the assignment this call makes under the tables it was made with, and
- * err[count + i] under the tables it writes. Codes,
- * selectors, tables and errors are bitwise those of aaac_assign_batch followed by
- * aaac_refine_batch with the same arguments. With S >= 16 one kernel does both: each wave assigns
+ * err[count + i] under the tables it writes. Codes, selectors, tables and errors are bitwise those
+ * of aaac_assign_batch followed by aaac_refine_batch with the same arguments. With S >= 16 one kernel does both: each wave assigns
  * a row and adds its terms into the refine bins at once, so W is read once. With S = 8 the call
  * makes the two launches. Workspace: as aaac_refine_batch.
  * Errors: as aaac_assign_batch and aaac_refine_batch.
