@@ -63,3 +63,16 @@ def test_stale_summaries_are_not_reported(tmp_path):
     out.write_text(json.dumps(res))
     assert pt.load_traffic(str(out), "assign") is None
     assert pt.load_traffic(str(tmp_path / "missing.json"), "refine") is None
+
+
+def test_committed_summaries_match_the_current_kernels():
+    """The committed HBM traffic summaries were taken on the kernel sources as they stand, so the
+    bench line's roofline.traffic is reported (a kernel edit needs a new counter run)."""
+    import os
+
+    prof = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "profiles")
+    for name, keys in (("hbm_traffic_assign_refine_32b_model.json", ("assign", "refine")),
+                       ("hbm_traffic_assign_refine_llama8b_layer.json", ("assign", "refine")),
+                       ("hbm_traffic_assign_refine_32b_model_fused.json", ("fused",))):
+        for key in keys:
+            assert pt.load_traffic(os.path.join(prof, name), key) is not None, (name, key)
